@@ -1,0 +1,174 @@
+/*
+ * ssa.h -- C ABI of the stratified sparse decode attention library (gfx950).
+ *
+ * One decode step of one attention layer, for every (sequence b, kv head h):
+ *   1. score every cached token cheaply from a fixed subset of RoPE frequency
+ *      pairs ("FASA: Frequency-aware Sparse Attention", section 3 stage 1
+ *      TIP; the group's queries are averaged as in PIVOT's proxy query);
+ *   2. read the top-k tokens deterministically ("Stratified Sparse Attention
+ *      speeds up decoding 2.96x at 1M context", section "Where sparse
+ *      attention loses quality");
+ *   3. Poisson-sample the remaining tail with probability proportional to
+ *      exp(approximate score) and 4. weight each sampled token by the inverse
+ *      of its inclusion probability (same page, section "How SSA stratifies
+ *      the cache"), then attend exactly over the union (FASA section 3 stage 2
+ *      FAC), merging split partials through the online-softmax state
+ *      (m, l, acc) ("S2O: Early Stopping for Sparse Attention via Online
+ *      Permutation", methodology part 3).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every array argument is a DEVICE pointer, owned by the caller, on
+ *           the device current at the call.  The library allocates nothing
+ *           and keeps no mutable global state.  q, k_cache and v_cache must
+ *           be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
+ *           Calls enqueue work and return; nothing is synchronised.
+ * Errors.   0 on success, a negative SSA_ERR_* code otherwise; no partial
+ *           work is enqueued when argument validation fails.  Host-visible
+ *           arguments (params, pointers, sizes) are validated; device-resident
+ *           values are not: seq_lens are clamped to [0, max_seq_len],
+ *           negative topk / sample_budget act as 0, and block_table entries
+ *           are clamped to [0, num_blocks) (a wrong entry reads a wrong block,
+ *           never out of bounds).
+ * Determinism. No floating-point atomics are used: identical inputs and
+ *           seeds give bitwise identical outputs, and calls are reentrant.
+ *
+ * Layouts (row-major, innermost last)
+ *   q            [B, Hq, d]                      bf16 (post-RoPE query at position L_b)
+ *   k_cache      [num_blocks, Hkv, 16, d]        bf16 (post-RoPE keys, interleaved pairs)
+ *   v_cache      [num_blocks, Hkv, 16, d]        bf16
+ *   block_table  [B, max_blocks_per_seq]         int32: token j of sequence b is row
+ *                                                j % 16 of block block_table[b][j / 16]
+ *   seq_lens, topk, sample_budget [B]            int32
+ *   seed         [B]                             uint64 (one Philox key per sequence)
+ *   out          [B, Hq, d]                      f32 or bf16 (params.out_dtype)
+ *
+ * Selection layout (ssa_select output, ssa_attend input).  A sequence's
+ * positions are cut into chunks of SSA_CHUNK_TOKENS; NC = ssa_num_chunks().
+ *   sel_idx   [B, Hkv, NC * SSA_CHUNK_TOKENS]  int32 token positions
+ *   sel_logw  [B, Hkv, NC * SSA_CHUNK_TOKENS]  f32   logit bias -log(pi_j): 0 on the
+ *                                                     deterministic set, >= 0 on samples
+ *   sel_count [B, Hkv, NC, 2]                  int32 (n_det, n_sampled) of each chunk
+ *   Segment c of a unit starts at c * SSA_CHUNK_TOKENS and holds the chunk's
+ *   deterministic tokens (ascending) followed by its sampled tokens
+ *   (ascending).  Chunks at or past L_b have count (0, 0).
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SSA_OK 0
+#define SSA_ERR_INVALID (-1)   /* bad params, null or misaligned pointer, bad size */
+#define SSA_ERR_WORKSPACE (-2) /* workspace smaller than ssa_workspace_bytes()     */
+#define SSA_ERR_HIP (-3)       /* a HIP call or kernel launch failed               */
+
+/* Output element types. */
+#define SSA_F32 0
+#define SSA_BF16 1
+
+#define SSA_BLOCK_TOKENS 16    /* tokens per KV-cache block (the only size supported) */
+#define SSA_CHUNK_TOKENS 4096  /* selection / split granularity                      */
+#define SSA_MAX_SEQ_LEN (1 << 26)
+
+/* Stage indices for ssa_decode_timed(). */
+#define SSA_STAGE_INIT 0     /* clear histograms and maxima                        */
+#define SSA_STAGE_INDEX 1    /* approximate scores + first-digit histogram + max   */
+#define SSA_STAGE_FILTER 2   /* threshold candidates, definite-tail weight sums    */
+#define SSA_STAGE_RESOLVE 3  /* exact top-k threshold, tie quota, tail normaliser  */
+#define SSA_STAGE_SAMPLE 4   /* deterministic set + Poisson sample, per chunk      */
+#define SSA_STAGE_ATTEND 5   /* gather attention over the selection, split-K       */
+#define SSA_STAGE_MERGE 6    /* merge of the split partials                        */
+#define SSA_NUM_STAGES 7
+
+typedef struct ssa_params {
+  int32_t batch;              /* B >= 1                                                  */
+  int32_t num_q_heads;        /* Hq, a multiple of Hkv, Hq / Hkv <= 16                   */
+  int32_t num_kv_heads;       /* Hkv >= 1                                                */
+  int32_t head_dim;           /* d: 64 or 128                                            */
+  int32_t block_size;         /* must be SSA_BLOCK_TOKENS                                */
+  int32_t max_blocks_per_seq; /* columns of block_table                                  */
+  int32_t num_blocks;         /* rows of k_cache / v_cache                               */
+  int32_t max_seq_len;        /* upper bound of seq_lens; <= max_blocks_per_seq * 16     */
+  int32_t pair_begin;         /* first scored RoPE pair (pairs are dims (2p, 2p+1));      */
+                              /*   a multiple of 4                                        */
+  int32_t pair_count;         /* 4, 8, 16, 32 or 64 pairs; pair_begin + pair_count <= d/2 */
+  int32_t num_splits;         /* split-K slices per unit; 0 = one per chunk              */
+  int32_t out_dtype;          /* SSA_F32 or SSA_BF16                                     */
+  float softmax_scale;        /* > 0; 0 selects 1 / sqrt(d)                              */
+} ssa_params;
+
+/* Bytes of device workspace that ssa_decode / ssa_score / ssa_select /
+ * ssa_attend need for these params (0 if params are invalid).  The workspace
+ * holds no state between calls. */
+size_t ssa_workspace_bytes(const ssa_params* p);
+
+/* ceil(max_seq_len / SSA_CHUNK_TOKENS) (0 if params are invalid). */
+int32_t ssa_num_chunks(const ssa_params* p);
+
+/* The whole decode step: scores, selection, sampling, attention, merge.
+ * topk[b] tokens are read deterministically and sample_budget[b] is the
+ * expected number of tail samples.  If topk[b] + sample_budget[b] >= L_b
+ * every token is read with weight 1 (dense attention).  Sampling for
+ * (b, h, token j) uses Philox4x32-10 keyed by seed[b] with counter
+ * (j >> 2, h, b, 0), word j & 3 (Salmon et al., SC'11). */
+int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
+               const int32_t* sample_budget, const uint64_t* seed, void* out, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* ssa_decode, recording hipEvent_t events[2*s] before and events[2*s+1] after
+ * the kernel(s) of stage s (SSA_STAGE_*); NULL entries are skipped, and a
+ * NULL array records nothing.  Same results as ssa_decode. */
+int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* const* events);
+
+/* Stage 1 alone: approximate scores, scores[(b*Hkv + h)*max_seq_len + j] (f32),
+ * for j < L_b; entries at or past L_b are left untouched.
+ *   s_j = (1/G) sum_g scale * sum_{p in pairs} (q_g[2p] k_j[2p] + q_g[2p+1] k_j[2p+1]). */
+int ssa_score(const ssa_params* p, const void* q, const void* k_cache,
+              const int32_t* block_table, const int32_t* seq_lens, float* scores,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages 2-4 alone, from a caller-provided score array laid out as ssa_score
+ * writes it.  If w_in is non-NULL, w_in[b*Hkv + h] replaces the computed tail
+ * normaliser W.  Writes the selection (layout above) and norm_out
+ * [B, Hkv, 2] = (M, W): the maximum score and the normaliser actually used. */
+int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
+               const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
+               const float* w_in, int32_t* sel_idx, float* sel_logw, int32_t* sel_count,
+               float* norm_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages 5-6 alone: attention over a caller-provided selection:
+ *   out_g = sum_A e^{l_gj + logw_j} v_j / sum_A e^{l_gj + logw_j},
+ *   l_gj = scale * q_g . k_j over the full head dimension. */
+int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
+               const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* Test hook: words[i] = the Philox word of (seed, b, h, token j0 + i), i < n. */
+int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t j0, int32_t n,
+                     uint32_t* words, void* stream);
+
+/* Test hook: y[i] = the library's specified float32 exp of x[i], i < n. */
+int ssa_debug_sexp(const float* x, float* y, int32_t n, void* stream);
+
+/* Static description of a status code. */
+const char* ssa_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

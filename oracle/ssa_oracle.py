@@ -1,0 +1,361 @@
+"""Plain CPU oracle for stratified sparse decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of the
+benchmark call it.  It shares no code with the HIP library and imports nothing
+from it.
+
+Sources (web pages; cited by title and section):
+
+* [SSA] "Stratified Sparse Attention speeds up decoding 2.96x at 1M context"
+  (news.hamidun.com).  Sections "Where sparse attention loses quality" (top-k /
+  top-p read deterministically, sampling covers the tail) and "How SSA
+  stratifies the cache" (the high-estimate tokens are read deterministically;
+  the rest of the cache is sampled with probability proportional to an
+  approximate attention estimate; each sampled token is corrected by its
+  inclusion probability so the mass outside the selected set is recovered;
+  top-k, top-p and top-k + sampling are special cases).
+* [FASA] "FASA: Frequency-aware Sparse Attention" (gist.science summary of
+  arXiv 2602.03152).  Section 2 (RoPE splits a head into 2-D frequency chunks;
+  low-frequency chunks carry contextual attention), section 3 stage 1 "TIP"
+  (online score = sum of the contributions of a fixed chunk subset; keep the
+  highest-scoring tokens) and stage 2 "FAC" (full-precision attention on the
+  selected tokens at their original positions).
+* [PIVOT] "PIVOT slashes sparse-attention indexer cost" (gyaansetu.com),
+  section "The two observations behind PIVOT": one proxy query, the mean of a
+  group of queries, is scored instead of each member.
+* [S2O] "S2O: Early Stopping for Sparse Attention via Online Permutation"
+  (gist.science summary of arXiv 2602.22575), methodology part 3 "Kernel
+  implementation": the online-softmax state (m, l, acc) is stored and resumed.
+
+Readings of points the pages leave open (each one is also listed in the design
+notes of the repository):
+
+R1  GQA aggregation: the score of a kv head is the mean over its query group of
+    the per-head partial logits (PIVOT's averaged proxy query).
+R2  Score scale: the partial dot product times the softmax scale (1/sqrt(d) by
+    default); "approximate attention estimate" is exp(score - max score).
+R3  Pairs: interleaved RoPE pairs (2p, 2p+1); the scored subset is a contiguous
+    pair range [pair_begin, pair_begin + pair_count), the same for every head.
+R4  Ranking is done on the float32 rounding of the score, ordered by the
+    float's bits (-0.0 below +0.0); ties go to the lower token index.
+R5  Dense rule: when topk + m >= L every token is read with weight 1.
+R6  Tail design: Poisson sampling.  w_j = sexp(s_j - M) with M the maximum
+    score over the whole sequence, W = sum of w_j over the tail, inclusion
+    probability pi_j = min(1, m * w_j / W); m is the expected sample size.
+R7  The inclusion decision is made in float32: include j iff
+    fl(u_j * W) < fl(m * w_j), with u_j a 24-bit uniform; pi_j (for the
+    weight) is min(1, fl(fl(m * w_j) / W)).
+R8  u_j comes from Philox4x32-10 (Salmon et al., SC'11) keyed by the 64-bit
+    seed (low word first) with counter (j >> 2, h, b, 0); word (j & 3) of the
+    output block, u_j = (word >> 8) * 2^-24.  This is element h * 2^34 + j of
+    subsequence b of the seed's stream in rocRAND's Philox4x32-10 layout.
+R9  sexp is a specified float32 exp (Cody-Waite reduction, degree-7 Taylor
+    polynomial, one rounding per operation, no fused multiply-add):
+    0 for x < -87.
+R10 Horvitz-Thompson weights: c_j = 1 on the deterministic set S and 1/pi_j on
+    the sample R; output = sum c e^l v / sum c e^l over S u R.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "BLOCK_TOKENS",
+    "gather_rows",
+    "approx_scores",
+    "order_key",
+    "topk_indices",
+    "sexp",
+    "philox4x32_10",
+    "philox_word",
+    "uniforms",
+    "tail_stratum",
+    "sample_tail",
+    "select_unit",
+    "ht_terms",
+    "attend_unit",
+    "decode",
+]
+
+# Inputs arrive as a paged cache of 16-token blocks (layout, not arithmetic).
+BLOCK_TOKENS = 16
+
+_F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Inputs: paged rows
+# ---------------------------------------------------------------------------
+
+def gather_rows(cache: np.ndarray, block_row: np.ndarray, h: int, L: int) -> np.ndarray:
+    """Rows 0..L-1 of kv head ``h`` of one sequence, as float64 [L, d].
+
+    ``cache`` is [num_blocks, Hkv, 16, d] (values exactly representable in
+    bf16, any float dtype); token j lives in block ``block_row[j // 16]`` at
+    offset ``j % 16``.  [S2O] methodology part 1 (index arrays drive the loads;
+    the physical layout is left in place).
+    """
+    j = np.arange(L)
+    return cache[block_row[j // BLOCK_TOKENS], h, j % BLOCK_TOKENS, :].astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: approximate scores ([FASA] stage 1 TIP; [PIVOT] proxy query)
+# ---------------------------------------------------------------------------
+
+def approx_scores(q_group: np.ndarray, K: np.ndarray, pair_begin: int, pair_count: int,
+                  scale: float) -> np.ndarray:
+    """Approximate score of every token for one (batch, kv head), float64 [L].
+
+    s_j = (1/G) * sum_g scale * sum_{p in I} (q_g[2p] k_j[2p] + q_g[2p+1] k_j[2p+1])
+    with I = [pair_begin, pair_begin + pair_count) (readings R1-R3).
+    ``q_group`` is [G, d], ``K`` is [L, d] (post-RoPE keys).
+    """
+    dims = np.arange(2 * pair_begin, 2 * (pair_begin + pair_count))
+    partial = scale * (q_group[:, dims].astype(np.float64) @ K[:, dims].T)  # [G, L]
+    return partial.mean(axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: deterministic stratum ([SSA] "Where sparse attention loses quality",
+# top-k; [FASA] TIP selection of the highest-scoring tokens)
+# ---------------------------------------------------------------------------
+
+def order_key(s32: np.ndarray) -> np.ndarray:
+    """Monotone map of float32 scores to uint32 (larger float -> larger key).
+
+    Negative floats have all bits flipped, non-negative ones get the sign bit
+    set, so -0.0 (0x7fffffff) ranks just below +0.0 (0x80000000) (reading R4).
+    """
+    bits = np.ascontiguousarray(s32, dtype=_F32).view(np.uint32)
+    neg = (bits >> np.uint32(31)) == 1
+    return np.where(neg, ~bits, bits | np.uint32(0x80000000)).astype(np.uint32)
+
+
+def topk_indices(s32: np.ndarray, k: int) -> np.ndarray:
+    """The k tokens first in the order (key descending, index ascending),
+    returned in ascending index order.  A full sort, no partial selection."""
+    key = order_key(s32)
+    idx = np.arange(key.size, dtype=np.int64)
+    order = np.lexsort((idx, ~key))  # primary: ~key ascending == key descending
+    return np.sort(order[:k])
+
+
+# ---------------------------------------------------------------------------
+# Step 3: tail weights -- the specified float32 exp (reading R9)
+# ---------------------------------------------------------------------------
+
+# Cody & Waite, "Software Manual for the Elementary Functions" (1980): reduce
+# x = n ln2 + r with ln2 split into a short head (so n * head is exact for
+# |n| < 2^9) and a float32 tail.  The head keeps 16 fractional bits of ln2.
+_LOG2E = _F32(1.0 / math.log(2.0))
+_LN2_HI = _F32(math.floor(math.log(2.0) * 2.0 ** 16) / 2.0 ** 16)
+_LN2_LO = _F32(math.log(2.0) - float(_LN2_HI))
+# Taylor coefficients 1/k!, k = 0..7, each rounded to float32.
+_TAYLOR = [_F32(1.0 / math.factorial(k)) for k in range(8)]
+_SEXP_MIN = _F32(-87.0)
+
+
+def sexp(x) -> np.ndarray:
+    """Specified float32 exp for x <= 0 (reading R9).
+
+    n = rint(fl(x * log2e)); r = fl(fl(x - fl(n * ln2_hi)) - fl(n * ln2_lo));
+    p = Horner over 1/k!, k = 7..0, one multiply then one add per step, each
+    rounded to float32; result = p * 2^n (exact); 0 when x < -87, which keeps
+    every non-zero result a normal float.
+    """
+    x = np.asarray(x, dtype=_F32)
+    low = x < _SEXP_MIN
+    x = np.where(low, _F32(0.0), x)  # keep the (discarded) lanes finite
+    t = np.multiply(x, _LOG2E, dtype=_F32)
+    n = np.rint(t).astype(_F32)
+    r = np.subtract(x, np.multiply(n, _LN2_HI, dtype=_F32), dtype=_F32)
+    r = np.subtract(r, np.multiply(n, _LN2_LO, dtype=_F32), dtype=_F32)
+    p = _TAYLOR[7]
+    for k in range(6, -1, -1):
+        p = np.multiply(p, r, dtype=_F32)
+        p = np.add(p, _TAYLOR[k], dtype=_F32)
+    y = np.ldexp(p, n.astype(np.int32)).astype(_F32)
+    return np.where(low, _F32(0.0), y).astype(_F32)
+
+
+# ---------------------------------------------------------------------------
+# Step 4: counter-based uniforms (reading R8)
+# ---------------------------------------------------------------------------
+
+_PHILOX_M0 = np.uint64(0xD2511F53)
+_PHILOX_M1 = np.uint64(0xCD9E8D57)
+_PHILOX_W0 = 0x9E3779B9
+_PHILOX_W1 = 0xBB67AE85
+_MASK32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+    numbers: as easy as 1, 2, 3", SC'11).  Vectorised over counters.
+
+    One round: (hi0, lo0) = M0 * c0 and (hi1, lo1) = M1 * c2 as 64-bit
+    products; the new counter is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0).
+    Between rounds the key is bumped by the Weyl constants (W0, W1).
+    Returns four uint32 arrays.
+    """
+    x = [np.asarray(c, dtype=np.uint64) & _MASK32 for c in (c0, c1, c2, c3)]
+    x = np.broadcast_arrays(*x)
+    x = [a.copy() for a in x]
+    ka, kb = k0 & 0xFFFFFFFF, k1 & 0xFFFFFFFF
+    for rnd in range(10):
+        p0 = _PHILOX_M0 * x[0]
+        p1 = _PHILOX_M1 * x[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _MASK32
+        x = [hi1 ^ x[1] ^ np.uint64(ka), lo1, hi0 ^ x[3] ^ np.uint64(kb), lo0]
+        ka = (ka + _PHILOX_W0) & 0xFFFFFFFF
+        kb = (kb + _PHILOX_W1) & 0xFFFFFFFF
+    return [a.astype(np.uint32) for a in x]
+
+
+def philox_word(seed: int, b: int, h: int, j) -> np.ndarray:
+    """The 32-bit random word of token(s) j of (batch b, kv head h)."""
+    j = np.asarray(j, dtype=np.int64)
+    words = philox4x32_10(j >> 2, np.full_like(j, h), np.full_like(j, b), np.zeros_like(j),
+                          seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    sel = (j & 3).astype(np.int64)
+    stacked = np.stack(words, axis=0)
+    return np.take_along_axis(stacked, sel[None, ...], axis=0)[0]
+
+
+def uniforms(seed: int, b: int, h: int, j) -> np.ndarray:
+    """u_j = (word >> 8) * 2^-24 as float32, in [0, 1)."""
+    w = philox_word(seed, b, h, j)
+    return ((w >> np.uint32(8)).astype(np.float64) * 2.0 ** -24).astype(_F32)
+
+
+# ---------------------------------------------------------------------------
+# Steps 2-4 together: the strata of one (batch, kv head)
+# ---------------------------------------------------------------------------
+
+def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None):
+    """Deterministic set S, tail T and inclusion probabilities of T.
+
+    Returns a dict with S, T (ascending int64), dense (bool), M, W (float32),
+    w (float32 tail weights), mw = fl(m * w) and pi = min(1, fl(mw / W)).
+    ``W_in`` replaces the computed normaliser (used to feed both
+    implementations the same normaliser).
+    """
+    s32 = np.asarray(s32, dtype=_F32)
+    L = s32.size
+    if L == 0:
+        e = np.zeros(0, np.int64)
+        return dict(S=e, T=e, dense=False, M=_F32(0), W=_F32(0), w=np.zeros(0, _F32),
+                    mw=np.zeros(0, _F32), pi=np.zeros(0, _F32))
+    M = _F32(s32[order_key(s32).argmax()])
+    if topk + m >= L:  # reading R5
+        e = np.zeros(0, np.int64)
+        return dict(S=np.arange(L, dtype=np.int64), T=e, dense=True, M=M, W=_F32(0),
+                    w=np.zeros(0, _F32), mw=np.zeros(0, _F32), pi=np.zeros(0, _F32))
+    k = min(topk, L)
+    S = topk_indices(s32, k)
+    in_s = np.zeros(L, bool)
+    in_s[S] = True
+    T = np.nonzero(~in_s)[0].astype(np.int64)
+    w = sexp(np.subtract(s32[T], M, dtype=_F32))
+    W = _F32(w.astype(np.float64).sum()) if W_in is None else _F32(W_in)
+    mw = np.multiply(_F32(m), w, dtype=_F32)
+    if W > 0:
+        pi = np.minimum(_F32(1.0), np.divide(mw, W, dtype=_F32)).astype(_F32)
+    else:
+        pi = np.zeros_like(w)
+    return dict(S=S, T=T, dense=False, M=M, W=W, w=w, mw=mw, pi=pi)
+
+
+def sample_tail(strata: dict, m: int, seed: int, b: int, h: int):
+    """Poisson sample of the tail (reading R7): returns (R, pi_R)."""
+    T, W = strata["T"], strata["W"]
+    if strata["dense"] or m == 0 or T.size == 0 or not (W > 0):
+        return np.zeros(0, np.int64), np.zeros(0, _F32)
+    u = uniforms(seed, b, h, T)
+    keep = np.multiply(u, W, dtype=_F32) < strata["mw"]
+    return T[keep], strata["pi"][keep]
+
+
+def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None):
+    """Full selection of one (batch, kv head): dict with S, R, pi_R, M, W, dense."""
+    st = tail_stratum(s32, topk, m, W_in)
+    R, pi_R = sample_tail(st, m, seed, b, h)
+    return dict(S=st["S"], R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"])
+
+
+# ---------------------------------------------------------------------------
+# Step 5: attention over S u R with Horvitz-Thompson weights
+# ([FASA] stage 2 FAC; [SSA] "How SSA stratifies the cache", correction by
+# inclusion probability)
+# ---------------------------------------------------------------------------
+
+def ht_terms(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, S, R, pi_R, scale: float,
+             shift):
+    """Unnormalised estimator terms with a caller-given per-head shift.
+
+    N_hat[g] = sum_{j in S} e^{l_gj - shift_g} v_j + sum_{j in R} e^{l_gj - shift_g} v_j / pi_j
+    D_hat[g] = the same sums without v_j, with l_gj = scale * q_g . k_j.
+    Returns (N_hat [G, d], D_hat [G]) in float64.
+    """
+    S = np.asarray(S, np.int64)
+    R = np.asarray(R, np.int64)
+    A = np.concatenate([S, R])
+    c = np.concatenate([np.ones(S.size), 1.0 / np.asarray(pi_R, np.float64)])
+    q = q_group.astype(np.float64)
+    logits = scale * (q @ K[A].T)  # [G, |A|]
+    e = c[None, :] * np.exp(logits - np.asarray(shift, np.float64)[:, None])
+    return e @ V[A], e.sum(axis=1)
+
+
+def attend_unit(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, S, R, pi_R,
+                scale: float) -> np.ndarray:
+    """Normalised HT attention output of one (batch, kv head), float64 [G, d]."""
+    G, d = q_group.shape
+    A = np.concatenate([np.asarray(S, np.int64), np.asarray(R, np.int64)])
+    if A.size == 0:
+        return np.zeros((G, d))
+    logits = scale * (q_group.astype(np.float64) @ K[A].T)
+    shift = logits.max(axis=1)
+    N, D = ht_terms(q_group, K, V, S, R, pi_R, scale, shift)
+    return N / D[:, None]
+
+
+# ---------------------------------------------------------------------------
+# The whole decode step
+# ---------------------------------------------------------------------------
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
+           pair_begin: int, pair_count: int, scale: float | None = None, units=None):
+    """Stratified sparse decode attention for every (batch, kv head).
+
+    q [B, Hq, d]; caches [num_blocks, Hkv, 16, d]; block_table [B, max_blocks];
+    seq_lens, topk, sample_budget, seed: [B] integers.  ``units`` optionally
+    restricts the work to a list of (b, h) pairs (other outputs stay zero).
+    Returns (out [B, Hq, d] float64, info dict keyed by (b, h)).
+    """
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, Hq, d))
+    info = {}
+    todo = units if units is not None else [(b, h) for b in range(B) for h in range(Hkv)]
+    for b, h in todo:
+        L = int(seq_lens[b])
+        qg = q[b, h * G:(h + 1) * G, :].astype(np.float64)
+        K = gather_rows(k_cache, block_table[b], h, L)
+        V = gather_rows(v_cache, block_table[b], h, L)
+        s64 = approx_scores(qg, K, pair_begin, pair_count, scale)
+        s32 = s64.astype(_F32)
+        sel = select_unit(s32, int(topk[b]), int(sample_budget[b]), int(seed[b]), b, h)
+        out[b, h * G:(h + 1) * G, :] = attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
+        info[(b, h)] = dict(scores=s64, **sel)
+    return out, info
