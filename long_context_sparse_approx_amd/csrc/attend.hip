@@ -1,0 +1,304 @@
+// Stages 5-6: exact attention over the selected tokens, split-K over chunks.
+//
+// "FASA: Frequency-aware Sparse Attention", section 3 stage 2 (FAC): full
+// precision attention on the selected tokens only, at their original
+// positions (the cache holds post-RoPE keys, so positions are kept).
+// "Stratified Sparse Attention speeds up decoding 2.96x at 1M context",
+// "How SSA stratifies the cache": sampled tokens carry the inverse inclusion
+// probability, applied here as the logit bias -log(pi_j) stored with the
+// selection.  "S2O: Early Stopping for Sparse Attention via Online
+// Permutation", methodology part 3: each split keeps the online-softmax
+// state (m, l, acc); the merge resumes from the stored states.
+//
+// One wavefront per (unit, split).  A tile is 32 selected tokens; both
+// products run on MFMA v_mfma_f32_16x16x32_bf16:
+//   QK:  D[16 tokens x 16 heads] = K_tile[16 x 32 dims] * Q^T[32 dims x 16 heads],
+//        two halves of 16 tokens, d/32 steps each; query heads beyond the
+//        group size are zero rows.
+//   PV:  D[16 heads x 16 cols] += P[16 heads x 32 tokens] * V[32 tokens x 16 cols],
+//        d/16 steps; P is split into bf16 hi + lo parts (two MFMAs) so the
+//        probabilities keep ~16 significant bits.
+// Layout choices that remove every LDS transpose:
+//   * QK's output D holds (token 4q+r, head n) in lane 16q+n; PV's A operand
+//     wants (head n, k-slot 8q+i) in lane 16q+n, so k-slot 8q+i is defined as
+//     token 4q+i (i < 4) or 16+4q+(i-4) (i >= 4): P never moves.
+//   * PV's output column n of step j is head dim n*(d/16)+j, so lane n's V
+//     operand for all steps is one contiguous d/16-element slice of each of
+//     its 8 token rows: a wave-wide load reads 4 full 256-byte rows.
+#include "ssa_device.h"
+#include "ssa_launch.h"
+
+namespace ssa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <int D>
+struct VSlice;
+template <>
+struct VSlice<128> {
+  using T = uint4;  // 8 dims
+  static __device__ __forceinline__ T zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  static __device__ __forceinline__ uint32_t word(const T& v, int w) {
+    return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+  }
+};
+template <>
+struct VSlice<64> {
+  using T = uint2;  // 4 dims
+  static __device__ __forceinline__ T zero() { return make_uint2(0u, 0u); }
+  static __device__ __forceinline__ uint32_t word(const T& v, int w) { return w == 0 ? v.x : v.y; }
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
+  constexpr int KK = D / 32;   // QK steps over the head dim
+  constexpr int DPL = D / 16;  // head dims per PV column = PV steps
+  using VS = VSlice<D>;
+
+  const int s = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const int h = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int ncL = (L + kChunk - 1) / kChunk;
+  const int c_begin = (int)((int64_t)s * ncL / a.nsplit);
+  const int c_end = (int)((int64_t)(s + 1) * ncL / a.nsplit);
+
+  // QK B operand (Q^T): lane holds head n16, dims kk*32 + q4*8 .. +8.
+  bf16x8 qf[KK];
+  {
+    const bool gv = n16 < a.G;
+    const uint16_t* qrow = a.q + (size_t)(b * a.Hq + h * a.G + (gv ? n16 : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (gv) v = *reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8);
+      qf[kk] = as_bf16x8(v);
+    }
+  }
+
+  float m_run = -INFINITY;  // state of head n16 (replicated over q4)
+  float l_run = 0.0f;
+  f32x4 acc[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  const size_t seg = (size_t)u * a.seg_ld;
+  for (int c = c_begin; c < c_end; ++c) {
+    const int32_t* cntp = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
+    // Counts and positions of a caller-provided selection are clamped to the
+    // segment and to [0, L) so that no value can address outside the buffers.
+    const int cnt = min(max(cntp[0], 0) + max(cntp[1], 0), kChunk);
+    const int32_t* idxp = a.sel_idx + seg + (size_t)c * kChunk;
+    const float* lwp = a.sel_logw + seg + (size_t)c * kChunk;
+    for (int t0 = 0; t0 < cnt; t0 += 32) {
+      // Lanes 0..31 resolve the tile's 32 items to cache rows.
+      int row = -1;
+      float lw = -INFINITY;
+      {
+        const int item = t0 + (lane & 31);
+        if (lane < 32 && item < cnt) {
+          const int idx = min(max(idxp[item], 0), L - 1);
+          lw = lwp[item];
+          int blk = btrow[idx >> 4];
+          blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+          row = (blk * a.Hkv + h) * kBlockTokens + (idx & 15);
+        }
+      }
+      // QK for the two 16-token halves: A = K rows (token n16 of the half).
+      f32x4 sc[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r = __shfl(row, 16 * hh + n16);
+        bf16x8 kf[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (r >= 0) v = *reinterpret_cast<const uint4*>(a.k_cache + (size_t)r * D + kk * 32 + q4 * 8);
+          kf[kk] = as_bf16x8(v);
+        }
+        f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], d, 0, 0, 0);
+        sc[hh] = d;
+      }
+      // V rows of this lane's 8 k-slots (issued before the softmax math).
+      typename VS::T vr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+        const int r = __shfl(row, tok);
+        vr[i] = VS::zero();
+        if (r >= 0)
+          vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)r * D + n16 * DPL);
+      }
+      // Logits of (head n16, slot tokens), online softmax update.
+      float x[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+        const float bias = __shfl(lw, tok);
+        x[i] = sc[i >> 2][i & 3] * a.scale + bias;
+        tmax = fmaxf(tmax, x[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __expf(m_run - m_new);
+      float psum = 0.0f;
+      uint32_t phi[4], plo[4];
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float p0 = __expf(x[i] - m_new);
+        const float p1 = __expf(x[i + 1] - m_new);
+        psum += p0 + p1;
+        const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+        const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
+        phi[i >> 1] = h0 | (h1 << 16);
+        plo[i >> 1] = l0 | (l1 << 16);
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // Rescale the accumulators: rows 4*q4 + r belong to head 4*q4 + r,
+      // whose alpha sits in lane 4*q4 + r.
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
+      }
+      const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+      const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) {
+        const int w = j >> 1;
+        uint32_t p[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w0 = VS::word(vr[2 * k], w), w1 = VS::word(vr[2 * k + 1], w);
+          p[k] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
+        }
+        const bf16x8 vb = as_bf16x8(make_uint4(p[0], p[1], p[2], p[3]));
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[j], 0, 0, 0);
+      }
+    }
+  }
+
+  // Write this split's state: acc rows are heads 4*q4 + r, column n16 holds
+  // dims n16*DPL .. +DPL.
+  const int stride = D + 2;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int g = 4 * q4 + r;
+    if (g < a.G) {
+      float* dst = a.part + ((size_t)(b * a.Hq + h * a.G + g) * a.nsplit + s) * stride + n16 * DPL;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
+    }
+  }
+  if (q4 == 0 && n16 < a.G) {
+    float* dst = a.part + ((size_t)(b * a.Hq + h * a.G + n16) * a.nsplit + s) * stride + D;
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+}
+
+// Merge of the split states of one (sequence, query head):
+//   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
+// in a fixed order (deterministic).
+constexpr int kMT = 256;
+
+__global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
+  __shared__ float red[kMT];
+  __shared__ float accsh[kMT];
+  const int bh = blockIdx.x;
+  const int D = a.d;
+  const int ns = a.nsplit;
+  const float* base = a.part + (size_t)bh * ns * (D + 2);
+  float mx = -INFINITY;
+  for (int s = threadIdx.x; s < ns; s += kMT) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
+  red[threadIdx.x] = mx;
+  __syncthreads();
+  for (int w = kMT / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  const float mstar = red[0];
+  __syncthreads();
+  float den = 0.0f;
+  for (int s = threadIdx.x; s < ns; s += kMT) {
+    const float* p = base + (size_t)s * (D + 2);
+    const float m = p[D];
+    if (m != -INFINITY) den += __expf(m - mstar) * p[D + 1];
+  }
+  red[threadIdx.x] = den;
+  __syncthreads();
+  for (int w = kMT / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float denom = red[0];
+  // threads split as (dim, split-phase): kMT / D phases over the splits
+  const int phases = kMT / D;
+  const int dim = threadIdx.x % D;
+  const int ph = threadIdx.x / D;
+  float o = 0.0f;
+  for (int s = ph; s < ns; s += phases) {
+    const float* p = base + (size_t)s * (D + 2);
+    const float m = p[D];
+    if (m != -INFINITY) o += __expf(m - mstar) * p[dim];
+  }
+  accsh[threadIdx.x] = o;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.0f;
+    for (int k = 0; k < phases; ++k) t += accsh[k * D + threadIdx.x];
+    const float res = (mstar == -INFINITY || denom <= 0.0f) ? 0.0f : t / denom;
+    if (a.out_dtype == SSA_BF16)
+      reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + threadIdx.x] = (uint16_t)f32_to_bf16_bits(res);
+    else
+      reinterpret_cast<float*>(a.out)[(size_t)bh * D + threadIdx.x] = res;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
+  dim3 grid(a.nsplit, a.B * a.Hkv);
+  if (a.d == 128)
+    attend_kernel<128><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 64)
+    attend_kernel<64><<<grid, 64, 0, stream>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
+  merge_kernel<<<a.B * a.Hq, kMT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

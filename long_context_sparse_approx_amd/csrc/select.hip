@@ -1,0 +1,399 @@
+// Stages 2-4: the deterministic stratum (exact top-k) and the Poisson tail
+// sample of every (batch, kv head).
+//
+// "Stratified Sparse Attention speeds up decoding 2.96x at 1M context",
+// sections "Where sparse attention loses quality" (top-k read
+// deterministically) and "How SSA stratifies the cache" (the rest of the
+// cache is sampled with probability proportional to an approximate attention
+// estimate and corrected by the inclusion probability).
+//
+//   top-k:  the k tokens with the largest float32 score order keys, ties to
+//           the lower index; found by a three-digit radix select (11/11/10
+//           bits) whose first digit histogram comes from stage 1;
+//   tail:   w_j = sexp(s_j - M), W = sum over the tail, computed directly in
+//           fp64 (never as total minus top-k, which cancels);
+//   sample: include j iff fl(u_j * W) < fl(m * w_j), u_j from Philox4x32-10
+//           keyed by the sequence's seed with counter (j >> 2, h, b, 0);
+//           pi_j = min(1, fl(m * w_j) / W); the logit bias is -log(pi_j).
+//
+// A sequence is processed in 4096-token chunks.  Each chunk's selected tokens
+// are written to its own segment in index order, so no grid-wide ordering is
+// needed and the attention stage splits work along chunk boundaries.  Every
+// sum has a fixed order and only integer atomics are used: results are
+// bitwise reproducible.
+#include "ssa_device.h"
+#include "ssa_launch.h"
+
+namespace ssa {
+
+namespace {
+
+constexpr int kNT = 256;             // threads per chunk workgroup
+constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
+
+struct UnitParams {
+  int L, k_eff, m;
+  bool dense;
+};
+
+__device__ __forceinline__ UnitParams unit_params(const SelectArgs& a, int b) {
+  UnitParams p;
+  p.L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int k = max(a.topk[b], 0);
+  p.m = max(a.sample_budget[b], 0);
+  p.dense = (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
+  p.k_eff = min(k, p.L);
+  return p;
+}
+
+// Coalesced copy of the chunk's scores into LDS (entries past L are unused).
+__device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, int L, float* sh) {
+  for (int i = threadIdx.x; i < kChunk; i += kNT) {
+    const int t = c0 + i;
+    sh[i] = t < L ? srow[t] : 0.0f;
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ filter
+// Per chunk: tokens whose first digit is above the threshold digit are in the
+// deterministic set; tokens on the threshold digit become candidates (written
+// in index order, second-digit histogram updated); tokens below it are tail
+// tokens, whose weights are summed here in fp64.
+__global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ float sh[kChunk];
+  __shared__ int scan_scr[kNT / 64];
+  __shared__ int pair[2];
+  __shared__ double dscr[kNT / 64];
+
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const UnitParams p = unit_params(a, b);
+  const int c0 = c * kChunk;
+  if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
+
+  int b1 = kBins;  // k = 0: every token is a tail token
+  if (p.k_eff > 0) {
+    for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = a.hist1[(size_t)u * kBins + i];
+    __syncthreads();
+    int rem;
+    find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
+  }
+  const float M = key_to_float(a.maxkey[u]);
+  stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
+
+  const int tb = threadIdx.x * kPer;
+  int above = 0;
+  uint32_t candmask = 0u;
+  double wsum = 0.0;
+  uint32_t keys[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = c0 + tb + i;
+    const float s = sh[tb + i];
+    const uint32_t key = order_key(s);
+    keys[i] = key;
+    const int bin = (int)(key >> kDigit1Shift);
+    if (t < p.L) {
+      if (bin > b1) {
+        ++above;
+      } else if (bin == b1) {
+        candmask |= 1u << i;
+      } else {
+        wsum += (double)sexp(s - M);
+      }
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
+  int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
+  uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+  int w = off;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (candmask & (1u << i)) {
+      cidx[w] = c0 + tb + i;
+      ckey[w] = keys[i];
+      ++w;
+      atomicAdd(&a.hist2[(size_t)u * kBins + ((keys[i] >> kDigit2Shift) & (kBins - 1))], 1u);
+    }
+  }
+  const int above_tot = block_sum_i32<kNT>(above, scan_scr);
+  const double wtot = block_sum_f64<kNT>(wsum, dscr);
+  if (threadIdx.x == 0) {
+    const size_t ci = (size_t)u * a.nchunk + c;
+    a.cand_cnt[ci] = total;
+    a.above_cnt[ci] = above_tot;
+    a.wpart[ci] = wtot;
+  }
+}
+
+// ------------------------------------------------------------------ resolve
+// One workgroup per unit: finish the radix select on the candidates (second
+// digit from the histogram, third digit from an LDS histogram of the
+// candidates that share the first two digits), then the tie quota per chunk
+// and the tail normaliser W.
+constexpr int kRT = 1024;
+constexpr int kRW = kRT / 64;
+
+__global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ int scan_scr[kRW];
+  __shared__ int pair[2];
+  __shared__ double dscr[kRW];
+
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv;
+  const UnitParams p = unit_params(a, b);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  UnitState st;
+  st.tkey = 0u;
+  st.ties_needed = 0;
+  st.M = 0.0f;
+  st.W = 0.0f;
+  st.flags = 0;
+  st.k_eff = p.k_eff;
+  st.m = p.m;
+  st.L = p.L;
+  const size_t cu = (size_t)u * a.nchunk;
+  double W = 0.0;
+
+  if (p.L == 0) {
+    st.flags = kFlagEmpty;
+  } else {
+    st.M = key_to_float(a.maxkey[u]);
+    if (p.dense) {
+      st.flags = kFlagDense;
+    } else {
+      const int nc = (p.L + kChunk - 1) / kChunk;
+      int total_ties = 0;
+      if (p.k_eff == 0) {
+        st.flags = kFlagNoTopk;
+        for (int c = threadIdx.x; c < nc; c += kRT) a.ties_before[cu + c] = 0;
+      } else {
+        int b1, rem1, b2, rem2, b3, rem3;
+        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist1[(size_t)u * kBins + i];
+        __syncthreads();
+        find_rank_bin<kRT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem1);
+        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist2[(size_t)u * kBins + i];
+        __syncthreads();
+        find_rank_bin<kRT>(hist, kBins, rem1, scan_scr, pair, &b2, &rem2);
+        const uint32_t prefix = ((uint32_t)b1 << 11) | (uint32_t)b2;
+        for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
+        __syncthreads();
+        for (int c = wave; c < nc; c += kRW) {
+          const int n = a.cand_cnt[cu + c];
+          const uint32_t* ck = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+          for (int i = lane; i < n; i += 64) {
+            const uint32_t key = ck[i];
+            if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+          }
+        }
+        __syncthreads();
+        find_rank_bin<kRT>(hist, kBins3, rem2, scan_scr, pair, &b3, &rem3);
+        st.tkey = (prefix << kDigit2Shift) | (uint32_t)b3;
+        st.ties_needed = rem3;
+        // Per chunk: ties on the threshold key and the weight of candidates
+        // strictly below it (both in a fixed order).
+        for (int c = wave; c < nc; c += kRW) {
+          const int n = a.cand_cnt[cu + c];
+          const uint32_t* ck = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+          int ties = 0;
+          double cs = 0.0;
+          for (int i = lane; i < n; i += 64) {
+            const uint32_t key = ck[i];
+            ties += key == st.tkey;
+            if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
+          }
+          ties = wave_sum(ties);
+          cs = wave_sum(cs);
+          if (lane == 0) {
+            a.tiecnt[cu + c] = ties;
+            a.ctail[cu + c] = cs;
+          }
+        }
+        __syncthreads();
+        int run = 0;
+        for (int c0 = 0; c0 < nc; c0 += kRT) {
+          const int c = c0 + threadIdx.x;
+          const int v = c < nc ? a.tiecnt[cu + c] : 0;
+          int tot;
+          const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
+          if (c < nc) a.ties_before[cu + c] = run + ex;
+          run += tot;
+        }
+        total_ties = run;
+      }
+      double acc = 0.0;
+      for (int c = threadIdx.x; c < nc; c += kRT)
+        acc += a.wpart[cu + c] + (p.k_eff > 0 ? a.ctail[cu + c] : 0.0);
+      W = block_sum_f64<kRT>(acc, dscr);
+      if (p.k_eff > 0) {
+        const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
+        W += (double)(total_ties - st.ties_needed) * wT;
+      }
+    }
+  }
+  st.W = a.w_in ? a.w_in[u] : (float)W;
+  if (!(st.flags & (kFlagEmpty | kFlagDense)) && p.m > 0 && p.L - p.k_eff > 0 && st.W > 0.0f)
+    st.flags |= kFlagSample;
+  if (threadIdx.x == 0) {
+    reinterpret_cast<UnitState*>(a.state)[u] = st;
+    if (a.norm_out) {
+      a.norm_out[2 * u] = st.M;
+      a.norm_out[2 * u + 1] = st.W;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ sample
+// Per chunk: decide membership of every token (deterministic set, sampled
+// tail token, or neither) and write the chunk's segment: deterministic tokens
+// in ascending order, then sampled tokens in ascending order.
+__global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
+  __shared__ float sh[kChunk];
+  __shared__ int scan_scr[kNT / 64];
+
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const int h = u - b * a.Hkv;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  const int c0 = c * kChunk;
+  int32_t* cnt = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
+  if (c0 >= st.L || (st.flags & kFlagEmpty)) {
+    if (threadIdx.x == 0) {
+      cnt[0] = 0;
+      cnt[1] = 0;
+    }
+    return;
+  }
+  stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, st.L, sh);
+  const bool dense = st.flags & kFlagDense;
+  const bool notopk = st.flags & kFlagNoTopk;
+  const int tb = threadIdx.x * kPer;
+
+  float s[kPer];
+  uint32_t validmask = 0u, smask = 0u, tiemask = 0u;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    s[i] = sh[tb + i];
+    const bool valid = c0 + tb + i < st.L;
+    validmask |= (uint32_t)valid << i;
+    if (valid && !dense && !notopk) {
+      const uint32_t key = order_key(s[i]);
+      smask |= (uint32_t)(key > st.tkey) << i;
+      tiemask |= (uint32_t)(key == st.tkey) << i;
+    }
+  }
+  if (dense) smask = validmask;
+  // Tokens on the threshold key join the deterministic set in index order
+  // until the quota is met.
+  int tot_unused;
+  int rank = block_exclusive_scan<kNT>(__popc(tiemask), scan_scr, &tot_unused);
+  rank += notopk || dense ? 0 : a.ties_before[(size_t)u * a.nchunk + c];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (tiemask & (1u << i)) {
+      if (rank < st.ties_needed) smask |= 1u << i;
+      ++rank;
+    }
+  }
+  const uint32_t tailmask = validmask & ~smask;
+  uint32_t rmask = 0u;
+  float logw[kPer];
+  if ((st.flags & kFlagSample) && tailmask) {
+    const uint64_t seed = a.seed[b];
+    const float mf = (float)st.m;
+#pragma unroll
+    for (int g = 0; g < kPer / 4; ++g) {
+      if (((tailmask >> (4 * g)) & 0xfu) == 0u) continue;
+      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
+      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        if (!(tailmask & (1u << i))) continue;
+        const float w = sexp(s[i] - st.M);
+        const float mw = mf * w;
+        const float uw = uniform24(words[r]) * st.W;
+        if (uw < mw) {
+          rmask |= 1u << i;
+          logw[i] = -__logf(fminf(1.0f, mw / st.W));
+        }
+      }
+    }
+  }
+  int totS, totR;
+  const int offS = block_exclusive_scan<kNT>(__popc(smask), scan_scr, &totS);
+  const int offR = block_exclusive_scan<kNT>(__popc(rmask), scan_scr, &totR);
+  int32_t* sidx = a.sel_idx + (size_t)u * a.seg_ld + c0;
+  float* slw = a.sel_logw + (size_t)u * a.seg_ld + c0;
+  int ws = offS, wr = totS + offR;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (smask & (1u << i)) {
+      sidx[ws] = c0 + tb + i;
+      slw[ws] = 0.0f;
+      ++ws;
+    }
+    if (rmask & (1u << i)) {
+      sidx[wr] = c0 + tb + i;
+      slw[wr] = logw[i];
+      ++wr;
+    }
+  }
+  if (threadIdx.x == 0) {
+    cnt[0] = totS;
+    cnt[1] = totR;
+  }
+}
+
+// ------------------------------------------------------------------ test hooks
+
+__global__ void debug_philox_kernel(uint64_t seed, int b, int h, int j0, int n, uint32_t* words) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t j = (uint32_t)(j0 + i);
+  const uint4 wd = philox_block(seed, b, h, j >> 2);
+  const uint32_t w4[4] = {wd.x, wd.y, wd.z, wd.w};
+  words[i] = w4[j & 3u];
+}
+
+__global__ void debug_sexp_kernel(const float* x, float* y, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = sexp(x[i]);
+}
+
+}  // namespace
+
+hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream) {
+  filter_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream) {
+  resolve_kernel<<<units, kRT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream) {
+  sample_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_philox(uint64_t seed, int b, int h, int j0, int n, uint32_t* words,
+                               hipStream_t stream) {
+  debug_philox_kernel<<<(n + 255) / 256, 256, 0, stream>>>(seed, b, h, j0, n, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_sexp(const float* x, float* y, int n, hipStream_t stream) {
+  debug_sexp_kernel<<<(n + 255) / 256, 256, 0, stream>>>(x, y, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssa

@@ -1,0 +1,396 @@
+// Host side of the C ABI declared in include/ssa.h: argument validation,
+// workspace carving and the launch sequence of each entry point.  No
+// allocation, no synchronisation, no global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "ssa.h"
+#include "ssa_launch.h"
+
+namespace {
+
+struct UnitStateBytes {
+  uint32_t words[8];  // layout of ssa::UnitState (32 bytes)
+};
+
+constexpr size_t kAlign = 256;
+constexpr int kBins = 2048;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool params_ok(const ssa_params* p) {
+  if (!p) return false;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1) return false;
+  if (p->num_q_heads % p->num_kv_heads != 0) return false;
+  const int G = p->num_q_heads / p->num_kv_heads;
+  if (G > 16) return false;
+  if (p->head_dim != 64 && p->head_dim != 128) return false;
+  if (p->block_size != SSA_BLOCK_TOKENS) return false;
+  if (p->max_blocks_per_seq < 1 || p->num_blocks < 1) return false;
+  if (p->max_seq_len < 1 || p->max_seq_len > SSA_MAX_SEQ_LEN) return false;
+  if ((int64_t)p->max_seq_len > (int64_t)p->max_blocks_per_seq * SSA_BLOCK_TOKENS) return false;
+  // cache rows are addressed with 32-bit row numbers
+  if ((int64_t)p->num_blocks * p->num_kv_heads * SSA_BLOCK_TOKENS >= ((int64_t)1 << 31)) return false;
+  const int pc = p->pair_count;
+  if (pc != 4 && pc != 8 && pc != 16 && pc != 32 && pc != 64) return false;
+  if (p->pair_begin < 0 || p->pair_begin % 4 != 0) return false;
+  if (p->pair_begin + pc > p->head_dim / 2) return false;
+  if (p->num_splits < 0) return false;
+  if (p->out_dtype != SSA_F32 && p->out_dtype != SSA_BF16) return false;
+  if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale)) return false;
+  if ((int64_t)p->batch * p->num_kv_heads > 65535) return false;  // grid.y
+  return true;
+}
+
+struct Dims {
+  int B, Hq, Hkv, G, d, U, NC, NS;
+  int64_t SEG;
+  float scale;
+};
+
+Dims dims_of(const ssa_params* p) {
+  Dims d;
+  d.B = p->batch;
+  d.Hq = p->num_q_heads;
+  d.Hkv = p->num_kv_heads;
+  d.G = d.Hq / d.Hkv;
+  d.d = p->head_dim;
+  d.U = d.B * d.Hkv;
+  d.NC = (p->max_seq_len + SSA_CHUNK_TOKENS - 1) / SSA_CHUNK_TOKENS;
+  d.SEG = (int64_t)d.NC * SSA_CHUNK_TOKENS;
+  d.NS = p->num_splits == 0 ? d.NC : (p->num_splits < d.NC ? p->num_splits : d.NC);
+  d.scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  return d;
+}
+
+struct Layout {
+  size_t scores, hist1, hist2, maxkey, cand_idx, cand_key, cand_cnt, above_cnt, wpart, tiecnt,
+      ctail, ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
+};
+
+Layout layout_of(const Dims& d) {
+  Layout l;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t U = (size_t)d.U, SEG = (size_t)d.SEG, NC = (size_t)d.NC;
+  l.scores = take(U * SEG * 4);
+  l.hist1 = take(U * kBins * 4);
+  l.hist2 = take(U * kBins * 4);
+  l.maxkey = take(U * 4);
+  l.cand_idx = take(U * SEG * 4);
+  l.cand_key = take(U * SEG * 4);
+  l.cand_cnt = take(U * NC * 4);
+  l.above_cnt = take(U * NC * 4);
+  l.wpart = take(U * NC * 8);
+  l.tiecnt = take(U * NC * 4);
+  l.ctail = take(U * NC * 8);
+  l.ties_before = take(U * NC * 4);
+  l.state = take(U * sizeof(UnitStateBytes));
+  l.sel_idx = take(U * SEG * 4);
+  l.sel_logw = take(U * SEG * 4);
+  l.sel_cnt = take(U * NC * 2 * 4);
+  l.part = take((size_t)d.B * d.Hq * d.NS * (d.d + 2) * 4);
+  l.total = off;
+  return l;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+struct Recorder {
+  void* const* ev;
+  hipStream_t s;
+  void begin(int stage) const {
+    if (ev && ev[2 * stage]) (void)hipEventRecord((hipEvent_t)ev[2 * stage], s);
+  }
+  void end(int stage) const {
+    if (ev && ev[2 * stage + 1]) (void)hipEventRecord((hipEvent_t)ev[2 * stage + 1], s);
+  }
+};
+
+int tokens_per_wg(const ssa_params* p, const Dims& d) {
+  const int it = ssa::indexer_tokens_per_iteration(p->pair_count);
+  const int64_t work = (int64_t)d.U * p->max_seq_len;
+  int64_t mult = work / ((int64_t)2048 * it);
+  if (mult < 1) mult = 1;
+  if (mult > 32) mult = 32;
+  return (int)(it * mult);
+}
+
+ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, float* scores,
+                          int64_t score_ld, void* ws, const Layout& l) {
+  ssa::IndexArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.scores = scores;
+  a.score_ld = score_ld;
+  a.hist1 = at<uint32_t>(ws, l.hist1);
+  a.maxkey = at<uint32_t>(ws, l.maxkey);
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.d = d.d;
+  a.pair_begin = p->pair_begin;
+  a.pair_count = p->pair_count;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.max_seq_len = p->max_seq_len;
+  a.tokens_per_wg = tokens_per_wg(p, d);
+  a.scale = d.scale;
+  return a;
+}
+
+ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* scores,
+                            int64_t score_ld, const int32_t* seq_lens, const int32_t* topk,
+                            const int32_t* sample_budget, const uint64_t* seed, const float* w_in,
+                            int32_t* sel_idx, float* sel_logw, int32_t* sel_cnt, float* norm_out,
+                            void* ws, const Layout& l) {
+  ssa::SelectArgs a;
+  a.scores = scores;
+  a.score_ld = score_ld;
+  a.seq_lens = seq_lens;
+  a.topk = topk;
+  a.sample_budget = sample_budget;
+  a.seed = seed;
+  a.w_in = w_in;
+  a.hist1 = at<uint32_t>(ws, l.hist1);
+  a.hist2 = at<uint32_t>(ws, l.hist2);
+  a.maxkey = at<uint32_t>(ws, l.maxkey);
+  a.cand_idx = at<int32_t>(ws, l.cand_idx);
+  a.cand_key = at<uint32_t>(ws, l.cand_key);
+  a.cand_cnt = at<int32_t>(ws, l.cand_cnt);
+  a.above_cnt = at<int32_t>(ws, l.above_cnt);
+  a.wpart = at<double>(ws, l.wpart);
+  a.tiecnt = at<int32_t>(ws, l.tiecnt);
+  a.ctail = at<double>(ws, l.ctail);
+  a.ties_before = at<int32_t>(ws, l.ties_before);
+  a.state = at<void>(ws, l.state);
+  a.sel_idx = sel_idx;
+  a.sel_logw = sel_logw;
+  a.sel_cnt = sel_cnt;
+  a.norm_out = norm_out;
+  a.Hkv = d.Hkv;
+  a.max_seq_len = p->max_seq_len;
+  a.nchunk = d.NC;
+  a.seg_ld = d.SEG;
+  return a;
+}
+
+ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* sel_idx, const float* sel_logw,
+                            const int32_t* sel_cnt, void* out, void* ws, const Layout& l) {
+  ssa::AttendArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.sel_idx = sel_idx;
+  a.sel_logw = sel_logw;
+  a.sel_cnt = sel_cnt;
+  a.part = at<float>(ws, l.part);
+  a.out = out;
+  a.B = d.B;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.G;
+  a.d = d.d;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.max_seq_len = p->max_seq_len;
+  a.nchunk = d.NC;
+  a.nsplit = d.NS;
+  a.out_dtype = p->out_dtype;
+  a.seg_ld = d.SEG;
+  a.scale = d.scale;
+  return a;
+}
+
+#define SSA_TRY(expr)                        \
+  do {                                       \
+    if ((expr) != hipSuccess) return SSA_ERR_HIP; \
+  } while (0)
+
+int check_ws(const ssa_params* p, void* ws, size_t ws_bytes, Layout* l) {
+  if (!params_ok(p)) return SSA_ERR_INVALID;
+  *l = layout_of(dims_of(p));
+  if (!ws || !aligned16(ws)) return SSA_ERR_INVALID;
+  if (ws_bytes < l->total) return SSA_ERR_WORKSPACE;
+  return SSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssa_workspace_bytes(const ssa_params* p) {
+  if (!params_ok(p)) return 0;
+  return layout_of(dims_of(p)).total;
+}
+
+int32_t ssa_num_chunks(const ssa_params* p) {
+  if (!params_ok(p)) return 0;
+  return dims_of(p).NC;
+}
+
+int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
+                     const int32_t* sample_budget, const uint64_t* seed, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+  Layout l;
+  const int rc = check_ws(p, workspace, workspace_bytes, &l);
+  if (rc != SSA_OK) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !topk || !sample_budget ||
+      !seed || !out)
+    return SSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SSA_ERR_INVALID;
+  const Dims d = dims_of(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Recorder rec{events, s};
+  float* scores = at<float>(workspace, l.scores);
+  int32_t* sel_idx = at<int32_t>(workspace, l.sel_idx);
+  float* sel_logw = at<float>(workspace, l.sel_logw);
+  int32_t* sel_cnt = at<int32_t>(workspace, l.sel_cnt);
+
+  const ssa::IndexArgs ia =
+      index_args(p, d, q, k_cache, block_table, seq_lens, scores, d.SEG, workspace, l);
+  const ssa::SelectArgs sa =
+      select_args(p, d, scores, d.SEG, seq_lens, topk, sample_budget, seed, nullptr, sel_idx,
+                  sel_logw, sel_cnt, nullptr, workspace, l);
+  const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
+                                         sel_logw, sel_cnt, out, workspace, l);
+  rec.begin(SSA_STAGE_INIT);
+  SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
+  rec.end(SSA_STAGE_INIT);
+  rec.begin(SSA_STAGE_INDEX);
+  SSA_TRY(ssa::launch_indexer(ia, d.U, s));
+  rec.end(SSA_STAGE_INDEX);
+  rec.begin(SSA_STAGE_FILTER);
+  SSA_TRY(ssa::launch_filter(sa, d.U, s));
+  rec.end(SSA_STAGE_FILTER);
+  rec.begin(SSA_STAGE_RESOLVE);
+  SSA_TRY(ssa::launch_resolve(sa, d.U, s));
+  rec.end(SSA_STAGE_RESOLVE);
+  rec.begin(SSA_STAGE_SAMPLE);
+  SSA_TRY(ssa::launch_sample(sa, d.U, s));
+  rec.end(SSA_STAGE_SAMPLE);
+  rec.begin(SSA_STAGE_ATTEND);
+  SSA_TRY(ssa::launch_attend(aa, s));
+  rec.end(SSA_STAGE_ATTEND);
+  rec.begin(SSA_STAGE_MERGE);
+  SSA_TRY(ssa::launch_merge(aa, s));
+  rec.end(SSA_STAGE_MERGE);
+  return SSA_OK;
+}
+
+int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
+               const int32_t* sample_budget, const uint64_t* seed, void* out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return ssa_decode_timed(p, q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget,
+                          seed, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int32_t* block_table,
+              const int32_t* seq_lens, float* scores, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  Layout l;
+  const int rc = check_ws(p, workspace, workspace_bytes, &l);
+  if (rc != SSA_OK) return rc;
+  if (!q || !k_cache || !block_table || !seq_lens || !scores) return SSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache)) return SSA_ERR_INVALID;
+  const Dims d = dims_of(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ssa::IndexArgs ia = index_args(p, d, q, k_cache, block_table, seq_lens, scores,
+                                       p->max_seq_len, workspace, l);
+  SSA_TRY(ssa::launch_init(ia.hist1, at<uint32_t>(workspace, l.hist2), ia.maxkey, d.U, s));
+  SSA_TRY(ssa::launch_indexer(ia, d.U, s));
+  return SSA_OK;
+}
+
+int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
+               const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
+               const float* w_in, int32_t* sel_idx, float* sel_logw, int32_t* sel_count,
+               float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout l;
+  const int rc = check_ws(p, workspace, workspace_bytes, &l);
+  if (rc != SSA_OK) return rc;
+  if (!scores || !seq_lens || !topk || !sample_budget || !seed || !sel_idx || !sel_logw ||
+      !sel_count || !norm_out)
+    return SSA_ERR_INVALID;
+  const Dims d = dims_of(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ssa::SelectArgs sa =
+      select_args(p, d, scores, p->max_seq_len, seq_lens, topk, sample_budget, seed, w_in,
+                  sel_idx, sel_logw, sel_count, norm_out, workspace, l);
+  SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
+  SSA_TRY(ssa::launch_score_hist(scores, p->max_seq_len, seq_lens, d.Hkv, p->max_seq_len, d.NC,
+                                 d.U, sa.hist1, sa.maxkey, s));
+  SSA_TRY(ssa::launch_filter(sa, d.U, s));
+  SSA_TRY(ssa::launch_resolve(sa, d.U, s));
+  SSA_TRY(ssa::launch_sample(sa, d.U, s));
+  return SSA_OK;
+}
+
+int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
+               const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  Layout l;
+  const int rc = check_ws(p, workspace, workspace_bytes, &l);
+  if (rc != SSA_OK) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !sel_idx || !sel_logw ||
+      !sel_count || !out)
+    return SSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SSA_ERR_INVALID;
+  const Dims d = dims_of(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
+                                         sel_logw, sel_count, out, workspace, l);
+  SSA_TRY(ssa::launch_attend(aa, s));
+  SSA_TRY(ssa::launch_merge(aa, s));
+  return SSA_OK;
+}
+
+int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t j0, int32_t n, uint32_t* words,
+                     void* stream) {
+  if (!words || n < 0 || j0 < 0 || b < 0 || h < 0) return SSA_ERR_INVALID;
+  if ((int64_t)j0 + n > INT32_MAX) return SSA_ERR_INVALID;
+  if (n == 0) return SSA_OK;
+  SSA_TRY(ssa::launch_debug_philox(seed, b, h, j0, n, words, static_cast<hipStream_t>(stream)));
+  return SSA_OK;
+}
+
+int ssa_debug_sexp(const float* x, float* y, int32_t n, void* stream) {
+  if (!x || !y || n < 0) return SSA_ERR_INVALID;
+  if (n == 0) return SSA_OK;
+  SSA_TRY(ssa::launch_debug_sexp(x, y, n, static_cast<hipStream_t>(stream)));
+  return SSA_OK;
+}
+
+const char* ssa_error_string(int code) {
+  switch (code) {
+    case SSA_OK: return "ok";
+    case SSA_ERR_INVALID: return "invalid argument";
+    case SSA_ERR_WORKSPACE: return "workspace too small";
+    case SSA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

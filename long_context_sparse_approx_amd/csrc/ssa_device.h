@@ -1,0 +1,245 @@
+// Device-side building blocks of the stratified sparse decode path (gfx950).
+//
+// Shared by the kernels in this directory only.  Everything here is written
+// for 64-lane wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssa.h"
+
+namespace ssa {
+
+constexpr int kBlockTokens = SSA_BLOCK_TOKENS;
+constexpr int kChunk = SSA_CHUNK_TOKENS;
+constexpr int kWave = 64;
+// Radix digits of the 32-bit order key: 11 + 11 + 10 bits.
+constexpr int kDigit1Shift = 21;
+constexpr int kDigit2Shift = 10;
+constexpr int kBins = 2048;
+constexpr int kBins3 = 1024;
+
+// Per-unit (batch, kv head) selection state written by the resolve stage.
+enum : int32_t {
+  kFlagEmpty = 1,     // L == 0: nothing to read
+  kFlagDense = 2,     // topk + m >= L: every token, weight 1
+  kFlagNoTopk = 4,    // topk == 0: every token is in the tail
+  kFlagSample = 8,    // Poisson sampling of the tail is active
+};
+
+struct UnitState {
+  uint32_t tkey;        // order key of the k-th largest score
+  int32_t ties_needed;  // tokens with key == tkey that join the deterministic set
+  float M;              // maximum score of the sequence
+  float W;              // tail normaliser used for sampling
+  int32_t flags;
+  int32_t k_eff;
+  int32_t m;
+  int32_t L;
+};
+static_assert(sizeof(UnitState) == 32, "the host reserves 32 bytes per unit");
+
+// ---------------------------------------------------------------- sizes
+
+__device__ __forceinline__ int clamp_len(int L, int max_seq_len) {
+  return L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
+}
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- ranking
+
+// Monotone float -> uint32 map: larger float, larger key; -0.0 just below +0.0.
+__device__ __forceinline__ uint32_t order_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- exp
+
+// The specified float32 exp used for tail weights (x <= 0): Cody-Waite
+// reduction x = n ln2 + r (ln2 split into a 16-fractional-bit head and a
+// float32 tail), degree-7 Taylor polynomial of e^r in Horner form, then an
+// exact scale by 2^n.  One rounding per operation, no fused multiply-add,
+// 0 for x < -87 (so every non-zero result is a normal float).  Both ranking
+// decisions that depend on it must be reproducible bit for bit off the GPU.
+__device__ __forceinline__ float sexp(float x) {
+#pragma clang fp contract(off)
+  const float kLog2e = 0x1.715476p+0f;   // float32(1 / ln 2)
+  const float kLn2Hi = 0x1.62e4p-1f;     // floor(ln2 * 2^16) / 2^16
+  const float kLn2Lo = 0x1.7f7d1cp-20f;  // float32(ln2 - head)
+  const bool low = x < -87.0f;
+  const float xs = low ? 0.0f : x;
+  const float n = __builtin_rintf(xs * kLog2e);
+  float r = xs - n * kLn2Hi;
+  r = r - n * kLn2Lo;
+  float p = 0x1.a01a02p-13f;             // 1/7!
+  p = p * r + 0x1.6c16c2p-10f;           // 1/6!
+  p = p * r + 0x1.111112p-7f;            // 1/5!
+  p = p * r + 0x1.555556p-5f;            // 1/4!
+  p = p * r + 0x1.555556p-3f;            // 1/3!
+  p = p * r + 0.5f;                      // 1/2!
+  p = p * r + 1.0f;                      // 1/1!
+  p = p * r + 1.0f;                      // 1/0!
+  const float y = __builtin_ldexpf(p, (int)n);
+  return low ? 0.0f : y;
+}
+
+// ---------------------------------------------------------------- Philox
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
+// -> 64-bit multiplies with the round function
+//   (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+// and a Weyl bump of the key between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// The four words for tokens 4*jq .. 4*jq+3 of (b, h): counter (jq, h, b, 0),
+// key = the 64-bit seed, low word first.
+__device__ __forceinline__ uint4 philox_block(uint64_t seed, int b, int h, uint32_t jq) {
+  return philox4x32_10(make_uint4(jq, (uint32_t)h, (uint32_t)b, 0u), (uint32_t)seed,
+                       (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ float uniform24(uint32_t word) {
+  return (float)(word >> 8) * 0x1.0p-24f;
+}
+
+// ---------------------------------------------------------------- reductions
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64);
+// `scratch` holds NT/64 ints in LDS.  Returns the exclusive prefix and writes
+// the block total to *total.  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) scratch[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = scratch[w];
+    base += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Deterministic block sum of doubles (fixed tree order); result in every thread.
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, double* scratch) {
+  constexpr int NW = NT / 64;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_sum_i32(int v, int* scratch) {
+  constexpr int NW = NT / 64;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+// Given a histogram `hist` of `nbins` bins in LDS and a rank k >= 1, find the
+// bin b* with count(bins > b*) < k <= count(bins >= b*), and the remaining rank
+// k - count(bins > b*).  Bins are scanned from the top.  Every thread of the
+// NT-thread block must call it; the answer is returned in every thread.
+template <int NT>
+__device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int nbins, int k, int* scan_scratch,
+                                              int* out_pair, int* bin_out, int* rem_out) {
+  const int per = nbins / NT;  // bins per thread (nbins is a multiple of NT)
+  const int top = nbins - 1 - threadIdx.x * per;  // this thread's highest bin
+  int mine = 0;
+  for (int i = 0; i < per; ++i) mine += (int)hist[top - i];
+  int total;
+  const int before = block_exclusive_scan<NT>(mine, scan_scratch, &total);
+  if (before < k && k <= before + mine) {
+    int run = before;
+    for (int i = 0; i < per; ++i) {
+      const int c = (int)hist[top - i];
+      if (run + c >= k) {
+        out_pair[0] = top - i;
+        out_pair[1] = k - run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  *bin_out = out_pair[0];
+  *rem_out = out_pair[1];
+  __syncthreads();
+}
+
+}  // namespace ssa

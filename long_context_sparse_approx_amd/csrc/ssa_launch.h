@@ -1,0 +1,84 @@
+// Kernel argument blocks and launchers of the stratified sparse decode path.
+// Internal to the library: the public interface is include/ssa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssa {
+
+struct IndexArgs {
+  const uint16_t* q;          // [B, Hq, d] bf16
+  const uint16_t* k_cache;    // [num_blocks, Hkv, 16, d] bf16
+  const int32_t* block_table; // [B, max_blocks]
+  const int32_t* seq_lens;    // [B]
+  float* scores;              // row (b*Hkv + h) of stride score_ld
+  int64_t score_ld;
+  uint32_t* hist1;            // [U, 2048]
+  uint32_t* maxkey;           // [U]
+  int Hq, Hkv, G, d, pair_begin, pair_count;
+  int max_blocks, num_blocks, max_seq_len, tokens_per_wg;
+  float scale;
+};
+
+struct SelectArgs {
+  const float* scores;        // row (b*Hkv + h) of stride score_ld
+  int64_t score_ld;
+  const int32_t* seq_lens;
+  const int32_t* topk;
+  const int32_t* sample_budget;
+  const uint64_t* seed;
+  const float* w_in;          // [U] or null
+  uint32_t* hist1;            // [U, 2048]
+  uint32_t* hist2;            // [U, 2048]
+  uint32_t* maxkey;           // [U]
+  int32_t* cand_idx;          // [U, seg_ld]
+  uint32_t* cand_key;         // [U, seg_ld]
+  int32_t* cand_cnt;          // [U, nchunk]
+  int32_t* above_cnt;         // [U, nchunk]
+  double* wpart;              // [U, nchunk]
+  int32_t* tiecnt;            // [U, nchunk]
+  double* ctail;              // [U, nchunk]
+  int32_t* ties_before;       // [U, nchunk]
+  void* state;                // [U] UnitState
+  int32_t* sel_idx;           // [U, seg_ld]
+  float* sel_logw;            // [U, seg_ld]
+  int32_t* sel_cnt;           // [U, nchunk, 2]
+  float* norm_out;            // [U, 2] or null
+  int Hkv, max_seq_len, nchunk;
+  int64_t seg_ld;             // nchunk * 4096
+};
+
+struct AttendArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const int32_t* sel_idx;
+  const float* sel_logw;
+  const int32_t* sel_cnt;
+  float* part;                // [B*Hq, nsplit, d + 2]: acc[d], m, l
+  void* out;                  // [B, Hq, d]
+  int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
+  int64_t seg_ld;
+  float scale;
+};
+
+int indexer_tokens_per_iteration(int pair_count);
+hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey, int units,
+                       hipStream_t stream);
+hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream);
+hipError_t launch_score_hist(const float* scores, int64_t score_ld, const int32_t* seq_lens,
+                             int Hkv, int max_seq_len, int nchunk, int units, uint32_t* hist1,
+                             uint32_t* maxkey, hipStream_t stream);
+hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_debug_philox(uint64_t seed, int b, int h, int j0, int n, uint32_t* words,
+                               hipStream_t stream);
+hipError_t launch_debug_sexp(const float* x, float* y, int n, hipStream_t stream);
+
+}  // namespace ssa

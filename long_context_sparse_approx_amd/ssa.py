@@ -1,0 +1,233 @@
+"""ctypes binding of libssa.so (include/ssa.h).  Argument marshalling only.
+
+torch supplies device memory and the current stream; every step of the decode
+path runs in the library's HIP kernels.  There is no fallback: if the library
+is missing the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssa.so")
+
+SSA_OK = 0
+SSA_ERR_INVALID = -1
+SSA_ERR_WORKSPACE = -2
+SSA_ERR_HIP = -3
+SSA_F32 = 0
+SSA_BF16 = 1
+BLOCK_TOKENS = 16
+CHUNK_TOKENS = 4096
+STAGES = ("init", "index", "filter", "resolve", "sample", "attend", "merge")
+EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_timed",
+           "ssa_score", "ssa_select", "ssa_attend", "ssa_debug_philox", "ssa_debug_sexp",
+           "ssa_error_string")
+
+
+class SsaParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("pair_begin", ctypes.c_int32), ("pair_count", ctypes.c_int32),
+                ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class SsaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed: {error_string(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(SsaParams)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(hipcc, gfx950); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssa_workspace_bytes.argtypes = [_PP]
+        L.ssa_workspace_bytes.restype = ctypes.c_size_t
+        L.ssa_num_chunks.argtypes = [_PP]
+        L.ssa_num_chunks.restype = ctypes.c_int32
+        common = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.ssa_decode.argtypes = common
+        L.ssa_decode.restype = ctypes.c_int
+        L.ssa_decode_timed.argtypes = common + [_P]
+        L.ssa_decode_timed.restype = ctypes.c_int
+        L.ssa_score.argtypes = [_PP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.ssa_score.restype = ctypes.c_int
+        L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 ctypes.c_size_t, _P]
+        L.ssa_select.restype = ctypes.c_int
+        L.ssa_attend.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.ssa_attend.restype = ctypes.c_int
+        L.ssa_debug_philox.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_int32, _P, _P]
+        L.ssa_debug_philox.restype = ctypes.c_int
+        L.ssa_debug_sexp.argtypes = [_P, _P, ctypes.c_int32, _P]
+        L.ssa_debug_sexp.restype = ctypes.c_int
+        L.ssa_error_string.argtypes = [ctypes.c_int]
+        L.ssa_error_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def error_string(code: int) -> str:
+    return lib().ssa_error_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != SSA_OK:
+        raise SsaError(code, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
+                max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
+                softmax_scale=0.0, block_size=BLOCK_TOKENS) -> SsaParams:
+    if pair_begin is None:
+        pair_begin = head_dim // 2 - pair_count
+    return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
+                     float(softmax_scale))
+
+
+def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
+    """Params from tensor shapes: q [B, Hq, d], k_cache [nblk, Hkv, 16, d]."""
+    B, Hq, d = q.shape
+    return make_params(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=d,
+                       max_blocks_per_seq=block_table.shape[1], num_blocks=k_cache.shape[0],
+                       max_seq_len=int(max_seq_len), **kw)
+
+
+def workspace_bytes(p: SsaParams) -> int:
+    n = lib().ssa_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        raise SsaError(SSA_ERR_INVALID, "ssa_workspace_bytes")
+    return int(n)
+
+
+def num_chunks(p: SsaParams) -> int:
+    return int(lib().ssa_num_chunks(ctypes.byref(p)))
+
+
+def alloc_workspace(p: SsaParams, device) -> torch.Tensor:
+    return torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def _ws(p, workspace, device):
+    if workspace is None:
+        workspace = alloc_workspace(p, device)
+    return workspace
+
+
+def decode(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
+           out=None, workspace=None, stream=None, events=None):
+    """One decode step; returns out [B, Hq, d] (f32 or bf16 per params)."""
+    if out is None:
+        dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=dt, device=q.device)
+    workspace = _ws(p, workspace, q.device)
+    args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(topk), _ptr(sample_budget), _ptr(seed), _ptr(out),
+            _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    if events is None:
+        _check(lib().ssa_decode(*args), "ssa_decode")
+    else:
+        _check(lib().ssa_decode_timed(*args, ctypes.c_void_p(events)), "ssa_decode_timed")
+    return out
+
+
+def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspace=None,
+          stream=None):
+    """Approximate scores [B, Hkv, max_seq_len] f32 (entries past L_b untouched)."""
+    if scores is None:
+        scores = torch.zeros((p.batch, p.num_kv_heads, p.max_seq_len), dtype=torch.float32,
+                             device=q.device)
+    workspace = _ws(p, workspace, q.device)
+    _check(lib().ssa_score(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(block_table),
+                           _ptr(seq_lens), _ptr(scores), _ptr(workspace),
+                           ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_score")
+    return scores
+
+
+def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None, workspace=None,
+           stream=None):
+    """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out)."""
+    dev = scores.device
+    nc = num_chunks(p)
+    U = p.batch * p.num_kv_heads
+    sel_idx = torch.empty((p.batch, p.num_kv_heads, nc * CHUNK_TOKENS), dtype=torch.int32, device=dev)
+    sel_logw = torch.empty((p.batch, p.num_kv_heads, nc * CHUNK_TOKENS), dtype=torch.float32,
+                           device=dev)
+    sel_count = torch.empty((p.batch, p.num_kv_heads, nc, 2), dtype=torch.int32, device=dev)
+    norm = torch.empty((p.batch, p.num_kv_heads, 2), dtype=torch.float32, device=dev)
+    workspace = _ws(p, workspace, dev)
+    assert w_in is None or w_in.numel() == U
+    _check(lib().ssa_select(ctypes.byref(p), _ptr(scores), _ptr(seq_lens), _ptr(topk),
+                            _ptr(sample_budget), _ptr(seed), _ptr(w_in), _ptr(sel_idx),
+                            _ptr(sel_logw), _ptr(sel_count), _ptr(norm), _ptr(workspace),
+                            ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_select")
+    return sel_idx, sel_logw, sel_count, norm
+
+
+def attend(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, sel_idx, sel_logw, sel_count,
+           out=None, workspace=None, stream=None):
+    """Attention over a given selection; returns out [B, Hq, d]."""
+    if out is None:
+        dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=dt, device=q.device)
+    workspace = _ws(p, workspace, q.device)
+    _check(lib().ssa_attend(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                            _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_logw),
+                            _ptr(sel_count), _ptr(out), _ptr(workspace),
+                            ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_attend")
+    return out
+
+
+def debug_philox(seed: int, b: int, h: int, j0: int, n: int, device="cuda"):
+    words = torch.empty(n, dtype=torch.int32, device=device)
+    _check(lib().ssa_debug_philox(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), b, h, j0, n,
+                                  _ptr(words), _stream(None)), "ssa_debug_philox")
+    return words
+
+
+def debug_sexp(x: torch.Tensor):
+    y = torch.empty_like(x)
+    _check(lib().ssa_debug_sexp(_ptr(x), _ptr(y), x.numel(), _stream(None)), "ssa_debug_sexp")
+    return y
+
+
+def decode_workload(wl, **kw):
+    """Convenience: params + decode for a synth.Workload."""
+    p = params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len, pair_begin=wl.pair_begin,
+                   pair_count=wl.pair_count, **kw)
+    return p, decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                     wl.sample_budget, wl.seed)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
