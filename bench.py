@@ -1,0 +1,307 @@
+"""Benchmark of one stratified sparse decode step (one attention layer).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1m|128k|32k|batched]
+
+A step is one ssa_decode call over the whole layer: scores, top-k, tail
+sampling, gather attention and merge, with inputs already resident in HBM.
+Prints one JSON line: KV-tokens/s/layer (sum of sequence lengths / step
+time), the per-stage times from HIP events recorded on the decode stream
+inside the timed region, the indexer's roofline against MI355X's 8 TB/s HBM
+peak, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-decode KV-tokens/s/layer + HBM GB/s vs peak at L=128K and L=1M"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+INDEXER_SOURCES = [os.path.join(ROOT, "long_context_sparse_approx_amd", "csrc", f)
+                   for f in ("indexer.hip", "ssa_device.h")]
+
+WORKLOADS = {
+    "1m": "1M-token decode: B=1, 32 q / 8 kv heads, d=128, L=1048576, bf16 paged KV "
+          "(16-token blocks, shuffled), RoPE theta=1e6, 256 planted keys per kv head, "
+          "50x budget = top-k 10486 + sampled 10486, split-K over 256 chunks",
+    "128k": "128K decode, batch 4: 32 q / 8 kv heads, d=128, L=131072 each, heavy-tailed keys "
+            "(90% N(0,1), 10% N(0,9)), 50x budget = top-k 1311 + sampled 1310",
+    "32k": "32K decode: B=1, 32 q / 8 kv heads, d=128, L=32768, 64 planted keys per kv head, "
+           "50x budget = top-k 328 + sampled 327",
+    "batched": "batched paged decode: B=32, L log-uniform in [8192, 131072], 32 q / 8 kv heads, "
+               "d=128, per-sequence 50x budget split top-k/sampled, seeds 1000+b",
+}
+
+
+class Hip:
+    """hipEvent helpers from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per indexer launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel changed since."""
+    path = os.path.join(PROFILES, f"indexer_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m or not t or m.group(1) != source_digest(INDEXER_SOURCES):
+        return None
+    return float(t.group(1))
+
+
+def run_gpu(args, name, steps, warmup, with_stage_events=True):
+    import torch
+
+    from long_context_sparse_approx_amd import ssa, synth
+
+    dev = "cuda:0"
+    t_gen = time.perf_counter()
+    wl = synth.make_workload(name, dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    ws = ssa.alloc_workspace(p, dev)
+    out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    call = (p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+            wl.sample_budget, wl.seed)
+    for _ in range(warmup):
+        ssa.decode(*call, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    nst = len(ssa.STAGES)
+    evs = []
+    for _ in range(steps):
+        arr = (ctypes.c_void_p * (2 * nst))(*[hip.event() for _ in range(2 * nst)])
+        evs.append(arr)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ssa.decode(*call, out=out, workspace=ws, stream=stream,
+                   events=ctypes.addressof(evs[i]) if with_stage_events else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = {s: 0.0 for s in ssa.STAGES}
+    gpu_ms = 0.0
+    for arr in evs:
+        for k, s in enumerate(ssa.STAGES):
+            stage_ms[s] += hip.elapsed_ms(arr[2 * k], arr[2 * k + 1]) / steps
+        gpu_ms += hip.elapsed_ms(arr[0], arr[2 * nst - 1]) / steps
+    for arr in evs:
+        for e in arr:
+            hip.destroy(e)
+
+    # Selected-set sizes of this step (deterministic: same kernels, same inputs).
+    sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
+    _, _, cnt, _ = ssa.select(p, sc, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                              workspace=ws)
+    cnt = cnt.sum(dim=2).cpu()
+    n_det, n_smp = int(cnt[..., 0].sum()), int(cnt[..., 1].sum())
+    del sc
+    torch.cuda.synchronize()
+
+    ms_step = (t1 - t0) * 1e3 / steps
+    tokens = float(sum(wl.lens))
+    d = wl.d
+    idx_bytes = tokens * wl.Hkv * (2 * wl.pair_count * 2)       # K pair subset
+    gather_bytes = (n_det + n_smp) * 2.0 * d * 2                # K and V rows
+    score_bytes = tokens * wl.Hkv * 4 * 4                       # 1 write + 3 reads
+    res = dict(wl=wl, p=p, ms_step=ms_step, gpu_ms=gpu_ms, stage_ms=stage_ms, tokens=tokens,
+               idx_bytes=idx_bytes, gather_bytes=gather_bytes, score_bytes=score_bytes,
+               n_det=n_det, n_smp=n_smp, t_gen=t_gen)
+    return res
+
+
+def unit_host_inputs(wl, b, h):
+    """Host copies of one (sequence, kv head): q group, the head's cache slab
+    [nblk, 1, 16, d] and the block-table row (exact bf16 values as float32)."""
+    G = wl.Hq // wl.Hkv
+    qg = wl.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype("float64")
+    kc = wl.k_cache[:, h:h + 1].float().cpu().numpy()
+    vc = wl.v_cache[:, h:h + 1].float().cpu().numpy()
+    bt = wl.block_table[b].cpu().numpy().astype("int64")
+    return qg, kc, vc, bt
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """The oracle as it stands, on a bounded sample of the workload's units."""
+    import numpy as np
+
+    from oracle import ssa_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    scale = 1.0 / math.sqrt(wl.d)
+    units = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
+    done, tokens, elapsed = 0, 0, 0.0
+    for b, h in units:
+        qg, kc, vc, bt = unit_host_inputs(wl, b, h)
+        L = wl.lens[b]
+        t0 = time.perf_counter()
+        K = orc.gather_rows(kc, bt, 0, L)
+        V = orc.gather_rows(vc, bt, 0, L)
+        s = orc.approx_scores(qg, K, wl.pair_begin, wl.pair_count, scale).astype(np.float32)
+        sel = orc.select_unit(s, int(wl.topk[b]), int(wl.sample_budget[b]),
+                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h)
+        orc.attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        tokens += L
+        del K, V, kc, vc
+        if elapsed >= budget_s:
+            break
+    # One unit is one kv head of one sequence; a layer has Hkv heads per token.
+    value = tokens / wl.Hkv / elapsed
+    return dict(value=value, unit="KV-tokens/s/layer", cores=int(threads), kind="oracle",
+                sample=f"{done} of {len(units)} (sequence, kv head) units of the same workload, "
+                       f"{tokens} token-heads in {elapsed:.1f} s; layer rate = token-heads / "
+                       f"{wl.Hkv} / time")
+
+
+def summarize(res, workload):
+    st = res["stage_ms"]
+    t_idx = st["index"] * 1e-3
+    achieved = res["idx_bytes"] / t_idx / 1e9
+    traffic = measured_traffic(workload)
+    roof = dict(bound="hbm", kernel="indexer", achieved=round(achieved, 1),
+                peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                traffic=traffic, algorithmic_bytes_per_launch=res["idx_bytes"],
+                launch_us=round(st["index"] * 1e3, 2))
+    step_s = res["ms_step"] * 1e-3
+    algo_total = res["idx_bytes"] + res["gather_bytes"]
+    return dict(
+        value=res["tokens"] / step_s, ms_per_step=res["ms_step"], roofline=roof,
+        stages_us={k: round(v * 1e3, 2) for k, v in st.items()},
+        gpu_step_us=round(res["gpu_ms"] * 1e3, 2),
+        hbm_gbps_algorithmic_step=round(algo_total / step_s / 1e9, 1),
+        gather_gbps_algorithmic=round(res["gather_bytes"] / (st["attend"] * 1e-3) / 1e9, 1),
+        selected=dict(deterministic=res["n_det"], sampled=res["n_smp"]),
+    )
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--also", default="128k", help="comma list of extra workloads ('' = none)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("steps must be >= 1 and warmup >= 0")
+
+    import torch
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {n} bytes read + {n} bytes written per copy", file=sys.stderr)
+        del a, b
+
+    res = run_gpu(args, args.workload, args.steps, args.warmup)
+    main_sum = summarize(res, args.workload)
+    also = {}
+    for name in [w for w in args.also.split(",") if w and w != args.workload]:
+        r2 = run_gpu(args, name, args.steps, args.warmup)
+        s2 = summarize(r2, name)
+        also[name] = dict(workload=WORKLOADS[name], value=s2["value"], unit="KV-tokens/s/layer",
+                          ms_per_step=s2["ms_per_step"], roofline=s2["roofline"],
+                          stages_us=s2["stages_us"],
+                          hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"])
+        del r2
+        torch.cuda.empty_cache()
+    cpu = None if args.no_cpu else cpu_baseline(res["wl"], args.cpu_budget)
+    wl = res["wl"]
+    line = {
+        "metric": METRIC,
+        "value": main_sum["value"],
+        "unit": "KV-tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_sum["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload], "batch": wl.B,
+                   "seq_len": wl.max_seq_len, "kv_tokens": int(res["tokens"]),
+                   "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.d,
+                   "scored_pairs": wl.pair_count, "splits": "one per 4096-token chunk",
+                   "parallelism": "none (one GPU)"},
+        "roofline": main_sum["roofline"],
+        "cpu_baseline": cpu,
+        "stages_us": main_sum["stages_us"],
+        "gpu_step_us": main_sum["gpu_step_us"],
+        "hbm_gbps_algorithmic_step": main_sum["hbm_gbps_algorithmic_step"],
+        "gather_gbps_algorithmic": main_sum["gather_gbps_algorithmic"],
+        "selected": main_sum["selected"],
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

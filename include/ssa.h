@@ -76,12 +76,12 @@ extern "C" {
 
 #define SSA_BLOCK_TOKENS 16    /* tokens per KV-cache block (the only size supported) */
 #define SSA_CHUNK_TOKENS 4096  /* selection / split granularity                      */
-#define SSA_MAX_SEQ_LEN (1 << 26)
+#define SSA_MAX_SEQ_LEN (1 << 24) /* 4096 chunks of 4096 tokens */
 
 /* Stage indices for ssa_decode_timed(). */
 #define SSA_STAGE_INIT 0     /* clear histograms and maxima                        */
 #define SSA_STAGE_INDEX 1    /* approximate scores + first-digit histogram + max   */
-#define SSA_STAGE_FILTER 2   /* threshold candidates, definite-tail weight sums    */
+#define SSA_STAGE_FILTER 2   /* first-digit threshold, candidates, tail weight sums */
 #define SSA_STAGE_RESOLVE 3  /* exact top-k threshold, tie quota, tail normaliser  */
 #define SSA_STAGE_SAMPLE 4   /* deterministic set + Poisson sample, per chunk      */
 #define SSA_STAGE_ATTEND 5   /* gather attention over the selection, split-K       */

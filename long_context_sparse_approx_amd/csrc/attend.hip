@@ -61,11 +61,15 @@ struct VSlice<64> {
   static __device__ __forceinline__ uint32_t word(const T& v, int w) { return w == 0 ? v.x : v.y; }
 };
 
+constexpr int kBatch = 256;  // selected items resolved to cache rows at a time
+
 template <int D>
 __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   constexpr int KK = D / 32;   // QK steps over the head dim
   constexpr int DPL = D / 16;  // head dims per PV column = PV steps
   using VS = VSlice<D>;
+  __shared__ int rows_sh[kBatch + 32];
+  __shared__ float lw_sh[kBatch + 32];
 
   const int s = blockIdx.x;
   const int u = blockIdx.y;
@@ -78,6 +82,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   const int ncL = (L + kChunk - 1) / kChunk;
   const int c_begin = (int)((int64_t)s * ncL / a.nsplit);
   const int c_end = (int)((int64_t)(s + 1) * ncL / a.nsplit);
+  const int max_row = a.num_blocks * a.Hkv * kBlockTokens - 1;
 
   // QK B operand (Q^T): lane holds head n16, dims kk*32 + q4*8 .. +8.
   bf16x8 qf[KK];
@@ -102,107 +107,125 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   const size_t seg = (size_t)u * a.seg_ld;
   for (int c = c_begin; c < c_end; ++c) {
     const int32_t* cntp = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
-    // Counts and positions of a caller-provided selection are clamped to the
-    // segment and to [0, L) so that no value can address outside the buffers.
+    // Counts and entries of a caller-provided selection are clamped to the
+    // segment, to [0, L) and to the cache so that no value can address
+    // outside the buffers.
     const int cnt = min(max(cntp[0], 0) + max(cntp[1], 0), kChunk);
     const int32_t* idxp = a.sel_idx + seg + (size_t)c * kChunk;
     const float* lwp = a.sel_logw + seg + (size_t)c * kChunk;
-    for (int t0 = 0; t0 < cnt; t0 += 32) {
-      // Lanes 0..31 resolve the tile's 32 items to cache rows.
-      int row = -1;
-      float lw = -INFINITY;
-      {
-        const int item = t0 + (lane & 31);
-        if (lane < 32 && item < cnt) {
-          const int idx = min(max(idxp[item], 0), L - 1);
-          lw = lwp[item];
-          int blk = btrow[idx >> 4];
-          blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-          row = (blk * a.Hkv + h) * kBlockTokens + (idx & 15);
+    for (int b0 = 0; b0 < cnt; b0 += kBatch) {
+      // Resolve up to kBatch items to cache rows (independent loads), into LDS.
+      const int nb = min(kBatch, cnt - b0);
+#pragma unroll
+      for (int k = 0; k < kBatch / 64; ++k) {
+        const int i = lane + 64 * k;
+        int row = -1;
+        float lw = -INFINITY;
+        if (i < nb) {
+          const int v = idxp[b0 + i];
+          lw = lwp[b0 + i];
+          if (a.idx_are_rows) {
+            row = min(max(v, 0), max_row);
+          } else {
+            const int idx = min(max(v, 0), L - 1);
+            int blk = btrow[idx >> 4];
+            blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+            row = (blk * a.Hkv + h) * kBlockTokens + (idx & 15);
+          }
+        }
+        rows_sh[i] = row;
+        lw_sh[i] = lw;
+      }
+      if (lane < 32) {
+        rows_sh[kBatch + lane] = -1;
+        lw_sh[kBatch + lane] = -INFINITY;
+      }
+      __syncthreads();
+      for (int t0 = 0; t0 < nb; t0 += 32) {
+        // QK for the two 16-token halves: A = K rows (token n16 of the half).
+        f32x4 sc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = rows_sh[t0 + 16 * hh + n16];
+          bf16x8 kf[KK];
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (r >= 0)
+              v = *reinterpret_cast<const uint4*>(a.k_cache + (size_t)r * D + kk * 32 + q4 * 8);
+            kf[kk] = as_bf16x8(v);
+          }
+          f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], d, 0, 0, 0);
+          sc[hh] = d;
+        }
+        // V rows of this lane's 8 k-slots (issued before the softmax math).
+        typename VS::T vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+          const int r = rows_sh[t0 + tok];
+          vr[i] = VS::zero();
+          if (r >= 0)
+            vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)r * D + n16 * DPL);
+        }
+        // Logits of (head n16, slot tokens), online softmax update.
+        float x[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+          x[i] = sc[i >> 2][i & 3] * a.scale + lw_sh[t0 + tok];
+          tmax = fmaxf(tmax, x[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __expf(m_run - m_new);
+        float psum = 0.0f;
+        uint32_t phi[4], plo[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float p0 = __expf(x[i] - m_new);
+          const float p1 = __expf(x[i + 1] - m_new);
+          psum += p0 + p1;
+          const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+          const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
+          const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
+          phi[i >> 1] = h0 | (h1 << 16);
+          plo[i >> 1] = l0 | (l1 << 16);
+        }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // Rescale the accumulators: rows 4*q4 + r belong to head 4*q4 + r,
+        // whose alpha sits in lane 4*q4 + r.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
+        }
+        const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+        const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          const int w = j >> 1;
+          uint32_t p[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t w0 = VS::word(vr[2 * k], w), w1 = VS::word(vr[2 * k + 1], w);
+            p[k] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
+          }
+          const bf16x8 vb = as_bf16x8(make_uint4(p[0], p[1], p[2], p[3]));
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[j], 0, 0, 0);
         }
       }
-      // QK for the two 16-token halves: A = K rows (token n16 of the half).
-      f32x4 sc[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = __shfl(row, 16 * hh + n16);
-        bf16x8 kf[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          uint4 v = make_uint4(0u, 0u, 0u, 0u);
-          if (r >= 0) v = *reinterpret_cast<const uint4*>(a.k_cache + (size_t)r * D + kk * 32 + q4 * 8);
-          kf[kk] = as_bf16x8(v);
-        }
-        f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], d, 0, 0, 0);
-        sc[hh] = d;
-      }
-      // V rows of this lane's 8 k-slots (issued before the softmax math).
-      typename VS::T vr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
-        const int r = __shfl(row, tok);
-        vr[i] = VS::zero();
-        if (r >= 0)
-          vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)r * D + n16 * DPL);
-      }
-      // Logits of (head n16, slot tokens), online softmax update.
-      float x[8];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
-        const float bias = __shfl(lw, tok);
-        x[i] = sc[i >> 2][i & 3] * a.scale + bias;
-        tmax = fmaxf(tmax, x[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __expf(m_run - m_new);
-      float psum = 0.0f;
-      uint32_t phi[4], plo[4];
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float p0 = __expf(x[i] - m_new);
-        const float p1 = __expf(x[i + 1] - m_new);
-        psum += p0 + p1;
-        const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-        const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
-        const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
-        phi[i >> 1] = h0 | (h1 << 16);
-        plo[i >> 1] = l0 | (l1 << 16);
-      }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // Rescale the accumulators: rows 4*q4 + r belong to head 4*q4 + r,
-      // whose alpha sits in lane 4*q4 + r.
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * q4 + r);
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
-      }
-      const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
-      const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
-#pragma unroll
-      for (int j = 0; j < DPL; ++j) {
-        const int w = j >> 1;
-        uint32_t p[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t w0 = VS::word(vr[2 * k], w), w1 = VS::word(vr[2 * k + 1], w);
-          p[k] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
-        }
-        const bf16x8 vb = as_bf16x8(make_uint4(p[0], p[1], p[2], p[3]));
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[j], 0, 0, 0);
-      }
+      __syncthreads();
     }
   }
 
@@ -227,15 +250,20 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 
 // Merge of the split states of one (sequence, query head):
 //   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
-// in a fixed order (deterministic).
+// in a fixed order (deterministic).  Each of the 4 waves takes every 4th
+// split; a lane owns d/64 consecutive dims, so one split's acc row is one
+// contiguous wave-wide load.
 constexpr int kMT = 256;
 
+template <int D>
 __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
+  constexpr int DPL = D / 64;
   __shared__ float red[kMT];
-  __shared__ float accsh[kMT];
+  __shared__ float accsh[4][D];
   const int bh = blockIdx.x;
-  const int D = a.d;
   const int ns = a.nsplit;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const float* base = a.part + (size_t)bh * ns * (D + 2);
   float mx = -INFINITY;
   for (int s = threadIdx.x; s < ns; s += kMT) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
@@ -260,26 +288,28 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
     __syncthreads();
   }
   const float denom = red[0];
-  // threads split as (dim, split-phase): kMT / D phases over the splits
-  const int phases = kMT / D;
-  const int dim = threadIdx.x % D;
-  const int ph = threadIdx.x / D;
-  float o = 0.0f;
-  for (int s = ph; s < ns; s += phases) {
+  float o[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
+#pragma unroll 4
+  for (int s = wave; s < ns; s += 4) {
     const float* p = base + (size_t)s * (D + 2);
     const float m = p[D];
-    if (m != -INFINITY) o += __expf(m - mstar) * p[dim];
+    const float e = (m != -INFINITY) ? __expf(m - mstar) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[j] += e * p[lane * DPL + j];
   }
-  accsh[threadIdx.x] = o;
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) accsh[wave][lane * DPL + j] = o[j];
   __syncthreads();
   if (threadIdx.x < D) {
-    float t = 0.0f;
-    for (int k = 0; k < phases; ++k) t += accsh[k * D + threadIdx.x];
+    const int dim = threadIdx.x;
+    const float t = ((accsh[0][dim] + accsh[1][dim]) + accsh[2][dim]) + accsh[3][dim];
     const float res = (mstar == -INFINITY || denom <= 0.0f) ? 0.0f : t / denom;
     if (a.out_dtype == SSA_BF16)
-      reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + threadIdx.x] = (uint16_t)f32_to_bf16_bits(res);
+      reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + dim] = (uint16_t)f32_to_bf16_bits(res);
     else
-      reinterpret_cast<float*>(a.out)[(size_t)bh * D + threadIdx.x] = res;
+      reinterpret_cast<float*>(a.out)[(size_t)bh * D + dim] = res;
   }
 }
 
@@ -297,7 +327,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
-  merge_kernel<<<a.B * a.Hq, kMT, 0, stream>>>(a);
+  if (a.d == 128)
+    merge_kernel<128><<<a.B * a.Hq, kMT, 0, stream>>>(a);
+  else if (a.d == 64)
+    merge_kernel<64><<<a.B * a.Hq, kMT, 0, stream>>>(a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@ namespace ssa {
 
 namespace {
 
+// Largest token tile of one indexer workgroup (its block ids are staged in LDS).
+constexpr int kMaxTileTokens = 8192;
+
 __device__ __forceinline__ float dot8(const float* qb, uint4 v) {
   float s = qb[0] * bf16_lo(v.x);
   s = __builtin_fmaf(qb[1], bf16_hi(v.x), s);
@@ -43,6 +46,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   constexpr int WG_TOK = 4 * WAVE_TOK;  // tokens per workgroup per iteration
   __shared__ float qsh[16 * 128];
   __shared__ uint32_t hist[kBins];
+  __shared__ int blk_sh[kMaxTileTokens / kBlockTokens];
   __shared__ uint32_t wmax[4];
 
   const int u = blockIdx.y;
@@ -57,8 +61,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int wave = tid >> 6;
   const int nd = 2 * a.pair_count;
 
-  // Stage the query group's scored slice in LDS, then fold it into the
-  // per-lane proxy query: qb = (scale / G) * sum_g q_g over this lane's 8 dims.
+  // Stage the query group's scored slice and the tile's block ids in LDS.
   for (int i = tid; i < a.G * nd; i += 256) {
     const int g = i / nd;
     const int e = i - g * nd;
@@ -66,8 +69,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
         a.q[(size_t)(b * a.Hq + h * a.G + g) * a.d + 2 * a.pair_begin + e];
     qsh[i] = __uint_as_float((uint32_t)bits << 16);
   }
+  const int blk0 = t0 / kBlockTokens;
+  const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
+  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  for (int i = tid; i < nblk; i += 256) {
+    int blk = btrow[blk0 + i];
+    blk_sh[i] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+  }
   for (int i = tid; i < kBins; i += 256) hist[i] = 0u;
   __syncthreads();
+  // Per-lane proxy query: qb = (scale / G) * sum_g q_g over this lane's 8 dims.
   const int sub = lane % LPT;
   float qb[8];
   const float qscale = a.scale / (float)a.G;
@@ -79,8 +90,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   }
 
   const size_t blk_stride = (size_t)a.Hkv * kBlockTokens * a.d;
-  const size_t head_off = (size_t)h * kBlockTokens * a.d + 2 * a.pair_begin + sub * 8;
-  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.d + 2 * a.pair_begin + sub * 8;
   float* srow = a.scores + (size_t)u * a.score_ld;
   uint32_t kmax = 0u;
 
@@ -91,10 +101,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
       const int t = base + r * TPI + lane / LPT;
       kv[r] = make_uint4(0u, 0u, 0u, 0u);
       if (t < t_end) {
-        int blk = btrow[t >> 4];
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        const uint16_t* p = a.k_cache + (size_t)blk * blk_stride + head_off + (size_t)(t & 15) * a.d;
-        kv[r] = *reinterpret_cast<const uint4*>(p);
+        const int blk = blk_sh[(t - t0) >> 4];
+        kv[r] = *reinterpret_cast<const uint4*>(kbase + (size_t)blk * blk_stride +
+                                                (size_t)(t & 15) * a.d);
       }
     }
 #pragma unroll
@@ -126,9 +135,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   }
 }
 
-// Clears the per-unit histograms and maxima that stage 1 accumulates into.
+// Clears the per-unit histograms and maxima.
 __global__ __launch_bounds__(256) void init_kernel(uint32_t* hist1, uint32_t* hist2,
-                                                   uint32_t* maxkey, int units) {
+                                                   uint32_t* maxkey) {
   const int u = blockIdx.x;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     hist1[(size_t)u * kBins + i] = 0u;
@@ -139,22 +148,19 @@ __global__ __launch_bounds__(256) void init_kernel(uint32_t* hist1, uint32_t* hi
 
 // First-digit histogram and maximum of a caller-provided score array (the
 // standalone selection entry point; the fused path gets both from stage 1).
-__global__ __launch_bounds__(256) void score_hist_kernel(const float* scores, int64_t score_ld,
-                                                         const int32_t* seq_lens, int Hkv,
-                                                         int max_seq_len, uint32_t* hist1,
-                                                         uint32_t* maxkey) {
+__global__ __launch_bounds__(256) void score_hist_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t wmax[4];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int b = u / Hkv;
-  const int L = clamp_len(seq_lens[b], max_seq_len);
+  const int b = u / a.Hkv;
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
   const int c0 = c * kChunk;
   if (c0 >= L) return;
   const int c1 = min(L, c0 + kChunk);
   for (int i = threadIdx.x; i < kBins; i += 256) hist[i] = 0u;
   __syncthreads();
-  const float* srow = scores + (size_t)u * score_ld;
+  const float* srow = a.scores + (size_t)u * a.score_ld;
   uint32_t kmax = 0u;
   for (int t = c0 + threadIdx.x; t < c1; t += 256) {
     const uint32_t key = order_key(srow[t]);
@@ -167,21 +173,22 @@ __global__ __launch_bounds__(256) void score_hist_kernel(const float* scores, in
   if (threadIdx.x == 0) {
     uint32_t mx = wmax[0];
     for (int w = 1; w < 4; ++w) mx = wmax[w] > mx ? wmax[w] : mx;
-    atomicMax(&maxkey[u], mx);
+    atomicMax(&a.maxkey[u], mx);
   }
   for (int i = threadIdx.x; i < kBins; i += 256) {
     const uint32_t n = hist[i];
-    if (n) atomicAdd(&hist1[(size_t)u * kBins + i], n);
+    if (n) atomicAdd(&a.hist1[(size_t)u * kBins + i], n);
   }
 }
 
 }  // namespace
 
 int indexer_tokens_per_iteration(int pair_count) { return 4 * (kWave / (pair_count / 4)) * 8; }
+int indexer_max_tokens_per_wg() { return kMaxTileTokens; }
 
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey, int units,
                        hipStream_t stream) {
-  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey, units);
+  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey);
   return hipGetLastError();
 }
 
@@ -199,12 +206,8 @@ hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_score_hist(const float* scores, int64_t score_ld, const int32_t* seq_lens,
-                             int Hkv, int max_seq_len, int nchunk, int units, uint32_t* hist1,
-                             uint32_t* maxkey, hipStream_t stream) {
-  dim3 grid(nchunk, units);
-  score_hist_kernel<<<grid, 256, 0, stream>>>(scores, score_ld, seq_lens, Hkv, max_seq_len,
-                                              hist1, maxkey);
+hipError_t launch_score_hist(const SelectArgs& a, int units, hipStream_t stream) {
+  score_hist_kernel<<<dim3(a.nchunk, units), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

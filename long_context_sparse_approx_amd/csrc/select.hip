@@ -31,79 +31,76 @@ namespace {
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 
-struct UnitParams {
-  int L, k_eff, m;
-  bool dense;
-};
-
-__device__ __forceinline__ UnitParams unit_params(const SelectArgs& a, int b) {
-  UnitParams p;
-  p.L = clamp_len(a.seq_lens[b], a.max_seq_len);
-  const int k = max(a.topk[b], 0);
-  p.m = max(a.sample_budget[b], 0);
-  p.dense = (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
-  p.k_eff = min(k, p.L);
-  return p;
-}
-
 // Coalesced copy of the chunk's scores into LDS (entries past L are unused).
+// All of a thread's loads are issued before the first LDS store.
 __device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, int L, float* sh) {
-  for (int i = threadIdx.x; i < kChunk; i += kNT) {
-    const int t = c0 + i;
-    sh[i] = t < L ? srow[t] : 0.0f;
+  float v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int t = c0 + threadIdx.x + k * kNT;
+    v[k] = t < L ? srow[t] : 0.0f;
   }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ filter
-// Per chunk: tokens whose first digit is above the threshold digit are in the
-// deterministic set; tokens on the threshold digit become candidates (written
-// in index order, second-digit histogram updated); tokens below it are tail
-// tokens, whose weights are summed here in fp64.
-__global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
+// ------------------------------------------------------------------ threshold
+// First radix digit of the k-th largest key of every unit, from the unit's
+// first-digit histogram (one workgroup per unit).
+__global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
-  __shared__ float sh[kChunk];
   __shared__ int scan_scr[kNT / 64];
   __shared__ int pair[2];
+  const int u = blockIdx.x;
+  const int b = u / a.Hkv;
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
+  if (p.dense || p.k_eff == 0 || p.L == 0) {
+    if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0};
+    return;
+  }
+  for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = a.hist1[(size_t)u * kBins + i];
+  __syncthreads();
+  int b1, rem;
+  find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
+  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, rem};
+}
+
+// ------------------------------------------------------------------ filter
+// Per chunk: tokens whose first digit is above the unit's threshold digit are
+// in the deterministic set; tokens on the threshold digit become candidates
+// (written in index order, second-digit histogram updated); tokens below it
+// are tail tokens, whose weights are summed here in fp64.
+__global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
+  __shared__ float sh[kChunk];
+  __shared__ int scan_scr[kNT / 64];
   __shared__ double dscr[kNT / 64];
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
-  const UnitParams p = unit_params(a, b);
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
-
-  int b1 = kBins;  // k = 0: every token is a tail token
-  if (p.k_eff > 0) {
-    for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = a.hist1[(size_t)u * kBins + i];
-    __syncthreads();
-    int rem;
-    find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
-  }
+  const int b1 = a.thresh[u].b1;     // 2048 when there is no deterministic set
   const float M = key_to_float(a.maxkey[u]);
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
 
   const int tb = threadIdx.x * kPer;
-  int above = 0;
   uint32_t candmask = 0u;
   double wsum = 0.0;
   uint32_t keys[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int t = c0 + tb + i;
     const float s = sh[tb + i];
     const uint32_t key = order_key(s);
     keys[i] = key;
     const int bin = (int)(key >> kDigit1Shift);
-    if (t < p.L) {
-      if (bin > b1) {
-        ++above;
-      } else if (bin == b1) {
+    if (c0 + tb + i < p.L) {
+      if (bin == b1)
         candmask |= 1u << i;
-      } else {
+      else if (bin < b1)
         wsum += (double)sexp(s - M);
-      }
     }
   }
   int total;
@@ -120,12 +117,10 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
       atomicAdd(&a.hist2[(size_t)u * kBins + ((keys[i] >> kDigit2Shift) & (kBins - 1))], 1u);
     }
   }
-  const int above_tot = block_sum_i32<kNT>(above, scan_scr);
   const double wtot = block_sum_f64<kNT>(wsum, dscr);
   if (threadIdx.x == 0) {
     const size_t ci = (size_t)u * a.nchunk + c;
     a.cand_cnt[ci] = total;
-    a.above_cnt[ci] = above_tot;
     a.wpart[ci] = wtot;
   }
 }
@@ -133,22 +128,33 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
 // ------------------------------------------------------------------ resolve
 // One workgroup per unit: finish the radix select on the candidates (second
 // digit from the histogram, third digit from an LDS histogram of the
-// candidates that share the first two digits), then the tie quota per chunk
-// and the tail normaliser W.
+// candidates sharing the first two digits), then the per-chunk tie counts,
+// the tie quota offsets and the tail normaliser W.  Candidate passes run over
+// the flattened candidate list, every thread on a fixed stride, so loads are
+// independent and every sum has a fixed order.
 constexpr int kRT = 1024;
 constexpr int kRW = kRT / 64;
+constexpr int kMaxResolveChunks = SSA_MAX_SEQ_LEN / kChunk;
+
+// Candidate passes: thread t serves chunk (t / tpc) + k * (kRT / tpc) and,
+// inside it, items (t % tpc) + i * tpc.  Every load is independent and every
+// thread's items are fixed by (nc, t): sums over them have a fixed order.
+__device__ __forceinline__ int threads_per_chunk(int nc) {
+  int tpc = kRT;
+  while (tpc > 1 && tpc * nc > kRT) tpc >>= 1;
+  return tpc;
+}
 
 __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
+  __shared__ int ties_sh[kMaxResolveChunks];
   __shared__ int scan_scr[kRW];
   __shared__ int pair[2];
   __shared__ double dscr[kRW];
 
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
-  const UnitParams p = unit_params(a, b);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -159,6 +165,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   st.m = p.m;
   st.L = p.L;
   const size_t cu = (size_t)u * a.nchunk;
+  const uint32_t* ckeys = a.cand_key + (size_t)u * a.seg_ld;
   double W = 0.0;
 
   if (p.L == 0) {
@@ -169,25 +176,28 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       st.flags = kFlagDense;
     } else {
       const int nc = (p.L + kChunk - 1) / kChunk;
+      const int tpc = threads_per_chunk(nc);
+      const int cstep = kRT / tpc;
+      const int csub = threadIdx.x % tpc;
+      double ctail = 0.0;
       int total_ties = 0;
       if (p.k_eff == 0) {
         st.flags = kFlagNoTopk;
-        for (int c = threadIdx.x; c < nc; c += kRT) a.ties_before[cu + c] = 0;
       } else {
-        int b1, rem1, b2, rem2, b3, rem3;
-        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist1[(size_t)u * kBins + i];
-        __syncthreads();
-        find_rank_bin<kRT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem1);
+        const Thresh1 t1 = a.thresh[u];
         for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist2[(size_t)u * kBins + i];
+        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         __syncthreads();
-        find_rank_bin<kRT>(hist, kBins, rem1, scan_scr, pair, &b2, &rem2);
-        const uint32_t prefix = ((uint32_t)b1 << 11) | (uint32_t)b2;
+        int b2, rem2, b3, rem3;
+        find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &b2, &rem2);
+        const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)b2;
         for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
         __syncthreads();
-        for (int c = wave; c < nc; c += kRW) {
+        for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
           const int n = a.cand_cnt[cu + c];
-          const uint32_t* ck = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
-          for (int i = lane; i < n; i += 64) {
+          const uint32_t* ck = ckeys + (size_t)c * kChunk;
+#pragma unroll 4
+          for (int i = csub; i < n; i += tpc) {
             const uint32_t key = ck[i];
             if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
           }
@@ -196,41 +206,39 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         find_rank_bin<kRT>(hist, kBins3, rem2, scan_scr, pair, &b3, &rem3);
         st.tkey = (prefix << kDigit2Shift) | (uint32_t)b3;
         st.ties_needed = rem3;
-        // Per chunk: ties on the threshold key and the weight of candidates
-        // strictly below it (both in a fixed order).
-        for (int c = wave; c < nc; c += kRW) {
+        // Ties on the threshold key per chunk (integer), and the weight of the
+        // candidates strictly below it.
+        double cs = 0.0;
+        for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
           const int n = a.cand_cnt[cu + c];
-          const uint32_t* ck = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+          const uint32_t* ck = ckeys + (size_t)c * kChunk;
           int ties = 0;
-          double cs = 0.0;
-          for (int i = lane; i < n; i += 64) {
+#pragma unroll 4
+          for (int i = csub; i < n; i += tpc) {
             const uint32_t key = ck[i];
             ties += key == st.tkey;
             if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
           }
-          ties = wave_sum(ties);
-          cs = wave_sum(cs);
-          if (lane == 0) {
-            a.tiecnt[cu + c] = ties;
-            a.ctail[cu + c] = cs;
-          }
+          if (ties) atomicAdd(&ties_sh[c], ties);
         }
-        __syncthreads();
+        ctail = block_sum_f64<kRT>(cs, dscr);
         int run = 0;
         for (int c0 = 0; c0 < nc; c0 += kRT) {
           const int c = c0 + threadIdx.x;
-          const int v = c < nc ? a.tiecnt[cu + c] : 0;
+          const int v = c < nc ? ties_sh[c] : 0;
           int tot;
           const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
-          if (c < nc) a.ties_before[cu + c] = run + ex;
+          if (c < nc) {
+            a.ties_before[cu + c] = run + ex;
+            a.tiecnt[cu + c] = v;
+          }
           run += tot;
         }
         total_ties = run;
       }
       double acc = 0.0;
-      for (int c = threadIdx.x; c < nc; c += kRT)
-        acc += a.wpart[cu + c] + (p.k_eff > 0 ? a.ctail[cu + c] : 0.0);
-      W = block_sum_f64<kRT>(acc, dscr);
+      for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
+      W = block_sum_f64<kRT>(acc, dscr) + ctail;
       if (p.k_eff > 0) {
         const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
         W += (double)(total_ties - st.ties_needed) * wT;
@@ -252,7 +260,9 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 // ------------------------------------------------------------------ sample
 // Per chunk: decide membership of every token (deterministic set, sampled
 // tail token, or neither) and write the chunk's segment: deterministic tokens
-// in ascending order, then sampled tokens in ascending order.
+// in ascending order, then sampled tokens in ascending order.  With emit_rows
+// the segment holds cache row numbers (for the fused attention stage) instead
+// of positions.
 __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   __shared__ float sh[kChunk];
   __shared__ int scan_scr[kNT / 64];
@@ -291,15 +301,26 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   }
   if (dense) smask = validmask;
   // Tokens on the threshold key join the deterministic set in index order
-  // until the quota is met.
-  int tot_unused;
-  int rank = block_exclusive_scan<kNT>(__popc(tiemask), scan_scr, &tot_unused);
-  rank += notopk || dense ? 0 : a.ties_before[(size_t)u * a.nchunk + c];
+  // until the quota is met.  Only a chunk that straddles the quota needs the
+  // ranks; the branch is uniform over the workgroup.
+  if (!dense && !notopk) {
+    const size_t ci = (size_t)u * a.nchunk + c;
+    const int before = a.ties_before[ci];
+    const int here = a.tiecnt[ci];
+    if (here > 0) {
+      if (before + here <= st.ties_needed) {
+        smask |= tiemask;
+      } else if (before < st.ties_needed) {
+        int tot_unused;
+        int rank = before + block_exclusive_scan<kNT>(__popc(tiemask), scan_scr, &tot_unused);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (tiemask & (1u << i)) {
-      if (rank < st.ties_needed) smask |= 1u << i;
-      ++rank;
+        for (int i = 0; i < kPer; ++i) {
+          if (tiemask & (1u << i)) {
+            if (rank < st.ties_needed) smask |= 1u << i;
+            ++rank;
+          }
+        }
+      }
     }
   }
   const uint32_t tailmask = validmask & ~smask;
@@ -322,28 +343,42 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
         const float uw = uniform24(words[r]) * st.W;
         if (uw < mw) {
           rmask |= 1u << i;
-          logw[i] = -__logf(fminf(1.0f, mw / st.W));
+          logw[i] = -logf(fminf(1.0f, mw / st.W));
         }
       }
     }
   }
-  int totS, totR;
-  const int offS = block_exclusive_scan<kNT>(__popc(smask), scan_scr, &totS);
-  const int offR = block_exclusive_scan<kNT>(__popc(rmask), scan_scr, &totR);
+  // One scan for both counts: deterministic count in the low 16 bits,
+  // sampled count in the high 16 bits (each at most 4096).
+  int packed_tot;
+  const int packed = block_exclusive_scan<kNT>(__popc(smask) | (__popc(rmask) << 16), scan_scr,
+                                               &packed_tot);
+  const int totS = packed_tot & 0xffff;
+  const int totR = packed_tot >> 16;
   int32_t* sidx = a.sel_idx + (size_t)u * a.seg_ld + c0;
   float* slw = a.sel_logw + (size_t)u * a.seg_ld + c0;
-  int ws = offS, wr = totS + offR;
+  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  int ws = packed & 0xffff, wr = totS + (packed >> 16);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    if (smask & (1u << i)) {
-      sidx[ws] = c0 + tb + i;
-      slw[ws] = 0.0f;
-      ++ws;
-    }
-    if (rmask & (1u << i)) {
-      sidx[wr] = c0 + tb + i;
-      slw[wr] = logw[i];
-      ++wr;
+    const uint32_t bit = 1u << i;
+    if ((smask | rmask) & bit) {
+      const int t = c0 + tb + i;
+      int v = t;
+      if (a.emit_rows) {
+        int blk = btrow[t >> 4];
+        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+        v = (blk * a.Hkv + h) * kBlockTokens + (t & 15);
+      }
+      if (smask & bit) {
+        sidx[ws] = v;
+        slw[ws] = 0.0f;
+        ++ws;
+      } else {
+        sidx[wr] = v;
+        slw[wr] = logw[i];
+        ++wr;
+      }
     }
   }
   if (threadIdx.x == 0) {
@@ -369,6 +404,11 @@ __global__ void debug_sexp_kernel(const float* x, float* y, int n) {
 }
 
 }  // namespace
+
+hipError_t launch_threshold(const SelectArgs& a, int units, hipStream_t stream) {
+  threshold_kernel<<<units, kNT, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream) {
   filter_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);

@@ -69,8 +69,8 @@ Dims dims_of(const ssa_params* p) {
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, maxkey, cand_idx, cand_key, cand_cnt, above_cnt, wpart, tiecnt,
-      ctail, ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
+  size_t scores, hist1, hist2, maxkey, thresh, cand_idx, cand_key, cand_cnt, wpart, tiecnt,
+      ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
 };
 
 Layout layout_of(const Dims& d) {
@@ -86,13 +86,12 @@ Layout layout_of(const Dims& d) {
   l.hist1 = take(U * kBins * 4);
   l.hist2 = take(U * kBins * 4);
   l.maxkey = take(U * 4);
+  l.thresh = take(U * sizeof(ssa::Thresh1));
   l.cand_idx = take(U * SEG * 4);
   l.cand_key = take(U * SEG * 4);
   l.cand_cnt = take(U * NC * 4);
-  l.above_cnt = take(U * NC * 4);
   l.wpart = take(U * NC * 8);
   l.tiecnt = take(U * NC * 4);
-  l.ctail = take(U * NC * 8);
   l.ties_before = take(U * NC * 4);
   l.state = take(U * sizeof(UnitStateBytes));
   l.sel_idx = take(U * SEG * 4);
@@ -123,8 +122,9 @@ int tokens_per_wg(const ssa_params* p, const Dims& d) {
   const int it = ssa::indexer_tokens_per_iteration(p->pair_count);
   const int64_t work = (int64_t)d.U * p->max_seq_len;
   int64_t mult = work / ((int64_t)2048 * it);
+  const int64_t cap = ssa::indexer_max_tokens_per_wg() / it;
+  if (mult > cap) mult = cap;
   if (mult < 1) mult = 1;
-  if (mult > 32) mult = 32;
   return (int)(it * mult);
 }
 
@@ -157,8 +157,9 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
 ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* scores,
                             int64_t score_ld, const int32_t* seq_lens, const int32_t* topk,
                             const int32_t* sample_budget, const uint64_t* seed, const float* w_in,
-                            int32_t* sel_idx, float* sel_logw, int32_t* sel_cnt, float* norm_out,
-                            void* ws, const Layout& l) {
+                            const int32_t* block_table, int emit_rows, int32_t* sel_idx,
+                            float* sel_logw, int32_t* sel_cnt, float* norm_out, void* ws,
+                            const Layout& l) {
   ssa::SelectArgs a;
   a.scores = scores;
   a.score_ld = score_ld;
@@ -167,16 +168,16 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.sample_budget = sample_budget;
   a.seed = seed;
   a.w_in = w_in;
+  a.block_table = block_table;
   a.hist1 = at<uint32_t>(ws, l.hist1);
   a.hist2 = at<uint32_t>(ws, l.hist2);
   a.maxkey = at<uint32_t>(ws, l.maxkey);
+  a.thresh = at<ssa::Thresh1>(ws, l.thresh);
   a.cand_idx = at<int32_t>(ws, l.cand_idx);
   a.cand_key = at<uint32_t>(ws, l.cand_key);
   a.cand_cnt = at<int32_t>(ws, l.cand_cnt);
-  a.above_cnt = at<int32_t>(ws, l.above_cnt);
   a.wpart = at<double>(ws, l.wpart);
   a.tiecnt = at<int32_t>(ws, l.tiecnt);
-  a.ctail = at<double>(ws, l.ctail);
   a.ties_before = at<int32_t>(ws, l.ties_before);
   a.state = at<void>(ws, l.state);
   a.sel_idx = sel_idx;
@@ -186,6 +187,9 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.Hkv = d.Hkv;
   a.max_seq_len = p->max_seq_len;
   a.nchunk = d.NC;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.emit_rows = emit_rows;
   a.seg_ld = d.SEG;
   return a;
 }
@@ -193,7 +197,8 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
 ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
                             const void* v_cache, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* sel_idx, const float* sel_logw,
-                            const int32_t* sel_cnt, void* out, void* ws, const Layout& l) {
+                            const int32_t* sel_cnt, int idx_are_rows, void* out, void* ws,
+                            const Layout& l) {
   ssa::AttendArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(k_cache);
@@ -216,6 +221,7 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
   a.nchunk = d.NC;
   a.nsplit = d.NS;
   a.out_dtype = p->out_dtype;
+  a.idx_are_rows = idx_are_rows;
   a.seg_ld = d.SEG;
   a.scale = d.scale;
   return a;
@@ -270,10 +276,10 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   const ssa::IndexArgs ia =
       index_args(p, d, q, k_cache, block_table, seq_lens, scores, d.SEG, workspace, l);
   const ssa::SelectArgs sa =
-      select_args(p, d, scores, d.SEG, seq_lens, topk, sample_budget, seed, nullptr, sel_idx,
-                  sel_logw, sel_cnt, nullptr, workspace, l);
+      select_args(p, d, scores, d.SEG, seq_lens, topk, sample_budget, seed, nullptr, block_table,
+                  /*emit_rows=*/1, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
   const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
-                                         sel_logw, sel_cnt, out, workspace, l);
+                                         sel_logw, sel_cnt, /*idx_are_rows=*/1, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
   rec.end(SSA_STAGE_INIT);
@@ -281,6 +287,7 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   SSA_TRY(ssa::launch_indexer(ia, d.U, s));
   rec.end(SSA_STAGE_INDEX);
   rec.begin(SSA_STAGE_FILTER);
+  SSA_TRY(ssa::launch_threshold(sa, d.U, s));
   SSA_TRY(ssa::launch_filter(sa, d.U, s));
   rec.end(SSA_STAGE_FILTER);
   rec.begin(SSA_STAGE_RESOLVE);
@@ -337,10 +344,10 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ssa::SelectArgs sa =
       select_args(p, d, scores, p->max_seq_len, seq_lens, topk, sample_budget, seed, w_in,
-                  sel_idx, sel_logw, sel_count, norm_out, workspace, l);
+                  nullptr, /*emit_rows=*/0, sel_idx, sel_logw, sel_count, norm_out, workspace, l);
   SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
-  SSA_TRY(ssa::launch_score_hist(scores, p->max_seq_len, seq_lens, d.Hkv, p->max_seq_len, d.NC,
-                                 d.U, sa.hist1, sa.maxkey, s));
+  SSA_TRY(ssa::launch_score_hist(sa, d.U, s));
+  SSA_TRY(ssa::launch_threshold(sa, d.U, s));
   SSA_TRY(ssa::launch_filter(sa, d.U, s));
   SSA_TRY(ssa::launch_resolve(sa, d.U, s));
   SSA_TRY(ssa::launch_sample(sa, d.U, s));
@@ -361,7 +368,8 @@ int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const vo
   const Dims d = dims_of(p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
-                                         sel_logw, sel_count, out, workspace, l);
+                                         sel_logw, sel_count, /*idx_are_rows=*/0, out, workspace,
+                                         l);
   SSA_TRY(ssa::launch_attend(aa, s));
   SSA_TRY(ssa::launch_merge(aa, s));
   return SSA_OK;

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "ssa.h"
+#include "ssa_launch.h"
 
 namespace ssa {
 
@@ -110,11 +111,10 @@ __device__ __forceinline__ float sexp(float x) {
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
-    const uint32_t lo0 = 0xD2511F53u * c.x;
-    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;  // one v_mad_u64_u32 each
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1,
+                   (uint32_t)(p0 >> 32) ^ c.w ^ k1, (uint32_t)p0);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -240,6 +240,24 @@ __device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int nbins, i
   *bin_out = out_pair[0];
   *rem_out = out_pair[1];
   __syncthreads();
+}
+
+// Selection parameters of sequence b as the kernels read them.
+struct SeqParams {
+  int L, k_eff, m;
+  bool dense;
+};
+
+__device__ __forceinline__ SeqParams seq_params(const int32_t* seq_lens, const int32_t* topk,
+                                                const int32_t* sample_budget, int b,
+                                                int max_seq_len) {
+  SeqParams p;
+  p.L = clamp_len(seq_lens[b], max_seq_len);
+  const int k = max(topk[b], 0);
+  p.m = max(sample_budget[b], 0);
+  p.dense = (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
+  p.k_eff = min(k, p.L);
+  return p;
 }
 
 }  // namespace ssa

@@ -7,6 +7,15 @@
 
 namespace ssa {
 
+// First radix digit of a unit's k-th largest order key, found once per unit
+// from the unit's first-digit histogram:
+//   b1  = digit of the k-th key (2048 when no deterministic set is needed),
+//   rem = rank of that key among the keys with digit b1.
+struct Thresh1 {
+  int32_t b1;
+  int32_t rem;
+};
+
 struct IndexArgs {
   const uint16_t* q;          // [B, Hq, d] bf16
   const uint16_t* k_cache;    // [num_blocks, Hkv, 16, d] bf16
@@ -29,23 +38,23 @@ struct SelectArgs {
   const int32_t* sample_budget;
   const uint64_t* seed;
   const float* w_in;          // [U] or null
+  const int32_t* block_table; // used when emit_rows
   uint32_t* hist1;            // [U, 2048]
   uint32_t* hist2;            // [U, 2048]
   uint32_t* maxkey;           // [U]
+  Thresh1* thresh;            // [U]
   int32_t* cand_idx;          // [U, seg_ld]
   uint32_t* cand_key;         // [U, seg_ld]
   int32_t* cand_cnt;          // [U, nchunk]
-  int32_t* above_cnt;         // [U, nchunk]
   double* wpart;              // [U, nchunk]
   int32_t* tiecnt;            // [U, nchunk]
-  double* ctail;              // [U, nchunk]
   int32_t* ties_before;       // [U, nchunk]
   void* state;                // [U] UnitState
-  int32_t* sel_idx;           // [U, seg_ld]
+  int32_t* sel_idx;           // [U, seg_ld]: positions, or cache rows when emit_rows
   float* sel_logw;            // [U, seg_ld]
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
-  int Hkv, max_seq_len, nchunk;
+  int Hkv, max_seq_len, nchunk, max_blocks, num_blocks, emit_rows;
   int64_t seg_ld;             // nchunk * 4096
 };
 
@@ -55,23 +64,24 @@ struct AttendArgs {
   const uint16_t* v_cache;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const int32_t* sel_idx;
+  const int32_t* sel_idx;     // positions, or cache rows when idx_are_rows
   const float* sel_logw;
   const int32_t* sel_cnt;
   float* part;                // [B*Hq, nsplit, d + 2]: acc[d], m, l
   void* out;                  // [B, Hq, d]
   int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
+  int idx_are_rows;
   int64_t seg_ld;
   float scale;
 };
 
 int indexer_tokens_per_iteration(int pair_count);
+int indexer_max_tokens_per_wg();
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey, int units,
                        hipStream_t stream);
 hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream);
-hipError_t launch_score_hist(const float* scores, int64_t score_ld, const int32_t* seq_lens,
-                             int Hkv, int max_seq_len, int nchunk, int units, uint32_t* hist1,
-                             uint32_t* maxkey, hipStream_t stream);
+hipError_t launch_score_hist(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_threshold(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
