@@ -8,14 +8,16 @@
 //
 // Memory shape.  The scored pairs are a contiguous dim range, so each token
 // contributes one contiguous 2*pair_count*2-byte slice of its key row (128 B
-// for 32 pairs at d = 128).  LPT lanes cover one token with one 16-byte load
-// each; a wave instruction therefore reads 64/LPT token slices and every lane
-// keeps UNR independent loads in flight.  The fp32 proxy query (scaled) lives
-// in registers; the products are exact bf16 x fp32 -> fp32 with fp32
-// accumulation.  The epilogue writes the score, counts the score's first
-// radix digit (top 11 bits of the order key) in an LDS histogram and tracks
-// the maximum order key; both are flushed with integer atomics, so the result
-// is independent of scheduling.
+// for 32 pairs at d = 128).  LPT lanes cover one token with one 16-byte
+// streaming load each; a wave instruction therefore reads 64/LPT token slices
+// and every lane keeps 8 independent loads (8 consecutive tokens) in flight.  The scaled proxy query
+// lives in registers as bf16 hi + lo parts and the slices are dotted with
+// v_dot2_f32_bf16 straight from the loaded words.  A DPP reduce-scatter
+// across the LPT lanes leaves each lane with complete token scores, so the
+// score stores are coalesced.  The epilogue counts each score's first radix
+// digit (top 11 bits of the order key) in an LDS histogram and tracks the
+// maximum order key; both are flushed with integer atomics, so the result is
+// independent of scheduling.
 #include "ssa_device.h"
 #include "ssa_launch.h"
 
@@ -26,28 +28,125 @@ namespace {
 // Largest token tile of one indexer workgroup (its block ids are staged in LDS).
 constexpr int kMaxTileTokens = 8192;
 
-__device__ __forceinline__ float dot8(const float* qb, uint4 v) {
-  float s = qb[0] * bf16_lo(v.x);
-  s = __builtin_fmaf(qb[1], bf16_hi(v.x), s);
-  s = __builtin_fmaf(qb[2], bf16_lo(v.y), s);
-  s = __builtin_fmaf(qb[3], bf16_hi(v.y), s);
-  s = __builtin_fmaf(qb[4], bf16_lo(v.z), s);
-  s = __builtin_fmaf(qb[5], bf16_hi(v.z), s);
-  s = __builtin_fmaf(qb[6], bf16_lo(v.w), s);
-  s = __builtin_fmaf(qb[7], bf16_hi(v.w), s);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load that does not keep the line in the caches (the key
+// slices are read once per step).
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float dot2(uint32_t k2, uint32_t q2, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k2),
+                                         __builtin_bit_cast(bf16x2, q2), acc, false);
+}
+
+// Partial score of one 8-dim key slice: the proxy query is held as two bf16
+// parts (hi + lo, ~16 significant bits); bf16 x bf16 products are exact and
+// accumulate in fp32.
+__device__ __forceinline__ float slice_dot(const uint32_t* qh, const uint32_t* ql, u32x4 k) {
+  float s = dot2(k.x, qh[0], 0.0f);
+  s = dot2(k.y, qh[1], s);
+  s = dot2(k.z, qh[2], s);
+  s = dot2(k.w, qh[3], s);
+  s = dot2(k.x, ql[0], s);
+  s = dot2(k.y, ql[1], s);
+  s = dot2(k.z, ql[2], s);
+  s = dot2(k.w, ql[3], s);
   return s;
+}
+
+// Value of the partner lane across lane-index bit `bit` (bits 0-2 within
+// 8-lane groups, bit 3 within 16-lane rows), through DPP.
+template <int BIT>
+__device__ __forceinline__ float partner(float x) {
+  constexpr int ctrl = BIT == 0 ? 0xB1 : (BIT == 1 ? 0x4E : (BIT == 2 ? 0x141 : 0x128));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl,
+                                                               0xf, 0xf, false));
+}
+
+// One reduce-scatter step across lane bit BIT on the first 2*H values: the
+// lane whose bit is 0 keeps the first H sums, its partner the last H.
+template <int BIT, int H>
+__device__ __forceinline__ void rs_step(float* v, bool upper) {
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float keep = upper ? v[H + i] : v[i];
+    const float send = upper ? v[i] : v[H + i];
+    v[i] = keep + partner<BIT>(send);
+  }
+}
+
+// LPT lanes cover one token's slice (LPT in 1..16, a power of two); each lane
+// holds partial sums of UNR = 8 tokens r.  After the reduce-scatter lane
+// position p (= lane % LPT, taken mod 8) holds the complete sums of
+// r = p * E + e, e < E, with E = 8 / min(LPT, 8).
+template <int LPT>
+__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
+  if constexpr (LPT == 16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += partner<3>(v[i]);
+  }
+  if constexpr (LPT >= 8) rs_step<2, 4>(v, (lane >> 2) & 1);
+  if constexpr (LPT >= 4) rs_step<1, (LPT >= 8 ? 2 : 4)>(v, (lane >> 1) & 1);
+  if constexpr (LPT >= 2) rs_step<0, (LPT >= 8 ? 1 : (LPT == 4 ? 2 : 4))>(v, lane & 1);
+}
+
+// One wave iteration over TPI * UNR consecutive tokens: lane group g (of LPT
+// lanes) takes tokens base + 8 g .. base + 8 g + 7, one 16-byte slice of each
+// per lane, all inside one cache block.  After the reduce-scatter, lane
+// position p of group g holds the complete scores of tokens
+// base + 8 g + p * E + e (e < E), so for LPT = 8 lane l holds token base + l
+// and the score stores are contiguous.  FULL: every token is below t_end (no
+// predication; all loads are issued back to back).
+template <int LPT, bool FULL>
+__device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uint64_t* blk_sh,
+                                                int d, int t0, int base, int t_end,
+                                                const uint32_t* qh, const uint32_t* ql,
+                                                float* srow, uint32_t* hist, uint32_t& kmax,
+                                                int lane) {
+  constexpr int UNR = 8;
+  constexpr int LG = LPT < 8 ? LPT : 8;
+  constexpr int E = UNR / LG;
+  const int grp = lane / LPT;
+  const int pos = (lane % LPT) % LG;
+  const bool writer = LPT <= 8 || (lane & 8) == 0;
+  const int tg = base + UNR * grp;  // first token of this lane's group (a multiple of 8)
+  const uint16_t* row0 = kbase + blk_sh[(tg - t0) >> 4] + (uint64_t)(tg & 15) * d;
+  u32x4 kv[UNR];
+#pragma unroll
+  for (int r = 0; r < UNR; ++r)
+    kv[r] = (FULL || tg + r < t_end) ? load_stream(row0 + (size_t)r * d) : u32x4{0u, 0u, 0u, 0u};
+  float v[UNR];
+#pragma unroll
+  for (int r = 0; r < UNR; ++r) v[r] = slice_dot(qh, ql, kv[r]);
+  reduce_scatter<LPT>(v, lane);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int t = tg + pos * E + e;
+    if (writer && (FULL || t < t_end)) {
+      srow[t] = v[e];
+      const uint32_t key = order_key(v[e]);
+      atomicAdd(&hist[key >> kDigit1Shift], 1u);
+      kmax = key > kmax ? key : kmax;
+    }
+  }
 }
 
 template <int LPT>
 __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
-  constexpr int TPI = kWave / LPT;      // tokens per wave-wide load
-  constexpr int UNR = 8;                // loads in flight per lane
-  constexpr int WAVE_TOK = TPI * UNR;   // tokens per wave per iteration
-  constexpr int WG_TOK = 4 * WAVE_TOK;  // tokens per workgroup per iteration
-  __shared__ float qsh[16 * 128];
-  __shared__ uint32_t hist[kBins];
-  __shared__ int blk_sh[kMaxTileTokens / kBlockTokens];
+  constexpr int TPI = kWave / LPT;           // tokens per wave-wide load
+  constexpr int UNR = 8;                     // loads in flight per lane
+  constexpr int WAVE_TOK = TPI * UNR;        // tokens per wave per iteration
+  constexpr int WG_TOK = 4 * WAVE_TOK;       // tokens per workgroup per iteration
+  // The query group's scored slice (at most 16 x 128 floats) is staged in the
+  // same LDS as the histogram, which is cleared once the slice is folded.
+  __shared__ uint32_t hist[16 * 128];
+  __shared__ uint64_t blk_sh[kMaxTileTokens / kBlockTokens];
   __shared__ uint32_t wmax[4];
+  static_assert(16 * 128 >= kBins, "histogram fits the staging buffer");
+  float* qsh = reinterpret_cast<float*>(hist);
 
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
@@ -61,7 +160,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int wave = tid >> 6;
   const int nd = 2 * a.pair_count;
 
-  // Stage the query group's scored slice and the tile's block ids in LDS.
+  // Stage the query group's scored slice and the tile's block offsets in LDS.
   for (int i = tid; i < a.G * nd; i += 256) {
     const int g = i / nd;
     const int e = i - g * nd;
@@ -72,54 +171,49 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int blk0 = t0 / kBlockTokens;
   const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.d;
   for (int i = tid; i < nblk; i += 256) {
     int blk = btrow[blk0 + i];
-    blk_sh[i] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    blk_sh[i] = (uint64_t)blk * blk_stride;
   }
+  __syncthreads();
+  // Per-lane proxy query over this lane's 8 dims, qbar = (scale / G) * sum_g q_g,
+  // split into bf16 hi and lo parts packed two dims per word.
+  const int sub = lane % LPT;
+  uint32_t qh[4], ql[4];
+  {
+    const float qscale = a.scale / (float)a.G;
+    float qf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = 0.0f;
+      for (int g = 0; g < a.G; ++g) s += qsh[g * nd + sub * 8 + i];
+      qf[i] = s * qscale;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h0 = f32_to_bf16_bits(qf[2 * i]), h1 = f32_to_bf16_bits(qf[2 * i + 1]);
+      const uint32_t l0 = f32_to_bf16_bits(qf[2 * i] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(qf[2 * i + 1] - __uint_as_float(h1 << 16));
+      qh[i] = h0 | (h1 << 16);
+      ql[i] = l0 | (l1 << 16);
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < kBins; i += 256) hist[i] = 0u;
   __syncthreads();
-  // Per-lane proxy query: qb = (scale / G) * sum_g q_g over this lane's 8 dims.
-  const int sub = lane % LPT;
-  float qb[8];
-  const float qscale = a.scale / (float)a.G;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float s = 0.0f;
-    for (int g = 0; g < a.G; ++g) s += qsh[g * nd + sub * 8 + i];
-    qb[i] = s * qscale;
-  }
 
-  const size_t blk_stride = (size_t)a.Hkv * kBlockTokens * a.d;
   const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.d + 2 * a.pair_begin + sub * 8;
   float* srow = a.scores + (size_t)u * a.score_ld;
   uint32_t kmax = 0u;
-
-  for (int base = t0 + wave * WAVE_TOK; base < t_end; base += WG_TOK) {
-    uint4 kv[UNR];
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      const int t = base + r * TPI + lane / LPT;
-      kv[r] = make_uint4(0u, 0u, 0u, 0u);
-      if (t < t_end) {
-        const int blk = blk_sh[(t - t0) >> 4];
-        kv[r] = *reinterpret_cast<const uint4*>(kbase + (size_t)blk * blk_stride +
-                                                (size_t)(t & 15) * a.d);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < UNR; ++r) {
-      float s = dot8(qb, kv[r]);
-#pragma unroll
-      for (int off = LPT / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      const int t = base + r * TPI + lane / LPT;
-      if (sub == 0 && t < t_end) {
-        srow[t] = s;
-        const uint32_t key = order_key(s);
-        atomicAdd(&hist[key >> kDigit1Shift], 1u);
-        kmax = key > kmax ? key : kmax;
-      }
-    }
-  }
+  int base = t0 + wave * WAVE_TOK;
+  for (; base + WAVE_TOK <= t_end; base += WG_TOK)
+    index_iteration<LPT, true>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, srow, hist, kmax,
+                               lane);
+  if (base < t_end)
+    index_iteration<LPT, false>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, srow, hist, kmax,
+                                lane);
 
   kmax = wave_max_u32(kmax);
   if (lane == 0) wmax[wave] = kmax;
