@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="1m", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="128k", help="comma list of extra workloads ('' = none)")
+    ap.add_argument("--also", default="128k", help="comma list of extra workloads, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -262,7 +262,7 @@ def main():
     res = run_gpu(args, args.workload, args.steps, args.warmup)
     main_sum = summarize(res, args.workload)
     also = {}
-    for name in [w for w in args.also.split(",") if w and w != args.workload]:
+    for name in [w for w in args.also.split(",") if w and w not in ("none", args.workload)]:
         r2 = run_gpu(args, name, args.steps, args.warmup)
         s2 = summarize(r2, name)
         also[name] = dict(workload=WORKLOADS[name], value=s2["value"], unit="KV-tokens/s/layer",
