@@ -1,0 +1,112 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (default split-K: one split per 4096-token chunk).
+
+The oracle checks sampled (sequence, kv head) units one by one: scores of
+every token of the unit, bit-exact selection given the oracle's float32 scores
+and normaliser, attention given the oracle's selection, and the fused decode
+output.  The rest of the output is checked through properties that hold at any
+size (finite, bounded by max|V|, identical on a second run).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_approx_amd import ssa, synth
+from oracle import ssa_oracle as orc
+
+from gpu_helpers import gpu_sets, jaccard, say, score_tolerance_ok, selection_arrays
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def unit_host(wl, b, h):
+    """Oracle inputs of one unit: q group [G, d], K and V rows [L, d] gathered
+    through the block table by the oracle's own paging rule."""
+    G = wl.Hq // wl.Hkv
+    qg = wl.q[b, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+    kc = wl.k_cache[:, h:h + 1].float().cpu().numpy()
+    vc = wl.v_cache[:, h:h + 1].float().cpu().numpy()
+    bt = wl.block_table[b].cpu().numpy().astype(np.int64)
+    L = wl.lens[b]
+    return qg, orc.gather_rows(kc, bt, 0, L), orc.gather_rows(vc, bt, 0, L)
+
+
+def check_fullsize(name, units):
+    wl = synth.make_workload(name, DEV)
+    say(f"[full] workload={name} B={wl.B} L={wl.lens[:4]}{'...' if wl.B > 4 else ''} units={units}")
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    scale = 1.0 / math.sqrt(wl.d)
+    G = wl.Hq // wl.Hkv
+    ws = ssa.alloc_workspace(p, DEV)
+    out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                     wl.sample_budget, wl.seed, workspace=ws).clone()
+    out2 = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                      wl.sample_budget, wl.seed, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "decode is not bitwise reproducible"
+    vmax_all = float(wl.v_cache.float().abs().max())
+    assert torch.isfinite(out).all() and float(out.abs().max()) <= vmax_all * (1 + 1e-6)
+    sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
+    torch.cuda.synchronize()
+
+    s32 = torch.zeros((wl.B, wl.Hkv, wl.max_seq_len), dtype=torch.float32)
+    w_in = torch.zeros((wl.B, wl.Hkv), dtype=torch.float32)
+    sels, inputs = {}, {}
+    for b, h in units:
+        qg, K, V = unit_host(wl, b, h)
+        inputs[(b, h)] = (qg, K, V)
+        s64 = orc.approx_scores(qg, K, wl.pair_begin, wl.pair_count, scale)
+        ok, ratio = score_tolerance_ok(sc[b, h, :s64.size].cpu().numpy(), s64)
+        assert ok, f"scores out of tolerance at {(b, h)} ({ratio})"
+        sel = orc.select_unit(s64.astype(np.float32), int(wl.topk[b]), int(wl.sample_budget[b]),
+                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h)
+        sels[(b, h)] = sel
+        s32[b, h, :s64.size] = torch.from_numpy(s64.astype(np.float32))
+        w_in[b, h] = float(sel["W"])
+        say(f"[full] {name} unit {(b, h)} scores ok (err/bound {ratio:.3g}); "
+            f"oracle |S|={sel['S'].size} |R|={sel['R'].size}")
+    si, sl, sn, _ = ssa.select(p, s32.to(DEV), wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                               w_in=w_in.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    si, sl, sn = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy()
+    for (b, h), sel in sels.items():
+        S, R, _ = gpu_sets(si, sl, sn, b, h)
+        assert np.array_equal(S, sel["S"]) and np.array_equal(R, sel["R"]), (b, h)
+    say(f"[full] {name} selection bit-exact on {len(units)} units")
+    ai, al, ac = selection_arrays(p, sels, DEV)
+    att = ssa.attend(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, ai, al, ac,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    att = att.double().cpu().numpy()
+    got = out.double().cpu().numpy()
+    for (b, h), sel in sels.items():
+        qg, K, V = inputs[(b, h)]
+        o = orc.attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
+        bound = 2e-3 * float(np.abs(V).max())
+        err_a = float(np.abs(att[b, h * G:(h + 1) * G] - o).max())
+        err_e = float(np.abs(got[b, h * G:(h + 1) * G] - o).max())
+        assert err_a <= bound, f"attention out of tolerance at {(b, h)}: {err_a} > {bound}"
+        assert err_e <= bound, f"fused decode out of tolerance at {(b, h)}: {err_e} > {bound}"
+        say(f"[full] {name} unit {(b, h)} attention err/bound {err_a / bound:.3g}, "
+            f"fused decode err/bound {err_e / bound:.3g}")
+
+
+def test_fullsize_1m():
+    check_fullsize("1m", [(0, 0), (0, 5)])
+
+
+def test_fullsize_128k():
+    check_fullsize("128k", [(0, 1), (3, 7)])
+
+
+def test_fullsize_32k():
+    check_fullsize("32k", [(0, 2)])
+
+
+def test_fullsize_batched():
+    check_fullsize("batched", [(0, 0), (17, 3), (31, 6)])
