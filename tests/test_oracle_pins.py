@@ -127,6 +127,25 @@ def test_uniforms_are_uniform():
     assert np.all(np.floor(u * 2**24) == u * 2**24)
 
 
+# ---------------------------------------------------------------- paging
+
+def test_gather_rows_follows_the_block_table():
+    """Brute force: write each token's own position into its paged slot with
+    plain loops, then gather it back."""
+    rng = np.random.default_rng(4)
+    L, Hkv, d = 77, 3, 4
+    nblk = (L + 15) // 16
+    phys = rng.permutation(nblk + 5)[:nblk]
+    cache = np.full((nblk + 5, Hkv, 16, d), -1.0)
+    for j in range(L):
+        for h in range(Hkv):
+            cache[phys[j // 16], h, j % 16, :] = [j, h, j % 16, phys[j // 16]]
+    for h in range(Hkv):
+        rows = orc.gather_rows(cache, phys, h, L)
+        assert rows.shape == (L, d)
+        assert np.array_equal(rows[:, 0], np.arange(L)) and np.all(rows[:, 1] == h)
+
+
 # ---------------------------------------------------------------- ranking
 
 def test_order_key_is_monotone():
