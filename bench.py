@@ -96,6 +96,7 @@ def measured_traffic(workload):
 
 
 def run_gpu(args, name, steps, warmup, with_stage_events=True):
+    """Times `steps` decode steps (after `warmup` untimed ones) of a workload."""
     import torch
 
     from long_context_sparse_approx_amd import ssa, synth
@@ -118,26 +119,63 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
 
     hip = Hip()
     nst = len(ssa.STAGES)
-    evs = []
-    for _ in range(steps):
-        arr = (ctypes.c_void_p * (2 * nst))(*[hip.event() for _ in range(2 * nst)])
-        evs.append(arr)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ssa.decode(*call, out=out, workspace=ws, stream=stream,
-                   events=ctypes.addressof(evs[i]) if with_stage_events else None)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ix = ssa.STAGES.index("index")
+
+    def event_arrays(n, stages):
+        arrs = []
+        for _ in range(n):
+            evs = [None] * (2 * nst)
+            for k in stages:
+                evs[2 * k], evs[2 * k + 1] = hip.event(), hip.event()
+            arrs.append((ctypes.c_void_p * (2 * nst))(*evs))
+        return arrs
+
+    def timed_loop(arrs, graphs=None):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if graphs is not None:
+                graphs[i % len(graphs)].replay()
+            else:
+                ssa.decode(*call, out=out, workspace=ws, stream=stream,
+                           events=ctypes.addressof(arrs[i]) if arrs else None)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    # Timed region: K whole steps; HIP events bracket only the indexer launch
+    # (on the decode stream), for its roofline.
+    graphs = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ssa.decode(*call, out=out, workspace=ws, stream=torch.cuda.current_stream())
+        graphs = [g]
+        for _ in range(warmup):
+            g.replay()
+        idx_arrs = None
+    else:
+        idx_arrs = event_arrays(steps, [ix])
+    ms_step = timed_loop(idx_arrs, graphs)
+    idx_ms = None
+    if idx_arrs:
+        idx_ms = sum(hip.elapsed_ms(a[2 * ix], a[2 * ix + 1]) for a in idx_arrs) / steps
+    # Separate pass (not the timed region): every stage bracketed by events.
     stage_ms = {s: 0.0 for s in ssa.STAGES}
     gpu_ms = 0.0
-    for arr in evs:
-        for k, s in enumerate(ssa.STAGES):
-            stage_ms[s] += hip.elapsed_ms(arr[2 * k], arr[2 * k + 1]) / steps
-        gpu_ms += hip.elapsed_ms(arr[0], arr[2 * nst - 1]) / steps
-    for arr in evs:
-        for e in arr:
-            hip.destroy(e)
+    if with_stage_events:
+        all_arrs = event_arrays(steps, range(nst))
+        timed_loop(all_arrs)
+        for arr in all_arrs:
+            for k, s in enumerate(ssa.STAGES):
+                stage_ms[s] += hip.elapsed_ms(arr[2 * k], arr[2 * k + 1]) / steps
+            gpu_ms += hip.elapsed_ms(arr[0], arr[2 * nst - 1]) / steps
+        for arr in all_arrs:
+            for e in arr:
+                hip.destroy(e)
+    for arr in idx_arrs or []:
+        hip.destroy(arr[2 * ix])
+        hip.destroy(arr[2 * ix + 1])
+    del graphs
 
     # Selected-set sizes of this step (deterministic: same kernels, same inputs).
     sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
@@ -148,13 +186,13 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
     del sc
     torch.cuda.synchronize()
 
-    ms_step = (t1 - t0) * 1e3 / steps
     tokens = float(sum(wl.lens))
     d = wl.d
     idx_bytes = tokens * wl.Hkv * (2 * wl.pair_count * 2)       # K pair subset
     gather_bytes = (n_det + n_smp) * 2.0 * d * 2                # K and V rows
     score_bytes = tokens * wl.Hkv * 4 * 4                       # 1 write + 3 reads
-    res = dict(wl=wl, p=p, ms_step=ms_step, gpu_ms=gpu_ms, stage_ms=stage_ms, tokens=tokens,
+    res = dict(wl=wl, p=p, ms_step=ms_step, idx_ms=idx_ms, gpu_ms=gpu_ms, stage_ms=stage_ms,
+               tokens=tokens,
                idx_bytes=idx_bytes, gather_bytes=gather_bytes, score_bytes=score_bytes,
                n_det=n_det, n_smp=n_smp, t_gen=t_gen)
     return res
@@ -210,13 +248,14 @@ def cpu_baseline(wl, budget_s=15.0):
 
 def summarize(res, workload):
     st = res["stage_ms"]
-    t_idx = st["index"] * 1e-3
-    achieved = res["idx_bytes"] / t_idx / 1e9
-    traffic = measured_traffic(workload)
-    roof = dict(bound="hbm", kernel="indexer", achieved=round(achieved, 1),
-                peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
-                traffic=traffic, algorithmic_bytes_per_launch=res["idx_bytes"],
-                launch_us=round(st["index"] * 1e3, 2))
+    roof = None
+    if res["idx_ms"]:
+        achieved = res["idx_bytes"] / (res["idx_ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", kernel="indexer", achieved=round(achieved, 1),
+                    peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
+                    traffic=measured_traffic(workload),
+                    algorithmic_bytes_per_launch=res["idx_bytes"],
+                    launch_us=round(res["idx_ms"] * 1e3, 2))
     step_s = res["ms_step"] * 1e-3
     algo_total = res["idx_bytes"] + res["gather_bytes"]
     return dict(
@@ -224,7 +263,8 @@ def summarize(res, workload):
         stages_us={k: round(v * 1e3, 2) for k, v in st.items()},
         gpu_step_us=round(res["gpu_ms"] * 1e3, 2),
         hbm_gbps_algorithmic_step=round(algo_total / step_s / 1e9, 1),
-        gather_gbps_algorithmic=round(res["gather_bytes"] / (st["attend"] * 1e-3) / 1e9, 1),
+        gather_gbps_algorithmic=(round(res["gather_bytes"] / (st["attend"] * 1e-3) / 1e9, 1)
+                                 if st["attend"] > 0 else None),
         selected=dict(deterministic=res["n_det"], sampled=res["n_smp"]),
     )
 
@@ -238,6 +278,10 @@ def main():
     ap.add_argument("--also", default="128k", help="comma list of extra workloads, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-stage-events", action="store_true",
+                    help="skip the separate per-stage breakdown pass")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (no indexer events)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -259,11 +303,11 @@ def main():
         print(f"copy calibration: {n} bytes read + {n} bytes written per launch", file=sys.stderr)
         del a, b
 
-    res = run_gpu(args, args.workload, args.steps, args.warmup)
+    res = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events)
     main_sum = summarize(res, args.workload)
     also = {}
     for name in [w for w in args.also.split(",") if w and w not in ("none", args.workload)]:
-        r2 = run_gpu(args, name, args.steps, args.warmup)
+        r2 = run_gpu(args, name, args.steps, args.warmup, not args.no_stage_events)
         s2 = summarize(r2, name)
         also[name] = dict(workload=WORKLOADS[name], value=s2["value"], unit="KV-tokens/s/layer",
                           ms_per_step=s2["ms_per_step"], roofline=s2["roofline"],
