@@ -248,21 +248,20 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   }
 }
 
-// Merge of the split states of one (sequence, query head):
+// Merge of the split states of one (sequence, query head), for one 64-dim
+// slice of the head (grid: B*Hq x d/64):
 //   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
 // in a fixed order (deterministic).  Each of the 4 waves takes every 4th
-// split; a lane owns d/64 consecutive dims, so one split's acc row is one
-// contiguous wave-wide load.
+// split; lane = dim, so one split's slice is one contiguous wave-wide load.
 constexpr int kMT = 256;
 
-template <int D>
 __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
-  constexpr int DPL = D / 64;
   __shared__ float red[kMT];
-  __shared__ float accsh[4][D];
+  __shared__ float accsh[4][64];
   const int bh = blockIdx.x;
+  const int D = a.d;
+  const int dim = blockIdx.y * 64 + (threadIdx.x & 63);
   const int ns = a.nsplit;
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const float* base = a.part + (size_t)bh * ns * (D + 2);
   float mx = -INFINITY;
@@ -288,23 +287,19 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
     __syncthreads();
   }
   const float denom = red[0];
-  float o[DPL];
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) o[j] = 0.0f;
-#pragma unroll 4
+  float o = 0.0f;
+#pragma unroll 8
   for (int s = wave; s < ns; s += 4) {
     const float* p = base + (size_t)s * (D + 2);
     const float m = p[D];
     const float e = (m != -INFINITY) ? __expf(m - mstar) : 0.0f;
-#pragma unroll
-    for (int j = 0; j < DPL; ++j) o[j] += e * p[lane * DPL + j];
+    o += e * p[dim];
   }
-#pragma unroll
-  for (int j = 0; j < DPL; ++j) accsh[wave][lane * DPL + j] = o[j];
+  accsh[wave][threadIdx.x & 63] = o;
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int dim = threadIdx.x;
-    const float t = ((accsh[0][dim] + accsh[1][dim]) + accsh[2][dim]) + accsh[3][dim];
+  if (threadIdx.x < 64) {
+    const float t = ((accsh[0][threadIdx.x] + accsh[1][threadIdx.x]) + accsh[2][threadIdx.x]) +
+                    accsh[3][threadIdx.x];
     const float res = (mstar == -INFINITY || denom <= 0.0f) ? 0.0f : t / denom;
     if (a.out_dtype == SSA_BF16)
       reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + dim] = (uint16_t)f32_to_bf16_bits(res);
@@ -327,12 +322,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
-  if (a.d == 128)
-    merge_kernel<128><<<a.B * a.Hq, kMT, 0, stream>>>(a);
-  else if (a.d == 64)
-    merge_kernel<64><<<a.B * a.Hq, kMT, 0, stream>>>(a);
-  else
-    return hipErrorInvalidValue;
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+  merge_kernel<<<dim3(a.B * a.Hq, a.d / 64), kMT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -21,6 +21,14 @@
 // needed and the attention stage splits work along chunk boundaries.  Every
 // sum has a fixed order and only integer atomics are used: results are
 // bitwise reproducible.
+//
+// Only one pass reads every score (the filter).  Besides the threshold-digit
+// candidates and the tail weights it lists, per chunk, the tokens above the
+// threshold digit and the tail tokens that pass a necessary inclusion test,
+// fl(u_j * W_lb) < fl(m * w_j), with W_lb <= W a lower bound of the
+// normaliser taken from the first-digit histogram (u_j * W_lb <= u_j * W and
+// rounding is monotone, so no token that the exact test would include is
+// dropped).  The final sample pass only visits these lists.
 #include "ssa_device.h"
 #include "ssa_launch.h"
 
@@ -46,31 +54,46 @@ __device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, in
 }
 
 // ------------------------------------------------------------------ threshold
-// First radix digit of the k-th largest key of every unit, from the unit's
-// first-digit histogram (one workgroup per unit).
+// Per unit, from the first-digit histogram: the digit of the k-th largest key
+// and a lower bound of W.  Every token whose first digit is below b1 is a
+// tail token and its key is at least the smallest key of its digit, so
+//   W >= sum_{digit < b1} count(digit) * exp(lowest score of digit - M);
+// the sum uses the specified exp (monotone up to ~1 ulp) and is shrunk by
+// 2^-10 to absorb that and the final rounding.
 __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ int scan_scr[kNT / 64];
   __shared__ int pair[2];
+  __shared__ double dscr[kNT / 64];
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
   const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
-  if (p.dense || p.k_eff == 0 || p.L == 0) {
-    if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0};
+  if (p.dense || p.L == 0) {
+    if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0};
     return;
   }
   for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = a.hist1[(size_t)u * kBins + i];
   __syncthreads();
-  int b1, rem;
-  find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
-  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, rem};
+  int b1 = kBins, rem = 0;
+  if (p.k_eff > 0) find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
+  const float M = key_to_float(a.maxkey[u]);
+  double lb = 0.0;
+  for (int bin = threadIdx.x; bin < b1; bin += kNT) {
+    const uint32_t n = hist[bin];
+    const float lo = key_to_float((uint32_t)bin << kDigit1Shift);
+    if (n && lo == lo) lb += (double)n * (double)sexp(lo - M);
+  }
+  lb = block_sum_f64<kNT>(lb, dscr);
+  float wlb = (float)(lb * (1.0 - 0x1.0p-10));
+  if (a.w_in) wlb = fminf(wlb, a.w_in[u]);
+  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, rem, wlb, 0};
 }
 
 // ------------------------------------------------------------------ filter
-// Per chunk: tokens whose first digit is above the unit's threshold digit are
-// in the deterministic set; tokens on the threshold digit become candidates
-// (written in index order, second-digit histogram updated); tokens below it
-// are tail tokens, whose weights are summed here in fp64.
+// Per chunk: tokens whose first digit is above b1 are listed (deterministic
+// set); tokens on b1 become candidates (index order, second-digit histogram);
+// tokens below b1 are tail tokens: their weights are summed in fp64 for W and
+// those passing the necessary inclusion test are listed with their weight.
 __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   __shared__ float sh[kChunk];
   __shared__ int scan_scr[kNT / 64];
@@ -79,42 +102,82 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   const int c = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
+  const int h = u - b * a.Hkv;
   const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
-  const int b1 = a.thresh[u].b1;     // 2048 when there is no deterministic set
+  const Thresh1 t1 = a.thresh[u];
+  const int b1 = t1.b1;              // 2048 when there is no deterministic set
   const float M = key_to_float(a.maxkey[u]);
+  const bool sampling = p.m > 0 && p.L - p.k_eff > 0;
+  const float mf = (float)p.m;
+  const uint64_t seed = a.seed[b];
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
 
   const int tb = threadIdx.x * kPer;
-  uint32_t candmask = 0u;
+  uint32_t candmask = 0u, abovemask = 0u, sampmask = 0u;
   double wsum = 0.0;
   uint32_t keys[kPer];
+  float w[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const float s = sh[tb + i];
-    const uint32_t key = order_key(s);
-    keys[i] = key;
-    const int bin = (int)(key >> kDigit1Shift);
-    if (c0 + tb + i < p.L) {
-      if (bin == b1)
-        candmask |= 1u << i;
-      else if (bin < b1)
-        wsum += (double)sexp(s - M);
+  for (int g = 0; g < kPer / 4; ++g) {
+    uint32_t tail4 = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const float s = sh[tb + i];
+      const uint32_t key = order_key(s);
+      keys[i] = key;
+      w[i] = 0.0f;
+      const int bin = (int)(key >> kDigit1Shift);
+      if (c0 + tb + i < p.L) {
+        if (bin > b1) {
+          abovemask |= 1u << i;
+        } else if (bin == b1) {
+          candmask |= 1u << i;
+        } else {
+          w[i] = sexp(s - M);
+          wsum += (double)w[i];
+          tail4 |= 1u << r;
+        }
+      }
+    }
+    if (sampling && tail4) {
+      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
+      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        if ((tail4 >> r) & 1u)
+          if (uniform24(words[r]) * t1.wlb < mf * w[i]) sampmask |= 1u << i;
+      }
     }
   }
   int total;
   const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
+  int lst_tot;
+  const int lst = block_exclusive_scan<kNT>(__popc(abovemask) | (__popc(sampmask) << 16),
+                                            scan_scr, &lst_tot);
+  const int n_above = lst_tot & 0xffff;
   int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
   uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
-  int w = off;
+  int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
+  float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
+  int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
+    const int t = c0 + tb + i;
     if (candmask & (1u << i)) {
-      cidx[w] = c0 + tb + i;
-      ckey[w] = keys[i];
-      ++w;
+      cidx[wc] = t;
+      ckey[wc] = keys[i];
+      ++wc;
       atomicAdd(&a.hist2[(size_t)u * kBins + ((keys[i] >> kDigit2Shift) & (kBins - 1))], 1u);
+    }
+    if (abovemask & (1u << i)) lidx[wa++] = t;
+    if (sampmask & (1u << i)) {
+      lidx[ws] = t;
+      lw[ws] = w[i];
+      ++ws;
     }
   }
   const double wtot = block_sum_f64<kNT>(wsum, dscr);
@@ -122,6 +185,8 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
     const size_t ci = (size_t)u * a.nchunk + c;
     a.cand_cnt[ci] = total;
     a.wpart[ci] = wtot;
+    a.list_cnt[2 * ci] = n_above;
+    a.list_cnt[2 * ci + 1] = lst_tot >> 16;
   }
 }
 
@@ -193,13 +258,37 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)b2;
         for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
         __syncthreads();
-        for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-          const int n = a.cand_cnt[cu + c];
-          const uint32_t* ck = ckeys + (size_t)c * kChunk;
-#pragma unroll 4
-          for (int i = csub; i < n; i += tpc) {
-            const uint32_t key = ck[i];
+        // When every thread serves at most one chunk (nc <= kRT / tpc), its
+        // first kKeep candidate keys stay in registers for the second pass.
+        constexpr int kKeep = 16;
+        const bool one_chunk = nc <= cstep;
+        const int cm = threadIdx.x / tpc;
+        const int nm = (one_chunk && cm < nc) ? a.cand_cnt[cu + cm] : 0;
+        const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
+        uint32_t kr[kKeep];
+        if (one_chunk) {
+#pragma unroll
+          for (int k = 0; k < kKeep; ++k) {
+            const int i = csub + k * tpc;
+            kr[k] = i < nm ? ckm[i] : 0u;
+          }
+#pragma unroll
+          for (int k = 0; k < kKeep; ++k) {
+            const int i = csub + k * tpc;
+            if (i < nm && (kr[k] >> kDigit2Shift) == prefix) atomicAdd(&hist[kr[k] & (kBins3 - 1)], 1u);
+          }
+          for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
+            const uint32_t key = ckm[i];
             if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+          }
+        } else {
+          for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
+            const int n = a.cand_cnt[cu + c];
+            const uint32_t* ck = ckeys + (size_t)c * kChunk;
+            for (int i = csub; i < n; i += tpc) {
+              const uint32_t key = ck[i];
+              if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+            }
           }
         }
         __syncthreads();
@@ -207,19 +296,37 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         st.tkey = (prefix << kDigit2Shift) | (uint32_t)b3;
         st.ties_needed = rem3;
         // Ties on the threshold key per chunk (integer), and the weight of the
-        // candidates strictly below it.
+        // candidates strictly below it (each thread over its fixed items, in
+        // order, then a fixed tree).
         double cs = 0.0;
-        for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-          const int n = a.cand_cnt[cu + c];
-          const uint32_t* ck = ckeys + (size_t)c * kChunk;
+        if (one_chunk) {
           int ties = 0;
-#pragma unroll 4
-          for (int i = csub; i < n; i += tpc) {
-            const uint32_t key = ck[i];
+#pragma unroll
+          for (int k = 0; k < kKeep; ++k) {
+            const int i = csub + k * tpc;
+            if (i < nm) {
+              ties += kr[k] == st.tkey;
+              if (kr[k] < st.tkey) cs += (double)sexp(key_to_float(kr[k]) - st.M);
+            }
+          }
+          for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
+            const uint32_t key = ckm[i];
             ties += key == st.tkey;
             if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
           }
-          if (ties) atomicAdd(&ties_sh[c], ties);
+          if (ties) atomicAdd(&ties_sh[cm], ties);
+        } else {
+          for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
+            const int n = a.cand_cnt[cu + c];
+            const uint32_t* ck = ckeys + (size_t)c * kChunk;
+            int ties = 0;
+            for (int i = csub; i < n; i += tpc) {
+              const uint32_t key = ck[i];
+              ties += key == st.tkey;
+              if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
+            }
+            if (ties) atomicAdd(&ties_sh[c], ties);
+          }
         }
         ctail = block_sum_f64<kRT>(cs, dscr);
         int run = 0;
@@ -258,22 +365,44 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 }
 
 // ------------------------------------------------------------------ sample
-// Per chunk: decide membership of every token (deterministic set, sampled
-// tail token, or neither) and write the chunk's segment: deterministic tokens
-// in ascending order, then sampled tokens in ascending order.  With emit_rows
-// the segment holds cache row numbers (for the fused attention stage) instead
-// of positions.
+// Per chunk: membership of the listed tokens only -- above-threshold tokens
+// and candidates above the threshold key (or within the tie quota) form the
+// deterministic set; the other candidates and the listed sampling candidates
+// take the exact inclusion test with the final W.  The chunk's segment is then
+// written from an LDS membership map: deterministic tokens ascending, then
+// sampled tokens ascending.  With emit_rows the segment holds cache row
+// numbers (for the fused attention stage) instead of positions.
+__device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, int b, int h,
+                                           int t, float w, int c0, uint8_t* flag, float* lwsh) {
+  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2);
+  const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+  const float mw = (float)st.m * w;
+  if (uniform24(words[t & 3]) * st.W < mw) {
+    flag[t - c0] = 2;
+    lwsh[t - c0] = -logf(fminf(1.0f, mw / st.W));
+  }
+}
+
 __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
-  __shared__ float sh[kChunk];
+  __shared__ uint8_t flag[kChunk];  // 0 none, 1 deterministic, 2 sampled
+  __shared__ float lwsh[kChunk];
+  __shared__ int blk_sh[kChunk / kBlockTokens];
   __shared__ int scan_scr[kNT / 64];
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
   const int h = u - b * a.Hkv;
-  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   const int c0 = c * kChunk;
-  int32_t* cnt = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
+  const size_t ci = (size_t)u * a.nchunk + c;
+  // Independent loads first: unit state, per-chunk counts, the chunk's block ids.
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  const int n_above = a.list_cnt[2 * ci];
+  const int n_samp = a.list_cnt[2 * ci + 1];
+  const int ncand = a.cand_cnt[ci];
+  const int before = a.ties_before[ci];
+  const uint64_t seed = a.seed[b];
+  int32_t* cnt = a.sel_cnt + ci * 2;
   if (c0 >= st.L || (st.flags & kFlagEmpty)) {
     if (threadIdx.x == 0) {
       cnt[0] = 0;
@@ -281,72 +410,56 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     }
     return;
   }
-  stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, st.L, sh);
+  const int nvalid = min(kChunk, st.L - c0);
   const bool dense = st.flags & kFlagDense;
-  const bool notopk = st.flags & kFlagNoTopk;
-  const int tb = threadIdx.x * kPer;
-
-  float s[kPer];
-  uint32_t validmask = 0u, smask = 0u, tiemask = 0u;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    s[i] = sh[tb + i];
-    const bool valid = c0 + tb + i < st.L;
-    validmask |= (uint32_t)valid << i;
-    if (valid && !dense && !notopk) {
-      const uint32_t key = order_key(s[i]);
-      smask |= (uint32_t)(key > st.tkey) << i;
-      tiemask |= (uint32_t)(key == st.tkey) << i;
-    }
+  const bool sampling = st.flags & kFlagSample;
+  if (a.emit_rows && threadIdx.x < (nvalid + kBlockTokens - 1) / kBlockTokens) {
+    int blk = a.block_table[(size_t)b * a.max_blocks + c0 / kBlockTokens + threadIdx.x];
+    blk_sh[threadIdx.x] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
   }
-  if (dense) smask = validmask;
-  // Tokens on the threshold key join the deterministic set in index order
-  // until the quota is met.  Only a chunk that straddles the quota needs the
-  // ranks; the branch is uniform over the workgroup.
-  if (!dense && !notopk) {
-    const size_t ci = (size_t)u * a.nchunk + c;
-    const int before = a.ties_before[ci];
-    const int here = a.tiecnt[ci];
-    if (here > 0) {
-      if (before + here <= st.ties_needed) {
-        smask |= tiemask;
-      } else if (before < st.ties_needed) {
-        int tot_unused;
-        int rank = before + block_exclusive_scan<kNT>(__popc(tiemask), scan_scr, &tot_unused);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          if (tiemask & (1u << i)) {
-            if (rank < st.ties_needed) smask |= 1u << i;
-            ++rank;
+  for (int i = threadIdx.x; i < kChunk; i += kNT) flag[i] = (dense && i < nvalid) ? 1 : 0;
+  __syncthreads();
+  if (!dense) {
+    const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
+    const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
+    for (int i = threadIdx.x; i < n_above; i += kNT) flag[lidx[i] - c0] = 1;
+    if (sampling)
+      for (int i = threadIdx.x; i < n_samp; i += kNT)
+        sample_one(st, seed, b, h, lidx[n_above + i], lw[n_above + i], c0, flag, lwsh);
+    if (!(st.flags & kFlagNoTopk)) {
+      // Threshold-digit candidates, in index order: key above T -> S; key == T
+      // -> S while the tie quota lasts; otherwise a tail token.
+      const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
+      const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+      int run = 0;  // ties seen in earlier rounds of this loop
+      for (int base = 0; base < ncand; base += kNT) {
+        const int i = base + threadIdx.x;
+        const bool v = i < ncand;
+        const uint32_t key = v ? ckey[i] : 0u;
+        const bool tie = v && key == st.tkey;
+        int tot;
+        const int rank = before + run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &tot);
+        run += tot;
+        if (v) {
+          const int t = cidx[i];
+          if (key > st.tkey || (tie && rank < st.ties_needed)) {
+            flag[t - c0] = 1;
+          } else if (sampling) {
+            sample_one(st, seed, b, h, t, sexp(key_to_float(key) - st.M), c0, flag, lwsh);
           }
         }
       }
     }
   }
-  const uint32_t tailmask = validmask & ~smask;
-  uint32_t rmask = 0u;
-  float logw[kPer];
-  if ((st.flags & kFlagSample) && tailmask) {
-    const uint64_t seed = a.seed[b];
-    const float mf = (float)st.m;
+  __syncthreads();
+  // Compaction from the membership map (16 consecutive positions per thread).
+  const int tb = threadIdx.x * kPer;
+  uint32_t smask = 0u, rmask = 0u;
 #pragma unroll
-    for (int g = 0; g < kPer / 4; ++g) {
-      if (((tailmask >> (4 * g)) & 0xfu) == 0u) continue;
-      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
-      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r;
-        if (!(tailmask & (1u << i))) continue;
-        const float w = sexp(s[i] - st.M);
-        const float mw = mf * w;
-        const float uw = uniform24(words[r]) * st.W;
-        if (uw < mw) {
-          rmask |= 1u << i;
-          logw[i] = -logf(fminf(1.0f, mw / st.W));
-        }
-      }
-    }
+  for (int i = 0; i < kPer; ++i) {
+    const uint8_t f = flag[tb + i];
+    smask |= (uint32_t)(f == 1) << i;
+    rmask |= (uint32_t)(f == 2) << i;
   }
   // One scan for both counts: deterministic count in the low 16 bits,
   // sampled count in the high 16 bits (each at most 4096).
@@ -357,26 +470,20 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   const int totR = packed_tot >> 16;
   int32_t* sidx = a.sel_idx + (size_t)u * a.seg_ld + c0;
   float* slw = a.sel_logw + (size_t)u * a.seg_ld + c0;
-  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
   int ws = packed & 0xffff, wr = totS + (packed >> 16);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const uint32_t bit = 1u << i;
     if ((smask | rmask) & bit) {
       const int t = c0 + tb + i;
-      int v = t;
-      if (a.emit_rows) {
-        int blk = btrow[t >> 4];
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        v = (blk * a.Hkv + h) * kBlockTokens + (t & 15);
-      }
+      const int v = a.emit_rows ? (blk_sh[(tb + i) >> 4] * a.Hkv + h) * kBlockTokens + (t & 15) : t;
       if (smask & bit) {
         sidx[ws] = v;
         slw[ws] = 0.0f;
         ++ws;
       } else {
         sidx[wr] = v;
-        slw[wr] = logw[i];
+        slw[wr] = lwsh[tb + i];
         ++wr;
       }
     }

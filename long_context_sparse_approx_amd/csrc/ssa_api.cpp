@@ -69,7 +69,8 @@ Dims dims_of(const ssa_params* p) {
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, maxkey, thresh, cand_idx, cand_key, cand_cnt, wpart, tiecnt,
+  size_t scores, hist1, hist2, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
+      list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
 };
 
@@ -90,6 +91,9 @@ Layout layout_of(const Dims& d) {
   l.cand_idx = take(U * SEG * 4);
   l.cand_key = take(U * SEG * 4);
   l.cand_cnt = take(U * NC * 4);
+  l.list_idx = take(U * SEG * 4);
+  l.list_w = take(U * SEG * 4);
+  l.list_cnt = take(U * NC * 2 * 4);
   l.wpart = take(U * NC * 8);
   l.tiecnt = take(U * NC * 4);
   l.ties_before = take(U * NC * 4);
@@ -176,6 +180,9 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.cand_idx = at<int32_t>(ws, l.cand_idx);
   a.cand_key = at<uint32_t>(ws, l.cand_key);
   a.cand_cnt = at<int32_t>(ws, l.cand_cnt);
+  a.list_idx = at<int32_t>(ws, l.list_idx);
+  a.list_w = at<float>(ws, l.list_w);
+  a.list_cnt = at<int32_t>(ws, l.list_cnt);
   a.wpart = at<double>(ws, l.wpart);
   a.tiecnt = at<int32_t>(ws, l.tiecnt);
   a.ties_before = at<int32_t>(ws, l.ties_before);

@@ -7,13 +7,17 @@
 
 namespace ssa {
 
-// First radix digit of a unit's k-th largest order key, found once per unit
-// from the unit's first-digit histogram:
-//   b1  = digit of the k-th key (2048 when no deterministic set is needed),
-//   rem = rank of that key among the keys with digit b1.
+// Per-unit facts derived from the first-digit histogram before the chunk
+// passes:
+//   b1  = first digit of the k-th largest key (2048 when there is no
+//         deterministic set),
+//   rem = rank of that key among the keys with digit b1,
+//   wlb = a lower bound of the tail normaliser W (0 when unknown).
 struct Thresh1 {
   int32_t b1;
   int32_t rem;
+  float wlb;
+  int32_t pad;
 };
 
 struct IndexArgs {
@@ -43,9 +47,12 @@ struct SelectArgs {
   uint32_t* hist2;            // [U, 2048]
   uint32_t* maxkey;           // [U]
   Thresh1* thresh;            // [U]
-  int32_t* cand_idx;          // [U, seg_ld]
+  int32_t* cand_idx;          // [U, seg_ld] threshold-digit candidates per chunk
   uint32_t* cand_key;         // [U, seg_ld]
   int32_t* cand_cnt;          // [U, nchunk]
+  int32_t* list_idx;          // [U, seg_ld] per chunk: above-threshold tokens, then
+  float* list_w;              //   sampling candidates with their tail weights
+  int32_t* list_cnt;          // [U, nchunk, 2] (n_above, n_sampling_candidates)
   double* wpart;              // [U, nchunk]
   int32_t* tiecnt;            // [U, nchunk]
   int32_t* ties_before;       // [U, nchunk]
