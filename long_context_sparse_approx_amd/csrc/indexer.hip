@@ -25,8 +25,9 @@ namespace ssa {
 
 namespace {
 
-// Largest token tile of one indexer workgroup (its block ids are staged in LDS).
-constexpr int kMaxTileTokens = 8192;
+// Largest token tile of one indexer workgroup (its block offsets and its
+// scores are staged in LDS).
+constexpr int kMaxTileTokens = 4096;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -99,12 +100,15 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
 // position p of group g holds the complete scores of tokens
 // base + 8 g + p * E + e (e < E), so for LPT = 8 lane l holds token base + l
 // and the score stores are contiguous.  FULL: every token is below t_end (no
-// predication; all loads are issued back to back).
+// predication; all loads are issued back to back).  Scores go to the
+// workgroup's LDS tile buffer; the tile is written to HBM in one burst at the
+// end (interleaving small score writes with the key stream costs far more HBM
+// time than the 4 bytes per token suggest).
 template <int LPT, bool FULL>
 __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uint64_t* blk_sh,
                                                 int d, int t0, int base, int t_end,
                                                 const uint32_t* qh, const uint32_t* ql,
-                                                float* srow, uint32_t* hist, uint32_t& kmax,
+                                                float* sbuf, uint32_t* hist, uint32_t& kmax,
                                                 int lane) {
   constexpr int UNR = 8;
   constexpr int LG = LPT < 8 ? LPT : 8;
@@ -126,7 +130,7 @@ __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uin
   for (int e = 0; e < E; ++e) {
     const int t = tg + pos * E + e;
     if (writer && (FULL || t < t_end)) {
-      srow[t] = v[e];
+      sbuf[t - t0] = v[e];
       const uint32_t key = order_key(v[e]);
       atomicAdd(&hist[key >> kDigit1Shift], 1u);
       kmax = key > kmax ? key : kmax;
@@ -144,6 +148,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   // same LDS as the histogram, which is cleared once the slice is folded.
   __shared__ uint32_t hist[16 * 128];
   __shared__ uint64_t blk_sh[kMaxTileTokens / kBlockTokens];
+  __shared__ float sbuf[kMaxTileTokens];
   __shared__ uint32_t wmax[4];
   static_assert(16 * 128 >= kBins, "histogram fits the staging buffer");
   float* qsh = reinterpret_cast<float*>(hist);
@@ -209,10 +214,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   uint32_t kmax = 0u;
   int base = t0 + wave * WAVE_TOK;
   for (; base + WAVE_TOK <= t_end; base += WG_TOK)
-    index_iteration<LPT, true>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, srow, hist, kmax,
+    index_iteration<LPT, true>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, sbuf, hist, kmax,
                                lane);
   if (base < t_end)
-    index_iteration<LPT, false>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, srow, hist, kmax,
+    index_iteration<LPT, false>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, sbuf, hist, kmax,
                                 lane);
 
   kmax = wave_max_u32(kmax);
@@ -226,6 +231,19 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   for (int i = tid; i < kBins; i += 256) {
     const uint32_t c = hist[i];
     if (c) atomicAdd(&a.hist1[(size_t)u * kBins + i], c);
+  }
+  // The tile's scores, written in one burst (16-byte stores when aligned).
+  const int n = t_end - t0;
+  float* dst = srow + t0;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+    for (int i = 4 * tid; i < n; i += 4 * 256) {
+      if (i + 4 <= n)
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(sbuf + i);
+      else
+        for (int j = i; j < n; ++j) dst[j] = sbuf[j];
+    }
+  } else {
+    for (int i = tid; i < n; i += 256) dst[i] = sbuf[i];
   }
 }
 
