@@ -115,43 +115,39 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
 
   const int tb = threadIdx.x * kPer;
-  uint32_t candmask = 0u, abovemask = 0u, sampmask = 0u;
+  const int nv = p.L - (c0 + tb);  // valid tokens of this thread: min(16, max(nv, 0))
+  uint32_t candmask = 0u, abovemask = 0u, tailmask = 0u, sampmask = 0u;
   double wsum = 0.0;
   uint32_t keys[kPer];
   float w[kPer];
+  // Branch-free: every token's weight and every group's uniforms are
+  // computed; masks select what counts.
 #pragma unroll
-  for (int g = 0; g < kPer / 4; ++g) {
-    uint32_t tail4 = 0u;
+  for (int i = 0; i < kPer; ++i) {
+    const float s = sh[tb + i];
+    const uint32_t key = order_key(s);
+    keys[i] = key;
+    const int bin = (int)(key >> kDigit1Shift);
+    const bool valid = i < nv;
+    abovemask |= (uint32_t)(valid && bin > b1) << i;
+    candmask |= (uint32_t)(valid && bin == b1) << i;
+    const bool tail = valid && bin < b1;
+    tailmask |= (uint32_t)tail << i;
+    w[i] = sexp(s - M);
+    wsum += tail ? (double)w[i] : 0.0;
+  }
+  if (sampling) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * g + r;
-      const float s = sh[tb + i];
-      const uint32_t key = order_key(s);
-      keys[i] = key;
-      w[i] = 0.0f;
-      const int bin = (int)(key >> kDigit1Shift);
-      if (c0 + tb + i < p.L) {
-        if (bin > b1) {
-          abovemask |= 1u << i;
-        } else if (bin == b1) {
-          candmask |= 1u << i;
-        } else {
-          w[i] = sexp(s - M);
-          wsum += (double)w[i];
-          tail4 |= 1u << r;
-        }
-      }
-    }
-    if (sampling && tail4) {
+    for (int g = 0; g < kPer / 4; ++g) {
       const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
       const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * g + r;
-        if ((tail4 >> r) & 1u)
-          if (uniform24(words[r]) * t1.wlb < mf * w[i]) sampmask |= 1u << i;
+        sampmask |= (uint32_t)(uniform24(words[r]) * t1.wlb < mf * w[i]) << i;
       }
     }
+    sampmask &= tailmask;
   }
   int total;
   const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
@@ -250,28 +246,30 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         st.flags = kFlagNoTopk;
       } else {
         const Thresh1 t1 = a.thresh[u];
-        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist2[(size_t)u * kBins + i];
-        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
-        __syncthreads();
-        int b2, rem2, b3, rem3;
-        find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &b2, &rem2);
-        const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)b2;
-        for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
-        __syncthreads();
-        // When every thread serves at most one chunk (nc <= kRT / tpc), its
-        // first kKeep candidate keys stay in registers for the second pass.
+        // Loads that do not depend on the second digit are issued first: the
+        // histogram, this thread's candidate count and (below) its keys.
         constexpr int kKeep = 16;
         const bool one_chunk = nc <= cstep;
         const int cm = threadIdx.x / tpc;
         const int nm = (one_chunk && cm < nc) ? a.cand_cnt[cu + cm] : 0;
         const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
         uint32_t kr[kKeep];
+        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist2[(size_t)u * kBins + i];
+        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         if (one_chunk) {
 #pragma unroll
           for (int k = 0; k < kKeep; ++k) {
             const int i = csub + k * tpc;
             kr[k] = i < nm ? ckm[i] : 0u;
           }
+        }
+        __syncthreads();
+        int b2, rem2, b3, rem3;
+        find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &b2, &rem2);
+        const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)b2;
+        for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
+        __syncthreads();
+        if (one_chunk) {
 #pragma unroll
           for (int k = 0; k < kKeep; ++k) {
             const int i = csub + k * tpc;
