@@ -251,55 +251,60 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 // Merge of the split states of one (sequence, query head), for one 64-dim
 // slice of the head (grid: B*Hq x d/64):
 //   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
-// in a fixed order (deterministic).  Each of the 4 waves takes every 4th
-// split; lane = dim, so one split's slice is one contiguous wave-wide load.
+// in a fixed order (deterministic).  The split weights e^{m_s - m*} are
+// computed once into LDS; each wave then takes every kMW-th split (lane =
+// dim, so one split's slice is one contiguous wave-wide load).
 constexpr int kMT = 256;
+constexpr int kMW = kMT / 64;
+constexpr int kMaxMergeSplits = SSA_MAX_SEQ_LEN / kChunk;
 
 __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
-  __shared__ float red[kMT];
-  __shared__ float accsh[4][64];
+  __shared__ float red[kMW];
+  __shared__ float esh[kMaxMergeSplits];
+  __shared__ float accsh[kMW][64];
   const int bh = blockIdx.x;
   const int D = a.d;
-  const int dim = blockIdx.y * 64 + (threadIdx.x & 63);
-  const int ns = a.nsplit;
+  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int dim = blockIdx.y * 64 + lane;
+  const int ns = a.nsplit;
   const float* base = a.part + (size_t)bh * ns * (D + 2);
   float mx = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += kMT) mx = fmaxf(mx, base[(size_t)s * (D + 2) + D]);
-  red[threadIdx.x] = mx;
-  __syncthreads();
-  for (int w = kMT / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-    __syncthreads();
+  for (int s = threadIdx.x; s < ns; s += kMT) {
+    const float m = base[(size_t)s * (D + 2) + D];
+    esh[s] = m;
+    mx = fmaxf(mx, m);
   }
-  const float mstar = red[0];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float mstar = red[0];
+#pragma unroll
+  for (int w = 1; w < kMW; ++w) mstar = fmaxf(mstar, red[w]);
   __syncthreads();
   float den = 0.0f;
   for (int s = threadIdx.x; s < ns; s += kMT) {
-    const float* p = base + (size_t)s * (D + 2);
-    const float m = p[D];
-    if (m != -INFINITY) den += __expf(m - mstar) * p[D + 1];
-  }
-  red[threadIdx.x] = den;
-  __syncthreads();
-  for (int w = kMT / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  const float denom = red[0];
-  float o = 0.0f;
-#pragma unroll 8
-  for (int s = wave; s < ns; s += 4) {
-    const float* p = base + (size_t)s * (D + 2);
-    const float m = p[D];
+    const float m = esh[s];
     const float e = (m != -INFINITY) ? __expf(m - mstar) : 0.0f;
-    o += e * p[dim];
+    esh[s] = e;
+    den += e * base[(size_t)s * (D + 2) + D + 1];
   }
-  accsh[wave][threadIdx.x & 63] = o;
+  den = wave_sum(den);
+  if (lane == 0) red[wave] = den;
+  __syncthreads();
+  float denom = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMW; ++w) denom += red[w];
+  float o = 0.0f;
+#pragma unroll 16
+  for (int s = wave; s < ns; s += kMW) o += esh[s] * base[(size_t)s * (D + 2) + dim];
+  accsh[wave][lane] = o;
   __syncthreads();
   if (threadIdx.x < 64) {
-    const float t = ((accsh[0][threadIdx.x] + accsh[1][threadIdx.x]) + accsh[2][threadIdx.x]) +
-                    accsh[3][threadIdx.x];
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) t += accsh[w][threadIdx.x];
     const float res = (mstar == -INFINITY || denom <= 0.0f) ? 0.0f : t / denom;
     if (a.out_dtype == SSA_BF16)
       reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + dim] = (uint16_t)f32_to_bf16_bits(res);

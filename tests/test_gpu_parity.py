@@ -308,3 +308,34 @@ def test_sexp_bit_exact():
     got = y.cpu().numpy()
     ref = orc.sexp(x)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_decode_replays_from_a_hip_graph():
+    """The step enqueues kernels only (no memset or allocation), so a caller
+    can capture it; every replay must equal the eager result bitwise."""
+    wl = make_case("ragged_b2")
+    say("[graph] capture and replay")
+    p = params_of(wl)
+    ws = ssa.alloc_workspace(p, DEV)
+    eager = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                       wl.sample_budget, wl.seed, workspace=ws).clone()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                   wl.sample_budget, wl.seed, out=out, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                   wl.sample_budget, wl.seed, out=out, workspace=ws,
+                   stream=torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        del junk
