@@ -39,7 +39,9 @@ R3  Pairs: interleaved RoPE pairs (2p, 2p+1); the scored subset is a contiguous
     pair range [pair_begin, pair_begin + pair_count), the same for every head.
 R4  Ranking is done on the float32 rounding of the score, ordered by the
     float's bits (-0.0 below +0.0); ties go to the lower token index.
-R5  Dense rule: when topk + m >= L every token is read with weight 1.
+R5  Dense rule: when k + m >= L every token is read with weight 1, k being
+    the size of the deterministic stratum (min(topk, L), further capped by the
+    top-p prefix of R11 when a top-p mass is given).
 R6  Tail design: Poisson sampling.  w_j = sexp(s_j - M) with M the maximum
     score over the whole sequence, W = sum of w_j over the tail, inclusion
     probability pi_j = min(1, m * w_j / W); m is the expected sample size.
@@ -55,11 +57,20 @@ R9  sexp is a specified float32 exp (Cody-Waite reduction, degree-7 Taylor
     0 for x < -87.
 R10 Horvitz-Thompson weights: c_j = 1 on the deterministic set S and 1/pi_j on
     the sample R; output = sum c e^l v / sum c e^l over S u R.
+R11 Top-p stratum: the approximate probability mass of token j is counted in
+    integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
+    top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
+    the target is tau = ceil(p * Q), evaluated exactly.  n_p is the length of
+    the shortest prefix of the order (key descending, index ascending) whose
+    units reach tau (0 when tau = 0).  The deterministic stratum is the first
+    min(topk, n_p) tokens of that order.  Integer mass makes the prefix
+    independent of summation order.  p is clamped to [0, 1]; NaN counts as 0.
 """
 
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -70,6 +81,10 @@ __all__ = [
     "order_key",
     "topk_indices",
     "sexp",
+    "MASS_FRAC_BITS",
+    "mass_units",
+    "mass_target",
+    "topp_count",
     "philox4x32_10",
     "philox_word",
     "uniforms",
@@ -184,6 +199,50 @@ def sexp(x) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Step 2 alternative: the top-p deterministic stratum ([SSA] "Where sparse
+# attention loses quality", top-p as a deterministic option; "How SSA
+# stratifies the cache", top-p as a special case) -- reading R11
+# ---------------------------------------------------------------------------
+
+MASS_FRAC_BITS = 38
+
+
+def mass_units(w32) -> np.ndarray:
+    """floor(w * 2^38) of float32 weights in [0, 1], as uint64 (exact: the
+    scaling by a power of two and the floor are both exact in float64)."""
+    w = np.asarray(w32, dtype=_F32).astype(np.float64)
+    return np.floor(w * 2.0 ** MASS_FRAC_BITS).astype(np.uint64)
+
+
+def mass_target(p, Q: int) -> int:
+    """tau = ceil(p * Q) as an exact rational, p a float32 clamped to [0, 1]."""
+    p = float(np.float32(p))
+    if not p > 0.0:  # also NaN
+        return 0
+    if p >= 1.0:
+        return int(Q)
+    prod = Fraction(p) * int(Q)
+    return -((-prod.numerator) // prod.denominator)
+
+
+def topp_count(s32: np.ndarray, p) -> int:
+    """n_p of reading R11: length of the shortest prefix of the order whose
+    mass units reach tau = ceil(p * Q)."""
+    s32 = np.asarray(s32, dtype=_F32)
+    if s32.size == 0:
+        return 0
+    key = order_key(s32)
+    M = _F32(s32[key.argmax()])
+    q = mass_units(sexp(np.subtract(s32, M, dtype=_F32)))
+    order = np.lexsort((np.arange(key.size), ~key))
+    cum = np.cumsum(q[order], dtype=np.uint64)  # Q < 2^24 * 2^38: no overflow
+    tau = mass_target(p, int(cum[-1]))
+    if tau == 0:
+        return 0
+    return int(np.searchsorted(cum, np.uint64(tau), side="left")) + 1
+
+
+# ---------------------------------------------------------------------------
 # Step 4: counter-based uniforms (reading R8)
 # ---------------------------------------------------------------------------
 
@@ -238,13 +297,14 @@ def uniforms(seed: int, b: int, h: int, j) -> np.ndarray:
 # Steps 2-4 together: the strata of one (batch, kv head)
 # ---------------------------------------------------------------------------
 
-def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None):
+def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None, top_p=None):
     """Deterministic set S, tail T and inclusion probabilities of T.
 
     Returns a dict with S, T (ascending int64), dense (bool), M, W (float32),
     w (float32 tail weights), mw = fl(m * w) and pi = min(1, fl(mw / W)).
     ``W_in`` replaces the computed normaliser (used to feed both
-    implementations the same normaliser).
+    implementations the same normaliser).  ``top_p`` (a float, or None for
+    top-k alone) caps the deterministic stratum at the top-p prefix (R11).
     """
     s32 = np.asarray(s32, dtype=_F32)
     L = s32.size
@@ -253,11 +313,13 @@ def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None):
         return dict(S=e, T=e, dense=False, M=_F32(0), W=_F32(0), w=np.zeros(0, _F32),
                     mw=np.zeros(0, _F32), pi=np.zeros(0, _F32))
     M = _F32(s32[order_key(s32).argmax()])
-    if topk + m >= L:  # reading R5
+    k = min(topk, L)
+    if top_p is not None:
+        k = min(k, topp_count(s32, top_p))
+    if k + m >= L:  # reading R5
         e = np.zeros(0, np.int64)
         return dict(S=np.arange(L, dtype=np.int64), T=e, dense=True, M=M, W=_F32(0),
                     w=np.zeros(0, _F32), mw=np.zeros(0, _F32), pi=np.zeros(0, _F32))
-    k = min(topk, L)
     S = topk_indices(s32, k)
     in_s = np.zeros(L, bool)
     in_s[S] = True
@@ -282,9 +344,10 @@ def sample_tail(strata: dict, m: int, seed: int, b: int, h: int):
     return T[keep], strata["pi"][keep]
 
 
-def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None):
+def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None,
+                top_p=None):
     """Full selection of one (batch, kv head): dict with S, R, pi_R, M, W, dense."""
-    st = tail_stratum(s32, topk, m, W_in)
+    st = tail_stratum(s32, topk, m, W_in, top_p)
     R, pi_R = sample_tail(st, m, seed, b, h)
     return dict(S=st["S"], R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"])
 
@@ -331,12 +394,14 @@ def attend_unit(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, S, R, pi_R,
 # ---------------------------------------------------------------------------
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
-           pair_begin: int, pair_count: int, scale: float | None = None, units=None):
+           pair_begin: int, pair_count: int, scale: float | None = None, units=None,
+           top_p=None):
     """Stratified sparse decode attention for every (batch, kv head).
 
     q [B, Hq, d]; caches [num_blocks, Hkv, 16, d]; block_table [B, max_blocks];
-    seq_lens, topk, sample_budget, seed: [B] integers.  ``units`` optionally
-    restricts the work to a list of (b, h) pairs (other outputs stay zero).
+    seq_lens, topk, sample_budget, seed: [B] integers; top_p: [B] float32 or
+    None.  ``units`` optionally restricts the work to a list of (b, h) pairs
+    (other outputs stay zero).
     Returns (out [B, Hq, d] float64, info dict keyed by (b, h)).
     """
     q = np.asarray(q)
@@ -355,7 +420,9 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed
         V = gather_rows(v_cache, block_table[b], h, L)
         s64 = approx_scores(qg, K, pair_begin, pair_count, scale)
         s32 = s64.astype(_F32)
-        sel = select_unit(s32, int(topk[b]), int(sample_budget[b]), int(seed[b]), b, h)
+        tp = None if top_p is None else np.float32(top_p[b])
+        sel = select_unit(s32, int(topk[b]), int(sample_budget[b]), int(seed[b]), b, h,
+                          top_p=tp)
         out[b, h * G:(h + 1) * G, :] = attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
         info[(b, h)] = dict(scores=s64, **sel)
     return out, info
