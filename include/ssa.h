@@ -5,7 +5,9 @@
  *   1. score every cached token cheaply from a fixed subset of RoPE frequency
  *      pairs ("FASA: Frequency-aware Sparse Attention", section 3 stage 1
  *      TIP; the group's queries are averaged as in PIVOT's proxy query);
- *   2. read the top-k tokens deterministically ("Stratified Sparse Attention
+ *   2. read the top-k tokens -- or the top-p prefix, the shortest run of
+ *      highest-scoring tokens holding a fraction p of the approximate
+ *      attention mass -- deterministically ("Stratified Sparse Attention
  *      speeds up decoding 2.96x at 1M context", section "Where sparse
  *      attention loses quality");
  *   3. Poisson-sample the remaining tail with probability proportional to
@@ -41,6 +43,7 @@
  *   block_table  [B, max_blocks_per_seq]         int32: token j of sequence b is row
  *                                                j % 16 of block block_table[b][j / 16]
  *   seq_lens, topk, sample_budget [B]            int32
+ *   top_p        [B]                             f32, optional (NULL = top-k only)
  *   seed         [B]                             uint64 (one Philox key per sequence)
  *   out          [B, Hq, d]                      f32 or bf16 (params.out_dtype)
  *
@@ -81,7 +84,8 @@ extern "C" {
 /* Stage indices for ssa_decode_timed(). */
 #define SSA_STAGE_INIT 0     /* clear histograms and maxima                        */
 #define SSA_STAGE_INDEX 1    /* approximate scores + first-digit histogram + max   */
-#define SSA_STAGE_FILTER 2   /* first-digit threshold, candidates, tail weight sums */
+#define SSA_STAGE_FILTER 2   /* (top-p mass histogram,) first-digit threshold,      */
+                             /* candidates, tail weight sums                        */
 #define SSA_STAGE_RESOLVE 3  /* exact top-k threshold, tie quota, tail normaliser  */
 #define SSA_STAGE_SAMPLE 4   /* deterministic set + Poisson sample, per chunk      */
 #define SSA_STAGE_ATTEND 5   /* gather attention over the selection, split-K       */
@@ -114,24 +118,35 @@ size_t ssa_workspace_bytes(const ssa_params* p);
 int32_t ssa_num_chunks(const ssa_params* p);
 
 /* The whole decode step: scores, selection, sampling, attention, merge.
- * topk[b] tokens are read deterministically and sample_budget[b] is the
- * expected number of tail samples.  If topk[b] + sample_budget[b] >= L_b
- * every token is read with weight 1 (dense attention).  Sampling for
- * (b, h, token j) uses Philox4x32-10 keyed by seed[b] with counter
- * (j >> 2, h, b, 0), word j & 3 (Salmon et al., SC'11). */
+ *
+ * Deterministic stratum.  Tokens are ordered by score (float32, larger first;
+ * ties to the lower position).  The stratum is the first k tokens of that
+ * order, k = min(topk[b], L_b) -- further capped, when top_p is non-NULL, by
+ * n_p, the length of the shortest prefix whose approximate mass reaches
+ * top_p[b].  Mass is counted exactly in integer units: token j holds
+ * floor(w_j * 2^38) units, w_j = exp(s_j - M) with the library's specified
+ * float32 exp (M the sequence's maximum score, so the top token holds 2^38),
+ * and the prefix must reach ceil(p * Q) units of the sequence's total Q
+ * (0 units -> n_p = 0).  top_p[b] is clamped to [0, 1]; NaN counts as 0.
+ * To use top-p alone pass topk[b] >= L_b.
+ *
+ * Tail.  sample_budget[b] (m) is the expected number of tail samples.  If
+ * k + m >= L_b every token is read with weight 1 (dense attention).
+ * Sampling for (b, h, token j) uses Philox4x32-10 keyed by seed[b] with
+ * counter (j >> 2, h, b, 0), word j & 3 (Salmon et al., SC'11). */
 int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
-               const int32_t* sample_budget, const uint64_t* seed, void* out, void* workspace,
-               size_t workspace_bytes, void* stream);
+               const float* top_p, const int32_t* sample_budget, const uint64_t* seed, void* out,
+               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ssa_decode, recording hipEvent_t events[2*s] before and events[2*s+1] after
  * the kernel(s) of stage s (SSA_STAGE_*); NULL entries are skipped, and a
  * NULL array records nothing.  Same results as ssa_decode. */
 int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                     const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream,
-                     void* const* events);
+                     const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+                     const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream, void* const* events);
 
 /* Stage 1 alone: approximate scores, scores[(b*Hkv + h)*max_seq_len + j] (f32),
  * for j < L_b; entries at or past L_b are left untouched.
@@ -141,13 +156,15 @@ int ssa_score(const ssa_params* p, const void* q, const void* k_cache,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages 2-4 alone, from a caller-provided score array laid out as ssa_score
- * writes it.  If w_in is non-NULL, w_in[b*Hkv + h] replaces the computed tail
- * normaliser W.  Writes the selection (layout above) and norm_out
- * [B, Hkv, 2] = (M, W): the maximum score and the normaliser actually used. */
+ * writes it; topk, top_p (may be NULL) and sample_budget as for ssa_decode.
+ * If w_in is non-NULL, w_in[b*Hkv + h] replaces the computed tail normaliser
+ * W.  Writes the selection (layout above) and norm_out [B, Hkv, 2] = (M, W):
+ * the maximum score and the normaliser actually used. */
 int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
-               const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
-               const float* w_in, int32_t* sel_idx, float* sel_logw, int32_t* sel_count,
-               float* norm_out, void* workspace, size_t workspace_bytes, void* stream);
+               const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+               const uint64_t* seed, const float* w_in, int32_t* sel_idx, float* sel_logw,
+               int32_t* sel_count, float* norm_out, void* workspace, size_t workspace_bytes,
+               void* stream);
 
 /* Stages 5-6 alone: attention over a caller-provided selection:
  *   out_g = sum_A e^{l_gj + logw_j} v_j / sum_A e^{l_gj + logw_j},

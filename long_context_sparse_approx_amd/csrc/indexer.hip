@@ -249,11 +249,16 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
 
 // Clears the per-unit histograms and maxima.
 __global__ __launch_bounds__(256) void init_kernel(uint32_t* hist1, uint32_t* hist2,
-                                                   uint32_t* maxkey) {
+                                                   uint32_t* maxkey, unsigned long long* hist1m,
+                                                   unsigned long long* hist2m) {
   const int u = blockIdx.x;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     hist1[(size_t)u * kBins + i] = 0u;
     hist2[(size_t)u * kBins + i] = 0u;
+    if (hist1m) {
+      hist1m[(size_t)u * kBins + i] = 0ull;
+      hist2m[(size_t)u * kBins + i] = 0ull;
+    }
   }
   if (threadIdx.x == 0) maxkey[u] = 0u;
 }
@@ -298,9 +303,10 @@ __global__ __launch_bounds__(256) void score_hist_kernel(SelectArgs a) {
 int indexer_tokens_per_iteration(int pair_count) { return 4 * (kWave / (pair_count / 4)) * 8; }
 int indexer_max_tokens_per_wg() { return kMaxTileTokens; }
 
-hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey, int units,
+hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
+                       unsigned long long* hist1m, unsigned long long* hist2m, int units,
                        hipStream_t stream) {
-  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey);
+  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey, hist1m, hist2m);
   return hipGetLastError();
 }
 

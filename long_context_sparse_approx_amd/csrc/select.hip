@@ -10,6 +10,11 @@
 //   top-k:  the k tokens with the largest float32 score order keys, ties to
 //           the lower index; found by a three-digit radix select (11/11/10
 //           bits) whose first digit histogram comes from stage 1;
+//   top-p:  optionally the stratum ends earlier, at the shortest prefix of
+//           that order whose mass units floor(2^38 sexp(s_j - M)) reach
+//           ceil(p * total); the same radix select runs on mass histograms
+//           (64-bit integer sums) beside the count histograms, and at each
+//           digit the bound reached first decides;
 //   tail:   w_j = sexp(s_j - M), W = sum over the tail, computed directly in
 //           fp64 (never as total minus top-k, which cancels);
 //   sample: include j iff fl(u_j * W) < fl(m * w_j), u_j from Philox4x32-10
@@ -53,29 +58,93 @@ __device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, in
   __syncthreads();
 }
 
+// ------------------------------------------------------------------ mass
+// Top-p only.  Per chunk: every token's mass units go to the unit's
+// first-digit mass histogram (integer atomics: the sums do not depend on the
+// order of arrival).
+__global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
+  __shared__ unsigned long long mh[kBins];
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / a.Hkv;
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
+  const int c0 = c * kChunk;
+  if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
+  const float M = key_to_float(a.maxkey[u]);
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  float v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int t = c0 + threadIdx.x + k * kNT;
+    v[k] = t < p.L ? srow[t] : 0.0f;
+  }
+  for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int t = c0 + threadIdx.x + k * kNT;
+    const unsigned long long q = mass_units(sexp(v[k] - M));
+    if (t < p.L && q != 0ull) atomicAdd(&mh[order_key(v[k]) >> kDigit1Shift], q);
+  }
+  __syncthreads();
+  unsigned long long* g = a.hist1m + (size_t)u * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kNT) {
+    const unsigned long long q = mh[i];
+    if (q != 0ull) atomicAdd(&g[i], q);
+  }
+}
+
 // ------------------------------------------------------------------ threshold
-// Per unit, from the first-digit histogram: the digit of the k-th largest key
-// and a lower bound of W.  Every token whose first digit is below b1 is a
-// tail token and its key is at least the smallest key of its digit, so
+// Per unit, from the first-digit histograms: the digit where the stratum
+// ends (count rank k, or with top-p whichever of rank k and the mass target
+// comes first) and a lower bound of W.  Every token whose first digit is
+// below b1 is a tail token and its key is at least the smallest key of its
+// digit, so
 //   W >= sum_{digit < b1} count(digit) * exp(lowest score of digit - M);
 // the sum uses the specified exp (monotone up to ~1 ulp) and is shrunk by
 // 2^-10 to absorb that and the final rounding.
 __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
+  __shared__ unsigned long long mh[kBins];
   __shared__ int scan_scr[kNT / 64];
   __shared__ int pair[2];
+  __shared__ unsigned long long scan_m[kNT / 64];
+  __shared__ unsigned long long pair_m[2];
   __shared__ double dscr[kNT / 64];
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
   if (p.dense || p.L == 0) {
-    if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0};
+    if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0, 0ull, 0, 0};
     return;
   }
-  for (int i = threadIdx.x; i < kBins; i += kNT) hist[i] = a.hist1[(size_t)u * kBins + i];
+  const bool topp = p.topp && p.k_eff > 0;
+  for (int i = threadIdx.x; i < kBins; i += kNT) {
+    hist[i] = a.hist1[(size_t)u * kBins + i];
+    if (topp) mh[i] = a.hist1m[(size_t)u * kBins + i];
+  }
   __syncthreads();
-  int b1 = kBins, rem = 0;
-  if (p.k_eff > 0) find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &b1, &rem);
+  DigitBound d{kBins, 0, 0ull, 0};
+  if (p.k_eff > 0) {
+    int bc, rc;
+    find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &bc, &rc);
+    d = DigitBound{bc, rc, 0ull, kBoundCount};
+    if (topp) {
+      unsigned long long qs = 0ull;
+      for (int i = threadIdx.x; i < kBins; i += kNT) qs += mh[i];
+      const unsigned long long tau = mass_target(p.p, block_sum_u64<kNT>(qs, scan_m));
+      if (tau == 0ull) {
+        d = DigitBound{kBins, 0, 0ull, 0};
+      } else {
+        int bm;
+        unsigned long long rm;
+        find_bin<kNT>(mh, kBins, tau, scan_m, pair_m, &bm, &rm);
+        d = combine_bounds(kBoundCount | kBoundMass, bc, rc, bm, rm);
+      }
+    }
+  }
+  const int b1 = d.bin;
+  const int above = count_above<kNT>(hist, kBins, b1, scan_scr);
   const float M = key_to_float(a.maxkey[u]);
   double lb = 0.0;
   for (int bin = threadIdx.x; bin < b1; bin += kNT) {
@@ -86,7 +155,7 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   lb = block_sum_f64<kNT>(lb, dscr);
   float wlb = (float)(lb * (1.0 - 0x1.0p-10));
   if (a.w_in) wlb = fminf(wlb, a.w_in[u]);
-  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, rem, wlb, 0};
+  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, d.rem, wlb, d.mode, d.rem_mass, above, 0};
 }
 
 // ------------------------------------------------------------------ filter
@@ -103,13 +172,16 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
   const int h = u - b * a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const Thresh1 t1 = a.thresh[u];
   const int b1 = t1.b1;              // 2048 when there is no deterministic set
   const float M = key_to_float(a.maxkey[u]);
-  const bool sampling = p.m > 0 && p.L - p.k_eff > 0;
+  // With top-p the stratum size is not known yet: list sampling candidates
+  // whenever there is a budget.
+  const bool sampling = p.m > 0 && (p.topp || p.L - p.k_eff > 0);
+  const bool mass = t1.mode & kBoundMass;
   const float mf = (float)p.m;
   const uint64_t seed = a.seed[b];
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
@@ -167,7 +239,9 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
       cidx[wc] = t;
       ckey[wc] = keys[i];
       ++wc;
-      atomicAdd(&a.hist2[(size_t)u * kBins + ((keys[i] >> kDigit2Shift) & (kBins - 1))], 1u);
+      const int d2 = (keys[i] >> kDigit2Shift) & (kBins - 1);
+      atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
+      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w[i]));
     }
     if (abovemask & (1u << i)) lidx[wa++] = t;
     if (sampmask & (1u << i)) {
@@ -208,14 +282,17 @@ __device__ __forceinline__ int threads_per_chunk(int nc) {
 
 __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
+  __shared__ unsigned long long mh[kBins];  // mass units per digit (top-p)
   __shared__ int ties_sh[kMaxResolveChunks];
   __shared__ int scan_scr[kRW];
   __shared__ int pair[2];
+  __shared__ unsigned long long scan_m[kRW];
+  __shared__ unsigned long long pair_m[2];
   __shared__ double dscr[kRW];
 
   const int u = blockIdx.x;
   const int b = u / a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.sample_budget, b, a.max_seq_len);
+  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -242,19 +319,23 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       const int csub = threadIdx.x % tpc;
       double ctail = 0.0;
       int total_ties = 0;
-      if (p.k_eff == 0) {
+      const Thresh1 t1 = a.thresh[u];
+      if (t1.mode == 0) {
         st.flags = kFlagNoTopk;
+        st.k_eff = 0;
       } else {
-        const Thresh1 t1 = a.thresh[u];
         // Loads that do not depend on the second digit are issued first: the
-        // histogram, this thread's candidate count and (below) its keys.
+        // histograms, this thread's candidate count and (below) its keys.
         constexpr int kKeep = 16;
         const bool one_chunk = nc <= cstep;
         const int cm = threadIdx.x / tpc;
         const int nm = (one_chunk && cm < nc) ? a.cand_cnt[cu + cm] : 0;
         const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
         uint32_t kr[kKeep];
-        for (int i = threadIdx.x; i < kBins; i += kRT) hist[i] = a.hist2[(size_t)u * kBins + i];
+        for (int i = threadIdx.x; i < kBins; i += kRT) {
+          hist[i] = a.hist2[(size_t)u * kBins + i];
+          if (t1.mode & kBoundMass) mh[i] = a.hist2m[(size_t)u * kBins + i];
+        }
         for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         if (one_chunk) {
 #pragma unroll
@@ -264,35 +345,65 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
           }
         }
         __syncthreads();
-        int b2, rem2, b3, rem3;
-        find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &b2, &rem2);
-        const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)b2;
-        for (int i = threadIdx.x; i < kBins3; i += kRT) hist[i] = 0u;
+        // Second digit.
+        DigitBound d2;
+        {
+          int bc = 0, rc = 0, bm = 0;
+          unsigned long long rm = 0ull;
+          if (t1.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &bc, &rc);
+          if (t1.mode & kBoundMass) find_bin<kRT>(mh, kBins, t1.rem_mass, scan_m, pair_m, &bm, &rm);
+          d2 = combine_bounds(t1.mode, bc, rc, bm, rm);
+        }
+        const int above2 = count_above<kRT>(hist, kBins, d2.bin, scan_scr);
+        const bool mass3 = d2.mode & kBoundMass;
+        const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)d2.bin;
+        for (int i = threadIdx.x; i < kBins3; i += kRT) {
+          hist[i] = 0u;
+          if (mass3) mh[i] = 0ull;
+        }
         __syncthreads();
+        // Third digit: LDS histograms of the candidates that share the prefix.
+        auto add3 = [&](uint32_t key) {
+          if ((key >> kDigit2Shift) == prefix) {
+            atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+            if (mass3) atomicAdd(&mh[key & (kBins3 - 1)], mass_units(sexp(key_to_float(key) - st.M)));
+          }
+        };
         if (one_chunk) {
 #pragma unroll
           for (int k = 0; k < kKeep; ++k) {
             const int i = csub + k * tpc;
-            if (i < nm && (kr[k] >> kDigit2Shift) == prefix) atomicAdd(&hist[kr[k] & (kBins3 - 1)], 1u);
+            if (i < nm) add3(kr[k]);
           }
-          for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
-            const uint32_t key = ckm[i];
-            if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
-          }
+          for (int i = csub + kKeep * tpc; i < nm; i += tpc) add3(ckm[i]);
         } else {
           for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
             const int n = a.cand_cnt[cu + c];
             const uint32_t* ck = ckeys + (size_t)c * kChunk;
-            for (int i = csub; i < n; i += tpc) {
-              const uint32_t key = ck[i];
-              if ((key >> kDigit2Shift) == prefix) atomicAdd(&hist[key & (kBins3 - 1)], 1u);
-            }
+            for (int i = csub; i < n; i += tpc) add3(ck[i]);
           }
         }
         __syncthreads();
-        find_rank_bin<kRT>(hist, kBins3, rem2, scan_scr, pair, &b3, &rem3);
-        st.tkey = (prefix << kDigit2Shift) | (uint32_t)b3;
-        st.ties_needed = rem3;
+        DigitBound d3;
+        {
+          int bc = 0, rc = 0, bm = 0;
+          unsigned long long rm = 0ull;
+          if (d2.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins3, d2.rem, scan_scr, pair, &bc, &rc);
+          if (mass3) find_bin<kRT>(mh, kBins3, d2.rem_mass, scan_m, pair_m, &bm, &rm);
+          d3 = combine_bounds(d2.mode, bc, rc, bm, rm);
+        }
+        const int above3 = count_above<kRT>(hist, kBins3, d3.bin, scan_scr);
+        st.tkey = (prefix << kDigit2Shift) | (uint32_t)d3.bin;
+        // Tokens on the last key all carry the same mass: the mass bound needs
+        // ceil(remaining units / units per token) of them.
+        int need = d3.rem;
+        if (d3.mode & kBoundMass) {
+          const unsigned long long qT = mass_units(sexp(key_to_float(st.tkey) - st.M));
+          const unsigned long long nmass = qT ? (d3.rem_mass + qT - 1ull) / qT : 1ull;
+          need = (d3.mode & kBoundCount) ? (int)min((unsigned long long)need, nmass) : (int)nmass;
+        }
+        st.ties_needed = need;
+        st.k_eff = t1.above + above2 + above3 + need;
         // Ties on the threshold key per chunk (integer), and the weight of the
         // candidates strictly below it (each thread over its fixed items, in
         // order, then a fixed tree).
@@ -344,14 +455,19 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       double acc = 0.0;
       for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
       W = block_sum_f64<kRT>(acc, dscr) + ctail;
-      if (p.k_eff > 0) {
+      if (t1.mode != 0) {
         const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
         W += (double)(total_ties - st.ties_needed) * wT;
+      }
+      // With a top-p mass the dense rule (k + m >= L) is only decidable now.
+      if (p.topp && (int64_t)st.k_eff + (int64_t)p.m >= (int64_t)p.L) {
+        st.flags = kFlagDense;
+        W = 0.0;
       }
     }
   }
   st.W = a.w_in ? a.w_in[u] : (float)W;
-  if (!(st.flags & (kFlagEmpty | kFlagDense)) && p.m > 0 && p.L - p.k_eff > 0 && st.W > 0.0f)
+  if (!(st.flags & (kFlagEmpty | kFlagDense)) && p.m > 0 && p.L - st.k_eff > 0 && st.W > 0.0f)
     st.flags |= kFlagSample;
   if (threadIdx.x == 0) {
     reinterpret_cast<UnitState*>(a.state)[u] = st;
@@ -509,6 +625,11 @@ __global__ void debug_sexp_kernel(const float* x, float* y, int n) {
 }
 
 }  // namespace
+
+hipError_t launch_mass(const SelectArgs& a, int units, hipStream_t stream) {
+  mass_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 hipError_t launch_threshold(const SelectArgs& a, int units, hipStream_t stream) {
   threshold_kernel<<<units, kNT, 0, stream>>>(a);

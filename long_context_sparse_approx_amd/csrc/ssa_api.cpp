@@ -69,7 +69,7 @@ Dims dims_of(const ssa_params* p) {
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
+  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
 };
@@ -86,6 +86,8 @@ Layout layout_of(const Dims& d) {
   l.scores = take(U * SEG * 4);
   l.hist1 = take(U * kBins * 4);
   l.hist2 = take(U * kBins * 4);
+  l.hist1m = take(U * kBins * 8);
+  l.hist2m = take(U * kBins * 8);
   l.maxkey = take(U * 4);
   l.thresh = take(U * sizeof(ssa::Thresh1));
   l.cand_idx = take(U * SEG * 4);
@@ -160,7 +162,8 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
 
 ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* scores,
                             int64_t score_ld, const int32_t* seq_lens, const int32_t* topk,
-                            const int32_t* sample_budget, const uint64_t* seed, const float* w_in,
+                            const float* top_p, const int32_t* sample_budget,
+                            const uint64_t* seed, const float* w_in,
                             const int32_t* block_table, int emit_rows, int32_t* sel_idx,
                             float* sel_logw, int32_t* sel_cnt, float* norm_out, void* ws,
                             const Layout& l) {
@@ -169,12 +172,15 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.score_ld = score_ld;
   a.seq_lens = seq_lens;
   a.topk = topk;
+  a.top_p = top_p;
   a.sample_budget = sample_budget;
   a.seed = seed;
   a.w_in = w_in;
   a.block_table = block_table;
   a.hist1 = at<uint32_t>(ws, l.hist1);
   a.hist2 = at<uint32_t>(ws, l.hist2);
+  a.hist1m = at<unsigned long long>(ws, l.hist1m);
+  a.hist2m = at<unsigned long long>(ws, l.hist2m);
   a.maxkey = at<uint32_t>(ws, l.maxkey);
   a.thresh = at<ssa::Thresh1>(ws, l.thresh);
   a.cand_idx = at<int32_t>(ws, l.cand_idx);
@@ -239,6 +245,25 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
     if ((expr) != hipSuccess) return SSA_ERR_HIP; \
   } while (0)
 
+// The selection stages of both entry points: clear, first-digit histogram
+// (fused into the indexer in ssa_decode), top-p mass histogram when asked
+// for, threshold, filter.
+hipError_t launch_init_for(const ssa::SelectArgs& a, int units, hipStream_t s) {
+  const bool topp = a.top_p != nullptr;
+  return ssa::launch_init(a.hist1, a.hist2, a.maxkey, topp ? a.hist1m : nullptr,
+                          topp ? a.hist2m : nullptr, units, s);
+}
+
+hipError_t launch_first_digit(const ssa::SelectArgs& a, int units, hipStream_t s) {
+  if (a.top_p) {
+    const hipError_t e = ssa::launch_mass(a, units, s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = ssa::launch_threshold(a, units, s);
+  if (e != hipSuccess) return e;
+  return ssa::launch_filter(a, units, s);
+}
+
 int check_ws(const ssa_params* p, void* ws, size_t ws_bytes, Layout* l) {
   if (!params_ok(p)) return SSA_ERR_INVALID;
   *l = layout_of(dims_of(p));
@@ -263,8 +288,9 @@ int32_t ssa_num_chunks(const ssa_params* p) {
 
 int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
-                     const int32_t* sample_budget, const uint64_t* seed, void* out,
-                     void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+                     const float* top_p, const int32_t* sample_budget, const uint64_t* seed,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* const* events) {
   Layout l;
   const int rc = check_ws(p, workspace, workspace_bytes, &l);
   if (rc != SSA_OK) return rc;
@@ -283,19 +309,18 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   const ssa::IndexArgs ia =
       index_args(p, d, q, k_cache, block_table, seq_lens, scores, d.SEG, workspace, l);
   const ssa::SelectArgs sa =
-      select_args(p, d, scores, d.SEG, seq_lens, topk, sample_budget, seed, nullptr, block_table,
-                  /*emit_rows=*/1, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
+      select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr,
+                  block_table, /*emit_rows=*/1, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
   const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
                                          sel_logw, sel_cnt, /*idx_are_rows=*/1, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
-  SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
+  SSA_TRY(launch_init_for(sa, d.U, s));
   rec.end(SSA_STAGE_INIT);
   rec.begin(SSA_STAGE_INDEX);
   SSA_TRY(ssa::launch_indexer(ia, d.U, s));
   rec.end(SSA_STAGE_INDEX);
   rec.begin(SSA_STAGE_FILTER);
-  SSA_TRY(ssa::launch_threshold(sa, d.U, s));
-  SSA_TRY(ssa::launch_filter(sa, d.U, s));
+  SSA_TRY(launch_first_digit(sa, d.U, s));
   rec.end(SSA_STAGE_FILTER);
   rec.begin(SSA_STAGE_RESOLVE);
   SSA_TRY(ssa::launch_resolve(sa, d.U, s));
@@ -314,10 +339,10 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
 
 int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
-               const int32_t* sample_budget, const uint64_t* seed, void* out, void* workspace,
-               size_t workspace_bytes, void* stream) {
-  return ssa_decode_timed(p, q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget,
-                          seed, out, workspace, workspace_bytes, stream, nullptr);
+               const float* top_p, const int32_t* sample_budget, const uint64_t* seed, void* out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  return ssa_decode_timed(p, q, k_cache, v_cache, block_table, seq_lens, topk, top_p,
+                          sample_budget, seed, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int32_t* block_table,
@@ -332,15 +357,17 @@ int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ssa::IndexArgs ia = index_args(p, d, q, k_cache, block_table, seq_lens, scores,
                                        p->max_seq_len, workspace, l);
-  SSA_TRY(ssa::launch_init(ia.hist1, at<uint32_t>(workspace, l.hist2), ia.maxkey, d.U, s));
+  SSA_TRY(ssa::launch_init(ia.hist1, at<uint32_t>(workspace, l.hist2), ia.maxkey, nullptr,
+                           nullptr, d.U, s));
   SSA_TRY(ssa::launch_indexer(ia, d.U, s));
   return SSA_OK;
 }
 
 int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
-               const int32_t* topk, const int32_t* sample_budget, const uint64_t* seed,
-               const float* w_in, int32_t* sel_idx, float* sel_logw, int32_t* sel_count,
-               float* norm_out, void* workspace, size_t workspace_bytes, void* stream) {
+               const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+               const uint64_t* seed, const float* w_in, int32_t* sel_idx, float* sel_logw,
+               int32_t* sel_count, float* norm_out, void* workspace, size_t workspace_bytes,
+               void* stream) {
   Layout l;
   const int rc = check_ws(p, workspace, workspace_bytes, &l);
   if (rc != SSA_OK) return rc;
@@ -350,12 +377,11 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
   const Dims d = dims_of(p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ssa::SelectArgs sa =
-      select_args(p, d, scores, p->max_seq_len, seq_lens, topk, sample_budget, seed, w_in,
+      select_args(p, d, scores, p->max_seq_len, seq_lens, topk, top_p, sample_budget, seed, w_in,
                   nullptr, /*emit_rows=*/0, sel_idx, sel_logw, sel_count, norm_out, workspace, l);
-  SSA_TRY(ssa::launch_init(sa.hist1, sa.hist2, sa.maxkey, d.U, s));
+  SSA_TRY(launch_init_for(sa, d.U, s));
   SSA_TRY(ssa::launch_score_hist(sa, d.U, s));
-  SSA_TRY(ssa::launch_threshold(sa, d.U, s));
-  SSA_TRY(ssa::launch_filter(sa, d.U, s));
+  SSA_TRY(launch_first_digit(sa, d.U, s));
   SSA_TRY(ssa::launch_resolve(sa, d.U, s));
   SSA_TRY(ssa::launch_sample(sa, d.U, s));
   return SSA_OK;

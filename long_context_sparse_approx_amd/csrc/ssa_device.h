@@ -24,18 +24,18 @@ constexpr int kBins3 = 1024;
 // Per-unit (batch, kv head) selection state written by the resolve stage.
 enum : int32_t {
   kFlagEmpty = 1,     // L == 0: nothing to read
-  kFlagDense = 2,     // topk + m >= L: every token, weight 1
-  kFlagNoTopk = 4,    // topk == 0: every token is in the tail
+  kFlagDense = 2,     // k + m >= L: every token, weight 1
+  kFlagNoTopk = 4,    // k == 0: every token is in the tail
   kFlagSample = 8,    // Poisson sampling of the tail is active
 };
 
 struct UnitState {
-  uint32_t tkey;        // order key of the k-th largest score
+  uint32_t tkey;        // order key of the stratum's last (k-th) token
   int32_t ties_needed;  // tokens with key == tkey that join the deterministic set
   float M;              // maximum score of the sequence
   float W;              // tail normaliser used for sampling
   int32_t flags;
-  int32_t k_eff;
+  int32_t k_eff;        // size k of the deterministic stratum
   int32_t m;
   int32_t L;
 };
@@ -102,6 +102,33 @@ __device__ __forceinline__ float sexp(float x) {
   return low ? 0.0f : y;
 }
 
+// ---------------------------------------------------------------- top-p mass
+
+// Approximate mass of a token in integer units: floor(w * 2^38) for a weight
+// w = sexp(s - M) in [0, 1].  The scaling by a power of two is exact and the
+// conversion truncates, so this is an exact floor; integer sums of these
+// units do not depend on their order.
+constexpr int kMassShift = 38;
+__device__ __forceinline__ unsigned long long mass_units(float w) {
+  return (unsigned long long)(w * 0x1.0p38f);
+}
+
+// ceil(p * Q) exactly, p clamped to [0, 1] (NaN as 0), Q < 2^62.
+// p = f * 2^e with f in [0.5, 1), so p * Q = (f * 2^24) * Q / 2^(24 - e) with
+// an integer numerator below 2^86.
+__device__ __forceinline__ unsigned long long mass_target(float p, unsigned long long Q) {
+  if (!(p > 0.0f)) return 0ull;
+  if (p >= 1.0f) return Q;
+  int e;
+  const float f = __builtin_frexpf(p, &e);
+  const unsigned long long mant = (unsigned long long)(f * 0x1.0p24f);  // exact, < 2^24
+  const unsigned __int128 num = (unsigned __int128)mant * Q;
+  const int sh = 24 - e;  // >= 25 for p < 1
+  if (sh >= 120) return num != 0 ? 1ull : 0ull;  // p * Q < 2^86 / 2^120 < 1
+  const unsigned __int128 den = (unsigned __int128)1 << sh;
+  return (unsigned long long)((num + den - 1) >> sh);
+}
+
 // ---------------------------------------------------------------- Philox
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32
@@ -150,33 +177,41 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
+// Inclusive prefix sum over the 64 lanes of a wave (int or 64-bit unsigned).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off);
+    const T o = __shfl_up(v, off);
     if (lane >= off) v += o;
   }
   return v;
 }
 
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64);
-// `scratch` holds NT/64 ints in LDS.  Returns the exclusive prefix and writes
-// the block total to *total.  Contains two barriers.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+// `scratch` holds NT/64 values in LDS.  Returns the exclusive prefix and
+// writes the block total to *total.  Contains two barriers.  The value type
+// is taken from the scratch array.
+template <int NT, typename T>
+__device__ __forceinline__ T block_exclusive_scan(typename same_type<T>::type v, T* scratch,
+                                                  T* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int inc = wave_inclusive_scan(v);
+  const T inc = wave_inclusive_scan(v);
   if (lane == 63) scratch[wave] = inc;
   __syncthreads();
-  int base = 0, tot = 0;
+  T base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const int s = scratch[w];
-    base += (w < wave) ? s : 0;
+    const T s = scratch[w];
+    base += (w < wave) ? s : (T)0;
     tot += s;
   }
   __syncthreads();
@@ -199,6 +234,20 @@ __device__ __forceinline__ double block_sum_f64(double v, double* scratch) {
 }
 
 template <int NT>
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v,
+                                                            unsigned long long* scratch) {
+  constexpr int NW = NT / 64;
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  unsigned long long t = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+template <int NT>
 __device__ __forceinline__ int block_sum_i32(int v, int* scratch) {
   constexpr int NW = NT / 64;
   v = wave_sum(v);
@@ -211,25 +260,28 @@ __device__ __forceinline__ int block_sum_i32(int v, int* scratch) {
   return t;
 }
 
-// Given a histogram `hist` of `nbins` bins in LDS and a rank k >= 1, find the
-// bin b* with count(bins > b*) < k <= count(bins >= b*), and the remaining rank
-// k - count(bins > b*).  Bins are scanned from the top.  Every thread of the
-// NT-thread block must call it; the answer is returned in every thread.
-template <int NT>
-__device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int nbins, int k, int* scan_scratch,
-                                              int* out_pair, int* bin_out, int* rem_out) {
+// Given a histogram `hist` of `nbins` bins in LDS and a target k >= 1 (a rank
+// for counts, mass units for masses), find the bin b* with
+// sum(bins > b*) < k <= sum(bins >= b*), and the remainder k - sum(bins > b*).
+// Bins are scanned from the top.  Every thread of the NT-thread block must
+// call it; the answer is returned in every thread.  T is uint32_t (counts,
+// summed as int) or unsigned long long (mass units).
+template <int NT, typename H, typename T>
+__device__ __forceinline__ void find_bin(const H* hist, int nbins, typename same_type<T>::type k,
+                                         T* scan_scratch,
+                                         T* out_pair, int* bin_out, T* rem_out) {
   const int per = nbins / NT;  // bins per thread (nbins is a multiple of NT)
   const int top = nbins - 1 - threadIdx.x * per;  // this thread's highest bin
-  int mine = 0;
-  for (int i = 0; i < per; ++i) mine += (int)hist[top - i];
-  int total;
-  const int before = block_exclusive_scan<NT>(mine, scan_scratch, &total);
+  T mine = 0;
+  for (int i = 0; i < per; ++i) mine += (T)hist[top - i];
+  T total;
+  const T before = block_exclusive_scan<NT>(mine, scan_scratch, &total);
   if (before < k && k <= before + mine) {
-    int run = before;
+    T run = before;
     for (int i = 0; i < per; ++i) {
-      const int c = (int)hist[top - i];
+      const T c = (T)hist[top - i];
       if (run + c >= k) {
-        out_pair[0] = top - i;
+        out_pair[0] = (T)(top - i);
         out_pair[1] = k - run;
         break;
       }
@@ -237,25 +289,66 @@ __device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int nbins, i
     }
   }
   __syncthreads();
-  *bin_out = out_pair[0];
+  *bin_out = (int)out_pair[0];
   *rem_out = out_pair[1];
   __syncthreads();
 }
 
-// Selection parameters of sequence b as the kernels read them.
+template <int NT>
+__device__ __forceinline__ void find_rank_bin(const uint32_t* hist, int nbins, int k,
+                                              int* scan_scratch, int* out_pair, int* bin_out,
+                                              int* rem_out) {
+  find_bin<NT>(hist, nbins, k, scan_scratch, out_pair, bin_out, rem_out);
+}
+
+// Sum of the counts of the bins above `bin` (every thread of the block calls).
+template <int NT>
+__device__ __forceinline__ int count_above(const uint32_t* hist, int nbins, int bin, int* scratch) {
+  int v = 0;
+  for (int i = bin + 1 + (int)threadIdx.x; i < nbins; i += NT) v += (int)hist[i];
+  return block_sum_i32<NT>(v, scratch);
+}
+
+// Where the stratum ends at one radix digit, given the open bounds `mode`:
+// the count bound ends in bin bc with remainder rc, the mass bound in bin bm
+// with remainder rm.  The bound reached first (the higher bin, as keys are
+// visited from the top) decides; both stay open when they share the bin.
+struct DigitBound {
+  int bin;
+  int rem;
+  unsigned long long rem_mass;
+  int mode;
+};
+
+__device__ __forceinline__ DigitBound combine_bounds(int mode, int bc, int rc, int bm,
+                                                     unsigned long long rm) {
+  if (mode == kBoundCount || (mode == (kBoundCount | kBoundMass) && bc > bm))
+    return DigitBound{bc, rc, 0ull, kBoundCount};
+  if (mode == kBoundMass || bm > bc) return DigitBound{bm, 0, rm, kBoundMass};
+  return DigitBound{bc, rc, rm, kBoundCount | kBoundMass};
+}
+
+// Selection parameters of sequence b as the kernels read them.  k_eff is the
+// count bound min(topk, L).  With a top-p mass the stratum may end earlier,
+// so only m >= L makes the unit dense before the selection is resolved.
 struct SeqParams {
   int L, k_eff, m;
   bool dense;
+  bool topp;
+  float p;
 };
 
 __device__ __forceinline__ SeqParams seq_params(const int32_t* seq_lens, const int32_t* topk,
+                                                const float* top_p,
                                                 const int32_t* sample_budget, int b,
                                                 int max_seq_len) {
   SeqParams p;
   p.L = clamp_len(seq_lens[b], max_seq_len);
   const int k = max(topk[b], 0);
   p.m = max(sample_budget[b], 0);
-  p.dense = (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
+  p.topp = top_p != nullptr;
+  p.p = p.topp ? top_p[b] : 1.0f;
+  p.dense = p.topp ? p.m >= p.L : (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
   p.k_eff = min(k, p.L);
   return p;
 }

@@ -7,18 +7,30 @@
 
 namespace ssa {
 
-// Per-unit facts derived from the first-digit histogram before the chunk
+// Which bound ends the deterministic stratum at the current radix digit:
+// the count (top-k), the mass (top-p), or both while they share the digit.
+enum : int32_t { kBoundCount = 1, kBoundMass = 2 };
+
+// Per-unit facts derived from the first-digit histograms before the chunk
 // passes:
-//   b1  = first digit of the k-th largest key (2048 when there is no
-//         deterministic set),
-//   rem = rank of that key among the keys with digit b1,
-//   wlb = a lower bound of the tail normaliser W (0 when unknown).
+//   b1       = first digit of the stratum's last key (2048 when the stratum
+//              is empty),
+//   rem      = rank of that key among the keys with digit b1 (count bound),
+//   rem_mass = mass units still needed within digit b1 (mass bound),
+//   mode     = kBoundCount | kBoundMass: the bounds still open at digit b1
+//              (0: empty stratum),
+//   above    = number of tokens whose first digit is above b1,
+//   wlb      = a lower bound of the tail normaliser W (0 when unknown).
 struct Thresh1 {
   int32_t b1;
   int32_t rem;
   float wlb;
+  int32_t mode;
+  unsigned long long rem_mass;
+  int32_t above;
   int32_t pad;
 };
+static_assert(sizeof(Thresh1) == 32, "one 32-byte record per unit");
 
 struct IndexArgs {
   const uint16_t* q;          // [B, Hq, d] bf16
@@ -39,12 +51,15 @@ struct SelectArgs {
   int64_t score_ld;
   const int32_t* seq_lens;
   const int32_t* topk;
+  const float* top_p;         // [B] or null (top-k only)
   const int32_t* sample_budget;
   const uint64_t* seed;
   const float* w_in;          // [U] or null
   const int32_t* block_table; // used when emit_rows
   uint32_t* hist1;            // [U, 2048]
   uint32_t* hist2;            // [U, 2048]
+  unsigned long long* hist1m; // [U, 2048] first-digit mass units (top-p)
+  unsigned long long* hist2m; // [U, 2048] second-digit mass units of the candidates (top-p)
   uint32_t* maxkey;           // [U]
   Thresh1* thresh;            // [U]
   int32_t* cand_idx;          // [U, seg_ld] threshold-digit candidates per chunk
@@ -84,10 +99,13 @@ struct AttendArgs {
 
 int indexer_tokens_per_iteration(int pair_count);
 int indexer_max_tokens_per_wg();
-hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey, int units,
+// Clears the histograms and maxima; the mass histograms only when non-null.
+hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
+                       unsigned long long* hist1m, unsigned long long* hist2m, int units,
                        hipStream_t stream);
 hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream);
 hipError_t launch_score_hist(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_mass(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_threshold(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);

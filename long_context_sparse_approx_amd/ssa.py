@@ -63,14 +63,14 @@ def lib() -> ctypes.CDLL:
         L.ssa_workspace_bytes.restype = ctypes.c_size_t
         L.ssa_num_chunks.argtypes = [_PP]
         L.ssa_num_chunks.restype = ctypes.c_int32
-        common = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        common = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_decode.argtypes = common
         L.ssa_decode.restype = ctypes.c_int
         L.ssa_decode_timed.argtypes = common + [_P]
         L.ssa_decode_timed.restype = ctypes.c_int
         L.ssa_score.argtypes = [_PP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_score.restype = ctypes.c_int
-        L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+        L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                  ctypes.c_size_t, _P]
         L.ssa_select.restype = ctypes.c_int
         L.ssa_attend.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -144,15 +144,23 @@ def _ws(p, workspace, device):
     return workspace
 
 
+def _check_top_p(top_p, B):
+    if top_p is not None:
+        assert top_p.dtype == torch.float32 and top_p.numel() == B, "top_p: [B] float32"
+
+
 def decode(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
-           out=None, workspace=None, stream=None, events=None):
-    """One decode step; returns out [B, Hq, d] (f32 or bf16 per params)."""
+           out=None, workspace=None, stream=None, events=None, top_p=None):
+    """One decode step; returns out [B, Hq, d] (f32 or bf16 per params).
+    ``top_p`` ([B] float32 on the device, optional) caps the deterministic
+    stratum at the top-p prefix."""
+    _check_top_p(top_p, p.batch)
     if out is None:
         dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
         out = torch.empty(q.shape, dtype=dt, device=q.device)
     workspace = _ws(p, workspace, q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-            _ptr(seq_lens), _ptr(topk), _ptr(sample_budget), _ptr(seed), _ptr(out),
+            _ptr(seq_lens), _ptr(topk), _ptr(top_p), _ptr(sample_budget), _ptr(seed), _ptr(out),
             _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
     if events is None:
         _check(lib().ssa_decode(*args), "ssa_decode")
@@ -175,8 +183,9 @@ def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspac
 
 
 def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None, workspace=None,
-           stream=None):
+           stream=None, top_p=None):
     """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out)."""
+    _check_top_p(top_p, p.batch)
     dev = scores.device
     nc = num_chunks(p)
     U = p.batch * p.num_kv_heads
@@ -188,7 +197,7 @@ def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None,
     workspace = _ws(p, workspace, dev)
     assert w_in is None or w_in.numel() == U
     _check(lib().ssa_select(ctypes.byref(p), _ptr(scores), _ptr(seq_lens), _ptr(topk),
-                            _ptr(sample_budget), _ptr(seed), _ptr(w_in), _ptr(sel_idx),
+                            _ptr(top_p), _ptr(sample_budget), _ptr(seed), _ptr(w_in), _ptr(sel_idx),
                             _ptr(sel_logw), _ptr(sel_count), _ptr(norm), _ptr(workspace),
                             ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_select")
     return sel_idx, sel_logw, sel_count, norm

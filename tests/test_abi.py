@@ -68,7 +68,7 @@ def test_invalid_params_rejected(lib, bad):
     assert lib.ssa_num_chunks(ctypes.byref(p)) == 0
     fake = ctypes.c_void_p(4096)
     rc = lib.ssa_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
-                        fake, ctypes.c_size_t(1 << 40), None)
+                        fake, fake, ctypes.c_size_t(1 << 40), None)
     assert rc == ssa.SSA_ERR_INVALID
 
 
@@ -76,8 +76,11 @@ def test_null_and_misaligned_pointers_rejected(lib):
     p = good()
     fake = ctypes.c_void_p(4096)
     big = ctypes.c_size_t(1 << 40)
-    args = [fake] * 9  # q, k, v, block_table, seq_lens, topk, sample_budget, seed, out
-    for i in range(9):
+    # q, k, v, block_table, seq_lens, topk, top_p, sample_budget, seed, out
+    args = [fake] * 10
+    for i in range(10):
+        if i == 6:  # top_p is optional
+            continue
         a = list(args)
         a[i] = None
         rc = lib.ssa_decode(ctypes.byref(p), *a, fake, big, None)
@@ -93,11 +96,11 @@ def test_small_workspace_rejected(lib):
     p = good()
     fake = ctypes.c_void_p(4096)
     n = ssa.workspace_bytes(p)
-    rc = lib.ssa_decode(ctypes.byref(p), *([fake] * 9), fake, ctypes.c_size_t(n - 256), None)
+    rc = lib.ssa_decode(ctypes.byref(p), *([fake] * 10), fake, ctypes.c_size_t(n - 256), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
     rc = lib.ssa_score(ctypes.byref(p), fake, fake, fake, fake, fake, fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
-    rc = lib.ssa_select(ctypes.byref(p), *([fake] * 10), fake, ctypes.c_size_t(16), None)
+    rc = lib.ssa_select(ctypes.byref(p), *([fake] * 11), fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
     rc = lib.ssa_attend(ctypes.byref(p), *([fake] * 9), fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE

@@ -35,18 +35,21 @@ def unit_host(wl, b, h):
     return qg, orc.gather_rows(kc, bt, 0, L), orc.gather_rows(vc, bt, 0, L)
 
 
-def check_fullsize(name, units):
+def check_fullsize(name, units, top_p=None):
     wl = synth.make_workload(name, DEV)
-    say(f"[full] workload={name} B={wl.B} L={wl.lens[:4]}{'...' if wl.B > 4 else ''} units={units}")
+    say(f"[full] workload={name} B={wl.B} L={wl.lens[:4]}{'...' if wl.B > 4 else ''} "
+        f"units={units} top_p={top_p}")
+    tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=DEV)
+    tp32 = None if top_p is None else np.float32(top_p)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count)
     scale = 1.0 / math.sqrt(wl.d)
     G = wl.Hq // wl.Hkv
     ws = ssa.alloc_workspace(p, DEV)
     out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
-                     wl.sample_budget, wl.seed, workspace=ws).clone()
+                     wl.sample_budget, wl.seed, workspace=ws, top_p=tp).clone()
     out2 = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
-                      wl.sample_budget, wl.seed, workspace=ws)
+                      wl.sample_budget, wl.seed, workspace=ws, top_p=tp)
     torch.cuda.synchronize()
     assert torch.equal(out, out2), "decode is not bitwise reproducible"
     vmax_all = float(wl.v_cache.float().abs().max())
@@ -64,14 +67,14 @@ def check_fullsize(name, units):
         ok, ratio = score_tolerance_ok(sc[b, h, :s64.size].cpu().numpy(), s64)
         assert ok, f"scores out of tolerance at {(b, h)} ({ratio})"
         sel = orc.select_unit(s64.astype(np.float32), int(wl.topk[b]), int(wl.sample_budget[b]),
-                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h)
+                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h, top_p=tp32)
         sels[(b, h)] = sel
         s32[b, h, :s64.size] = torch.from_numpy(s64.astype(np.float32))
         w_in[b, h] = float(sel["W"])
         say(f"[full] {name} unit {(b, h)} scores ok (err/bound {ratio:.3g}); "
             f"oracle |S|={sel['S'].size} |R|={sel['R'].size}")
     si, sl, sn, _ = ssa.select(p, s32.to(DEV), wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
-                               w_in=w_in.to(DEV), workspace=ws)
+                               w_in=w_in.to(DEV), workspace=ws, top_p=tp)
     torch.cuda.synchronize()
     si, sl, sn = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy()
     for (b, h), sel in sels.items():
@@ -98,6 +101,12 @@ def check_fullsize(name, units):
 
 def test_fullsize_1m():
     check_fullsize("1m", [(0, 0), (0, 5)])
+
+
+def test_fullsize_1m_top_p():
+    """Top-p 0.02 capped at the top-k budget: the mass bound ends the stratum
+    (about 8k of the 10486 tokens) on this workload."""
+    check_fullsize("1m", [(0, 0), (0, 5)], top_p=0.02)
 
 
 def test_fullsize_128k():
