@@ -5,9 +5,11 @@
 A step is one ssa_decode call over the whole layer: scores, top-k, tail
 sampling, gather attention and merge, with inputs already resident in HBM.
 Prints one JSON line: KV-tokens/s/layer (sum of sequence lengths / step
-time), the per-stage times from HIP events recorded on the decode stream
-inside the timed region, the indexer's roofline against MI355X's 8 TB/s HBM
-peak, and the CPU oracle timed on a bounded sample of the same workload.
+time), the indexer's roofline against MI355X's 8 TB/s HBM peak (HIP events
+around the indexer launch inside the timed region), per-stage times from a
+separate event-bracketed pass, the same workload with a top-p capped
+deterministic stratum, and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 from __future__ import annotations
@@ -95,17 +97,21 @@ def measured_traffic(workload):
     return float(t.group(1))
 
 
-def run_gpu(args, name, steps, warmup, with_stage_events=True):
-    """Times `steps` decode steps (after `warmup` untimed ones) of a workload."""
+def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None):
+    """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
+    ``top_p`` (a float) caps every sequence's deterministic stratum at the
+    top-p prefix; ``wl`` reuses an already generated workload."""
     import torch
 
     from long_context_sparse_approx_amd import ssa, synth
 
     dev = "cuda:0"
     t_gen = time.perf_counter()
-    wl = synth.make_workload(name, dev)
+    if wl is None:
+        wl = synth.make_workload(name, dev)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
+    tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=dev)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count)
     ws = ssa.alloc_workspace(p, dev)
@@ -114,7 +120,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
     call = (p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
             wl.sample_budget, wl.seed)
     for _ in range(warmup):
-        ssa.decode(*call, out=out, workspace=ws, stream=stream)
+        ssa.decode(*call, out=out, workspace=ws, stream=stream, top_p=tp)
     torch.cuda.synchronize()
 
     hip = Hip()
@@ -137,7 +143,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
             if graphs is not None:
                 graphs[i % len(graphs)].replay()
             else:
-                ssa.decode(*call, out=out, workspace=ws, stream=stream,
+                ssa.decode(*call, out=out, workspace=ws, stream=stream, top_p=tp,
                            events=ctypes.addressof(arrs[i]) if arrs else None)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
@@ -148,7 +154,8 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
     if args.graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            ssa.decode(*call, out=out, workspace=ws, stream=torch.cuda.current_stream())
+            ssa.decode(*call, out=out, workspace=ws, stream=torch.cuda.current_stream(),
+                       top_p=tp)
         graphs = [g]
         for _ in range(warmup):
             g.replay()
@@ -180,7 +187,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True):
     # Selected-set sizes of this step (deterministic: same kernels, same inputs).
     sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
     _, _, cnt, _ = ssa.select(p, sc, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
-                              workspace=ws)
+                              workspace=ws, top_p=tp)
     cnt = cnt.sum(dim=2).cpu()
     n_det, n_smp = int(cnt[..., 0].sum()), int(cnt[..., 1].sum())
     del sc
@@ -282,6 +289,8 @@ def main():
                     help="skip the separate per-stage breakdown pass")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured in a HIP graph (no indexer events)")
+    ap.add_argument("--top-p", type=float, default=0.02,
+                    help="also time the main workload with this top-p stratum cap (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -315,6 +324,17 @@ def main():
                           hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"])
         del r2
         torch.cuda.empty_cache()
+    variants = {}
+    if args.top_p > 0:
+        r3 = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events,
+                     top_p=args.top_p, wl=res["wl"])
+        s3 = summarize(r3, args.workload)
+        variants["top_p"] = dict(
+            policy=f"deterministic stratum = min(top-k, top-p {args.top_p} prefix); "
+                   "same budget m for the tail",
+            value=s3["value"], unit="KV-tokens/s/layer", ms_per_step=s3["ms_per_step"],
+            stages_us=s3["stages_us"], selected=s3["selected"])
+        del r3
     cpu = None if args.no_cpu else cpu_baseline(res["wl"], args.cpu_budget)
     wl = res["wl"]
     line = {
@@ -343,6 +363,7 @@ def main():
         "gather_gbps_algorithmic": main_sum["gather_gbps_algorithmic"],
         "selected": main_sum["selected"],
         "also": also,
+        "variants": variants,
     }
     print(json.dumps(line), flush=True)
 
