@@ -18,6 +18,8 @@
 // digit (top 11 bits of the order key) in an LDS histogram and tracks the
 // maximum order key; both are flushed with integer atomics, so the result is
 // independent of scheduling.
+#include <atomic>
+
 #include "ssa_device.h"
 #include "ssa_launch.h"
 
@@ -25,9 +27,11 @@ namespace ssa {
 
 namespace {
 
-// Largest token tile of one indexer workgroup (its block offsets and its
-// scores are staged in LDS).
-constexpr int kMaxTileTokens = 4096;
+// Largest token tile of one indexer workgroup (its block ids and its scores
+// are staged in LDS: 8192 tokens keep four workgroups per CU resident, so a
+// 1M-token, 8-head layer runs as a single round of workgroups and every
+// workgroup writes its scores in one burst at its end).
+constexpr int kMaxTileTokens = 8192;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -103,10 +107,12 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
 // predication; all loads are issued back to back).  Scores go to the
 // workgroup's LDS tile buffer; the tile is written to HBM in one burst at the
 // end (interleaving small score writes with the key stream costs far more HBM
-// time than the 4 bytes per token suggest).
+// time than the 4 bytes per token suggest).  The first-digit histogram holds
+// two 16-bit counts per word (a tile has at most 8192 tokens).
 template <int LPT, bool FULL>
-__device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uint64_t* blk_sh,
-                                                int d, int t0, int base, int t_end,
+__device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uint32_t* blk_sh,
+                                                uint64_t blk_stride, int d, int t0, int base,
+                                                int t_end,
                                                 const uint32_t* qh, const uint32_t* ql,
                                                 float* sbuf, uint32_t* hist, uint32_t& kmax,
                                                 int lane) {
@@ -117,7 +123,8 @@ __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uin
   const int pos = (lane % LPT) % LG;
   const bool writer = LPT <= 8 || (lane & 8) == 0;
   const int tg = base + UNR * grp;  // first token of this lane's group (a multiple of 8)
-  const uint16_t* row0 = kbase + blk_sh[(tg - t0) >> 4] + (uint64_t)(tg & 15) * d;
+  const uint16_t* row0 =
+      kbase + (uint64_t)blk_sh[(tg - t0) >> 4] * blk_stride + (uint64_t)(tg & 15) * d;
   u32x4 kv[UNR];
 #pragma unroll
   for (int r = 0; r < UNR; ++r)
@@ -132,7 +139,8 @@ __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uin
     if (writer && (FULL || t < t_end)) {
       sbuf[t - t0] = v[e];
       const uint32_t key = order_key(v[e]);
-      atomicAdd(&hist[key >> kDigit1Shift], 1u);
+      const uint32_t bin = key >> kDigit1Shift;
+      atomicAdd(&hist[bin >> 1], 1u << (16 * (bin & 1u)));
       kmax = key > kmax ? key : kmax;
     }
   }
@@ -145,13 +153,13 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   constexpr int WAVE_TOK = TPI * UNR;        // tokens per wave per iteration
   constexpr int WG_TOK = 4 * WAVE_TOK;       // tokens per workgroup per iteration
   // The query group's scored slice (at most 16 x 128 floats) is staged in the
-  // same LDS as the histogram, which is cleared once the slice is folded.
-  __shared__ uint32_t hist[16 * 128];
-  __shared__ uint64_t blk_sh[kMaxTileTokens / kBlockTokens];
+  // score tile buffer before the first score lands there.
+  __shared__ uint32_t hist[kBins / 2];
+  __shared__ uint32_t blk_sh[kMaxTileTokens / kBlockTokens];
   __shared__ float sbuf[kMaxTileTokens];
   __shared__ uint32_t wmax[4];
-  static_assert(16 * 128 >= kBins, "histogram fits the staging buffer");
-  float* qsh = reinterpret_cast<float*>(hist);
+  static_assert(16 * 128 <= kMaxTileTokens, "query slice fits the tile buffer");
+  float* qsh = sbuf;
 
   const int u = blockIdx.y;
   const int b = u / a.Hkv;
@@ -178,9 +186,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
   const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.d;
   for (int i = tid; i < nblk; i += 256) {
-    int blk = btrow[blk0 + i];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    blk_sh[i] = (uint64_t)blk * blk_stride;
+    const int blk = btrow[blk0 + i];
+    blk_sh[i] = (uint32_t)(blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk));
   }
   __syncthreads();
   // Per-lane proxy query over this lane's 8 dims, qbar = (scale / G) * sum_g q_g,
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < kBins; i += 256) hist[i] = 0u;
+  for (int i = tid; i < kBins / 2; i += 256) hist[i] = 0u;
   __syncthreads();
 
   const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.d + 2 * a.pair_begin + sub * 8;
@@ -214,11 +221,11 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   uint32_t kmax = 0u;
   int base = t0 + wave * WAVE_TOK;
   for (; base + WAVE_TOK <= t_end; base += WG_TOK)
-    index_iteration<LPT, true>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, sbuf, hist, kmax,
-                               lane);
+    index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.d, t0, base, t_end, qh, ql, sbuf,
+                               hist, kmax, lane);
   if (base < t_end)
-    index_iteration<LPT, false>(kbase, blk_sh, a.d, t0, base, t_end, qh, ql, sbuf, hist, kmax,
-                                lane);
+    index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.d, t0, base, t_end, qh, ql, sbuf,
+                                hist, kmax, lane);
 
   kmax = wave_max_u32(kmax);
   if (lane == 0) wmax[wave] = kmax;
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
     atomicMax(&a.maxkey[u], mx);
   }
   for (int i = tid; i < kBins; i += 256) {
-    const uint32_t c = hist[i];
+    const uint32_t c = (hist[i >> 1] >> (16 * (i & 1))) & 0xffffu;
     if (c) atomicAdd(&a.hist1[(size_t)u * kBins + i], c);
   }
   // The tile's scores, written in one burst (16-byte stores when aligned).
@@ -302,6 +309,37 @@ __global__ __launch_bounds__(256) void score_hist_kernel(SelectArgs a) {
 
 int indexer_tokens_per_iteration(int pair_count) { return 4 * (kWave / (pair_count / 4)) * 8; }
 int indexer_max_tokens_per_wg() { return kMaxTileTokens; }
+
+// Workgroups of the indexer instance for `pair_count` that the current device
+// holds at once (CUs x resident workgroups per CU), cached per device.
+int indexer_resident_workgroups(int pair_count) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][5];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  int slot = 0;
+  while (slot < 4 && (4 << slot) != pair_count) ++slot;
+  if (dev < kMaxDevices) {
+    const int c = cache[dev][slot].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  const void* fn = nullptr;
+  switch (pair_count / 4) {
+    case 1: fn = reinterpret_cast<const void*>(&indexer_kernel<1>); break;
+    case 2: fn = reinterpret_cast<const void*>(&indexer_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void*>(&indexer_kernel<4>); break;
+    case 8: fn = reinterpret_cast<const void*>(&indexer_kernel<8>); break;
+    case 16: fn = reinterpret_cast<const void*>(&indexer_kernel<16>); break;
+    default: return 0;
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess) return 0;
+  const int c = cus * per_cu;
+  if (dev < kMaxDevices && c > 0) cache[dev][slot].store(c, std::memory_order_relaxed);
+  return c;
+}
 
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
                        unsigned long long* hist1m, unsigned long long* hist2m, int units,

@@ -124,14 +124,21 @@ struct Recorder {
   }
 };
 
+// Indexer tile: every unit gets an equal share of the workgroups the device
+// holds at once, so a layer that fits runs as one round (no tail round) and
+// each workgroup streams one large tile; at least one iteration, at most the
+// kernel's tile capacity.
 int tokens_per_wg(const ssa_params* p, const Dims& d) {
   const int it = ssa::indexer_tokens_per_iteration(p->pair_count);
-  const int64_t work = (int64_t)d.U * p->max_seq_len;
-  int64_t mult = work / ((int64_t)2048 * it);
-  const int64_t cap = ssa::indexer_max_tokens_per_wg() / it;
-  if (mult > cap) mult = cap;
-  if (mult < 1) mult = 1;
-  return (int)(it * mult);
+  const int cap = ssa::indexer_max_tokens_per_wg() / it * it;
+  int resident = ssa::indexer_resident_workgroups(p->pair_count);
+  if (resident <= 0) resident = 1024;
+  const int per_unit = resident / d.U > 0 ? resident / d.U : 1;
+  int64_t tpw = ((int64_t)p->max_seq_len + per_unit - 1) / per_unit;
+  tpw = (tpw + it - 1) / it * it;
+  if (tpw > cap) tpw = cap;
+  if (tpw < it) tpw = it;
+  return (int)tpw;
 }
 
 ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,

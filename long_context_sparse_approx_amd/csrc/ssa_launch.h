@@ -99,6 +99,7 @@ struct AttendArgs {
 
 int indexer_tokens_per_iteration(int pair_count);
 int indexer_max_tokens_per_wg();
+int indexer_resident_workgroups(int pair_count);  // 0 if unknown
 // Clears the histograms and maxima; the mass histograms only when non-null.
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
                        unsigned long long* hist1m, unsigned long long* hist2m, int units,
