@@ -41,7 +41,7 @@ R4  Ranking is done on the float32 rounding of the score, ordered by the
     float's bits (-0.0 below +0.0); ties go to the lower token index.
 R5  Dense rule: when k + m >= L every token is read with weight 1, k being
     the size of the deterministic stratum (min(topk, L), further capped by the
-    top-p prefix of R11 when a top-p mass is given).
+    top-p prefix of R15 when a top-p mass is given).
 R6  Tail design: Poisson sampling.  w_j = sexp(s_j - M) with M the maximum
     score over the whole sequence, W = sum of w_j over the tail, inclusion
     probability pi_j = min(1, m * w_j / W); m is the expected sample size.
@@ -57,7 +57,7 @@ R9  sexp is a specified float32 exp (Cody-Waite reduction, degree-7 Taylor
     0 for x < -87.
 R10 Horvitz-Thompson weights: c_j = 1 on the deterministic set S and 1/pi_j on
     the sample R; output = sum c e^l v / sum c e^l over S u R.
-R11 Top-p stratum: the approximate probability mass of token j is counted in
+R15 Top-p stratum: the approximate probability mass of token j is counted in
     integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
     top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
     the target is tau = ceil(p * Q), evaluated exactly.  n_p is the length of
@@ -201,7 +201,7 @@ def sexp(x) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Step 2 alternative: the top-p deterministic stratum ([SSA] "Where sparse
 # attention loses quality", top-p as a deterministic option; "How SSA
-# stratifies the cache", top-p as a special case) -- reading R11
+# stratifies the cache", top-p as a special case) -- reading R15
 # ---------------------------------------------------------------------------
 
 MASS_FRAC_BITS = 38
@@ -226,7 +226,7 @@ def mass_target(p, Q: int) -> int:
 
 
 def topp_count(s32: np.ndarray, p) -> int:
-    """n_p of reading R11: length of the shortest prefix of the order whose
+    """n_p of reading R15: length of the shortest prefix of the order whose
     mass units reach tau = ceil(p * Q)."""
     s32 = np.asarray(s32, dtype=_F32)
     if s32.size == 0:
@@ -304,7 +304,7 @@ def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None, top_p=None):
     w (float32 tail weights), mw = fl(m * w) and pi = min(1, fl(mw / W)).
     ``W_in`` replaces the computed normaliser (used to feed both
     implementations the same normaliser).  ``top_p`` (a float, or None for
-    top-k alone) caps the deterministic stratum at the top-p prefix (R11).
+    top-k alone) caps the deterministic stratum at the top-p prefix (R15).
     """
     s32 = np.asarray(s32, dtype=_F32)
     L = s32.size
