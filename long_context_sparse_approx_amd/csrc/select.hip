@@ -34,29 +34,13 @@
 // normaliser taken from the first-digit histogram (u_j * W_lb <= u_j * W and
 // rounding is monotone, so no token that the exact test would include is
 // dropped).  The final sample pass only visits these lists.
+#include "select_device.h"
 #include "ssa_device.h"
 #include "ssa_launch.h"
 
 namespace ssa {
 
 namespace {
-
-constexpr int kNT = 256;             // threads per chunk workgroup
-constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
-
-// Coalesced copy of the chunk's scores into LDS (entries past L are unused).
-// All of a thread's loads are issued before the first LDS store.
-__device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, int L, float* sh) {
-  float v[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int t = c0 + threadIdx.x + k * kNT;
-    v[k] = t < L ? srow[t] : 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
-  __syncthreads();
-}
 
 // ------------------------------------------------------------------ mass
 // Top-p only.  Per chunk: every token's mass units go to the unit's
@@ -176,88 +160,9 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const Thresh1 t1 = a.thresh[u];
-  const int b1 = t1.b1;              // 2048 when there is no deterministic set
   const float M = key_to_float(a.maxkey[u]);
-  // With top-p the stratum size is not known yet: list sampling candidates
-  // whenever there is a budget.
-  const bool sampling = p.m > 0 && (p.topp || p.L - p.k_eff > 0);
-  const bool mass = t1.mode & kBoundMass;
-  const float mf = (float)p.m;
-  const uint64_t seed = a.seed[b];
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
-
-  const int tb = threadIdx.x * kPer;
-  const int nv = p.L - (c0 + tb);  // valid tokens of this thread: min(16, max(nv, 0))
-  uint32_t candmask = 0u, abovemask = 0u, tailmask = 0u, sampmask = 0u;
-  double wsum = 0.0;
-  uint32_t keys[kPer];
-  float w[kPer];
-  // Branch-free: every token's weight and every group's uniforms are
-  // computed; masks select what counts.
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const float s = sh[tb + i];
-    const uint32_t key = order_key(s);
-    keys[i] = key;
-    const int bin = (int)(key >> kDigit1Shift);
-    const bool valid = i < nv;
-    abovemask |= (uint32_t)(valid && bin > b1) << i;
-    candmask |= (uint32_t)(valid && bin == b1) << i;
-    const bool tail = valid && bin < b1;
-    tailmask |= (uint32_t)tail << i;
-    w[i] = sexp(s - M);
-    wsum += tail ? (double)w[i] : 0.0;
-  }
-  if (sampling) {
-#pragma unroll
-    for (int g = 0; g < kPer / 4; ++g) {
-      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
-      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r;
-        sampmask |= (uint32_t)(uniform24(words[r]) * t1.wlb < mf * w[i]) << i;
-      }
-    }
-    sampmask &= tailmask;
-  }
-  int total;
-  const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
-  int lst_tot;
-  const int lst = block_exclusive_scan<kNT>(__popc(abovemask) | (__popc(sampmask) << 16),
-                                            scan_scr, &lst_tot);
-  const int n_above = lst_tot & 0xffff;
-  int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
-  uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
-  int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
-  float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
-  int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int t = c0 + tb + i;
-    if (candmask & (1u << i)) {
-      cidx[wc] = t;
-      ckey[wc] = keys[i];
-      ++wc;
-      const int d2 = (keys[i] >> kDigit2Shift) & (kBins - 1);
-      atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
-      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w[i]));
-    }
-    if (abovemask & (1u << i)) lidx[wa++] = t;
-    if (sampmask & (1u << i)) {
-      lidx[ws] = t;
-      lw[ws] = w[i];
-      ++ws;
-    }
-  }
-  const double wtot = block_sum_f64<kNT>(wsum, dscr);
-  if (threadIdx.x == 0) {
-    const size_t ci = (size_t)u * a.nchunk + c;
-    a.cand_cnt[ci] = total;
-    a.wpart[ci] = wtot;
-    a.list_cnt[2 * ci] = n_above;
-    a.list_cnt[2 * ci + 1] = lst_tot >> 16;
-  }
+  filter_chunk(a, p, t1, M, u, b, h, c, sh, scan_scr, dscr);
 }
 
 // ------------------------------------------------------------------ resolve
@@ -329,7 +234,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         constexpr int kKeep = 16;
         const bool one_chunk = nc <= cstep;
         const int cm = threadIdx.x / tpc;
-        const int nm = (one_chunk && cm < nc) ? a.cand_cnt[cu + cm] : 0;
+        const int nm = (one_chunk && cm < nc) ? clamp_count(a.cand_cnt[cu + cm], kChunk) : 0;
         const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
         uint32_t kr[kKeep];
         for (int i = threadIdx.x; i < kBins; i += kRT) {
@@ -378,7 +283,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
           for (int i = csub + kKeep * tpc; i < nm; i += tpc) add3(ckm[i]);
         } else {
           for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-            const int n = a.cand_cnt[cu + c];
+            const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
             const uint32_t* ck = ckeys + (size_t)c * kChunk;
             for (int i = csub; i < n; i += tpc) add3(ck[i]);
           }
@@ -426,7 +331,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
           if (ties) atomicAdd(&ties_sh[cm], ties);
         } else {
           for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-            const int n = a.cand_cnt[cu + c];
+            const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
             const uint32_t* ck = ckeys + (size_t)c * kChunk;
             int ties = 0;
             for (int i = csub; i < n; i += tpc) {
@@ -487,7 +392,9 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 // sampled tokens ascending.  With emit_rows the segment holds cache row
 // numbers (for the fused attention stage) instead of positions.
 __device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, int b, int h,
-                                           int t, float w, int c0, uint8_t* flag, float* lwsh) {
+                                           int t, float w, int c0, int nvalid, uint8_t* flag,
+                                           float* lwsh) {
+  if ((unsigned)(t - c0) >= (unsigned)nvalid) return;  // not a position of this chunk
   const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2);
   const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
   const float mw = (float)st.m * w;
@@ -511,9 +418,11 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   const size_t ci = (size_t)u * a.nchunk + c;
   // Independent loads first: unit state, per-chunk counts, the chunk's block ids.
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
-  const int n_above = a.list_cnt[2 * ci];
-  const int n_samp = a.list_cnt[2 * ci + 1];
-  const int ncand = a.cand_cnt[ci];
+  // Counts are clamped to the segment and positions checked against the
+  // chunk, so no value in the workspace can address outside it.
+  const int n_above = clamp_count(a.list_cnt[2 * ci], kChunk);
+  const int n_samp = clamp_count(a.list_cnt[2 * ci + 1], kChunk - n_above);
+  const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
   const int before = a.ties_before[ci];
   const uint64_t seed = a.seed[b];
   int32_t* cnt = a.sel_cnt + ci * 2;
@@ -536,10 +445,13 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   if (!dense) {
     const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
     const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
-    for (int i = threadIdx.x; i < n_above; i += kNT) flag[lidx[i] - c0] = 1;
+    for (int i = threadIdx.x; i < n_above; i += kNT) {
+      const int t = lidx[i];
+      if ((unsigned)(t - c0) < (unsigned)nvalid) flag[t - c0] = 1;
+    }
     if (sampling)
       for (int i = threadIdx.x; i < n_samp; i += kNT)
-        sample_one(st, seed, b, h, lidx[n_above + i], lw[n_above + i], c0, flag, lwsh);
+        sample_one(st, seed, b, h, lidx[n_above + i], lw[n_above + i], c0, nvalid, flag, lwsh);
     if (!(st.flags & kFlagNoTopk)) {
       // Threshold-digit candidates, in index order: key above T -> S; key == T
       // -> S while the tie quota lasts; otherwise a tail token.
@@ -557,9 +469,10 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
         if (v) {
           const int t = cidx[i];
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
-            flag[t - c0] = 1;
+            if ((unsigned)(t - c0) < (unsigned)nvalid) flag[t - c0] = 1;
           } else if (sampling) {
-            sample_one(st, seed, b, h, t, sexp(key_to_float(key) - st.M), c0, flag, lwsh);
+            sample_one(st, seed, b, h, t, sexp(key_to_float(key) - st.M), c0, nvalid, flag,
+                       lwsh);
           }
         }
       }

@@ -1,0 +1,119 @@
+// Chunk filter of the selection (internal to the library).
+#pragma once
+
+#include "ssa_device.h"
+#include "ssa_launch.h"
+
+namespace ssa {
+
+constexpr int kNT = 256;             // threads per chunk workgroup
+constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
+
+// Coalesced copy of the chunk's scores into LDS (entries past L are unused).
+// All of a thread's loads are issued before the first LDS store.
+__device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, int L, float* sh) {
+  float v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int t = c0 + threadIdx.x + k * kNT;
+    v[k] = t < L ? srow[t] : 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
+  __syncthreads();
+}
+
+// Filter of chunk c of unit u by a 256-thread workgroup.  `sh` holds the
+// chunk's scores (entries at or past L are ignored); t1 is the unit's
+// first-digit threshold and M its maximum score.  Writes the chunk's
+// candidates (positions and keys, second-digit histogram), its lists (tokens
+// above the threshold digit, then tail tokens passing the necessary
+// inclusion test fl(u * W_lb) < fl(m * w) with their weights), its
+// candidate and list counts and its fp64 tail weight sum.
+// Branch-free: every token's weight and every group's uniforms are computed;
+// masks select what counts.
+__device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParams& p,
+                                             const Thresh1& t1, float M, int u, int b, int h,
+                                             int c, const float* sh, int* scan_scr,
+                                             double* dscr) {
+  const int c0 = c * kChunk;
+  const int b1 = t1.b1;  // 2048 when there is no deterministic set
+  // With top-p the stratum size is not known yet: list sampling candidates
+  // whenever there is a budget.
+  const bool sampling = p.m > 0 && (p.topp || p.L - p.k_eff > 0);
+  const bool mass = t1.mode & kBoundMass;
+  const float mf = (float)p.m;
+  const uint64_t seed = a.seed[b];
+  const int tb = threadIdx.x * kPer;
+  const int nv = p.L - (c0 + tb);  // valid tokens of this thread: min(16, max(nv, 0))
+  uint32_t candmask = 0u, abovemask = 0u, tailmask = 0u, sampmask = 0u;
+  double wsum = 0.0;
+  uint32_t keys[kPer];
+  float w[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const float s = sh[tb + i];
+    const uint32_t key = order_key(s);
+    keys[i] = key;
+    const int bin = (int)(key >> kDigit1Shift);
+    const bool valid = i < nv;
+    abovemask |= (uint32_t)(valid && bin > b1) << i;
+    candmask |= (uint32_t)(valid && bin == b1) << i;
+    const bool tail = valid && bin < b1;
+    tailmask |= (uint32_t)tail << i;
+    w[i] = sexp(s - M);
+    wsum += tail ? (double)w[i] : 0.0;
+  }
+  if (sampling) {
+#pragma unroll
+    for (int g = 0; g < kPer / 4; ++g) {
+      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
+      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * g + r;
+        sampmask |= (uint32_t)(uniform24(words[r]) * t1.wlb < mf * w[i]) << i;
+      }
+    }
+    sampmask &= tailmask;
+  }
+  int total;
+  const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
+  int lst_tot;
+  const int lst = block_exclusive_scan<kNT>(__popc(abovemask) | (__popc(sampmask) << 16),
+                                            scan_scr, &lst_tot);
+  const int n_above = lst_tot & 0xffff;
+  int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
+  uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+  int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
+  float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
+  int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = c0 + tb + i;
+    if (candmask & (1u << i)) {
+      cidx[wc] = t;
+      ckey[wc] = keys[i];
+      ++wc;
+      const int d2 = (keys[i] >> kDigit2Shift) & (kBins - 1);
+      atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
+      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w[i]));
+    }
+    if (abovemask & (1u << i)) lidx[wa++] = t;
+    if (sampmask & (1u << i)) {
+      lidx[ws] = t;
+      lw[ws] = w[i];
+      ++ws;
+    }
+  }
+  const double wtot = block_sum_f64<kNT>(wsum, dscr);
+  if (threadIdx.x == 0) {
+    const size_t ci = (size_t)u * a.nchunk + c;
+    a.cand_cnt[ci] = total;
+    a.wpart[ci] = wtot;
+    a.list_cnt[2 * ci] = n_above;
+    a.list_cnt[2 * ci + 1] = lst_tot >> 16;
+  }
+}
+
+}  // namespace ssa

@@ -47,6 +47,10 @@ __device__ __forceinline__ int clamp_len(int L, int max_seq_len) {
   return L < 0 ? 0 : (L > max_seq_len ? max_seq_len : L);
 }
 
+__device__ __forceinline__ int clamp_count(int n, int cap) {
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
 // ---------------------------------------------------------------- bf16
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
