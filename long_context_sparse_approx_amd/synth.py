@@ -78,8 +78,13 @@ class Workload:
         return self.q.shape[0]
 
     @property
+    def T(self):
+        """Query positions per sequence (q is [B, Hq, d] when 1, else [B, T, Hq, d])."""
+        return 1 if self.q.dim() == 3 else self.q.shape[1]
+
+    @property
     def Hq(self):
-        return self.q.shape[1]
+        return self.q.shape[-2]
 
     @property
     def Hkv(self):
@@ -87,7 +92,7 @@ class Workload:
 
     @property
     def d(self):
-        return self.q.shape[2]
+        return self.q.shape[-1]
 
     @property
     def max_seq_len(self):
@@ -131,11 +136,15 @@ def _lens(cfg, gen, device):
 
 
 def make_workload(name_or_cfg, device="cpu", *, L=None, B=None, topk=None, m=None,
-                  seeds=None, data_seed=None, chunk_tokens=1 << 16, **overrides) -> Workload:
+                  seeds=None, data_seed=None, chunk_tokens=1 << 16, num_queries=1,
+                  **overrides) -> Workload:
     """Build a workload from a named config (or a config dict) with overrides.
 
     ``L`` may be an int (all sequences) or a list; ``topk``/``m`` may be ints or
     "rule".  Generation is chunked over tokens to bound temporary memory.
+    With ``num_queries`` T > 1 the step carries T query positions per sequence
+    (the last T cache positions, their keys already cached): q is
+    [B, T, Hq, d] and the planted keys follow the mean of all T queries.
     """
     if isinstance(name_or_cfg, str):
         name, cfg = name_or_cfg, dict(CONFIGS[name_or_cfg])
@@ -167,18 +176,28 @@ def make_workload(name_or_cfg, device="cpu", *, L=None, B=None, topk=None, m=Non
     block_table = torch.zeros((B, max_blocks), dtype=torch.int32, device=device)
     k_cache = torch.zeros((total, Hkv, BLOCK, d), dtype=torch.bfloat16, device=device)
     v_cache = torch.zeros_like(k_cache)
-    q_all = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=device)
+    T = int(num_queries)
+    q_all = torch.empty((B, Hq, d) if T == 1 else (B, T, Hq, d), dtype=torch.bfloat16,
+                        device=device)
     off = 0
     for b in range(B):
         L_ = lens[b]
         phys = perm[off:off + nblk[b]]
         off += nblk[b]
         block_table[b, :nblk[b]] = phys
-        qb = torch.randn((1, Hq, d), generator=gen, device=device, dtype=torch.float32)
-        cq, sq = rope_tables(torch.tensor([L_], device=device), d, cfg["theta"])
-        qb = apply_rope(qb, cq, sq)[0].to(torch.bfloat16)
-        q_all[b] = qb
-        qbar = qb.float().view(Hkv, G, d).mean(dim=1)  # [Hkv, d]
+        if T == 1:
+            qb = torch.randn((1, Hq, d), generator=gen, device=device, dtype=torch.float32)
+            cq, sq = rope_tables(torch.tensor([L_], device=device), d, cfg["theta"])
+            qb = apply_rope(qb, cq, sq)[0].to(torch.bfloat16)
+            q_all[b] = qb
+            qbar = qb.float().view(Hkv, G, d).mean(dim=1)  # [Hkv, d]
+        else:
+            qb = torch.randn((T, Hq, d), generator=gen, device=device, dtype=torch.float32)
+            pos = torch.arange(L_ - T, L_, device=device)
+            cq, sq = rope_tables(pos, d, cfg["theta"])
+            qb = apply_rope(qb, cq, sq).to(torch.bfloat16)
+            q_all[b] = qb
+            qbar = qb.float().view(T, Hkv, G, d).mean(dim=(0, 2))  # [Hkv, d]
         uhat = qbar / qbar.norm(dim=-1, keepdim=True)
         planted = int(cfg["planted"])
         plant_pos = []

@@ -23,7 +23,9 @@ Sources (web pages; cited by title and section):
   selected tokens at their original positions).
 * [PIVOT] "PIVOT slashes sparse-attention indexer cost" (gyaansetu.com),
   section "The two observations behind PIVOT": one proxy query, the mean of a
-  group of queries, is scored instead of each member.
+  group of consecutive queries, is scored instead of each member, and the
+  group's candidate set serves its members (section "Two operating modes":
+  reusing it as is is the faster mode).
 * [S2O] "S2O: Early Stopping for Sparse Attention via Online Permutation"
   (gist.science summary of arXiv 2602.22575), methodology part 3 "Kernel
   implementation": the online-softmax state (m, l, acc) is stored and resumed.
@@ -57,6 +59,17 @@ R9  sexp is a specified float32 exp (Cody-Waite reduction, degree-7 Taylor
     0 for x < -87.
 R10 Horvitz-Thompson weights: c_j = 1 on the deterministic set S and 1/pi_j on
     the sample R; output = sum c e^l v / sum c e^l over S u R.
+R16 Multi-query decode (PIVOT reuse): a step may carry T query positions per
+    sequence; with P the cache length (the T new tokens included), query t sits
+    at position P - T + t and attends to tokens [0, P - T + t].  Queries are
+    grouped g consecutive at a time (the last group may be smaller); a group's
+    proxy score of token j is the mean over its members and their query heads
+    of the partial logits (R1 over the group), over the group's span (the
+    last member's causal length).  One selection per (sequence, group, kv
+    head), drawn with Philox counter (j >> 2, h, b, group); every member
+    attends over it restricted to its own span, with the group's inclusion
+    probabilities (the restriction of a Horvitz-Thompson sum to a subset of
+    the population stays unbiased for that subset).
 R15 Top-p stratum: the approximate probability mass of token j is counted in
     integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
     top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
@@ -94,6 +107,9 @@ __all__ = [
     "ht_terms",
     "attend_unit",
     "decode",
+    "member_span",
+    "group_span",
+    "decode_multi",
 ]
 
 # Inputs arrive as a paged cache of 16-token blocks (layout, not arithmetic).
@@ -277,19 +293,20 @@ def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
     return [a.astype(np.uint32) for a in x]
 
 
-def philox_word(seed: int, b: int, h: int, j) -> np.ndarray:
-    """The 32-bit random word of token(s) j of (batch b, kv head h)."""
+def philox_word(seed: int, b: int, h: int, j, grp: int = 0) -> np.ndarray:
+    """The 32-bit random word of token(s) j of (batch b, kv head h, query
+    group grp): counter (j >> 2, h, b, grp) (R8, R16)."""
     j = np.asarray(j, dtype=np.int64)
-    words = philox4x32_10(j >> 2, np.full_like(j, h), np.full_like(j, b), np.zeros_like(j),
+    words = philox4x32_10(j >> 2, np.full_like(j, h), np.full_like(j, b), np.full_like(j, grp),
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
     sel = (j & 3).astype(np.int64)
     stacked = np.stack(words, axis=0)
     return np.take_along_axis(stacked, sel[None, ...], axis=0)[0]
 
 
-def uniforms(seed: int, b: int, h: int, j) -> np.ndarray:
+def uniforms(seed: int, b: int, h: int, j, grp: int = 0) -> np.ndarray:
     """u_j = (word >> 8) * 2^-24 as float32, in [0, 1)."""
-    w = philox_word(seed, b, h, j)
+    w = philox_word(seed, b, h, j, grp)
     return ((w >> np.uint32(8)).astype(np.float64) * 2.0 ** -24).astype(_F32)
 
 
@@ -334,21 +351,22 @@ def tail_stratum(s32: np.ndarray, topk: int, m: int, W_in=None, top_p=None):
     return dict(S=S, T=T, dense=False, M=M, W=W, w=w, mw=mw, pi=pi)
 
 
-def sample_tail(strata: dict, m: int, seed: int, b: int, h: int):
+def sample_tail(strata: dict, m: int, seed: int, b: int, h: int, grp: int = 0):
     """Poisson sample of the tail (reading R7): returns (R, pi_R)."""
     T, W = strata["T"], strata["W"]
     if strata["dense"] or m == 0 or T.size == 0 or not (W > 0):
         return np.zeros(0, np.int64), np.zeros(0, _F32)
-    u = uniforms(seed, b, h, T)
+    u = uniforms(seed, b, h, T, grp)
     keep = np.multiply(u, W, dtype=_F32) < strata["mw"]
     return T[keep], strata["pi"][keep]
 
 
 def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None,
-                top_p=None):
-    """Full selection of one (batch, kv head): dict with S, R, pi_R, M, W, dense."""
+                top_p=None, grp: int = 0):
+    """Full selection of one (batch, [query group,] kv head): dict with S, R,
+    pi_R, M, W, dense."""
     st = tail_stratum(s32, topk, m, W_in, top_p)
-    R, pi_R = sample_tail(st, m, seed, b, h)
+    R, pi_R = sample_tail(st, m, seed, b, h, grp)
     return dict(S=st["S"], R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"])
 
 
@@ -425,4 +443,64 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed
                           top_p=tp)
         out[b, h * G:(h + 1) * G, :] = attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
         info[(b, h)] = dict(scores=s64, **sel)
+    return out, info
+
+
+# ---------------------------------------------------------------------------
+# Multi-query decode with a shared proxy per query group (reading R16;
+# [PIVOT] "The two observations behind PIVOT", reuse mode)
+# ---------------------------------------------------------------------------
+
+def member_span(P: int, T: int, t: int) -> int:
+    """Causal length of query t of T: it sits at position P - T + t (R16)."""
+    return max(P - T + t + 1, 0)
+
+
+def group_span(P: int, T: int, g: int, grp: int) -> int:
+    """Causal length of group grp's last member: P - T + min((grp+1) g, T), >= 0."""
+    return max(P - T + min((grp + 1) * g, T), 0)
+
+
+def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
+                 pair_begin: int, pair_count: int, query_group: int,
+                 scale: float | None = None, units=None, top_p=None):
+    """T query positions per sequence, g = query_group per shared selection.
+
+    q [B, T, Hq, d]; seq_lens are the cache lengths P_b (the T new tokens
+    included).  ``units`` optionally restricts the work to (b, grp, h)
+    triples.  Returns (out [B, T, Hq, d] float64, info keyed by (b, grp, h)
+    with the group's scores and selection).
+    """
+    q = np.asarray(q)
+    B, T, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    g = int(query_group)
+    NG = -(-T // g)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.zeros((B, T, Hq, d))
+    info = {}
+    todo = units if units is not None else [(b, c, h) for b in range(B) for c in range(NG)
+                                            for h in range(Hkv)]
+    for b, c, h in todo:
+        P = int(seq_lens[b])
+        members = list(range(c * g, min((c + 1) * g, T)))
+        Lg = group_span(P, T, g, c)
+        K = gather_rows(k_cache, block_table[b], h, Lg)
+        V = gather_rows(v_cache, block_table[b], h, Lg)
+        # every member's query heads of this kv head, stacked: their mean is the proxy
+        qstack = np.concatenate([q[b, t, h * G:(h + 1) * G, :] for t in members]).astype(np.float64)
+        s64 = approx_scores(qstack, K, pair_begin, pair_count, scale)
+        tp = None if top_p is None else np.float32(top_p[b])
+        sel = select_unit(s64.astype(_F32), int(topk[b]), int(sample_budget[b]), int(seed[b]),
+                          b, h, top_p=tp, grp=c)
+        for t in members:
+            Lt = member_span(P, T, t)
+            S = sel["S"][sel["S"] < Lt]
+            keep = sel["R"] < Lt
+            qg = q[b, t, h * G:(h + 1) * G, :].astype(np.float64)
+            out[b, t, h * G:(h + 1) * G, :] = attend_unit(qg, K[:Lt], V[:Lt], S, sel["R"][keep],
+                                                          sel["pi_R"][keep], scale)
+        info[(b, c, h)] = dict(scores=s64, span=Lg, **sel)
     return out, info
