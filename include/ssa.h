@@ -36,8 +36,20 @@
  * Determinism. No floating-point atomics are used: identical inputs and
  *           seeds give bitwise identical outputs, and calls are reentrant.
  *
+ * Query positions.  A step carries T >= 1 query positions per sequence
+ *   (params.num_queries; multi-token decode).  seq_lens[b] = P_b is the cache
+ *   length with the T new tokens' keys already in it: query t sits at
+ *   position P_b - T + t and attends to tokens [0, P_b - T + t].  Queries are
+ *   grouped g = params.query_group consecutive at a time (the last group may
+ *   be smaller); a group is scored once with its proxy query, the mean of its
+ *   members' queries ("PIVOT slashes sparse-attention indexer cost", "The two
+ *   observations behind PIVOT"), and its one selection serves every member,
+ *   each restricted to its own span.  NG = ceil(T / g) groups per sequence.
+ *   Selection units are u = (b * NG + group) * Hkv + h.  T = g = 1 is plain
+ *   one-token decode.
+ *
  * Layouts (row-major, innermost last)
- *   q            [B, Hq, d]                      bf16 (post-RoPE query at position L_b)
+ *   q            [B, T, Hq, d]                   bf16 (post-RoPE queries)
  *   k_cache      [num_blocks, Hkv, 16, d]        bf16 (post-RoPE keys, interleaved pairs)
  *   v_cache      [num_blocks, Hkv, 16, d]        bf16
  *   block_table  [B, max_blocks_per_seq]         int32: token j of sequence b is row
@@ -45,14 +57,14 @@
  *   seq_lens, topk, sample_budget [B]            int32
  *   top_p        [B]                             f32, optional (NULL = top-k only)
  *   seed         [B]                             uint64 (one Philox key per sequence)
- *   out          [B, Hq, d]                      f32 or bf16 (params.out_dtype)
+ *   out          [B, T, Hq, d]                   f32 or bf16 (params.out_dtype)
  *
  * Selection layout (ssa_select output, ssa_attend input).  A sequence's
  * positions are cut into chunks of SSA_CHUNK_TOKENS; NC = ssa_num_chunks().
- *   sel_idx   [B, Hkv, NC * SSA_CHUNK_TOKENS]  int32 token positions
- *   sel_logw  [B, Hkv, NC * SSA_CHUNK_TOKENS]  f32   logit bias -log(pi_j): 0 on the
+ *   sel_idx   [B, NG, Hkv, NC * SSA_CHUNK_TOKENS]  int32 token positions
+ *   sel_logw  [B, NG, Hkv, NC * SSA_CHUNK_TOKENS]  f32   logit bias -log(pi_j): 0 on the
  *                                                     deterministic set, >= 0 on samples
- *   sel_count [B, Hkv, NC, 2]                  int32 (n_det, n_sampled) of each chunk
+ *   sel_count [B, NG, Hkv, NC, 2]                  int32 (n_det, n_sampled) of each chunk
  *   Segment c of a unit starts at c * SSA_CHUNK_TOKENS and holds the chunk's
  *   deterministic tokens (ascending) followed by its sampled tokens
  *   (ascending).  Chunks at or past L_b have count (0, 0).
@@ -104,9 +116,12 @@ typedef struct ssa_params {
   int32_t pair_begin;         /* first scored RoPE pair (pairs are dims (2p, 2p+1));      */
                               /*   a multiple of 4                                        */
   int32_t pair_count;         /* 4, 8, 16, 32 or 64 pairs; pair_begin + pair_count <= d/2 */
-  int32_t num_splits;         /* split-K slices per unit; 0 = one per chunk              */
+  int32_t num_splits;         /* split-K slices per query position and kv head;          */
+                              /*   0 = one per chunk                                      */
   int32_t out_dtype;          /* SSA_F32 or SSA_BF16                                     */
   float softmax_scale;        /* > 0; 0 selects 1 / sqrt(d)                              */
+  int32_t num_queries;        /* T >= 1 query positions per sequence                     */
+  int32_t query_group;        /* g >= 1 consecutive queries sharing one selection        */
 } ssa_params;
 
 /* Bytes of device workspace that ssa_decode / ssa_score / ssa_select /
@@ -148,15 +163,19 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache,
                      const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
                      void* stream, void* const* events);
 
-/* Stage 1 alone: approximate scores, scores[(b*Hkv + h)*max_seq_len + j] (f32),
- * for j < L_b; entries at or past L_b are left untouched.
- *   s_j = (1/G) sum_g scale * sum_{p in pairs} (q_g[2p] k_j[2p] + q_g[2p+1] k_j[2p+1]). */
+/* Stage 1 alone: approximate scores, scores[u * max_seq_len + j] (f32) of
+ * selection unit u = (b * NG + group) * Hkv + h, for j below the group's span
+ * (its last member's causal length); later entries are left untouched.
+ *   s_j = (1/(n G)) sum over the group's n members and G heads of
+ *         scale * sum_{p in pairs} (q[2p] k_j[2p] + q[2p+1] k_j[2p+1]). */
 int ssa_score(const ssa_params* p, const void* q, const void* k_cache,
               const int32_t* block_table, const int32_t* seq_lens, float* scores,
               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Stages 2-4 alone, from a caller-provided score array laid out as ssa_score
- * writes it; topk, top_p (may be NULL) and sample_budget as for ssa_decode.
+ * writes it (one row per selection unit, valid over the unit's span); topk,
+ * top_p (may be NULL) and sample_budget as for ssa_decode.  Sampling for
+ * (b, group, h, token j) uses counter (j >> 2, h, b, group).
  * If w_in is non-NULL, w_in[b*Hkv + h] replaces the computed tail normaliser
  * W.  Writes the selection (layout above) and norm_out [B, Hkv, 2] = (M, W):
  * the maximum score and the normaliser actually used. */
@@ -166,16 +185,18 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
                int32_t* sel_count, float* norm_out, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* Stages 5-6 alone: attention over a caller-provided selection:
+/* Stages 5-6 alone: attention over a caller-provided selection (one per
+ * selection unit), for every query position t and head g of the unit's group:
  *   out_g = sum_A e^{l_gj + logw_j} v_j / sum_A e^{l_gj + logw_j},
- *   l_gj = scale * q_g . k_j over the full head dimension. */
+ *   l_gj = scale * q_g . k_j over the full head dimension, A = the unit's
+ *   selected positions below the query's span (later ones are ignored). */
 int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
                const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
                size_t workspace_bytes, void* stream);
 
-/* Test hook: words[i] = the Philox word of (seed, b, h, token j0 + i), i < n. */
-int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t j0, int32_t n,
+/* Test hook: words[i] = the Philox word of (seed, b, h, group, token j0 + i), i < n. */
+int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t group, int32_t j0, int32_t n,
                      uint32_t* words, void* stream);
 
 /* Test hook: y[i] = the library's specified float32 exp of x[i], i < n. */

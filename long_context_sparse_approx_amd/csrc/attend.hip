@@ -10,7 +10,10 @@
 // Permutation", methodology part 3: each split keeps the online-softmax
 // state (m, l, acc); the merge resumes from the stored states.
 //
-// One wavefront per (unit, split).  A tile is 32 selected tokens; both
+// One wavefront per (attention unit, split): an attention unit is one query
+// position t of sequence b with one kv head h; it reads the selection of its
+// query group's unit, restricted to its own causal span [0, P - T + t].
+// A tile is 32 selected tokens; both
 // products run on MFMA v_mfma_f32_16x16x32_bf16:
 //   QK:  D[16 tokens x 16 heads] = K_tile[16 x 32 dims] * Q^T[32 dims x 16 heads],
 //        two halves of 16 tokens, d/32 steps each; query heads beyond the
@@ -72,13 +75,16 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   __shared__ float lw_sh[kBatch + 32];
 
   const int s = blockIdx.x;
-  const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const int h = u - b * a.Hkv;
+  const int au = blockIdx.y;
+  const int bt = au / a.Hkv;  // b * T + t
+  const int h = au - bt * a.Hkv;
+  const int b = bt / a.T;
+  const int t = bt - b * a.T;
+  const int u = (b * a.NG + t / a.g) * a.Hkv + h;  // the selection unit
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int L = member_span(clamp_len(a.seq_lens[b], a.max_seq_len), a.T, t);
   const int ncL = (L + kChunk - 1) / kChunk;
   const int c_begin = (int)((int64_t)s * ncL / a.nsplit);
   const int c_end = (int)((int64_t)(s + 1) * ncL / a.nsplit);
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   bf16x8 qf[KK];
   {
     const bool gv = n16 < a.G;
-    const uint16_t* qrow = a.q + (size_t)(b * a.Hq + h * a.G + (gv ? n16 : 0)) * D;
+    const uint16_t* qrow = a.q + (size_t)(bt * a.Hq + h * a.G + (gv ? n16 : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -107,9 +113,9 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   const size_t seg = (size_t)u * a.seg_ld;
   for (int c = c_begin; c < c_end; ++c) {
     const int32_t* cntp = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
-    // Counts and entries of a caller-provided selection are clamped to the
-    // segment, to [0, L) and to the cache so that no value can address
-    // outside the buffers.
+    // Counts of a caller-provided selection are clamped to the segment and
+    // rows to the cache; positions at or past the member's span are masked:
+    // no value can address outside the buffers.
     const int cnt = min(max(cntp[0], 0) + max(cntp[1], 0), kChunk);
     const int32_t* idxp = a.sel_idx + seg + (size_t)c * kChunk;
     const float* lwp = a.sel_logw + seg + (size_t)c * kChunk;
@@ -126,11 +132,13 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
           lw = lwp[b0 + i];
           if (a.idx_are_rows) {
             row = min(max(v, 0), max_row);
-          } else {
-            const int idx = min(max(v, 0), L - 1);
+          } else if (v < L) {  // positions past the member's span are masked
+            const int idx = max(v, 0);
             int blk = btrow[idx >> 4];
             blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
             row = (blk * a.Hkv + h) * kBlockTokens + (idx & 15);
+          } else {
+            lw = -INFINITY;
           }
         }
         rows_sh[i] = row;
@@ -183,13 +191,16 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __expf(m_run - m_new);
+        // A tile of masked entries only (m_new still -inf) must add nothing:
+        // exponentiate against 0 instead of -inf.
+        const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+        const float alpha = __expf(m_run - m_ref);
         float psum = 0.0f;
         uint32_t phi[4], plo[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-          const float p0 = __expf(x[i] - m_new);
-          const float p1 = __expf(x[i + 1] - m_new);
+          const float p0 = __expf(x[i] - m_ref);
+          const float p1 = __expf(x[i + 1] - m_ref);
           psum += p0 + p1;
           const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
           const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
@@ -236,20 +247,20 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   for (int r = 0; r < 4; ++r) {
     const int g = 4 * q4 + r;
     if (g < a.G) {
-      float* dst = a.part + ((size_t)(b * a.Hq + h * a.G + g) * a.nsplit + s) * stride + n16 * DPL;
+      float* dst = a.part + ((size_t)(bt * a.Hq + h * a.G + g) * a.nsplit + s) * stride + n16 * DPL;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
     }
   }
   if (q4 == 0 && n16 < a.G) {
-    float* dst = a.part + ((size_t)(b * a.Hq + h * a.G + n16) * a.nsplit + s) * stride + D;
+    float* dst = a.part + ((size_t)(bt * a.Hq + h * a.G + n16) * a.nsplit + s) * stride + D;
     dst[0] = m_run;
     dst[1] = l_run;
   }
 }
 
-// Merge of the split states of one (sequence, query head), for one 64-dim
-// slice of the head (grid: B*Hq x d/64):
+// Merge of the split states of one (query position, query head), for one
+// 64-dim slice of the head (grid: B*T*Hq x d/64):
 //   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
 // in a fixed order (deterministic).  The split weights e^{m_s - m*} are
 // computed once into LDS; each wave then takes every kMW-th split (lane =
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
-  dim3 grid(a.nsplit, a.B * a.Hkv);
+  dim3 grid(a.nsplit, a.B * a.T * a.Hkv);
   if (a.d == 128)
     attend_kernel<128><<<grid, 64, 0, stream>>>(a);
   else if (a.d == 64)
@@ -328,7 +339,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
-  merge_kernel<<<dim3(a.B * a.Hq, a.d / 64), kMT, 0, stream>>>(a);
+  merge_kernel<<<dim3(a.B * a.T * a.Hq, a.d / 64), kMT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -162,9 +162,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   float* qsh = sbuf;
 
   const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const int h = u - b * a.Hkv;
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const int h = ui.h;
+  const int L = ui.L;
   const int t0 = blockIdx.x * a.tokens_per_wg;
   if (t0 >= L) return;  // uniform over the workgroup
   const int t_end = min(L, t0 + a.tokens_per_wg);
@@ -172,14 +173,30 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nd = 2 * a.pair_count;
-
-  // Stage the query group's scored slice and the tile's block offsets in LDS.
-  for (int i = tid; i < a.G * nd; i += 256) {
-    const int g = i / nd;
-    const int e = i - g * nd;
-    const uint16_t bits =
-        a.q[(size_t)(b * a.Hq + h * a.G + g) * a.d + 2 * a.pair_begin + e];
-    qsh[i] = __uint_as_float((uint32_t)bits << 16);
+  const int sub = lane % LPT;
+  // Proxy query: the mean over the group's members (consecutive query
+  // positions) and their G query heads, accumulated member by member.
+  const int t_first = ui.grp * a.g;
+  const int t_last = min(t_first + a.g, a.T);
+  float qf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qf[i] = 0.0f;
+  for (int t = t_first; t < t_last; ++t) {
+    for (int i = tid; i < a.G * nd; i += 256) {
+      const int g = i / nd;
+      const int e = i - g * nd;
+      const uint16_t bits =
+          a.q[((size_t)(b * a.T + t) * a.Hq + h * a.G + g) * a.d + 2 * a.pair_begin + e];
+      qsh[i] = __uint_as_float((uint32_t)bits << 16);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = 0.0f;
+      for (int g = 0; g < a.G; ++g) s += qsh[g * nd + sub * 8 + i];
+      qf[i] += s;
+    }
+    __syncthreads();
   }
   const int blk0 = t0 / kBlockTokens;
   const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
@@ -190,19 +207,14 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
     blk_sh[i] = (uint32_t)(blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk));
   }
   __syncthreads();
-  // Per-lane proxy query over this lane's 8 dims, qbar = (scale / G) * sum_g q_g,
-  // split into bf16 hi and lo parts packed two dims per word.
-  const int sub = lane % LPT;
+  // Per-lane proxy query over this lane's 8 dims, qbar = (scale / (G n)) *
+  // sum over the n members and G heads, split into bf16 hi and lo parts
+  // packed two dims per word.
   uint32_t qh[4], ql[4];
   {
-    const float qscale = a.scale / (float)a.G;
-    float qf[8];
+    const float qscale = a.scale / (float)(a.G * (t_last - t_first));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float s = 0.0f;
-      for (int g = 0; g < a.G; ++g) s += qsh[g * nd + sub * 8 + i];
-      qf[i] = s * qscale;
-    }
+    for (int i = 0; i < 8; ++i) qf[i] *= qscale;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t h0 = f32_to_bf16_bits(qf[2 * i]), h1 = f32_to_bf16_bits(qf[2 * i + 1]);
@@ -212,7 +224,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
       ql[i] = l0 | (l1 << 16);
     }
   }
-  __syncthreads();
   for (int i = tid; i < kBins / 2; i += 256) hist[i] = 0u;
   __syncthreads();
 
@@ -277,8 +288,7 @@ __global__ __launch_bounds__(256) void score_hist_kernel(SelectArgs a) {
   __shared__ uint32_t wmax[4];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int L = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len).L;
   const int c0 = c * kChunk;
   if (c0 >= L) return;
   const int c1 = min(L, c0 + kChunk);

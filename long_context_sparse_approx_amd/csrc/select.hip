@@ -50,8 +50,9 @@ __global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
   __shared__ unsigned long long mh[kBins];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
   const float M = key_to_float(a.maxkey[u]);
@@ -96,8 +97,9 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ unsigned long long pair_m[2];
   __shared__ double dscr[kNT / 64];
   const int u = blockIdx.x;
-  const int b = u / a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   if (p.dense || p.L == 0) {
     if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0, 0ull, 0, 0};
     return;
@@ -154,15 +156,16 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const int h = u - b * a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const int h = ui.h;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const Thresh1 t1 = a.thresh[u];
   const float M = key_to_float(a.maxkey[u]);
   stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
-  filter_chunk(a, p, t1, M, u, b, h, c, sh, scan_scr, dscr);
+  filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, sh, scan_scr, dscr);
 }
 
 // ------------------------------------------------------------------ resolve
@@ -196,8 +199,9 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ double dscr[kRW];
 
   const int u = blockIdx.x;
-  const int b = u / a.Hkv;
-  const SeqParams p = seq_params(a.seq_lens, a.topk, a.top_p, a.sample_budget, b, a.max_seq_len);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -392,10 +396,10 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 // sampled tokens ascending.  With emit_rows the segment holds cache row
 // numbers (for the fused attention stage) instead of positions.
 __device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, int b, int h,
-                                           int t, float w, int c0, int nvalid, uint8_t* flag,
-                                           float* lwsh) {
+                                           int grp, int t, float w, int c0, int nvalid,
+                                           uint8_t* flag, float* lwsh) {
   if ((unsigned)(t - c0) >= (unsigned)nvalid) return;  // not a position of this chunk
-  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2);
+  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, grp);
   const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
   const float mw = (float)st.m * w;
   if (uniform24(words[t & 3]) * st.W < mw) {
@@ -412,8 +416,9 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int b = u / a.Hkv;
-  const int h = u - b * a.Hkv;
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const int h = ui.h;
   const int c0 = c * kChunk;
   const size_t ci = (size_t)u * a.nchunk + c;
   // Independent loads first: unit state, per-chunk counts, the chunk's block ids.
@@ -451,7 +456,8 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     }
     if (sampling)
       for (int i = threadIdx.x; i < n_samp; i += kNT)
-        sample_one(st, seed, b, h, lidx[n_above + i], lw[n_above + i], c0, nvalid, flag, lwsh);
+        sample_one(st, seed, b, h, ui.grp, lidx[n_above + i], lw[n_above + i], c0, nvalid, flag,
+                   lwsh);
     if (!(st.flags & kFlagNoTopk)) {
       // Threshold-digit candidates, in index order: key above T -> S; key == T
       // -> S while the tie quota lasts; otherwise a tail token.
@@ -471,8 +477,8 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
             if ((unsigned)(t - c0) < (unsigned)nvalid) flag[t - c0] = 1;
           } else if (sampling) {
-            sample_one(st, seed, b, h, t, sexp(key_to_float(key) - st.M), c0, nvalid, flag,
-                       lwsh);
+            sample_one(st, seed, b, h, ui.grp, t, sexp(key_to_float(key) - st.M), c0, nvalid,
+                       flag, lwsh);
           }
         }
       }
@@ -523,11 +529,12 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------------ test hooks
 
-__global__ void debug_philox_kernel(uint64_t seed, int b, int h, int j0, int n, uint32_t* words) {
+__global__ void debug_philox_kernel(uint64_t seed, int b, int h, int grp, int j0, int n,
+                                    uint32_t* words) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const uint32_t j = (uint32_t)(j0 + i);
-  const uint4 wd = philox_block(seed, b, h, j >> 2);
+  const uint4 wd = philox_block(seed, b, h, j >> 2, grp);
   const uint32_t w4[4] = {wd.x, wd.y, wd.z, wd.w};
   words[i] = w4[j & 3u];
 }
@@ -564,9 +571,9 @@ hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_philox(uint64_t seed, int b, int h, int j0, int n, uint32_t* words,
-                               hipStream_t stream) {
-  debug_philox_kernel<<<(n + 255) / 256, 256, 0, stream>>>(seed, b, h, j0, n, words);
+hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int n,
+                               uint32_t* words, hipStream_t stream) {
+  debug_philox_kernel<<<(n + 255) / 256, 256, 0, stream>>>(seed, b, h, grp, j0, n, words);
   return hipGetLastError();
 }
 

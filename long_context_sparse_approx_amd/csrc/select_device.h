@@ -23,7 +23,7 @@ __device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, in
   __syncthreads();
 }
 
-// Filter of chunk c of unit u by a 256-thread workgroup.  `sh` holds the
+// Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  `sh` holds the
 // chunk's scores (entries at or past L are ignored); t1 is the unit's
 // first-digit threshold and M its maximum score.  Writes the chunk's
 // candidates (positions and keys, second-digit histogram), its lists (tokens
@@ -34,7 +34,7 @@ __device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, in
 // masks select what counts.
 __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParams& p,
                                              const Thresh1& t1, float M, int u, int b, int h,
-                                             int c, const float* sh, int* scan_scr,
+                                             int grp, int c, const float* sh, int* scan_scr,
                                              double* dscr) {
   const int c0 = c * kChunk;
   const int b1 = t1.b1;  // 2048 when there is no deterministic set
@@ -67,7 +67,7 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   if (sampling) {
 #pragma unroll
     for (int g = 0; g < kPer / 4; ++g) {
-      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2);
+      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2, grp);
       const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {

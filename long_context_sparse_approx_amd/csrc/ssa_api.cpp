@@ -43,12 +43,16 @@ bool params_ok(const ssa_params* p) {
   if (p->num_splits < 0) return false;
   if (p->out_dtype != SSA_F32 && p->out_dtype != SSA_BF16) return false;
   if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale)) return false;
-  if ((int64_t)p->batch * p->num_kv_heads > 65535) return false;  // grid.y
+  if (p->num_queries < 1 || p->num_queries > 256 || p->query_group < 1) return false;
+  const int64_t ng = (p->num_queries + p->query_group - 1) / p->query_group;
+  // grid.y of the per-unit and per-(query position, kv head) launches
+  if ((int64_t)p->batch * ng * p->num_kv_heads > 65535) return false;
+  if ((int64_t)p->batch * p->num_queries * p->num_kv_heads > 65535) return false;
   return true;
 }
 
 struct Dims {
-  int B, Hq, Hkv, G, d, U, NC, NS;
+  int B, Hq, Hkv, G, d, T, g, NG, U, NC, NS;
   int64_t SEG;
   float scale;
 };
@@ -60,7 +64,10 @@ Dims dims_of(const ssa_params* p) {
   d.Hkv = p->num_kv_heads;
   d.G = d.Hq / d.Hkv;
   d.d = p->head_dim;
-  d.U = d.B * d.Hkv;
+  d.T = p->num_queries;
+  d.g = p->query_group < p->num_queries ? p->query_group : p->num_queries;
+  d.NG = (d.T + d.g - 1) / d.g;
+  d.U = d.B * d.NG * d.Hkv;  // selection units
   d.NC = (p->max_seq_len + SSA_CHUNK_TOKENS - 1) / SSA_CHUNK_TOKENS;
   d.SEG = (int64_t)d.NC * SSA_CHUNK_TOKENS;
   d.NS = p->num_splits == 0 ? d.NC : (p->num_splits < d.NC ? p->num_splits : d.NC);
@@ -103,7 +110,7 @@ Layout layout_of(const Dims& d) {
   l.sel_idx = take(U * SEG * 4);
   l.sel_logw = take(U * SEG * 4);
   l.sel_cnt = take(U * NC * 2 * 4);
-  l.part = take((size_t)d.B * d.Hq * d.NS * (d.d + 2) * 4);
+  l.part = take((size_t)d.B * d.T * d.Hq * d.NS * (d.d + 2) * 4);
   l.total = off;
   return l;
 }
@@ -153,6 +160,9 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
   a.score_ld = score_ld;
   a.hist1 = at<uint32_t>(ws, l.hist1);
   a.maxkey = at<uint32_t>(ws, l.maxkey);
+  a.T = d.T;
+  a.g = d.g;
+  a.NG = d.NG;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
   a.G = d.G;
@@ -204,6 +214,9 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.sel_logw = sel_logw;
   a.sel_cnt = sel_cnt;
   a.norm_out = norm_out;
+  a.T = d.T;
+  a.g = d.g;
+  a.NG = d.NG;
   a.Hkv = d.Hkv;
   a.max_seq_len = p->max_seq_len;
   a.nchunk = d.NC;
@@ -230,6 +243,9 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
   a.sel_cnt = sel_cnt;
   a.part = at<float>(ws, l.part);
   a.out = out;
+  a.T = d.T;
+  a.g = d.g;
+  a.NG = d.NG;
   a.B = d.B;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -315,11 +331,15 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
 
   const ssa::IndexArgs ia =
       index_args(p, d, q, k_cache, block_table, seq_lens, scores, d.SEG, workspace, l);
+  // One query per sequence: the selection can hold cache rows (one dependent
+  // load less in the gather).  Several: positions, so that every member
+  // applies its own causal span.
+  const int rows = d.T == 1 ? 1 : 0;
   const ssa::SelectArgs sa =
       select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr,
-                  block_table, /*emit_rows=*/1, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
+                  block_table, rows, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
   const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
-                                         sel_logw, sel_cnt, /*idx_are_rows=*/1, out, workspace, l);
+                                         sel_logw, sel_cnt, rows, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(launch_init_for(sa, d.U, s));
   rec.end(SSA_STAGE_INIT);
@@ -415,12 +435,13 @@ int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const vo
   return SSA_OK;
 }
 
-int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t j0, int32_t n, uint32_t* words,
-                     void* stream) {
-  if (!words || n < 0 || j0 < 0 || b < 0 || h < 0) return SSA_ERR_INVALID;
+int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t group, int32_t j0, int32_t n,
+                     uint32_t* words, void* stream) {
+  if (!words || n < 0 || j0 < 0 || b < 0 || h < 0 || group < 0) return SSA_ERR_INVALID;
   if ((int64_t)j0 + n > INT32_MAX) return SSA_ERR_INVALID;
   if (n == 0) return SSA_OK;
-  SSA_TRY(ssa::launch_debug_philox(seed, b, h, j0, n, words, static_cast<hipStream_t>(stream)));
+  SSA_TRY(ssa::launch_debug_philox(seed, b, h, group, j0, n, words,
+                                   static_cast<hipStream_t>(stream)));
   return SSA_OK;
 }
 

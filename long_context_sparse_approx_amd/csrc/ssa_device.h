@@ -152,10 +152,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// The four words for tokens 4*jq .. 4*jq+3 of (b, h): counter (jq, h, b, 0),
-// key = the 64-bit seed, low word first.
-__device__ __forceinline__ uint4 philox_block(uint64_t seed, int b, int h, uint32_t jq) {
-  return philox4x32_10(make_uint4(jq, (uint32_t)h, (uint32_t)b, 0u), (uint32_t)seed,
+// The four words for tokens 4*jq .. 4*jq+3 of (b, h, query group grp):
+// counter (jq, h, b, grp), key = the 64-bit seed, low word first.
+__device__ __forceinline__ uint4 philox_block(uint64_t seed, int b, int h, uint32_t jq,
+                                              int grp) {
+  return philox4x32_10(make_uint4(jq, (uint32_t)h, (uint32_t)b, (uint32_t)grp), (uint32_t)seed,
                        (uint32_t)(seed >> 32));
 }
 
@@ -332,7 +333,32 @@ __device__ __forceinline__ DigitBound combine_bounds(int mode, int bc, int rc, i
   return DigitBound{bc, rc, rm, kBoundCount | kBoundMass};
 }
 
-// Selection parameters of sequence b as the kernels read them.  k_eff is the
+// A selection unit: (sequence b, query group grp, kv head h), numbered
+// u = (b * NG + grp) * Hkv + h.  With T query positions per sequence (the last
+// T of its P cached tokens) and groups of g consecutive queries, the unit's
+// span is the causal length of the group's last member.
+struct UnitInfo {
+  int b, grp, h, L;
+};
+
+__device__ __forceinline__ int member_span(int P, int T, int t) {
+  const int L = P - T + t + 1;
+  return L < 0 ? 0 : L;
+}
+
+__device__ __forceinline__ UnitInfo unit_info(int u, int Hkv, int NG, int T, int g,
+                                              const int32_t* seq_lens, int max_seq_len) {
+  UnitInfo r;
+  const int bg = u / Hkv;
+  r.h = u - bg * Hkv;
+  r.b = bg / NG;
+  r.grp = bg - r.b * NG;
+  const int last = min((r.grp + 1) * g, T) - 1;
+  r.L = member_span(clamp_len(seq_lens[r.b], max_seq_len), T, last);
+  return r;
+}
+
+// Selection parameters of a unit as the kernels read them.  k_eff is the
 // count bound min(topk, L).  With a top-p mass the stratum may end earlier,
 // so only m >= L makes the unit dense before the selection is resolved.
 struct SeqParams {
@@ -342,12 +368,10 @@ struct SeqParams {
   float p;
 };
 
-__device__ __forceinline__ SeqParams seq_params(const int32_t* seq_lens, const int32_t* topk,
-                                                const float* top_p,
-                                                const int32_t* sample_budget, int b,
-                                                int max_seq_len) {
+__device__ __forceinline__ SeqParams seq_params(int L, const int32_t* topk, const float* top_p,
+                                                const int32_t* sample_budget, int b) {
   SeqParams p;
-  p.L = clamp_len(seq_lens[b], max_seq_len);
+  p.L = L;
   const int k = max(topk[b], 0);
   p.m = max(sample_budget[b], 0);
   p.topp = top_p != nullptr;

@@ -37,17 +37,21 @@ struct IndexArgs {
   const uint16_t* k_cache;    // [num_blocks, Hkv, 16, d] bf16
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* seq_lens;    // [B]
-  float* scores;              // row (b*Hkv + h) of stride score_ld
+  float* scores;              // row u of stride score_ld
   int64_t score_ld;
   uint32_t* hist1;            // [U, 2048]
   uint32_t* maxkey;           // [U]
+  int T, g, NG;               // queries per sequence, queries per group, groups
   int Hq, Hkv, G, d, pair_begin, pair_count;
   int max_blocks, num_blocks, max_seq_len, tokens_per_wg;
   float scale;
 };
 
+// Units: selection units u = (b * NG + grp) * Hkv + h (one per sequence,
+// query group and kv head); attention units (b * T + t) * Hkv + h (one per
+// query position and kv head).
 struct SelectArgs {
-  const float* scores;        // row (b*Hkv + h) of stride score_ld
+  const float* scores;        // row u of stride score_ld
   int64_t score_ld;
   const int32_t* seq_lens;
   const int32_t* topk;
@@ -76,6 +80,7 @@ struct SelectArgs {
   float* sel_logw;            // [U, seg_ld]
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
+  int T, g, NG;
   int Hkv, max_seq_len, nchunk, max_blocks, num_blocks, emit_rows;
   int64_t seg_ld;             // nchunk * 4096
 };
@@ -89,8 +94,9 @@ struct AttendArgs {
   const int32_t* sel_idx;     // positions, or cache rows when idx_are_rows
   const float* sel_logw;
   const int32_t* sel_cnt;
-  float* part;                // [B*Hq, nsplit, d + 2]: acc[d], m, l
-  void* out;                  // [B, Hq, d]
+  float* part;                // [B*T*Hq, nsplit, d + 2]: acc[d], m, l
+  void* out;                  // [B, T, Hq, d]
+  int T, g, NG;
   int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
   int idx_are_rows;
   int64_t seg_ld;
@@ -113,8 +119,8 @@ hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
-hipError_t launch_debug_philox(uint64_t seed, int b, int h, int j0, int n, uint32_t* words,
-                               hipStream_t stream);
+hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int n,
+                               uint32_t* words, hipStream_t stream);
 hipError_t launch_debug_sexp(const float* x, float* y, int n, hipStream_t stream);
 
 }  // namespace ssa

@@ -37,7 +37,8 @@ class SsaParams(ctypes.Structure):
                 ("num_blocks", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("pair_begin", ctypes.c_int32), ("pair_count", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("num_queries", ctypes.c_int32),
+                ("query_group", ctypes.c_int32)]
 
 
 class SsaError(RuntimeError):
@@ -76,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.ssa_attend.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_attend.restype = ctypes.c_int
         L.ssa_debug_philox.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
-                                       ctypes.c_int32, ctypes.c_int32, _P, _P]
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
         L.ssa_debug_philox.restype = ctypes.c_int
         L.ssa_debug_sexp.argtypes = [_P, _P, ctypes.c_int32, _P]
         L.ssa_debug_sexp.restype = ctypes.c_int
@@ -107,20 +108,32 @@ def _stream(stream):
 
 def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                 max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
-                softmax_scale=0.0, block_size=BLOCK_TOKENS) -> SsaParams:
+                softmax_scale=0.0, block_size=BLOCK_TOKENS, num_queries=1,
+                query_group=1) -> SsaParams:
     if pair_begin is None:
         pair_begin = head_dim // 2 - pair_count
     return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
-                     float(softmax_scale))
+                     float(softmax_scale), int(num_queries), int(query_group))
 
 
 def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
-    """Params from tensor shapes: q [B, Hq, d], k_cache [nblk, Hkv, 16, d]."""
-    B, Hq, d = q.shape
+    """Params from tensor shapes: q [B, Hq, d] or [B, T, Hq, d] (T query
+    positions per sequence), k_cache [nblk, Hkv, 16, d]."""
+    if q.dim() == 3:
+        B, Hq, d = q.shape
+        T = 1
+    else:
+        B, T, Hq, d = q.shape
+    kw.setdefault("num_queries", T)
     return make_params(batch=B, num_q_heads=Hq, num_kv_heads=k_cache.shape[1], head_dim=d,
                        max_blocks_per_seq=block_table.shape[1], num_blocks=k_cache.shape[0],
                        max_seq_len=int(max_seq_len), **kw)
+
+
+def num_groups(p: SsaParams) -> int:
+    g = min(p.query_group, p.num_queries)
+    return -(-p.num_queries // g)
 
 
 def workspace_bytes(p: SsaParams) -> int:
@@ -171,10 +184,11 @@ def decode(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk, sampl
 
 def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspace=None,
           stream=None):
-    """Approximate scores [B, Hkv, max_seq_len] f32 (entries past L_b untouched)."""
+    """Approximate scores [B, NG*Hkv, max_seq_len] f32, one row per selection
+    unit (group-major; entries past the unit's span untouched)."""
     if scores is None:
-        scores = torch.zeros((p.batch, p.num_kv_heads, p.max_seq_len), dtype=torch.float32,
-                             device=q.device)
+        scores = torch.zeros((p.batch, num_groups(p) * p.num_kv_heads, p.max_seq_len),
+                             dtype=torch.float32, device=q.device)
     workspace = _ws(p, workspace, q.device)
     _check(lib().ssa_score(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(block_table),
                            _ptr(seq_lens), _ptr(scores), _ptr(workspace),
@@ -184,16 +198,17 @@ def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspac
 
 def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None, workspace=None,
            stream=None, top_p=None):
-    """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out)."""
+    """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out),
+    each [B, NG*Hkv, ...] (one row per selection unit)."""
     _check_top_p(top_p, p.batch)
     dev = scores.device
     nc = num_chunks(p)
-    U = p.batch * p.num_kv_heads
-    sel_idx = torch.empty((p.batch, p.num_kv_heads, nc * CHUNK_TOKENS), dtype=torch.int32, device=dev)
-    sel_logw = torch.empty((p.batch, p.num_kv_heads, nc * CHUNK_TOKENS), dtype=torch.float32,
-                           device=dev)
-    sel_count = torch.empty((p.batch, p.num_kv_heads, nc, 2), dtype=torch.int32, device=dev)
-    norm = torch.empty((p.batch, p.num_kv_heads, 2), dtype=torch.float32, device=dev)
+    UH = num_groups(p) * p.num_kv_heads
+    U = p.batch * UH
+    sel_idx = torch.empty((p.batch, UH, nc * CHUNK_TOKENS), dtype=torch.int32, device=dev)
+    sel_logw = torch.empty((p.batch, UH, nc * CHUNK_TOKENS), dtype=torch.float32, device=dev)
+    sel_count = torch.empty((p.batch, UH, nc, 2), dtype=torch.int32, device=dev)
+    norm = torch.empty((p.batch, UH, 2), dtype=torch.float32, device=dev)
     workspace = _ws(p, workspace, dev)
     assert w_in is None or w_in.numel() == U
     _check(lib().ssa_select(ctypes.byref(p), _ptr(scores), _ptr(seq_lens), _ptr(topk),
@@ -217,9 +232,9 @@ def attend(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, sel_idx, se
     return out
 
 
-def debug_philox(seed: int, b: int, h: int, j0: int, n: int, device="cuda"):
+def debug_philox(seed: int, b: int, h: int, j0: int, n: int, device="cuda", group: int = 0):
     words = torch.empty(n, dtype=torch.int32, device=device)
-    _check(lib().ssa_debug_philox(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), b, h, j0, n,
+    _check(lib().ssa_debug_philox(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), b, h, group, j0, n,
                                   _ptr(words), _stream(None)), "ssa_debug_philox")
     return words
 

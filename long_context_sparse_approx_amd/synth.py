@@ -176,8 +176,8 @@ def make_workload(name_or_cfg, device="cpu", *, L=None, B=None, topk=None, m=Non
     block_table = torch.zeros((B, max_blocks), dtype=torch.int32, device=device)
     k_cache = torch.zeros((total, Hkv, BLOCK, d), dtype=torch.bfloat16, device=device)
     v_cache = torch.zeros_like(k_cache)
-    T = int(num_queries)
-    q_all = torch.empty((B, Hq, d) if T == 1 else (B, T, Hq, d), dtype=torch.bfloat16,
+    nq = int(num_queries)
+    q_all = torch.empty((B, Hq, d) if nq == 1 else (B, nq, Hq, d), dtype=torch.bfloat16,
                         device=device)
     off = 0
     for b in range(B):
@@ -185,19 +185,19 @@ def make_workload(name_or_cfg, device="cpu", *, L=None, B=None, topk=None, m=Non
         phys = perm[off:off + nblk[b]]
         off += nblk[b]
         block_table[b, :nblk[b]] = phys
-        if T == 1:
+        if nq == 1:
             qb = torch.randn((1, Hq, d), generator=gen, device=device, dtype=torch.float32)
             cq, sq = rope_tables(torch.tensor([L_], device=device), d, cfg["theta"])
             qb = apply_rope(qb, cq, sq)[0].to(torch.bfloat16)
             q_all[b] = qb
             qbar = qb.float().view(Hkv, G, d).mean(dim=1)  # [Hkv, d]
         else:
-            qb = torch.randn((T, Hq, d), generator=gen, device=device, dtype=torch.float32)
-            pos = torch.arange(L_ - T, L_, device=device)
+            qb = torch.randn((nq, Hq, d), generator=gen, device=device, dtype=torch.float32)
+            pos = torch.arange(L_ - nq, L_, device=device)
             cq, sq = rope_tables(pos, d, cfg["theta"])
             qb = apply_rope(qb, cq, sq).to(torch.bfloat16)
             q_all[b] = qb
-            qbar = qb.float().view(T, Hkv, G, d).mean(dim=(0, 2))  # [Hkv, d]
+            qbar = qb.float().view(nq, Hkv, G, d).mean(dim=(0, 2))  # [Hkv, d]
         uhat = qbar / qbar.norm(dim=-1, keepdim=True)
         planted = int(cfg["planted"])
         plant_pos = []

@@ -59,7 +59,8 @@ def test_workspace_size_for_valid_params(lib):
     dict(pair_count=0), dict(pair_begin=2), dict(pair_begin=-4), dict(pair_begin=40),
     dict(max_seq_len=1025), dict(max_seq_len=0), dict(block_size=32), dict(num_splits=-1),
     dict(out_dtype=7), dict(softmax_scale=-1.0), dict(softmax_scale=float("nan")),
-    dict(batch=0), dict(num_kv_heads=0), dict(num_blocks=0),
+    dict(batch=0), dict(num_kv_heads=0), dict(num_blocks=0), dict(num_queries=0),
+    dict(query_group=0), dict(num_queries=257), dict(batch=4000, num_queries=4),
     dict(num_blocks=1 << 24, num_kv_heads=8),
 ])
 def test_invalid_params_rejected(lib, bad):
@@ -107,9 +108,10 @@ def test_small_workspace_rejected(lib):
 
 
 def test_debug_hooks_validate(lib):
-    assert lib.ssa_debug_philox(0, 0, 0, 0, -1, ctypes.c_void_p(4096), None) == ssa.SSA_ERR_INVALID
-    assert lib.ssa_debug_philox(0, 0, 0, 2**31 - 4, 8, ctypes.c_void_p(4096), None) == ssa.SSA_ERR_INVALID
-    assert lib.ssa_debug_philox(0, 0, 0, 0, 0, ctypes.c_void_p(4096), None) == ssa.SSA_OK
+    assert lib.ssa_debug_philox(0, 0, 0, 0, 0, -1, ctypes.c_void_p(4096), None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_debug_philox(0, 0, 0, 0, 2**31 - 4, 8, ctypes.c_void_p(4096), None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_debug_philox(0, 0, 0, -1, 0, 4, ctypes.c_void_p(4096), None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_debug_philox(0, 0, 0, 0, 0, 0, ctypes.c_void_p(4096), None) == ssa.SSA_OK
     assert lib.ssa_debug_sexp(None, ctypes.c_void_p(4096), 4, None) == ssa.SSA_ERR_INVALID
 
 
