@@ -97,10 +97,13 @@ def measured_traffic(workload):
     return float(t.group(1))
 
 
-def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None):
+def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None,
+            num_queries=1, query_group=1):
     """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
     ``top_p`` (a float) caps every sequence's deterministic stratum at the
-    top-p prefix; ``wl`` reuses an already generated workload."""
+    top-p prefix; ``wl`` reuses an already generated workload; with
+    ``num_queries`` T > 1 each step carries T query positions per sequence,
+    ``query_group`` of them sharing one selection."""
     import torch
 
     from long_context_sparse_approx_amd import ssa, synth
@@ -108,12 +111,13 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     dev = "cuda:0"
     t_gen = time.perf_counter()
     if wl is None:
-        wl = synth.make_workload(name, dev)
+        wl = synth.make_workload(name, dev, num_queries=num_queries)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=dev)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
-                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count,
+                       query_group=query_group)
     ws = ssa.alloc_workspace(p, dev)
     out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -195,7 +199,8 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
 
     tokens = float(sum(wl.lens))
     d = wl.d
-    idx_bytes = tokens * wl.Hkv * (2 * wl.pair_count * 2)       # K pair subset
+    groups = ssa.num_groups(p)
+    idx_bytes = tokens * wl.Hkv * groups * (2 * wl.pair_count * 2)  # K pair subset per group
     gather_bytes = (n_det + n_smp) * 2.0 * d * 2                # K and V rows
     score_bytes = tokens * wl.Hkv * 4 * 4                       # 1 write + 3 reads
     res = dict(wl=wl, p=p, ms_step=ms_step, idx_ms=idx_ms, gpu_ms=gpu_ms, stage_ms=stage_ms,
@@ -291,6 +296,9 @@ def main():
                     help="time replays of one step captured in a HIP graph (no indexer events)")
     ap.add_argument("--top-p", type=float, default=0.02,
                     help="also time the main workload with this top-p stratum cap (0 = skip)")
+    ap.add_argument("--multi", type=int, default=4,
+                    help="also time the main workload with this many query positions per "
+                         "step, one shared selection vs one per query (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -335,6 +343,26 @@ def main():
             value=s3["value"], unit="KV-tokens/s/layer", ms_per_step=s3["ms_per_step"],
             stages_us=s3["stages_us"], selected=s3["selected"])
         del r3
+    if args.multi > 1:
+        T = args.multi
+        mq = dict(queries_per_step=T,
+                  policy="T query positions per sequence (the last T cache positions); a group "
+                         "of g consecutive queries is scored once with its mean query and "
+                         "shares one selection; every query attends over it within its "
+                         "causal span",
+                  unit="query-KV-tokens/s/layer")
+        wl_m = None
+        for g in (T, 1):
+            r4 = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events,
+                         wl=wl_m, num_queries=T, query_group=g)
+            wl_m = r4["wl"]
+            s4 = summarize(r4, args.workload)
+            mq[f"group_{g}"] = dict(value=T * s4["value"], ms_per_step=s4["ms_per_step"],
+                                    stages_us=s4["stages_us"], selected=s4["selected"])
+            del r4
+        del wl_m
+        torch.cuda.empty_cache()
+        variants["multi_query"] = mq
     cpu = None if args.no_cpu else cpu_baseline(res["wl"], args.cpu_budget)
     wl = res["wl"]
     line = {
