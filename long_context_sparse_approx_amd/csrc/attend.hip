@@ -10,10 +10,12 @@
 // Permutation", methodology part 3: each split keeps the online-softmax
 // state (m, l, acc); the merge resumes from the stored states.
 //
-// One wavefront per (attention unit, split): an attention unit is one query
-// position t of sequence b with one kv head h; it reads the selection of its
-// query group's unit, restricted to its own causal span [0, P - T + t].
-// A tile is 32 selected tokens; both
+// One wavefront per (selection unit, member block, split).  The 16 query
+// columns of the tiles hold up to 16 / G members of the unit's query group
+// (consecutive query positions) times their G heads, so one pass over the
+// selected K/V rows serves them all; column (member t, head) masks the
+// positions past its own causal span [0, P - T + t] and keeps its own
+// online-softmax state.  A tile is 32 selected tokens; both
 // products run on MFMA v_mfma_f32_16x16x32_bf16:
 //   QK:  D[16 tokens x 16 heads] = K_tile[16 x 32 dims] * Q^T[32 dims x 16 heads],
 //        two halves of 16 tokens, d/32 steps each; query heads beyond the
@@ -73,32 +75,43 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   using VS = VSlice<D>;
   __shared__ int rows_sh[kBatch + 32];
   __shared__ float lw_sh[kBatch + 32];
+  __shared__ int pos_sh[kBatch + 32];
 
   const int s = blockIdx.x;
-  const int au = blockIdx.y;
-  const int bt = au / a.Hkv;  // b * T + t
-  const int h = au - bt * a.Hkv;
-  const int b = bt / a.T;
-  const int t = bt - b * a.T;
-  const int u = (b * a.NG + t / a.g) * a.Hkv + h;  // the selection unit
+  const int u = blockIdx.y / a.mblocks;  // selection unit (b, grp, h)
+  const int mb = blockIdx.y - u * a.mblocks;
+  const int bg = u / a.Hkv;
+  const int h = u - bg * a.Hkv;
+  const int b = bg / a.NG;
+  const int grp = bg - b * a.NG;
+  const int t_a = grp * a.g + mb * a.mpw;  // first member of this block
+  const int nmem = min(min(a.mpw, (grp + 1) * a.g - t_a), a.T - t_a);
+  if (nmem <= 0) return;  // uniform over the wave
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-  const int L = member_span(clamp_len(a.seq_lens[b], a.max_seq_len), a.T, t);
+  const int P = clamp_len(a.seq_lens[b], a.max_seq_len);
+  // Column n16 = (member t_a + n16 / G, head n16 % G); columns past the
+  // block's members have an empty span.
+  const bool col_valid = n16 < nmem * a.G;
+  const int col_t = t_a + (col_valid ? n16 / a.G : 0);
+  const int col_g = col_valid ? n16 - (n16 / a.G) * a.G : 0;
+  const int L_col = col_valid ? member_span(P, a.T, col_t) : 0;
+  const int L = member_span(P, a.T, t_a + nmem - 1);  // the block's widest span
   const int ncL = (L + kChunk - 1) / kChunk;
   const int c_begin = (int)((int64_t)s * ncL / a.nsplit);
   const int c_end = (int)((int64_t)(s + 1) * ncL / a.nsplit);
   const int max_row = a.num_blocks * a.Hkv * kBlockTokens - 1;
 
-  // QK B operand (Q^T): lane holds head n16, dims kk*32 + q4*8 .. +8.
+  // QK B operand (Q^T): lane holds column n16, dims kk*32 + q4*8 .. +8.
   bf16x8 qf[KK];
   {
-    const bool gv = n16 < a.G;
-    const uint16_t* qrow = a.q + (size_t)(bt * a.Hq + h * a.G + (gv ? n16 : 0)) * D;
+    const uint16_t* qrow =
+        a.q + ((size_t)(b * a.T + col_t) * a.Hq + h * a.G + col_g) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (gv) v = *reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8);
+      if (col_valid) v = *reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8);
       qf[kk] = as_bf16x8(v);
     }
   }
@@ -125,28 +138,30 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int k = 0; k < kBatch / 64; ++k) {
         const int i = lane + 64 * k;
-        int row = -1;
+        int row = -1, pos = 0;  // rows given directly carry no position
         float lw = -INFINITY;
         if (i < nb) {
           const int v = idxp[b0 + i];
           lw = lwp[b0 + i];
           if (a.idx_are_rows) {
             row = min(max(v, 0), max_row);
-          } else if (v < L) {  // positions past the member's span are masked
-            const int idx = max(v, 0);
-            int blk = btrow[idx >> 4];
+          } else if (v < L) {  // positions past every member's span are dropped
+            pos = max(v, 0);
+            int blk = btrow[pos >> 4];
             blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-            row = (blk * a.Hkv + h) * kBlockTokens + (idx & 15);
+            row = (blk * a.Hkv + h) * kBlockTokens + (pos & 15);
           } else {
             lw = -INFINITY;
           }
         }
         rows_sh[i] = row;
         lw_sh[i] = lw;
+        pos_sh[i] = pos;
       }
       if (lane < 32) {
         rows_sh[kBatch + lane] = -1;
         lw_sh[kBatch + lane] = -INFINITY;
+        pos_sh[kBatch + lane] = 0;
       }
       __syncthreads();
       for (int t0 = 0; t0 < nb; t0 += 32) {
@@ -179,13 +194,15 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
           if (r >= 0)
             vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)r * D + n16 * DPL);
         }
-        // Logits of (head n16, slot tokens), online softmax update.
+        // Logits of (column n16, slot tokens), online softmax update; a
+        // column ignores positions past its member's span.
         float x[8];
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
-          x[i] = sc[i >> 2][i & 3] * a.scale + lw_sh[t0 + tok];
+          x[i] = pos_sh[t0 + tok] < L_col ? sc[i >> 2][i & 3] * a.scale + lw_sh[t0 + tok]
+                                          : -INFINITY;
           tmax = fmaxf(tmax, x[i]);
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
@@ -212,7 +229,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
         psum += __shfl_xor(psum, 32);
         l_run = l_run * alpha + psum;
         m_run = m_new;
-        // Rescale the accumulators: rows 4*q4 + r belong to head 4*q4 + r,
+        // Rescale the accumulators: rows 4*q4 + r belong to column 4*q4 + r,
         // whose alpha sits in lane 4*q4 + r.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -240,20 +257,22 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
     }
   }
 
-  // Write this split's state: acc rows are heads 4*q4 + r, column n16 holds
-  // dims n16*DPL .. +DPL.
+  // Write this split's state: acc rows are query columns 4*q4 + r (member,
+  // head); lane column n16 holds dims n16*DPL .. +DPL.
   const int stride = D + 2;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int g = 4 * q4 + r;
-    if (g < a.G) {
-      float* dst = a.part + ((size_t)(bt * a.Hq + h * a.G + g) * a.nsplit + s) * stride + n16 * DPL;
+    const int col = 4 * q4 + r;
+    if (col < nmem * a.G) {
+      const int qrow = (b * a.T + t_a + col / a.G) * a.Hq + h * a.G + col % a.G;
+      float* dst = a.part + ((size_t)qrow * a.nsplit + s) * stride + n16 * DPL;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
     }
   }
-  if (q4 == 0 && n16 < a.G) {
-    float* dst = a.part + ((size_t)(bt * a.Hq + h * a.G + n16) * a.nsplit + s) * stride + D;
+  if (q4 == 0 && col_valid) {
+    const int qrow = (b * a.T + col_t) * a.Hq + h * a.G + col_g;
+    float* dst = a.part + ((size_t)qrow * a.nsplit + s) * stride + D;
     dst[0] = m_run;
     dst[1] = l_run;
   }
@@ -327,7 +346,7 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
-  dim3 grid(a.nsplit, a.B * a.T * a.Hkv);
+  dim3 grid(a.nsplit, a.B * a.NG * a.Hkv * a.mblocks);
   if (a.d == 128)
     attend_kernel<128><<<grid, 64, 0, stream>>>(a);
   else if (a.d == 64)

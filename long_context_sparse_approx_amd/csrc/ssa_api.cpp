@@ -47,7 +47,13 @@ bool params_ok(const ssa_params* p) {
   const int64_t ng = (p->num_queries + p->query_group - 1) / p->query_group;
   // grid.y of the per-unit and per-(query position, kv head) launches
   if ((int64_t)p->batch * ng * p->num_kv_heads > 65535) return false;
-  if ((int64_t)p->batch * p->num_queries * p->num_kv_heads > 65535) return false;
+  // attention: one wave per (selection unit, block of 16 / G members)
+  {
+    const int G = p->num_q_heads / p->num_kv_heads;
+    const int g = p->query_group < p->num_queries ? p->query_group : p->num_queries;
+    const int64_t mblocks = (g + 16 / G - 1) / (16 / G);
+    if ((int64_t)p->batch * ng * p->num_kv_heads * mblocks > 65535) return false;
+  }
   return true;
 }
 
@@ -246,6 +252,8 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
   a.T = d.T;
   a.g = d.g;
   a.NG = d.NG;
+  a.mpw = 16 / d.G;  // G <= 16
+  a.mblocks = (d.g + a.mpw - 1) / a.mpw;
   a.B = d.B;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;

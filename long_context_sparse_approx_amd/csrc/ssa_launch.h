@@ -97,6 +97,7 @@ struct AttendArgs {
   float* part;                // [B*T*Hq, nsplit, d + 2]: acc[d], m, l
   void* out;                  // [B, T, Hq, d]
   int T, g, NG;
+  int mpw, mblocks;           // members per attention wave (16 / G), waves per group
   int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
   int idx_are_rows;
   int64_t seg_ld;
