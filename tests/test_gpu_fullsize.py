@@ -119,3 +119,61 @@ def test_fullsize_32k():
 
 def test_fullsize_batched():
     check_fullsize("batched", [(0, 0), (17, 3), (31, 6)])
+
+
+def test_fullsize_1m_multi_query():
+    """The 1M workload with 4 query positions per step sharing one selection
+    (the bench's multi-query configuration), sampled (sequence, group, kv
+    head) units checked one by one."""
+    T = 4
+    wl = synth.make_workload("1m", DEV, num_queries=T)
+    units = [(0, 0, 0), (0, 0, 5)]
+    say(f"[full] 1m multi-query T={T} units={units}")
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count, query_group=T)
+    scale = 1.0 / math.sqrt(wl.d)
+    G = wl.Hq // wl.Hkv
+    ws = ssa.alloc_workspace(p, DEV)
+    out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                     wl.sample_budget, wl.seed, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
+    torch.cuda.synchronize()
+    P = wl.lens[0]
+    s32 = torch.zeros(sc.shape, dtype=torch.float32)
+    w_in = torch.zeros(sc.shape[:2], dtype=torch.float32)
+    sels, inputs = {}, {}
+    for b, c, h in units:
+        qs = wl.q[b, :, h * G:(h + 1) * G].float().cpu().numpy().astype(np.float64)
+        kc = wl.k_cache[:, h:h + 1].float().cpu().numpy()
+        vc = wl.v_cache[:, h:h + 1].float().cpu().numpy()
+        bt = wl.block_table[b].cpu().numpy().astype(np.int64)
+        K, V = orc.gather_rows(kc, bt, 0, P), orc.gather_rows(vc, bt, 0, P)
+        s64 = orc.approx_scores(qs.reshape(-1, wl.d), K, wl.pair_begin, wl.pair_count, scale)
+        ok, ratio = score_tolerance_ok(sc[b, c * wl.Hkv + h, :P].cpu().numpy(), s64)
+        assert ok, f"scores out of tolerance at {(b, c, h)} ({ratio})"
+        sel = orc.select_unit(s64.astype(np.float32), int(wl.topk[b]), int(wl.sample_budget[b]),
+                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h, grp=c)
+        sels[(b, c, h)] = sel
+        inputs[(b, c, h)] = (qs, K, V)
+        s32[b, c * wl.Hkv + h, :P] = torch.from_numpy(s64.astype(np.float32))
+        w_in[b, c * wl.Hkv + h] = float(sel["W"])
+    si, sl, sn, _ = ssa.select(p, s32.to(DEV), wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                               w_in=w_in.to(DEV), workspace=ws)
+    torch.cuda.synchronize()
+    si, sl, sn = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy()
+    got = out.double().cpu().numpy()
+    for (b, c, h), sel in sels.items():
+        S, R, _ = gpu_sets(si, sl, sn, b, c * wl.Hkv + h)
+        assert np.array_equal(S, sel["S"]) and np.array_equal(R, sel["R"]), (b, c, h)
+        qs, K, V = inputs[(b, c, h)]
+        bound = 2e-3 * float(np.abs(V).max())
+        for t in range(T):
+            Lt = orc.member_span(P, T, t)
+            keep = sel["R"] < Lt
+            o = orc.attend_unit(qs[t], K[:Lt], V[:Lt], sel["S"][sel["S"] < Lt], sel["R"][keep],
+                                sel["pi_R"][keep], scale)
+            err = float(np.abs(got[b, t, h * G:(h + 1) * G] - o).max())
+            assert err <= bound, f"member {t} of {(b, c, h)}: {err} > {bound}"
+        say(f"[full] 1m multi-query unit {(b, c, h)}: selection bit-exact, members within bound")
