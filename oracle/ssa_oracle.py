@@ -27,8 +27,11 @@ Sources (web pages; cited by title and section):
   group's candidate set serves its members (section "Two operating modes":
   reusing it as is is the faster mode).
 * [S2O] "S2O: Early Stopping for Sparse Attention via Online Permutation"
-  (gist.science summary of arXiv 2602.22575), methodology part 3 "Kernel
-  implementation": the online-softmax state (m, l, acc) is stored and resumed.
+  (gist.science summary of arXiv 2602.22575), methodology part 2 "Early-
+  stopping rule" (blocks visited in descending estimated importance stop once
+  a block's marginal gain falls below a threshold relative to the
+  accumulated score) and part 3 "Kernel implementation" (the online-softmax
+  state (m, l, acc) is stored and resumed).
 
 Readings of points the pages leave open (each one is also listed in the design
 notes of the repository):
@@ -70,6 +73,15 @@ R16 Multi-query decode (PIVOT reuse): a step may carry T query positions per
     attends over it restricted to its own span, with the group's inclusion
     probabilities (the restriction of a Horvitz-Thompson sum to a subset of
     the population stays unbiased for that subset).
+R17 Early stopping (S2O): with a gain threshold tau > 0 the deterministic
+    stratum S, in its order (key descending, index ascending), is visited in
+    blocks of 64 consecutive tokens; block i's gain D_i is its mass in R15's
+    integer units and C_i the mass of blocks 0..i; the visit stops after the
+    first block with D_i < tau * C_i (exact), and S's later blocks are
+    skipped: neither read exactly nor sampled.  The tail sample (over the
+    complement of the whole S, normaliser W over it) is unchanged.  tau is
+    clamped to 1 (NaN and tau <= 0: no stopping); a stratum of more than
+    16384 tokens is not truncated.
 R15 Top-p stratum: the approximate probability mass of token j is counted in
     integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
     top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
@@ -107,6 +119,9 @@ __all__ = [
     "ht_terms",
     "attend_unit",
     "decode",
+    "STOP_BLOCK",
+    "STOP_MAX_STRATUM",
+    "stop_count",
     "member_span",
     "group_span",
     "decode_multi",
@@ -259,6 +274,33 @@ def topp_count(s32: np.ndarray, p) -> int:
 
 
 # ---------------------------------------------------------------------------
+# Early stopping over the deterministic stratum ([S2O] methodology part 2) --
+# reading R17
+# ---------------------------------------------------------------------------
+
+STOP_BLOCK = 64
+STOP_MAX_STRATUM = 16384
+
+
+def stop_count(q_ordered, tau) -> int:
+    """Tokens of the stratum kept by the early-stopping rule: q_ordered are the
+    stratum's mass units in its order; blocks of 64, stop after the first
+    block whose gain D_i < tau * C_i (C_i = mass of blocks 0..i)."""
+    n = len(q_ordered)
+    tau = float(np.float32(tau))
+    if not tau > 0.0 or n > STOP_MAX_STRATUM:
+        return n
+    tau = Fraction(min(tau, 1.0))
+    acc = 0
+    for i in range(-(-n // STOP_BLOCK)):
+        gain = sum(int(x) for x in q_ordered[i * STOP_BLOCK:(i + 1) * STOP_BLOCK])
+        acc += gain
+        if gain < tau * acc:
+            return min((i + 1) * STOP_BLOCK, n)
+    return n
+
+
+# ---------------------------------------------------------------------------
 # Step 4: counter-based uniforms (reading R8)
 # ---------------------------------------------------------------------------
 
@@ -362,12 +404,19 @@ def sample_tail(strata: dict, m: int, seed: int, b: int, h: int, grp: int = 0):
 
 
 def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None,
-                top_p=None, grp: int = 0):
+                top_p=None, grp: int = 0, stop_tau=None):
     """Full selection of one (batch, [query group,] kv head): dict with S, R,
-    pi_R, M, W, dense."""
+    pi_R, M, W, dense (and S_full, the stratum before early stopping)."""
     st = tail_stratum(s32, topk, m, W_in, top_p)
     R, pi_R = sample_tail(st, m, seed, b, h, grp)
-    return dict(S=st["S"], R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"])
+    S = st["S"]
+    S_full = S
+    if stop_tau is not None and not st["dense"] and S.size:
+        s32 = np.asarray(s32, dtype=_F32)
+        order = np.lexsort((S, ~order_key(s32[S])))  # key descending, index ascending
+        q = mass_units(sexp(np.subtract(s32[S[order]], st["M"], dtype=_F32)))
+        S = np.sort(S[order[:stop_count(q, stop_tau)]])
+    return dict(S=S, R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"], S_full=S_full)
 
 
 # ---------------------------------------------------------------------------
@@ -413,7 +462,7 @@ def attend_unit(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, S, R, pi_R,
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
            pair_begin: int, pair_count: int, scale: float | None = None, units=None,
-           top_p=None):
+           top_p=None, stop_tau=None):
     """Stratified sparse decode attention for every (batch, kv head).
 
     q [B, Hq, d]; caches [num_blocks, Hkv, 16, d]; block_table [B, max_blocks];
@@ -440,7 +489,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed
         s32 = s64.astype(_F32)
         tp = None if top_p is None else np.float32(top_p[b])
         sel = select_unit(s32, int(topk[b]), int(sample_budget[b]), int(seed[b]), b, h,
-                          top_p=tp)
+                          top_p=tp, stop_tau=stop_tau)
         out[b, h * G:(h + 1) * G, :] = attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
         info[(b, h)] = dict(scores=s64, **sel)
     return out, info
@@ -463,7 +512,7 @@ def group_span(P: int, T: int, g: int, grp: int) -> int:
 
 def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
                  pair_begin: int, pair_count: int, query_group: int,
-                 scale: float | None = None, units=None, top_p=None):
+                 scale: float | None = None, units=None, top_p=None, stop_tau=None):
     """T query positions per sequence, g = query_group per shared selection.
 
     q [B, T, Hq, d]; seq_lens are the cache lengths P_b (the T new tokens
@@ -494,7 +543,7 @@ def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget
         s64 = approx_scores(qstack, K, pair_begin, pair_count, scale)
         tp = None if top_p is None else np.float32(top_p[b])
         sel = select_unit(s64.astype(_F32), int(topk[b]), int(sample_budget[b]), int(seed[b]),
-                          b, h, top_p=tp, grp=c)
+                          b, h, top_p=tp, grp=c, stop_tau=stop_tau)
         for t in members:
             Lt = member_span(P, T, t)
             S = sel["S"][sel["S"] < Lt]
