@@ -122,6 +122,7 @@ typedef struct ssa_params {
   float softmax_scale;        /* > 0; 0 selects 1 / sqrt(d)                              */
   int32_t num_queries;        /* T >= 1 query positions per sequence                     */
   int32_t query_group;        /* g >= 1 consecutive queries sharing one selection        */
+  float early_stop;           /* tau of the early-stopping rule below; <= 0 or NaN = off */
 } ssa_params;
 
 /* Bytes of device workspace that ssa_decode / ssa_score / ssa_select /
@@ -144,6 +145,15 @@ int32_t ssa_num_chunks(const ssa_params* p);
  * and the prefix must reach ceil(p * Q) units of the sequence's total Q
  * (0 units -> n_p = 0).  top_p[b] is clamped to [0, 1]; NaN counts as 0.
  * To use top-p alone pass topk[b] >= L_b.
+ *
+ * Early stopping ("S2O: Early Stopping for Sparse Attention via Online
+ * Permutation", methodology part 2).  With params.early_stop = tau > 0 the
+ * stratum, in its order, is visited in blocks of 64 tokens; a block's gain is
+ * its mass in the units above and the visit stops after the first block whose
+ * gain is below tau times the mass of the blocks visited so far (exact
+ * comparison; tau above 1 acts as 1).  The rest of the stratum is skipped:
+ * neither read nor sampled; the tail sample is unchanged.  A stratum of more
+ * than 16384 tokens is visited whole.
  *
  * Tail.  sample_budget[b] (m) is the expected number of tail samples.  If
  * k + m >= L_b every token is read with weight 1 (dense attention).

@@ -387,6 +387,120 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ early stopping
+// "S2O: Early Stopping for Sparse Attention via Online Permutation",
+// methodology part 2.  One 1024-thread workgroup per unit: the stratum's
+// (key, position) pairs are rebuilt from the chunk lists, sorted in LDS into
+// the stratum's order (key descending, position ascending), cut into 64-token
+// blocks whose gains are their mass units, and the visit stops after the first
+// block whose gain is below tau times the mass so far (exact integer
+// arithmetic).  The positions past the stop are marked in the unit's bitmap,
+// which the sample kernel drops from the stratum.
+constexpr int kStopBlock = 64;
+constexpr int kStopMax = 16384;  // largest stratum that is truncated
+
+// gain < tau * acc, exactly, for 0 < tau (tau >= 1 compares with acc).
+__device__ __forceinline__ bool gain_below(unsigned long long gain, unsigned long long acc,
+                                           float tau) {
+  if (tau >= 1.0f) return gain < acc;
+  int e;
+  const float f = __builtin_frexpf(tau, &e);
+  const unsigned long long mant = (unsigned long long)(f * 0x1.0p24f);  // tau = mant 2^(e-24)
+  const unsigned __int128 rhs = (unsigned __int128)mant * acc;          // < 2^86
+  const int D = 24 - e;                                                 // >= 24
+  if (gain == 0ull) return rhs != 0;
+  if (D >= 86 || (64 - __builtin_clzll(gain)) + D > 127) return false;  // lhs >= 2^86 > rhs
+  return ((unsigned __int128)gain << D) < rhs;
+}
+
+__global__ __launch_bounds__(kRT) void stop_kernel(SelectArgs a) {
+  __shared__ unsigned long long buf[kStopMax];  // ((~key) << 32) | position, sorted ascending
+  __shared__ unsigned long long scan_m[kRW];
+  __shared__ int n_sh;
+  __shared__ int first_sh;
+  const int u = blockIdx.x;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  const int tid = threadIdx.x;
+  if (st.flags & (kFlagEmpty | kFlagDense | kFlagNoTopk)) return;  // uniform
+  if (st.k_eff <= kStopBlock || st.k_eff > kStopMax) return;       // nothing to cut
+  const int nc = (st.L + kChunk - 1) / kChunk;
+  if (tid == 0) {
+    n_sh = 0;
+    first_sh = 0x7fffffff;
+  }
+  __syncthreads();
+  // The stratum: every listed token above the threshold digit, and the
+  // candidates above the threshold key or within the tie quota.
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  for (int c = tid; c < nc; c += kRT) {
+    const size_t ci = (size_t)u * a.nchunk + c;
+    const int na = clamp_count(a.list_cnt[2 * ci], kChunk);
+    const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
+    const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+    const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+    const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
+    for (int i = 0; i < na; ++i) {
+      const int pos = min(max(lidx[i], 0), st.L - 1);
+      const uint32_t key = order_key(srow[pos]);
+      const int slot = atomicAdd(&n_sh, 1);
+      if (slot < kStopMax) buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)pos;
+    }
+    int tie = a.ties_before[ci];
+    for (int i = 0; i < ncand; ++i) {
+      const uint32_t key = ckey[i];
+      const bool in_s = key > st.tkey || (key == st.tkey && tie < st.ties_needed);
+      tie += key == st.tkey;
+      if (in_s) {
+        const int slot = atomicAdd(&n_sh, 1);
+        if (slot < kStopMax)
+          buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)min(max(cidx[i], 0), st.L - 1);
+      }
+    }
+  }
+  __syncthreads();
+  const int n = min(n_sh, kStopMax);
+  int P = kStopBlock;
+  while (P < n) P <<= 1;
+  for (int i = n + tid; i < P; i += kRT) buf[i] = ~0ull;
+  __syncthreads();
+  // Bitonic sort, ascending.
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P; i += kRT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long x = buf[i], y = buf[ixj];
+          if ((x > y) == ((i & k) == 0)) {
+            buf[i] = y;
+            buf[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // Block gains and the running mass (blocks in thread order).
+  const int nb = (n + kStopBlock - 1) / kStopBlock;
+  unsigned long long gain = 0ull;
+  if (tid < nb) {
+    const int r1 = min(n, (tid + 1) * kStopBlock);
+    for (int r = tid * kStopBlock; r < r1; ++r) {
+      const uint32_t key = ~(uint32_t)(buf[r] >> 32);
+      gain += mass_units(sexp(key_to_float(key) - st.M));
+    }
+  }
+  unsigned long long tot;
+  const unsigned long long acc = block_exclusive_scan<kRT>(gain, scan_m, &tot) + gain;
+  if (tid < nb && gain_below(gain, acc, a.stop_tau)) atomicMin(&first_sh, tid);
+  __syncthreads();
+  const int kept = first_sh == 0x7fffffff ? n : min(n, (first_sh + 1) * kStopBlock);
+  uint32_t* bits = a.stop_bits + (size_t)u * (a.seg_ld / 32);
+  for (int r = kept + tid; r < n; r += kRT) {
+    const uint32_t pos = (uint32_t)buf[r];
+    atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+  }
+}
+
 // ------------------------------------------------------------------ sample
 // Per chunk: membership of the listed tokens only -- above-threshold tokens
 // and candidates above the threshold key (or within the tie quota) form the
@@ -494,6 +608,10 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     smask |= (uint32_t)(f == 1) << i;
     rmask |= (uint32_t)(f == 2) << i;
   }
+  if (a.stop_bits && !dense) {  // positions cut from the stratum by early stopping
+    const uint32_t word = a.stop_bits[(size_t)u * (a.seg_ld / 32) + ((c0 + tb) >> 5)];
+    smask &= ~((word >> ((c0 + tb) & 31)) & 0xffffu);
+  }
   // One scan for both counts: deterministic count in the low 16 bits,
   // sampled count in the high 16 bits (each at most 4096).
   int packed_tot;
@@ -563,6 +681,11 @@ hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream) {
 
 hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream) {
   resolve_kernel<<<units, kRT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream) {
+  stop_kernel<<<units, kRT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -82,7 +82,7 @@ Dims dims_of(const ssa_params* p) {
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
+  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, stop_bits, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
 };
@@ -102,6 +102,7 @@ Layout layout_of(const Dims& d) {
   l.hist1m = take(U * kBins * 8);
   l.hist2m = take(U * kBins * 8);
   l.maxkey = take(U * 4);
+  l.stop_bits = take(U * (SEG / 32) * 4);
   l.thresh = take(U * sizeof(ssa::Thresh1));
   l.cand_idx = take(U * SEG * 4);
   l.cand_key = take(U * SEG * 4);
@@ -220,6 +221,9 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.sel_logw = sel_logw;
   a.sel_cnt = sel_cnt;
   a.norm_out = norm_out;
+  // early stopping is on for tau > 0 (NaN compares false)
+  a.stop_tau = p->early_stop > 1.0f ? 1.0f : p->early_stop;
+  a.stop_bits = p->early_stop > 0.0f ? at<uint32_t>(ws, l.stop_bits) : nullptr;
   a.T = d.T;
   a.g = d.g;
   a.NG = d.NG;
@@ -282,7 +286,14 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
 hipError_t launch_init_for(const ssa::SelectArgs& a, int units, hipStream_t s) {
   const bool topp = a.top_p != nullptr;
   return ssa::launch_init(a.hist1, a.hist2, a.maxkey, topp ? a.hist1m : nullptr,
-                          topp ? a.hist2m : nullptr, units, s);
+                          topp ? a.hist2m : nullptr, a.stop_bits, a.seg_ld / 32, units, s);
+}
+
+// The resolve stage, then the early-stopping cut when it is on.
+hipError_t launch_resolve_for(const ssa::SelectArgs& a, int units, hipStream_t s) {
+  const hipError_t e = ssa::launch_resolve(a, units, s);
+  if (e != hipSuccess || !a.stop_bits) return e;
+  return ssa::launch_stop(a, units, s);
 }
 
 hipError_t launch_first_digit(const ssa::SelectArgs& a, int units, hipStream_t s) {
@@ -358,7 +369,7 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   SSA_TRY(launch_first_digit(sa, d.U, s));
   rec.end(SSA_STAGE_FILTER);
   rec.begin(SSA_STAGE_RESOLVE);
-  SSA_TRY(ssa::launch_resolve(sa, d.U, s));
+  SSA_TRY(launch_resolve_for(sa, d.U, s));
   rec.end(SSA_STAGE_RESOLVE);
   rec.begin(SSA_STAGE_SAMPLE);
   SSA_TRY(ssa::launch_sample(sa, d.U, s));
@@ -393,7 +404,7 @@ int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int
   const ssa::IndexArgs ia = index_args(p, d, q, k_cache, block_table, seq_lens, scores,
                                        p->max_seq_len, workspace, l);
   SSA_TRY(ssa::launch_init(ia.hist1, at<uint32_t>(workspace, l.hist2), ia.maxkey, nullptr,
-                           nullptr, d.U, s));
+                           nullptr, nullptr, 0, d.U, s));
   SSA_TRY(ssa::launch_indexer(ia, d.U, s));
   return SSA_OK;
 }
@@ -417,7 +428,7 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
   SSA_TRY(launch_init_for(sa, d.U, s));
   SSA_TRY(ssa::launch_score_hist(sa, d.U, s));
   SSA_TRY(launch_first_digit(sa, d.U, s));
-  SSA_TRY(ssa::launch_resolve(sa, d.U, s));
+  SSA_TRY(launch_resolve_for(sa, d.U, s));
   SSA_TRY(ssa::launch_sample(sa, d.U, s));
   return SSA_OK;
 }

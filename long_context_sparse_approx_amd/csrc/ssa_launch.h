@@ -80,6 +80,8 @@ struct SelectArgs {
   float* sel_logw;            // [U, seg_ld]
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
+  uint32_t* stop_bits;        // [U, seg_ld / 32] positions skipped by early stopping, or null
+  float stop_tau;             // early-stopping threshold (used when stop_bits is set)
   int T, g, NG;
   int Hkv, max_seq_len, nchunk, max_blocks, num_blocks, emit_rows;
   int64_t seg_ld;             // nchunk * 4096
@@ -107,16 +109,18 @@ struct AttendArgs {
 int indexer_tokens_per_iteration(int pair_count);
 int indexer_max_tokens_per_wg();
 int indexer_resident_workgroups(int pair_count);  // 0 if unknown
-// Clears the histograms and maxima; the mass histograms only when non-null.
+// Clears the histograms and maxima; the mass histograms and the early-stopping
+// bitmap (stop_words words per unit) only when non-null.
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
-                       unsigned long long* hist1m, unsigned long long* hist2m, int units,
-                       hipStream_t stream);
+                       unsigned long long* hist1m, unsigned long long* hist2m,
+                       uint32_t* stop_bits, int64_t stop_words, int units, hipStream_t stream);
 hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream);
 hipError_t launch_score_hist(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_mass(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_threshold(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_filter(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
+hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);

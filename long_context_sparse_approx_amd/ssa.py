@@ -38,7 +38,7 @@ class SsaParams(ctypes.Structure):
                 ("pair_begin", ctypes.c_int32), ("pair_count", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("num_queries", ctypes.c_int32),
-                ("query_group", ctypes.c_int32)]
+                ("query_group", ctypes.c_int32), ("early_stop", ctypes.c_float)]
 
 
 class SsaError(RuntimeError):
@@ -109,12 +109,13 @@ def _stream(stream):
 def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                 max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
                 softmax_scale=0.0, block_size=BLOCK_TOKENS, num_queries=1,
-                query_group=1) -> SsaParams:
+                query_group=1, early_stop=0.0) -> SsaParams:
     if pair_begin is None:
         pair_begin = head_dim // 2 - pair_count
     return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
-                     float(softmax_scale), int(num_queries), int(query_group))
+                     float(softmax_scale), int(num_queries), int(query_group),
+                     float(early_stop))
 
 
 def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
