@@ -98,7 +98,7 @@ def measured_traffic(workload):
 
 
 def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None,
-            num_queries=1, query_group=1):
+            num_queries=1, query_group=1, early_stop=0.0):
     """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
     ``top_p`` (a float) caps every sequence's deterministic stratum at the
     top-p prefix; ``wl`` reuses an already generated workload; with
@@ -117,7 +117,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=dev)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
-                       query_group=query_group)
+                       query_group=query_group, early_stop=early_stop)
     ws = ssa.alloc_workspace(p, dev)
     out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -296,6 +296,9 @@ def main():
                     help="time replays of one step captured in a HIP graph (no indexer events)")
     ap.add_argument("--top-p", type=float, default=0.02,
                     help="also time the main workload with this top-p stratum cap (0 = skip)")
+    ap.add_argument("--early-stop", type=float, default=0.01,
+                    help="also time the main workload with this early-stopping threshold "
+                         "(0 = skip)")
     ap.add_argument("--multi", type=int, default=4,
                     help="also time the main workload with this many query positions per "
                          "step, one shared selection vs one per query (0 = skip)")
@@ -343,6 +346,17 @@ def main():
             value=s3["value"], unit="KV-tokens/s/layer", ms_per_step=s3["ms_per_step"],
             stages_us=s3["stages_us"], selected=s3["selected"])
         del r3
+    if args.early_stop > 0:
+        r5 = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events,
+                     wl=res["wl"], early_stop=args.early_stop)
+        s5 = summarize(r5, args.workload)
+        variants["early_stop"] = dict(
+            policy=f"deterministic stratum visited in 64-token blocks of its order, stopping "
+                   f"after the first block whose gain is below {args.early_stop} of the mass "
+                   "so far; same tail sample",
+            value=s5["value"], unit="KV-tokens/s/layer", ms_per_step=s5["ms_per_step"],
+            stages_us=s5["stages_us"], selected=s5["selected"])
+        del r5
     if args.multi > 1:
         T = args.multi
         mq = dict(queries_per_step=T,

@@ -413,91 +413,219 @@ __device__ __forceinline__ bool gain_below(unsigned long long gain, unsigned lon
   return ((unsigned __int128)gain << D) < rhs;
 }
 
+// First chunk c with pre[c + 1] > f (pre: exclusive prefix of per-chunk counts,
+// nc + 1 entries, in LDS).
+__device__ __forceinline__ int chunk_of(const int* pre, int nc, int f) {
+  int lo = 0, hi = nc - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= f) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __global__ __launch_bounds__(kRT) void stop_kernel(SelectArgs a) {
   __shared__ unsigned long long buf[kStopMax];  // ((~key) << 32) | position, sorted ascending
+  __shared__ int pre[kMaxResolveChunks + 1];    // exclusive prefix of per-chunk list counts
   __shared__ unsigned long long scan_m[kRW];
-  __shared__ int n_sh;
+  __shared__ int scan_scr[kRW];
   __shared__ int first_sh;
+  __shared__ int n_sh;
+  __shared__ int strad_sh;
   const int u = blockIdx.x;
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   const int tid = threadIdx.x;
   if (st.flags & (kFlagEmpty | kFlagDense | kFlagNoTopk)) return;  // uniform
   if (st.k_eff <= kStopBlock || st.k_eff > kStopMax) return;       // nothing to cut
   const int nc = (st.L + kChunk - 1) / kChunk;
-  if (tid == 0) {
-    n_sh = 0;
-    first_sh = 0x7fffffff;
-  }
-  __syncthreads();
-  // The stratum: every listed token above the threshold digit, and the
-  // candidates above the threshold key or within the tie quota.
+  const size_t cu = (size_t)u * a.nchunk;
   const float* srow = a.scores + (size_t)u * a.score_ld;
-  for (int c = tid; c < nc; c += kRT) {
-    const size_t ci = (size_t)u * a.nchunk + c;
-    const int na = clamp_count(a.list_cnt[2 * ci], kChunk);
-    const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
-    const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + (size_t)c * kChunk;
-    const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + (size_t)c * kChunk;
-    const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + (size_t)c * kChunk;
-    for (int i = 0; i < na; ++i) {
-      const int pos = min(max(lidx[i], 0), st.L - 1);
-      const uint32_t key = order_key(srow[pos]);
-      const int slot = atomicAdd(&n_sh, 1);
-      if (slot < kStopMax) buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)pos;
+  const size_t seg = (size_t)u * a.seg_ld;
+  if (tid == 0) first_sh = 0x7fffffff;
+  // The stratum, in the flattened (chunk, list position) order: first every
+  // listed token above the threshold digit (all in the stratum), then the
+  // candidates above the threshold key or within the tie quota (a tie's rank
+  // is its position among the ties in this order, i.e. in index order).
+  auto prefix = [&](bool cand) {
+    int run = 0;
+    for (int c0 = 0; c0 < nc; c0 += kRT) {
+      const int c = c0 + tid;
+      const int v = c < nc ? clamp_count(cand ? a.cand_cnt[cu + c] : a.list_cnt[2 * (cu + c)],
+                                         kChunk)
+                           : 0;
+      int tot;
+      const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
+      if (c < nc) pre[c] = run + ex;
+      run += tot;
     }
-    int tie = a.ties_before[ci];
-    for (int i = 0; i < ncand; ++i) {
-      const uint32_t key = ckey[i];
-      const bool in_s = key > st.tkey || (key == st.tkey && tie < st.ties_needed);
-      tie += key == st.tkey;
-      if (in_s) {
-        const int slot = atomicAdd(&n_sh, 1);
-        if (slot < kStopMax)
-          buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)min(max(cidx[i], 0), st.L - 1);
-      }
+    if (tid == 0) pre[nc] = run;
+    __syncthreads();
+    return run;
+  };
+  int n = min(prefix(false), kStopMax);
+  for (int f = tid; f < n; f += kRT) {
+    const int c = chunk_of(pre, nc, f);
+    const int pos = min(max(a.list_idx[seg + (size_t)c * kChunk + (f - pre[c])], 0), st.L - 1);
+    buf[f] = ((unsigned long long)~order_key(srow[pos]) << 32) | (uint32_t)pos;
+  }
+  __syncthreads();
+  // Candidates: the slot order is free (the buffer is sorted next), so slots
+  // come from a wave-aggregated LDS counter.  A tie (key == T) is in the
+  // stratum iff its global tie rank is below the quota: all ties of a chunk
+  // are in when the chunk's ties end within the quota, none when they start
+  // past it; only the one chunk straddling the quota ranks its ties (one wave,
+  // in index order).
+  const int ncand = prefix(true);
+  if (tid == 0) n_sh = n;
+  if (tid == 0) strad_sh = -1;
+  __syncthreads();
+  for (int c = tid; c < nc; c += kRT) {
+    const int tb = a.ties_before[cu + c];
+    const int tc = a.tiecnt[cu + c];
+    if (tb < st.ties_needed && st.ties_needed < tb + tc) strad_sh = c;
+  }
+  __syncthreads();
+  const int strad = strad_sh;
+  const int lane = tid & 63;
+  for (int f = tid; f - lane < ncand; f += kRT) {
+    bool in_s = false;
+    uint32_t key = 0u;
+    int pos = 0;
+    if (f < ncand) {
+      const int c = chunk_of(pre, nc, f);
+      const size_t at = seg + (size_t)c * kChunk + (f - pre[c]);
+      key = a.cand_key[at];
+      pos = min(max(a.cand_idx[at], 0), st.L - 1);
+      const int tb = a.ties_before[cu + c];
+      in_s = key > st.tkey ||
+             (key == st.tkey && c != strad && tb + a.tiecnt[cu + c] <= st.ties_needed);
+    }
+    const uint64_t m = __ballot(in_s);
+    int base = 0;
+    if (lane == 0 && m) base = atomicAdd(&n_sh, __popcll(m));
+    base = __shfl(base, 0);
+    const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
+    if (in_s && slot < kStopMax) buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)pos;
+  }
+  __syncthreads();
+  if (strad >= 0 && tid < 64) {  // the straddling chunk's ties, in index order
+    const int nca = pre[strad + 1] - pre[strad];
+    const size_t at0 = seg + (size_t)strad * kChunk;
+    int rank = a.ties_before[cu + strad];
+    for (int i0 = 0; i0 < nca; i0 += 64) {
+      const int i = i0 + tid;
+      const uint32_t key = i < nca ? a.cand_key[at0 + i] : 0u;
+      const bool tie = i < nca && key == st.tkey;
+      const uint64_t tm = __ballot(tie);
+      const int r = rank + __popcll(tm & ((1ull << tid) - 1ull));
+      const bool in_s = tie && r < st.ties_needed;
+      const uint64_t m = __ballot(in_s);
+      int base = 0;
+      if (tid == 0 && m) base = atomicAdd(&n_sh, __popcll(m));
+      base = __shfl(base, 0);
+      const int slot = base + __popcll(m & ((1ull << tid) - 1ull));
+      if (in_s && slot < kStopMax)
+        buf[slot] = ((unsigned long long)~key << 32) |
+                    (uint32_t)min(max(a.cand_idx[at0 + i], 0), st.L - 1);
+      rank += __popcll(tm);
     }
   }
   __syncthreads();
-  const int n = min(n_sh, kStopMax);
-  int P = kStopBlock;
-  while (P < n) P <<= 1;
-  for (int i = n + tid; i < P; i += kRT) buf[i] = ~0ull;
+  n = min(n_sh, kStopMax);
   __syncthreads();
-  // Bitonic sort, ascending.
-  for (int k = 2; k <= P; k <<= 1) {
+  // Bitonic sort of kStopMax elements, ascending (padding sorts last).  Thread
+  // t holds elements 16t .. 16t + 15 in registers: pairs closer than 16 are
+  // exchanged inside a thread, pairs closer than 1024 across the lanes of a
+  // wave, the rest through LDS.
+  constexpr int E = kStopMax / kRT;  // 16
+  static_assert(E == 16, "16 elements per thread");
+  unsigned long long v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * tid + e;
+    v[e] = i < n ? buf[i] : ~0ull;
+  }
+  for (int k = 2; k <= kStopMax; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += kRT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long x = buf[i], y = buf[ixj];
-          if ((x > y) == ((i & k) == 0)) {
-            buf[i] = y;
-            buf[ixj] = x;
-          }
+      if (j >= 1024) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) buf[E * tid + e] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = E * tid + e;
+          const unsigned long long o = buf[i ^ j];
+          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+          v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
+        }
+      } else if (j >= E) {
+        const int lx = j / E;  // partner lane offset, < 64
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = E * tid + e;
+          const unsigned long long o = __shfl_xor(v[e], lx);
+          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+          v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
+        }
+      } else {
+        auto cx = [&](int e0, int e1) {  // e0 < e1 = e0 + j inside this thread
+          const int i = E * tid + e0;
+          const bool asc = (i & k) == 0;
+          const unsigned long long x = v[e0], y = v[e1];
+          const bool swap = asc ? x > y : x < y;
+          v[e0] = swap ? y : x;
+          v[e1] = swap ? x : y;
+        };
+        switch (j) {
+          case 8:
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cx(e, e + 8);
+            break;
+          case 4:
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if ((e & 4) == 0) cx(e, e + 4);
+            break;
+          case 2:
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if ((e & 2) == 0) cx(e, e + 2);
+            break;
+          default:
+#pragma unroll
+            for (int e = 0; e < E; e += 2) cx(e, e + 1);
+            break;
         }
       }
-      __syncthreads();
     }
   }
-  // Block gains and the running mass (blocks in thread order).
-  const int nb = (n + kStopBlock - 1) / kStopBlock;
-  unsigned long long gain = 0ull;
-  if (tid < nb) {
-    const int r1 = min(n, (tid + 1) * kStopBlock);
-    for (int r = tid * kStopBlock; r < r1; ++r) {
-      const uint32_t key = ~(uint32_t)(buf[r] >> 32);
-      gain += mass_units(sexp(key_to_float(key) - st.M));
+  // Block gains: a 64-token block is 4 consecutive threads' elements.
+  unsigned long long part = 0ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (E * tid + e < n) {
+      const uint32_t key = ~(uint32_t)(v[e] >> 32);
+      part += mass_units(sexp(key_to_float(key) - st.M));
     }
   }
+  part += __shfl_xor(part, 1);
+  part += __shfl_xor(part, 2);
+  const bool leader = (tid & 3) == 0 && E * tid < n;  // first thread of block tid / 4
+  const unsigned long long gain = leader ? part : 0ull;
   unsigned long long tot;
   const unsigned long long acc = block_exclusive_scan<kRT>(gain, scan_m, &tot) + gain;
-  if (tid < nb && gain_below(gain, acc, a.stop_tau)) atomicMin(&first_sh, tid);
+  if (leader && gain_below(gain, acc, a.stop_tau)) atomicMin(&first_sh, tid >> 2);
   __syncthreads();
   const int kept = first_sh == 0x7fffffff ? n : min(n, (first_sh + 1) * kStopBlock);
   uint32_t* bits = a.stop_bits + (size_t)u * (a.seg_ld / 32);
-  for (int r = kept + tid; r < n; r += kRT) {
-    const uint32_t pos = (uint32_t)buf[r];
-    atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int r = E * tid + e;
+    if (r >= kept && r < n) {
+      const uint32_t pos = (uint32_t)v[e];
+      atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+    }
   }
 }
 
