@@ -536,26 +536,29 @@ __global__ __launch_bounds__(kRT) void stop_kernel(SelectArgs a) {
   // Bitonic sort of kStopMax elements, ascending (padding sorts last).  Thread
   // t holds elements 16t .. 16t + 15 in registers: pairs closer than 16 are
   // exchanged inside a thread, pairs closer than 1024 across the lanes of a
-  // wave, the rest through LDS.
+  // wave, the rest through LDS.  In LDS, element 16t + e sits at e * 1024 + t,
+  // so a wave's accesses are 64 consecutive words (no bank conflicts); the
+  // unsorted slots are taken in that same order (the start order is free).
   constexpr int E = kStopMax / kRT;  // 16
   static_assert(E == 16, "16 elements per thread");
   unsigned long long v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = E * tid + e;
-    v[e] = i < n ? buf[i] : ~0ull;
+    const int slot = e * kRT + tid;
+    v[e] = slot < n ? buf[slot] : ~0ull;
   }
   for (int k = 2; k <= kStopMax; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       if (j >= 1024) {
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) buf[E * tid + e] = v[e];
+        for (int e = 0; e < E; ++e) buf[e * kRT + tid] = v[e];
         __syncthreads();
+        const int pt = tid ^ (j / E);  // partner thread, same register
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int i = E * tid + e;
-          const unsigned long long o = buf[i ^ j];
+          const unsigned long long o = buf[e * kRT + pt];
           const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
           v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
         }
