@@ -20,7 +20,9 @@ Sources (web pages; cited by title and section):
   low-frequency chunks carry contextual attention), section 3 stage 1 "TIP"
   (online score = sum of the contributions of a fixed chunk subset; keep the
   highest-scoring tokens) and stage 2 "FAC" (full-precision attention on the
-  selected tokens at their original positions).
+  selected tokens at their original positions); section 3, variants (FASA-M
+  keeps only the dominant key components on the GPU and moves the other key
+  components and the values to host memory).
 * [PIVOT] "PIVOT slashes sparse-attention indexer cost" (gyaansetu.com),
   section "The two observations behind PIVOT": one proxy query, the mean of a
   group of consecutive queries, is scored instead of each member, and the
@@ -62,6 +64,14 @@ R9  sexp is a specified float32 exp (Cody-Waite reduction, degree-7 Taylor
     0 for x < -87.
 R10 Horvitz-Thompson weights: c_j = 1 on the deterministic set S and 1/pi_j on
     the sample R; output = sum c e^l v / sum c e^l over S u R.
+R15 Top-p stratum: the approximate probability mass of token j is counted in
+    integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
+    top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
+    the target is tau = ceil(p * Q), evaluated exactly.  n_p is the length of
+    the shortest prefix of the order (key descending, index ascending) whose
+    units reach tau (0 when tau = 0).  The deterministic stratum is the first
+    min(topk, n_p) tokens of that order.  Integer mass makes the prefix
+    independent of summation order.  p is clamped to [0, 1]; NaN counts as 0.
 R16 Multi-query decode (PIVOT reuse): a step may carry T query positions per
     sequence; with P the cache length (the T new tokens included), query t sits
     at position P - T + t and attends to tokens [0, P - T + t].  Queries are
@@ -82,14 +92,15 @@ R17 Early stopping (S2O): with a gain threshold tau > 0 the deterministic
     complement of the whole S, normaliser W over it) is unchanged.  tau is
     clamped to 1 (NaN and tau <= 0: no stopping); a stratum of more than
     16384 tokens is not truncated.
-R15 Top-p stratum: the approximate probability mass of token j is counted in
-    integer units, q_j = floor(w_j * 2^38) with w_j = sexp(s_j - M) (so the
-    top token holds exactly 2^38 units); Q = sum of q_j over the sequence and
-    the target is tau = ceil(p * Q), evaluated exactly.  n_p is the length of
-    the shortest prefix of the order (key descending, index ascending) whose
-    units reach tau (0 when tau = 0).  The deterministic stratum is the first
-    min(topk, n_p) tokens of that order.  Integer mass makes the prefix
-    independent of summation order.  p is clamped to [0, 1]; NaN counts as 0.
+R18 Split keys (FASA-M): a key row is held as two rows under the same row
+    number: the scored dims [2 pair_begin, 2 (pair_begin + pair_count)) in
+    one array and the remaining dims, in their order ([0, 2 pair_begin) then
+    the dims above the scored range), in another; values are unchanged.
+    Appending T new tokens per sequence writes token t of sequence b at
+    position seq_lens[b] - T + t (seq_lens counting the new tokens), row
+    pos mod 16 of block block_table[b][pos // 16]; negative positions are
+    skipped.  A step over split keys computes what it computes over the
+    whole keys they hold.
 """
 
 from __future__ import annotations
@@ -125,6 +136,9 @@ __all__ = [
     "member_span",
     "group_span",
     "decode_multi",
+    "split_keys",
+    "join_keys",
+    "append_kv",
 ]
 
 # Inputs arrive as a paged cache of 16-token blocks (layout, not arithmetic).
@@ -553,3 +567,40 @@ def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget
                                                           sel["pi_R"][keep], scale)
         info[(b, c, h)] = dict(scores=s64, span=Lg, **sel)
     return out, info
+
+
+# ---------------------------------------------------------------------------
+# reading R18: split keys and appending to the cache
+# ---------------------------------------------------------------------------
+
+def split_keys(k_cache: np.ndarray, pair_begin: int, pair_count: int):
+    """[FASA] section 3, variants (FASA-M: the dominant key components stay
+    resident, the other components move): (k_dom, k_rest) of whole keys
+    [..., d], k_dom the scored dims, k_rest the others in dim order."""
+    lo, hi = 2 * pair_begin, 2 * (pair_begin + pair_count)
+    k_dom = k_cache[..., lo:hi].copy()
+    k_rest = np.concatenate([k_cache[..., :lo], k_cache[..., hi:]], axis=-1)
+    return k_dom, k_rest
+
+
+def join_keys(k_dom: np.ndarray, k_rest: np.ndarray, pair_begin: int) -> np.ndarray:
+    """Whole keys from (k_dom, k_rest): the inverse of split_keys."""
+    lo = 2 * pair_begin
+    return np.concatenate([k_rest[..., :lo], k_dom, k_rest[..., lo:]], axis=-1)
+
+
+def append_kv(k_cache: np.ndarray, v_cache: np.ndarray, block_table, seq_lens,
+              k_new: np.ndarray, v_new: np.ndarray):
+    """Copies of the paged caches [nblk, Hkv, 16, d] with the new tokens
+    k_new, v_new [B, T, Hkv, d] written at positions seq_lens[b] - T + t
+    (negative positions skipped)."""
+    k, v = k_cache.copy(), v_cache.copy()
+    B, T = k_new.shape[:2]
+    for b in range(B):
+        pos = int(seq_lens[b]) - T + np.arange(T)
+        keep = pos >= 0
+        blk = np.asarray(block_table[b])[pos[keep] // BLOCK_TOKENS]
+        slot = pos[keep] % BLOCK_TOKENS
+        k[blk, :, slot, :] = k_new[b, keep]
+        v[blk, :, slot, :] = v_new[b, keep]
+    return k, v
