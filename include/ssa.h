@@ -22,8 +22,8 @@
  * ---------------------------------------
  * Memory.   Every array argument is a DEVICE pointer, owned by the caller, on
  *           the device current at the call.  The library allocates nothing
- *           and keeps no mutable global state.  q, k_cache and v_cache must
- *           be 16-byte aligned.
+ *           and keeps no mutable global state.  q, k_cache, k_rest, v_cache,
+ *           k_new and v_new must be 16-byte aligned.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
  *           Calls enqueue work and return; nothing is synchronised.
  * Errors.   0 on success, a negative SSA_ERR_* code otherwise; no partial
@@ -59,6 +59,20 @@
  *   seed         [B]                             uint64 (one Philox key per sequence)
  *   out          [B, T, Hq, d]                   f32 or bf16 (params.out_dtype)
  *
+ * Split keys (params.key_layout = SSA_KEYS_SPLIT; "FASA: Frequency-aware
+ * Sparse Attention", section 3, variants: FASA-M keeps the dominant key
+ * components on the GPU and moves the rest of the key and the whole value
+ * cache to host memory).  A key row is stored as two rows of the same row
+ * number: the scored dims and the others.
+ *   k_cache (k_dom) [num_blocks, Hkv, 16, 2 * pair_count]      dims [2 pb, 2 (pb + pc))
+ *   k_rest          [num_blocks, Hkv, 16, d - 2 * pair_count]  dims [0, 2 pb) then
+ *                                                              [2 (pb + pc), d)
+ *   The indexer reads k_dom only; attention reads the selected rows of
+ *   k_dom, k_rest and v_cache.  k_rest and v_cache may be pinned host
+ *   memory that the device can address (hipHostMalloc; pass the address
+ *   that hipHostGetDevicePointer returns): then the GPU holds
+ *   2 * pair_count of the 4 * d key and value elements per token.
+ *
  * Selection layout (ssa_select output, ssa_attend input).  A sequence's
  * positions are cut into chunks of SSA_CHUNK_TOKENS; NC = ssa_num_chunks().
  *   sel_idx   [B, NG, Hkv, NC * SSA_CHUNK_TOKENS]  int32 token positions
@@ -88,6 +102,10 @@ extern "C" {
 /* Output element types. */
 #define SSA_F32 0
 #define SSA_BF16 1
+
+/* Key layouts. */
+#define SSA_KEYS_WHOLE 0 /* k_cache holds whole key rows                           */
+#define SSA_KEYS_SPLIT 1 /* k_cache holds the scored dims, k_rest the others       */
 
 #define SSA_BLOCK_TOKENS 16    /* tokens per KV-cache block (the only size supported) */
 #define SSA_CHUNK_TOKENS 4096  /* selection / split granularity                      */
@@ -123,6 +141,7 @@ typedef struct ssa_params {
   int32_t num_queries;        /* T >= 1 query positions per sequence                     */
   int32_t query_group;        /* g >= 1 consecutive queries sharing one selection        */
   float early_stop;           /* tau of the early-stopping rule below; <= 0 or NaN = off */
+  int32_t key_layout;         /* SSA_KEYS_WHOLE or SSA_KEYS_SPLIT                         */
 } ssa_params;
 
 /* Bytes of device workspace that ssa_decode / ssa_score / ssa_select /
@@ -166,8 +185,20 @@ int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const vo
 
 /* ssa_decode, recording hipEvent_t events[2*s] before and events[2*s+1] after
  * the kernel(s) of stage s (SSA_STAGE_*); NULL entries are skipped, and a
- * NULL array records nothing.  Same results as ssa_decode. */
+ * NULL array records nothing.  Same results as ssa_decode.  ssa_decode and
+ * ssa_decode_timed take whole keys (params.key_layout = SSA_KEYS_WHOLE). */
 int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+                     const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream, void* const* events);
+
+/* ssa_decode over split keys (params.key_layout = SSA_KEYS_SPLIT): k_dom
+ * holds the scored dims and k_rest the others (layouts above; k_rest may be
+ * NULL only when 2 * pair_count = d).  events as for ssa_decode_timed (may be
+ * NULL).  The same arithmetic in the same order as ssa_decode: the output is
+ * bitwise that of ssa_decode on the whole keys the two arrays hold. */
+int ssa_decode_split(const ssa_params* p, const void* q, const void* k_dom, const void* k_rest,
                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
                      const int32_t* topk, const float* top_p, const int32_t* sample_budget,
                      const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
@@ -177,7 +208,8 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache,
  * selection unit u = (b * NG + group) * Hkv + h, for j below the group's span
  * (its last member's causal length); later entries are left untouched.
  *   s_j = (1/(n G)) sum over the group's n members and G heads of
- *         scale * sum_{p in pairs} (q[2p] k_j[2p] + q[2p+1] k_j[2p+1]). */
+ *         scale * sum_{p in pairs} (q[2p] k_j[2p] + q[2p+1] k_j[2p+1]).
+ * k_cache holds whole keys or, with SSA_KEYS_SPLIT, the scored dims only. */
 int ssa_score(const ssa_params* p, const void* q, const void* k_cache,
               const int32_t* block_table, const int32_t* seq_lens, float* scores,
               void* workspace, size_t workspace_bytes, void* stream);
@@ -204,6 +236,35 @@ int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const vo
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
                const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
                size_t workspace_bytes, void* stream);
+
+/* ssa_attend over split keys (params.key_layout = SSA_KEYS_SPLIT); k_rest
+ * as for ssa_decode_split.  Bitwise the output of ssa_attend on the whole
+ * keys. */
+int ssa_attend_split(const ssa_params* p, const void* q, const void* k_dom, const void* k_rest,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* sel_idx, const float* sel_logw, const int32_t* sel_count,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Append num_tokens = T new tokens per sequence to the cache: token t of
+ * sequence b goes to position seq_lens[b] - T + t (seq_lens counting the new
+ * tokens, as for ssa_decode), row (pos % 16) of block block_table[b][pos / 16];
+ * positions below 0 are skipped.  k_new, v_new: [B, T, Hkv, d] bf16
+ * (post-RoPE keys).  With SSA_KEYS_WHOLE k_cache receives whole key rows and
+ * k_rest must be NULL; with SSA_KEYS_SPLIT k_cache receives the scored dims
+ * and k_rest the others (NULL only when 2 * pair_count = d).  v_cache
+ * receives the values.  Caches may be pinned host memory as above.  Rows
+ * that two new tokens of one call share receive one of them.  Needs no
+ * workspace; B * T may be as large as the cache (bulk fill, e.g. after a
+ * prefill).  Requires Hkv * d <= 8192. */
+int ssa_append_kv(const ssa_params* p, int32_t num_tokens, const void* k_new, const void* v_new,
+                  const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
+                  void* k_rest, void* v_cache, void* stream);
+
+/* The device address of pinned host memory (hipHostMalloc), for passing
+ * offloaded caches (k_rest, v_cache) to the calls above: *dev_ptr receives
+ * the address kernels use for host_ptr.  SSA_ERR_INVALID if host_ptr is not
+ * pinned, device-mapped memory (the caller must not pass it then). */
+int ssa_host_device_address(const void* host_ptr, void** dev_ptr);
 
 /* Test hook: words[i] = the Philox word of (seed, b, h, group, token j0 + i), i < n. */
 int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t group, int32_t j0, int32_t n,

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
 
-SOURCES = ["indexer.hip", "select.hip", "attend.hip", "ssa_api.cpp"]
+SOURCES = ["indexer.hip", "select.hip", "attend.hip", "append.hip", "ssa_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; contraction
 # of separate multiplies and adds into fma is off so that the specified exp and

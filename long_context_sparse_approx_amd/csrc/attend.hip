@@ -68,7 +68,12 @@ struct VSlice<64> {
 
 constexpr int kBatch = 256;  // selected items resolved to cache rows at a time
 
-template <int D>
+// SPLIT: the keys are held in two arrays of the same row numbering: the
+// scored dims (2 * pair_count per row) apart from the others ("FASA:
+// Frequency-aware Sparse Attention", section 3, variants: FASA-M keeps the
+// dominant key components resident and moves the rest of the key and the
+// values elsewhere); a row is put back together from its 16-byte slices.
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   constexpr int KK = D / 32;   // QK steps over the head dim
   constexpr int DPL = D / 16;  // head dims per PV column = PV steps
@@ -113,6 +118,26 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (col_valid) v = *reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8);
       qf[kk] = as_bf16x8(v);
+    }
+  }
+
+  // This lane's key slices: dims kk*32 + q4*8 .. +8 of row r are at
+  // kb[kk] + r * kld[kk].
+  const uint16_t* kb[KK];
+  uint32_t kld[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int dim = kk * 32 + q4 * 8;
+    if (!SPLIT) {
+      kb[kk] = a.k_cache + dim;
+      kld[kk] = D;
+    } else {
+      const int lo = 2 * a.pair_begin;
+      const int nd = 2 * a.pair_count;
+      const bool scored = dim >= lo && dim < lo + nd;
+      const uint16_t* rest = a.k_rest ? a.k_rest : a.k_cache;  // no rest dims when nd == D
+      kb[kk] = scored ? a.k_cache + (dim - lo) : rest + (dim < lo ? dim : dim - nd);
+      kld[kk] = scored ? nd : D - nd;
     }
   }
 
@@ -174,8 +199,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (r >= 0)
-              v = *reinterpret_cast<const uint4*>(a.k_cache + (size_t)r * D + kk * 32 + q4 * 8);
+            if (r >= 0) v = *reinterpret_cast<const uint4*>(kb[kk] + (size_t)r * kld[kk]);
             kf[kk] = as_bf16x8(v);
           }
           f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -347,10 +371,17 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
   dim3 grid(a.nsplit, a.B * a.NG * a.Hkv * a.mblocks);
-  if (a.d == 128)
-    attend_kernel<128><<<grid, 64, 0, stream>>>(a);
+  // Split keys whose scored dims cover the whole head (no rest array) are
+  // addressed exactly like whole keys.
+  const bool split = a.k_rest != nullptr;
+  if (a.d == 128 && !split)
+    attend_kernel<128, false><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 128)
+    attend_kernel<128, true><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 64 && !split)
+    attend_kernel<64, false><<<grid, 64, 0, stream>>>(a);
   else if (a.d == 64)
-    attend_kernel<64><<<grid, 64, 0, stream>>>(a);
+    attend_kernel<64, true><<<grid, 64, 0, stream>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

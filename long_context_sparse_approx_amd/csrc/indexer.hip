@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const int blk0 = t0 / kBlockTokens;
   const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
-  const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.d;
+  const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.key_ld;
   for (int i = tid; i < nblk; i += 256) {
     const int blk = btrow[blk0 + i];
     blk_sh[i] = (uint32_t)(blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk));
@@ -227,15 +227,15 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   for (int i = tid; i < kBins / 2; i += 256) hist[i] = 0u;
   __syncthreads();
 
-  const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.d + 2 * a.pair_begin + sub * 8;
+  const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.key_ld + a.key_off + sub * 8;
   float* srow = a.scores + (size_t)u * a.score_ld;
   uint32_t kmax = 0u;
   int base = t0 + wave * WAVE_TOK;
   for (; base + WAVE_TOK <= t_end; base += WG_TOK)
-    index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.d, t0, base, t_end, qh, ql, sbuf,
+    index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
                                hist, kmax, lane);
   if (base < t_end)
-    index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.d, t0, base, t_end, qh, ql, sbuf,
+    index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
                                 hist, kmax, lane);
 
   kmax = wave_max_u32(kmax);

@@ -44,6 +44,7 @@ bool params_ok(const ssa_params* p) {
   if (p->out_dtype != SSA_F32 && p->out_dtype != SSA_BF16) return false;
   if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale)) return false;
   if (p->num_queries < 1 || p->num_queries > 256 || p->query_group < 1) return false;
+  if (p->key_layout != SSA_KEYS_WHOLE && p->key_layout != SSA_KEYS_SPLIT) return false;
   const int64_t ng = (p->num_queries + p->query_group - 1) / p->query_group;
   // grid.y of the per-unit and per-(query position, kv head) launches
   if ((int64_t)p->batch * ng * p->num_kv_heads > 65535) return false;
@@ -180,6 +181,9 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
   a.num_blocks = p->num_blocks;
   a.max_seq_len = p->max_seq_len;
   a.tokens_per_wg = tokens_per_wg(p, d);
+  const bool split = p->key_layout == SSA_KEYS_SPLIT;
+  a.key_ld = split ? 2 * p->pair_count : d.d;
+  a.key_off = split ? 0 : 2 * p->pair_begin;
   a.scale = d.scale;
   return a;
 }
@@ -237,14 +241,22 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   return a;
 }
 
-ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
+// Keys as the kernels take them: whole rows (rest null), or the scored dims
+// and the others.
+struct Keys {
+  const void* main;
+  const void* rest;
+};
+
+ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, Keys keys,
                             const void* v_cache, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* sel_idx, const float* sel_logw,
                             const int32_t* sel_cnt, int idx_are_rows, void* out, void* ws,
                             const Layout& l) {
   ssa::AttendArgs a;
   a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.k_cache = static_cast<const uint16_t*>(keys.main);
+  a.k_rest = static_cast<const uint16_t*>(keys.rest);
   a.v_cache = static_cast<const uint16_t*>(v_cache);
   a.block_table = block_table;
   a.seq_lens = seq_lens;
@@ -270,6 +282,8 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, c
   a.nsplit = d.NS;
   a.out_dtype = p->out_dtype;
   a.idx_are_rows = idx_are_rows;
+  a.pair_begin = p->pair_begin;
+  a.pair_count = p->pair_count;
   a.seg_ld = d.SEG;
   a.scale = d.scale;
   return a;
@@ -314,32 +328,29 @@ int check_ws(const ssa_params* p, void* ws, size_t ws_bytes, Layout* l) {
   return SSA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ssa_workspace_bytes(const ssa_params* p) {
-  if (!params_ok(p)) return 0;
-  return layout_of(dims_of(p)).total;
+// Split keys need the rest array unless the scored dims are the whole head.
+bool split_keys_ok(const ssa_params* p, const void* k_dom, const void* k_rest) {
+  if (p->key_layout != SSA_KEYS_SPLIT || !k_dom || !aligned16(k_dom)) return false;
+  if (2 * p->pair_count == p->head_dim) return true;
+  return k_rest && aligned16(k_rest);
 }
 
-int32_t ssa_num_chunks(const ssa_params* p) {
-  if (!params_ok(p)) return 0;
-  return dims_of(p).NC;
+// Rest array as the kernels take it: null when there are no rest dims.
+const void* rest_of(const ssa_params* p, const void* k_rest) {
+  return 2 * p->pair_count == p->head_dim ? nullptr : k_rest;
 }
 
-int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
-                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
-                     const float* top_p, const int32_t* sample_budget, const uint64_t* seed,
-                     void* out, void* workspace, size_t workspace_bytes, void* stream,
-                     void* const* events) {
+int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cache,
+                const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
+                const float* top_p, const int32_t* sample_budget, const uint64_t* seed, void* out,
+                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
   Layout l;
   const int rc = check_ws(p, workspace, workspace_bytes, &l);
   if (rc != SSA_OK) return rc;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !topk || !sample_budget ||
+  if (!q || !keys.main || !v_cache || !block_table || !seq_lens || !topk || !sample_budget ||
       !seed || !out)
     return SSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(keys.main) || !aligned16(v_cache)) return SSA_ERR_INVALID;
   const Dims d = dims_of(p);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Recorder rec{events, s};
@@ -349,7 +360,7 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   int32_t* sel_cnt = at<int32_t>(workspace, l.sel_cnt);
 
   const ssa::IndexArgs ia =
-      index_args(p, d, q, k_cache, block_table, seq_lens, scores, d.SEG, workspace, l);
+      index_args(p, d, q, keys.main, block_table, seq_lens, scores, d.SEG, workspace, l);
   // One query per sequence: the selection can hold cache rows (one dependent
   // load less in the gather).  Several: positions, so that every member
   // applies its own causal span.
@@ -357,7 +368,7 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   const ssa::SelectArgs sa =
       select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr,
                   block_table, rows, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
-  const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
+  const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, sel_idx,
                                          sel_logw, sel_cnt, rows, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(launch_init_for(sa, d.U, s));
@@ -381,6 +392,61 @@ int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, co
   SSA_TRY(ssa::launch_merge(aa, s));
   rec.end(SSA_STAGE_MERGE);
   return SSA_OK;
+}
+
+int attend_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cache,
+                const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
+                const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Layout l;
+  const int rc = check_ws(p, workspace, workspace_bytes, &l);
+  if (rc != SSA_OK) return rc;
+  if (!q || !keys.main || !v_cache || !block_table || !seq_lens || !sel_idx || !sel_logw ||
+      !sel_count || !out)
+    return SSA_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(keys.main) || !aligned16(v_cache)) return SSA_ERR_INVALID;
+  const Dims d = dims_of(p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, sel_idx,
+                                         sel_logw, sel_count, /*idx_are_rows=*/0, out, workspace,
+                                         l);
+  SSA_TRY(ssa::launch_attend(aa, s));
+  SSA_TRY(ssa::launch_merge(aa, s));
+  return SSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssa_workspace_bytes(const ssa_params* p) {
+  if (!params_ok(p)) return 0;
+  return layout_of(dims_of(p)).total;
+}
+
+int32_t ssa_num_chunks(const ssa_params* p) {
+  if (!params_ok(p)) return 0;
+  return dims_of(p).NC;
+}
+
+int ssa_decode_timed(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
+                     const float* top_p, const int32_t* sample_budget, const uint64_t* seed,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream,
+                     void* const* events) {
+  if (!p || p->key_layout != SSA_KEYS_WHOLE) return SSA_ERR_INVALID;
+  return decode_impl(p, q, Keys{k_cache, nullptr}, v_cache, block_table, seq_lens, topk, top_p,
+                     sample_budget, seed, out, workspace, workspace_bytes, stream, events);
+}
+
+int ssa_decode_split(const ssa_params* p, const void* q, const void* k_dom, const void* k_rest,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+                     const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
+                     void* stream, void* const* events) {
+  if (!params_ok(p) || !split_keys_ok(p, k_dom, k_rest)) return SSA_ERR_INVALID;
+  return decode_impl(p, q, Keys{k_dom, rest_of(p, k_rest)}, v_cache, block_table, seq_lens, topk,
+                     top_p, sample_budget, seed, out, workspace, workspace_bytes, stream, events);
 }
 
 int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
@@ -437,20 +503,69 @@ int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const vo
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
                const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,
                size_t workspace_bytes, void* stream) {
-  Layout l;
-  const int rc = check_ws(p, workspace, workspace_bytes, &l);
-  if (rc != SSA_OK) return rc;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !sel_idx || !sel_logw ||
-      !sel_count || !out)
+  if (!p || p->key_layout != SSA_KEYS_WHOLE) return SSA_ERR_INVALID;
+  return attend_impl(p, q, Keys{k_cache, nullptr}, v_cache, block_table, seq_lens, sel_idx,
+                     sel_logw, sel_count, out, workspace, workspace_bytes, stream);
+}
+
+int ssa_attend_split(const ssa_params* p, const void* q, const void* k_dom, const void* k_rest,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                     const int32_t* sel_idx, const float* sel_logw, const int32_t* sel_count,
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!params_ok(p) || !split_keys_ok(p, k_dom, k_rest)) return SSA_ERR_INVALID;
+  return attend_impl(p, q, Keys{k_dom, rest_of(p, k_rest)}, v_cache, block_table, seq_lens,
+                     sel_idx, sel_logw, sel_count, out, workspace, workspace_bytes, stream);
+}
+
+int ssa_append_kv(const ssa_params* p, int32_t num_tokens, const void* k_new, const void* v_new,
+                  const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
+                  void* k_rest, void* v_cache, void* stream) {
+  if (!params_ok(p) || num_tokens < 0) return SSA_ERR_INVALID;
+  if (!k_new || !v_new || !block_table || !seq_lens || !k_cache || !v_cache)
     return SSA_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return SSA_ERR_INVALID;
-  const Dims d = dims_of(p);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const ssa::AttendArgs aa = attend_args(p, d, q, k_cache, v_cache, block_table, seq_lens, sel_idx,
-                                         sel_logw, sel_count, /*idx_are_rows=*/0, out, workspace,
-                                         l);
-  SSA_TRY(ssa::launch_attend(aa, s));
-  SSA_TRY(ssa::launch_merge(aa, s));
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return SSA_ERR_INVALID;
+  if (p->key_layout == SSA_KEYS_WHOLE) {
+    if (k_rest) return SSA_ERR_INVALID;
+  } else if (!split_keys_ok(p, k_cache, k_rest)) {
+    return SSA_ERR_INVALID;
+  }
+  if ((int64_t)p->num_kv_heads * p->head_dim > 8192) return SSA_ERR_INVALID;
+  const int64_t ntok = (int64_t)p->batch * num_tokens;
+  if (ntok == 0) return SSA_OK;
+  if ((ntok + 3) / 4 > INT32_MAX) return SSA_ERR_INVALID;
+  ssa::AppendArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.k_rest = p->key_layout == SSA_KEYS_SPLIT
+                 ? static_cast<uint16_t*>(const_cast<void*>(rest_of(p, k_rest)))
+                 : nullptr;
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.B = p->batch;
+  a.T = num_tokens;
+  a.Hkv = p->num_kv_heads;
+  a.d = p->head_dim;
+  a.pair_begin = p->pair_begin;
+  a.pair_count = p->pair_count;
+  a.max_blocks = p->max_blocks_per_seq;
+  a.num_blocks = p->num_blocks;
+  a.max_seq_len = p->max_seq_len;
+  SSA_TRY(ssa::launch_append(a, static_cast<hipStream_t>(stream)));
+  return SSA_OK;
+}
+
+int ssa_host_device_address(const void* host_ptr, void** dev_ptr) {
+  if (!host_ptr || !dev_ptr) return SSA_ERR_INVALID;
+  *dev_ptr = nullptr;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host_ptr), 0) != hipSuccess || !d) {
+    (void)hipGetLastError();  // leave no sticky error for the next call
+    return SSA_ERR_INVALID;
+  }
+  *dev_ptr = d;
   return SSA_OK;
 }
 

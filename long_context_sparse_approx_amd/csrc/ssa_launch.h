@@ -33,8 +33,8 @@ struct Thresh1 {
 static_assert(sizeof(Thresh1) == 32, "one 32-byte record per unit");
 
 struct IndexArgs {
-  const uint16_t* q;          // [B, Hq, d] bf16
-  const uint16_t* k_cache;    // [num_blocks, Hkv, 16, d] bf16
+  const uint16_t* q;          // [B, T, Hq, d] bf16
+  const uint16_t* k_cache;    // [num_blocks, Hkv, 16, key_ld] bf16
   const int32_t* block_table; // [B, max_blocks]
   const int32_t* seq_lens;    // [B]
   float* scores;              // row u of stride score_ld
@@ -44,6 +44,8 @@ struct IndexArgs {
   int T, g, NG;               // queries per sequence, queries per group, groups
   int Hq, Hkv, G, d, pair_begin, pair_count;
   int max_blocks, num_blocks, max_seq_len, tokens_per_wg;
+  int key_ld;                 // elements per key row: d (whole keys) or 2 * pair_count
+  int key_off;                // first scored element of a row: 2 * pair_begin or 0
   float scale;
 };
 
@@ -89,7 +91,8 @@ struct SelectArgs {
 
 struct AttendArgs {
   const uint16_t* q;
-  const uint16_t* k_cache;
+  const uint16_t* k_cache;    // whole keys [rows, d], or the scored dims [rows, 2 * pair_count]
+  const uint16_t* k_rest;     // split keys: the other dims [rows, d - 2 * pair_count]; else null
   const uint16_t* v_cache;
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -102,8 +105,21 @@ struct AttendArgs {
   int mpw, mblocks;           // members per attention wave (16 / G), waves per group
   int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
   int idx_are_rows;
+  int pair_begin, pair_count; // the scored dims, for split keys
   int64_t seg_ld;
   float scale;
+};
+
+// Appending new tokens' keys and values to the cache (whole or split keys).
+struct AppendArgs {
+  const uint16_t* k_new;      // [B, T, Hkv, d]
+  const uint16_t* v_new;      // [B, T, Hkv, d]
+  const int32_t* block_table; // [B, max_blocks]
+  const int32_t* seq_lens;    // [B], lengths including the new tokens
+  uint16_t* k_cache;          // whole keys, or the scored dims when k_rest is set
+  uint16_t* k_rest;           // the other dims, or null
+  uint16_t* v_cache;
+  int B, T, Hkv, d, pair_begin, pair_count, max_blocks, num_blocks, max_seq_len;
 };
 
 int indexer_tokens_per_iteration(int pair_count);
@@ -123,6 +139,7 @@ hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int n,
                                uint32_t* words, hipStream_t stream);

@@ -22,11 +22,14 @@ SSA_ERR_WORKSPACE = -2
 SSA_ERR_HIP = -3
 SSA_F32 = 0
 SSA_BF16 = 1
+SSA_KEYS_WHOLE = 0
+SSA_KEYS_SPLIT = 1
 BLOCK_TOKENS = 16
 CHUNK_TOKENS = 4096
 STAGES = ("init", "index", "filter", "resolve", "sample", "attend", "merge")
 EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_timed",
-           "ssa_score", "ssa_select", "ssa_attend", "ssa_debug_philox", "ssa_debug_sexp",
+           "ssa_decode_split", "ssa_score", "ssa_select", "ssa_attend", "ssa_attend_split",
+           "ssa_append_kv", "ssa_host_device_address", "ssa_debug_philox", "ssa_debug_sexp",
            "ssa_error_string")
 
 
@@ -38,7 +41,8 @@ class SsaParams(ctypes.Structure):
                 ("pair_begin", ctypes.c_int32), ("pair_count", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("num_queries", ctypes.c_int32),
-                ("query_group", ctypes.c_int32), ("early_stop", ctypes.c_float)]
+                ("query_group", ctypes.c_int32), ("early_stop", ctypes.c_float),
+                ("key_layout", ctypes.c_int32)]
 
 
 class SsaError(RuntimeError):
@@ -69,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.ssa_decode.restype = ctypes.c_int
         L.ssa_decode_timed.argtypes = common + [_P]
         L.ssa_decode_timed.restype = ctypes.c_int
+        L.ssa_decode_split.argtypes = ([_PP, _P, _P, _P] + common[3:] + [_P])
+        L.ssa_decode_split.restype = ctypes.c_int
         L.ssa_score.argtypes = [_PP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_score.restype = ctypes.c_int
         L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -76,6 +82,13 @@ def lib() -> ctypes.CDLL:
         L.ssa_select.restype = ctypes.c_int
         L.ssa_attend.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_attend.restype = ctypes.c_int
+        L.ssa_attend_split.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]
+        L.ssa_attend_split.restype = ctypes.c_int
+        L.ssa_append_kv.argtypes = [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.ssa_append_kv.restype = ctypes.c_int
+        L.ssa_host_device_address.argtypes = [_P, ctypes.POINTER(ctypes.c_void_p)]
+        L.ssa_host_device_address.restype = ctypes.c_int
         L.ssa_debug_philox.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
         L.ssa_debug_philox.restype = ctypes.c_int
@@ -100,6 +113,26 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def host_device_address(t: torch.Tensor) -> int:
+    """Device address of a pinned host tensor (torch's pin_memory), through
+    the library; raises for memory the device cannot address."""
+    assert not t.is_cuda and t.is_pinned(), "a pinned host tensor"
+    out = ctypes.c_void_p()
+    _check(lib().ssa_host_device_address(ctypes.c_void_p(t.data_ptr()), ctypes.byref(out)),
+           "ssa_host_device_address")
+    return int(out.value)
+
+
+def _kv_ptr(t):
+    """A cache argument: a device tensor, or a pinned host tensor (offloaded
+    cache), passed by the address kernels use."""
+    if t is None:
+        return None
+    if t.is_cuda:
+        return ctypes.c_void_p(t.data_ptr())
+    return ctypes.c_void_p(host_device_address(t))
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -109,13 +142,13 @@ def _stream(stream):
 def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                 max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
                 softmax_scale=0.0, block_size=BLOCK_TOKENS, num_queries=1,
-                query_group=1, early_stop=0.0) -> SsaParams:
+                query_group=1, early_stop=0.0, key_layout=SSA_KEYS_WHOLE) -> SsaParams:
     if pair_begin is None:
         pair_begin = head_dim // 2 - pair_count
     return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
                      float(softmax_scale), int(num_queries), int(query_group),
-                     float(early_stop))
+                     float(early_stop), int(key_layout))
 
 
 def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
@@ -183,6 +216,39 @@ def decode(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk, sampl
     return out
 
 
+def decode_split(p: SsaParams, q, k_dom, k_rest, v_cache, block_table, seq_lens, topk,
+                 sample_budget, seed, out=None, workspace=None, stream=None, events=None,
+                 top_p=None):
+    """One decode step over split keys (p.key_layout == SSA_KEYS_SPLIT):
+    k_dom [nblk, Hkv, 16, 2*pair_count] on the device; k_rest
+    [nblk, Hkv, 16, d - 2*pair_count] and v_cache on the device or in pinned
+    host memory."""
+    _check_top_p(top_p, p.batch)
+    if out is None:
+        dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=dt, device=q.device)
+    workspace = _ws(p, workspace, q.device)
+    _check(lib().ssa_decode_split(
+        ctypes.byref(p), _ptr(q), _ptr(k_dom), _kv_ptr(k_rest), _kv_ptr(v_cache),
+        _ptr(block_table), _ptr(seq_lens), _ptr(topk), _ptr(top_p), _ptr(sample_budget),
+        _ptr(seed), _ptr(out), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        _stream(stream), None if events is None else ctypes.c_void_p(events)),
+        "ssa_decode_split")
+    return out
+
+
+def append_kv(p: SsaParams, k_new, v_new, block_table, seq_lens, k_cache, k_rest, v_cache,
+              stream=None):
+    """Write k_new, v_new [B, T, Hkv, d] at positions seq_lens[b] - T + t of
+    the cache (whole keys: k_rest None; split keys: k_cache gets the scored
+    dims, k_rest the others)."""
+    assert k_new.shape == v_new.shape and k_new.dim() == 4 and k_new.shape[0] == p.batch
+    _check(lib().ssa_append_kv(ctypes.byref(p), int(k_new.shape[1]), _ptr(k_new), _ptr(v_new),
+                               _ptr(block_table), _ptr(seq_lens), _kv_ptr(k_cache),
+                               _kv_ptr(k_rest), _kv_ptr(v_cache), _stream(stream)),
+           "ssa_append_kv")
+
+
 def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspace=None,
           stream=None):
     """Approximate scores [B, NG*Hkv, max_seq_len] f32, one row per selection
@@ -230,6 +296,21 @@ def attend(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, sel_idx, se
                             _ptr(block_table), _ptr(seq_lens), _ptr(sel_idx), _ptr(sel_logw),
                             _ptr(sel_count), _ptr(out), _ptr(workspace),
                             ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_attend")
+    return out
+
+
+def attend_split(p: SsaParams, q, k_dom, k_rest, v_cache, block_table, seq_lens, sel_idx,
+                 sel_logw, sel_count, out=None, workspace=None, stream=None):
+    """attend() over split keys."""
+    if out is None:
+        dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=dt, device=q.device)
+    workspace = _ws(p, workspace, q.device)
+    _check(lib().ssa_attend_split(ctypes.byref(p), _ptr(q), _ptr(k_dom), _kv_ptr(k_rest),
+                                  _kv_ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                  _ptr(sel_idx), _ptr(sel_logw), _ptr(sel_count), _ptr(out),
+                                  _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                  _stream(stream)), "ssa_attend_split")
     return out
 
 

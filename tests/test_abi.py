@@ -118,3 +118,55 @@ def test_debug_hooks_validate(lib):
 def test_error_strings(lib):
     for code in (0, -1, -2, -3, 99):
         assert isinstance(ssa.error_string(code), str) and ssa.error_string(code)
+
+
+def test_key_layouts_checked(lib):
+    """Whole-key entry points refuse split params and the split ones whole
+    params; split keys need an aligned rest array unless the scored pairs
+    cover the head; append checks its layout, sizes and pointers."""
+    fake = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 8)
+    big = ctypes.c_size_t(1 << 40)
+    assert lib.ssa_workspace_bytes(ctypes.byref(good(key_layout=2))) == 0
+    ps = good(key_layout=ssa.SSA_KEYS_SPLIT)
+    pw = good()
+    assert ssa.workspace_bytes(ps) == ssa.workspace_bytes(pw)
+    ten = [fake] * 10
+    assert lib.ssa_decode(ctypes.byref(ps), *ten, fake, big, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_attend(ctypes.byref(ps), *([fake] * 9), fake, big, None) == ssa.SSA_ERR_INVALID
+
+    def split(p, k_rest, k_dom=fake):
+        return lib.ssa_decode_split(ctypes.byref(p), fake, k_dom, k_rest, *([fake] * 8), fake,
+                                    ctypes.c_size_t(16), None, None)
+
+    def attend_split(p, k_rest):
+        return lib.ssa_attend_split(ctypes.byref(p), fake, fake, k_rest, *([fake] * 7), fake,
+                                    ctypes.c_size_t(16), None)
+
+    assert split(pw, fake) == ssa.SSA_ERR_INVALID
+    assert split(ps, None) == ssa.SSA_ERR_INVALID
+    assert split(ps, mis) == ssa.SSA_ERR_INVALID
+    assert split(ps, fake, k_dom=mis) == ssa.SSA_ERR_INVALID
+    assert attend_split(pw, fake) == ssa.SSA_ERR_INVALID
+    assert attend_split(ps, None) == ssa.SSA_ERR_INVALID
+    # past the layout checks the (too small) workspace is what fails
+    assert split(ps, fake) == ssa.SSA_ERR_WORKSPACE
+    assert attend_split(ps, fake) == ssa.SSA_ERR_WORKSPACE
+    whole_head = good(key_layout=ssa.SSA_KEYS_SPLIT, pair_begin=0, pair_count=64)
+    assert split(whole_head, None) == ssa.SSA_ERR_WORKSPACE
+
+    def append(p, n, k_rest, k_cache=fake):
+        return lib.ssa_append_kv(ctypes.byref(p), n, fake, fake, fake, fake, k_cache, k_rest,
+                                 fake, None)
+
+    assert append(pw, 1, fake) == ssa.SSA_ERR_INVALID        # whole keys take no rest array
+    assert append(ps, 1, None) == ssa.SSA_ERR_INVALID        # split keys need one
+    assert append(pw, -1, None) == ssa.SSA_ERR_INVALID
+    assert append(pw, 1, None, k_cache=mis) == ssa.SSA_ERR_INVALID
+    assert append(good(num_kv_heads=128, num_q_heads=128), 1, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_append_kv(ctypes.byref(pw), 1, None, fake, fake, fake, fake, None, fake,
+                             None) == ssa.SSA_ERR_INVALID
+    assert append(pw, 0, None) == ssa.SSA_OK                  # nothing to write
+    assert append(ps, 0, fake) == ssa.SSA_OK
+    assert lib.ssa_host_device_address(None, ctypes.byref(ctypes.c_void_p())) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_host_device_address(fake, None) == ssa.SSA_ERR_INVALID

@@ -177,3 +177,32 @@ def test_fullsize_1m_multi_query():
             err = float(np.abs(got[b, t, h * G:(h + 1) * G] - o).max())
             assert err <= bound, f"member {t} of {(b, c, h)}: {err} > {bound}"
         say(f"[full] 1m multi-query unit {(b, c, h)}: selection bit-exact, members within bound")
+
+
+def test_fullsize_1m_split_keys():
+    """The 1M workload over split keys (FASA-M layout), the rest of the keys
+    and the values first on the device, then in pinned host memory: both
+    bitwise equal to the whole-key decode (which the 1M test above checks
+    against the oracle)."""
+    wl = synth.make_workload("1m", DEV)
+    say("[full] 1m split keys: device, then host-offloaded rest and values")
+    pw = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                        pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    ps = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
+                        key_layout=ssa.SSA_KEYS_SPLIT)
+    args = (wl.block_table, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed)
+    ws = ssa.alloc_workspace(pw, DEV)
+    ref = ssa.decode(pw, wl.q, wl.k_cache, wl.v_cache, *args, workspace=ws).clone()
+    lo, hi = 2 * wl.pair_begin, 2 * (wl.pair_begin + wl.pair_count)
+    k_dom = wl.k_cache[..., lo:hi].contiguous()
+    k_rest = torch.cat([wl.k_cache[..., :lo], wl.k_cache[..., hi:]], dim=-1).contiguous()
+    out = ssa.decode_split(ps, wl.q, k_dom, k_rest, wl.v_cache, *args, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(ref, out)
+    k_rest_h = k_rest.cpu().pin_memory()
+    v_h = wl.v_cache.cpu().pin_memory()
+    del k_rest
+    out_h = ssa.decode_split(ps, wl.q, k_dom, k_rest_h, v_h, *args, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, out_h)
