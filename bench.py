@@ -97,13 +97,30 @@ def measured_traffic(workload):
     return float(t.group(1))
 
 
+def split_keys(wl, host):
+    """(k_dom, k_rest, v) of the workload's cache in the split key layout,
+    cut with torch slicing; with ``host`` the rest of the keys and the values
+    live in pinned host memory."""
+    import torch
+
+    lo, hi = 2 * wl.pair_begin, 2 * (wl.pair_begin + wl.pair_count)
+    k_dom = wl.k_cache[..., lo:hi].contiguous()
+    k_rest = torch.cat([wl.k_cache[..., :lo], wl.k_cache[..., hi:]], dim=-1).contiguous()
+    v = wl.v_cache
+    if host:
+        k_rest, v = k_rest.cpu().pin_memory(), v.cpu().pin_memory()
+    return k_dom, k_rest, v
+
+
 def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None,
-            num_queries=1, query_group=1, early_stop=0.0):
+            num_queries=1, query_group=1, early_stop=0.0, keys="whole"):
     """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
     ``top_p`` (a float) caps every sequence's deterministic stratum at the
     top-p prefix; ``wl`` reuses an already generated workload; with
     ``num_queries`` T > 1 each step carries T query positions per sequence,
-    ``query_group`` of them sharing one selection."""
+    ``query_group`` of them sharing one selection.  ``keys`` = "split" runs
+    over split keys on the device, "split_host" with the rest of the keys and
+    the values in pinned host memory."""
     import torch
 
     from long_context_sparse_approx_amd import ssa, synth
@@ -115,16 +132,24 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=dev)
+    split = keys != "whole"
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
-                       query_group=query_group, early_stop=early_stop)
+                       query_group=query_group, early_stop=early_stop,
+                       key_layout=ssa.SSA_KEYS_SPLIT if split else ssa.SSA_KEYS_WHOLE)
     ws = ssa.alloc_workspace(p, dev)
     out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    call = (p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
-            wl.sample_budget, wl.seed)
+    tail = (wl.block_table, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed)
+    if split:
+        k_dom, k_rest, v_split = split_keys(wl, keys == "split_host")
+        call = (p, wl.q, k_dom, k_rest, v_split) + tail
+        step = ssa.decode_split
+    else:
+        call = (p, wl.q, wl.k_cache, wl.v_cache) + tail
+        step = ssa.decode
     for _ in range(warmup):
-        ssa.decode(*call, out=out, workspace=ws, stream=stream, top_p=tp)
+        step(*call, out=out, workspace=ws, stream=stream, top_p=tp)
     torch.cuda.synchronize()
 
     hip = Hip()
@@ -147,15 +172,15 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
             if graphs is not None:
                 graphs[i % len(graphs)].replay()
             else:
-                ssa.decode(*call, out=out, workspace=ws, stream=stream, top_p=tp,
-                           events=ctypes.addressof(arrs[i]) if arrs else None)
+                step(*call, out=out, workspace=ws, stream=stream, top_p=tp,
+                     events=ctypes.addressof(arrs[i]) if arrs else None)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
     # Timed region: K whole steps; HIP events bracket only the indexer launch
     # (on the decode stream), for its roofline.
     graphs = None
-    if args.graph:
+    if args.graph and not split:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             ssa.decode(*call, out=out, workspace=ws, stream=torch.cuda.current_stream(),
@@ -189,7 +214,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     del graphs
 
     # Selected-set sizes of this step (deterministic: same kernels, same inputs).
-    sc = ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, workspace=ws)
+    sc = ssa.score(p, wl.q, call[2], wl.block_table, wl.seq_lens, workspace=ws)
     _, _, cnt, _ = ssa.select(p, sc, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
                               workspace=ws, top_p=tp)
     cnt = cnt.sum(dim=2).cpu()
@@ -203,11 +228,68 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     idx_bytes = tokens * wl.Hkv * groups * (2 * wl.pair_count * 2)  # K pair subset per group
     gather_bytes = (n_det + n_smp) * 2.0 * d * 2                # K and V rows
     score_bytes = tokens * wl.Hkv * 4 * 4                       # 1 write + 3 reads
+    if split:
+        del call, k_dom, k_rest, v_split
     res = dict(wl=wl, p=p, ms_step=ms_step, idx_ms=idx_ms, gpu_ms=gpu_ms, stage_ms=stage_ms,
                tokens=tokens,
                idx_bytes=idx_bytes, gather_bytes=gather_bytes, score_bytes=score_bytes,
                n_det=n_det, n_smp=n_smp, t_gen=t_gen)
     return res
+
+
+def append_bench(wl, steps, warmup):
+    """Cache append in the split key layout: a bulk fill of every token of the
+    workload (HBM-bound: each token's key and value rows read once and written
+    once) and a one-token append per sequence, as in every decode step."""
+    import torch
+
+    from long_context_sparse_approx_amd import ssa
+
+    dev = "cuda:0"
+    B, Hkv, d = wl.B, wl.Hkv, wl.d
+    T = max(wl.lens)
+    assert B == 1, "bulk fill measured on one sequence"
+    pos = torch.arange(T, device=dev)
+    rows = wl.block_table[0, (pos // 16).long()].long()
+    slot = (pos % 16).long()
+    k_new = wl.k_cache[rows, :, slot, :].unsqueeze(0).contiguous()  # [1, T, Hkv, d]
+    v_new = wl.v_cache[rows, :, slot, :].unsqueeze(0).contiguous()
+    del rows, slot, pos
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count,
+                       key_layout=ssa.SSA_KEYS_SPLIT)
+    pc2 = 2 * wl.pair_count
+    nblk = wl.k_cache.shape[0]
+    k_dom = torch.empty((nblk, Hkv, 16, pc2), dtype=torch.bfloat16, device=dev)
+    k_rest = torch.empty((nblk, Hkv, 16, d - pc2), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(wl.v_cache)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    bulk_ms = timed(lambda: ssa.append_kv(p, k_new, v_new, wl.block_table, wl.seq_lens, k_dom,
+                                          k_rest, v), max(3, steps // 5))
+    ok = (torch.equal(k_dom, wl.k_cache[..., 2 * wl.pair_begin:2 * wl.pair_begin + pc2])
+          and torch.equal(v, wl.v_cache))
+    one_k, one_v = k_new[:, -1:].contiguous(), v_new[:, -1:].contiguous()
+    one_ms = timed(lambda: ssa.append_kv(p, one_k, one_v, wl.block_table, wl.seq_lens, k_dom,
+                                         k_rest, v), steps)
+    nbytes = 2.0 * T * Hkv * (2 * d * 2)  # key + value rows, read once and written once
+    gbps = nbytes / (bulk_ms * 1e-3) / 1e9
+    del k_new, v_new, k_dom, k_rest, v
+    torch.cuda.empty_cache()
+    return dict(bulk_tokens=T, bulk_ms=round(bulk_ms, 4), bulk_bytes=nbytes,
+                bulk_gbps=round(gbps, 1), bulk_frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4),
+                bulk_rebuilds_cache_bitwise=bool(ok), one_token_us=round(one_ms * 1e3, 2))
 
 
 def unit_host_inputs(wl, b, h):
@@ -302,6 +384,8 @@ def main():
     ap.add_argument("--multi", type=int, default=4,
                     help="also time the main workload with this many query positions per "
                          "step, one shared selection vs one per query (0 = skip)")
+    ap.add_argument("--no-split-keys", dest="split_keys", action="store_false",
+                    help="skip the split-key (device and host-offloaded) and append timings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -357,6 +441,26 @@ def main():
             value=s5["value"], unit="KV-tokens/s/layer", ms_per_step=s5["ms_per_step"],
             stages_us=s5["stages_us"], selected=s5["selected"])
         del r5
+    if args.split_keys:
+        sk = dict(policy="FASA-M layout: the scored RoPE pairs of every key in one array (the "
+                         "indexer reads only it), the other dims in another; attention "
+                         "reads the selected rows of both",
+                  resident_bytes_per_token_head=dict(
+                      whole=4 * res["wl"].d,
+                      split_host=4 * res["wl"].pair_count),
+                  unit="KV-tokens/s/layer")
+        for keys in ("split", "split_host"):
+            r6 = run_gpu(args, args.workload, args.steps if keys == "split" else 5,
+                         args.warmup if keys == "split" else 1, not args.no_stage_events,
+                         wl=res["wl"], keys=keys)
+            s6 = summarize(r6, args.workload)
+            sk[keys] = dict(value=s6["value"], ms_per_step=s6["ms_per_step"],
+                            stages_us=s6["stages_us"],
+                            indexer_gbps=s6["roofline"]["achieved"] if s6["roofline"] else None)
+            del r6
+            torch.cuda.empty_cache()
+        sk["append"] = append_bench(res["wl"], args.steps, args.warmup)
+        variants["split_keys"] = sk
     if args.multi > 1:
         T = args.multi
         mq = dict(queries_per_step=T,

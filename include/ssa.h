@@ -255,7 +255,7 @@ int ssa_attend_split(const ssa_params* p, const void* q, const void* k_dom, cons
  * receives the values.  Caches may be pinned host memory as above.  Rows
  * that two new tokens of one call share receive one of them.  Needs no
  * workspace; B * T may be as large as the cache (bulk fill, e.g. after a
- * prefill).  Requires Hkv * d <= 8192. */
+ * prefill), below 2^31.  Requires Hkv * d <= 8192. */
 int ssa_append_kv(const ssa_params* p, int32_t num_tokens, const void* k_new, const void* v_new,
                   const int32_t* block_table, const int32_t* seq_lens, void* k_cache,
                   void* k_rest, void* v_cache, void* stream);

@@ -533,7 +533,7 @@ int ssa_append_kv(const ssa_params* p, int32_t num_tokens, const void* k_new, co
   if ((int64_t)p->num_kv_heads * p->head_dim > 8192) return SSA_ERR_INVALID;
   const int64_t ntok = (int64_t)p->batch * num_tokens;
   if (ntok == 0) return SSA_OK;
-  if ((ntok + 3) / 4 > INT32_MAX) return SSA_ERR_INVALID;
+  if (ntok > INT32_MAX) return SSA_ERR_INVALID;
   ssa::AppendArgs a;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
