@@ -268,11 +268,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
 // Clears the per-unit histograms and maxima.
 __global__ __launch_bounds__(256) void init_kernel(uint32_t* hist1, uint32_t* hist2,
                                                    uint32_t* maxkey, unsigned long long* hist1m,
-                                                   unsigned long long* hist2m, uint32_t* stop_bits,
-                                                   int64_t stop_words) {
+                                                   unsigned long long* hist2m) {
   const int u = blockIdx.x;
-  if (stop_bits)
-    for (int64_t i = threadIdx.x; i < stop_words; i += 256) stop_bits[u * stop_words + i] = 0u;
   for (int i = threadIdx.x; i < kBins; i += 256) {
     hist1[(size_t)u * kBins + i] = 0u;
     hist2[(size_t)u * kBins + i] = 0u;
@@ -355,10 +352,9 @@ int indexer_resident_workgroups(int pair_count) {
 }
 
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
-                       unsigned long long* hist1m, unsigned long long* hist2m,
-                       uint32_t* stop_bits, int64_t stop_words, int units, hipStream_t stream) {
-  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey, hist1m, hist2m, stop_bits,
-                                         stop_words);
+                       unsigned long long* hist1m, unsigned long long* hist2m, int units,
+                       hipStream_t stream) {
+  init_kernel<<<units, 256, 0, stream>>>(hist1, hist2, maxkey, hist1m, hist2m);
   return hipGetLastError();
 }
 

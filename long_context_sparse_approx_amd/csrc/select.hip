@@ -188,10 +188,27 @@ __device__ __forceinline__ int threads_per_chunk(int nc) {
   return tpc;
 }
 
+// Early stopping: where each chunk's words above the threshold key (its
+// listed tokens above the threshold digit, then its candidates above the key;
+// packed << 16 in cnt) start in the unit's word array, and their total.
+__device__ __forceinline__ void stop_offsets(const SelectArgs& a, int u, size_t cu, int nc,
+                                          const int* cnt, int* scan_scr) {
+  int run = 0;
+  for (int c0 = 0; c0 < nc; c0 += kRT) {
+    const int c = c0 + threadIdx.x;
+    const int w = c < nc ? clamp_count(a.list_cnt[2 * (cu + c)], kChunk) + (cnt[c] >> 16) : 0;
+    int tot;
+    const int ex = block_exclusive_scan<kRT>(w, scan_scr, &tot);
+    if (c < nc) a.stop_off[cu + c] = run + ex;
+    run += tot;
+  }
+  if (threadIdx.x == 0) a.stop_n[u] = run;
+}
+
 __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ unsigned long long mh[kBins];  // mass units per digit (top-p)
-  __shared__ int ties_sh[kMaxResolveChunks];
+  __shared__ int ties_sh[kMaxResolveChunks];  // ties + (candidates above the key << 16)
   __shared__ int scan_scr[kRW];
   __shared__ int pair[2];
   __shared__ unsigned long long scan_m[kRW];
@@ -313,9 +330,10 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         }
         st.ties_needed = need;
         st.k_eff = t1.above + above2 + above3 + need;
-        // Ties on the threshold key per chunk (integer), and the weight of the
-        // candidates strictly below it (each thread over its fixed items, in
-        // order, then a fixed tree).
+        // Ties on the threshold key per chunk and candidates above it
+        // (integer, packed as ties + (above << 16): each at most 4096), and
+        // the weight of the candidates strictly below it (each thread over
+        // its fixed items, in order, then a fixed tree).
         double cs = 0.0;
         if (one_chunk) {
           int ties = 0;
@@ -323,13 +341,13 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
           for (int k = 0; k < kKeep; ++k) {
             const int i = csub + k * tpc;
             if (i < nm) {
-              ties += kr[k] == st.tkey;
+              ties += kr[k] == st.tkey ? 1 : (kr[k] > st.tkey ? 0x10000 : 0);
               if (kr[k] < st.tkey) cs += (double)sexp(key_to_float(kr[k]) - st.M);
             }
           }
           for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
             const uint32_t key = ckm[i];
-            ties += key == st.tkey;
+            ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
             if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
           }
           if (ties) atomicAdd(&ties_sh[cm], ties);
@@ -340,7 +358,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
             int ties = 0;
             for (int i = csub; i < n; i += tpc) {
               const uint32_t key = ck[i];
-              ties += key == st.tkey;
+              ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
               if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
             }
             if (ties) atomicAdd(&ties_sh[c], ties);
@@ -350,7 +368,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         int run = 0;
         for (int c0 = 0; c0 < nc; c0 += kRT) {
           const int c = c0 + threadIdx.x;
-          const int v = c < nc ? ties_sh[c] : 0;
+          const int v = c < nc ? ties_sh[c] & 0xffff : 0;
           int tot;
           const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
           if (c < nc) {
@@ -360,6 +378,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
           run += tot;
         }
         total_ties = run;
+        if (a.stop_off) stop_offsets(a, u, cu, nc, ties_sh, scan_scr);
       }
       double acc = 0.0;
       for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
@@ -389,15 +408,34 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------------ early stopping
 // "S2O: Early Stopping for Sparse Attention via Online Permutation",
-// methodology part 2.  One 1024-thread workgroup per unit: the stratum's
-// (key, position) pairs are rebuilt from the chunk lists, sorted in LDS into
-// the stratum's order (key descending, position ascending), cut into 64-token
-// blocks whose gains are their mass units, and the visit stops after the first
-// block whose gain is below tau times the mass so far (exact integer
-// arithmetic).  The positions past the stop are marked in the unit's bitmap,
-// which the sample kernel drops from the stratum.
+// methodology part 2.  The deterministic stratum, in its order (key
+// descending, position ascending), is cut into 64-token blocks whose gains are
+// their mass units; the visit stops after the first block whose gain is below
+// tau times the mass so far (exact integer arithmetic).  A token's word is
+// ((~key) << 32) | position, so ascending words are the stratum's order, and
+// the cut is published as the last word kept: the sample kernel drops every
+// deterministic token whose word is larger.  The stratum is the tokens above
+// the threshold key T (at most 16384 when a cut applies) followed by the
+// first ties on T (one mass value, ranked by position), so only the former
+// are ordered, in five steps that spread over the device and use no global
+// atomics:
+//   stop_gather: each chunk writes its words above T (its listed tokens
+//     above the threshold digit, then its candidates above T) at the offset
+//     the resolve kernel computed for it;
+//   stop_sort: one workgroup sorts each 1024-word slice (4 words per thread
+//     in registers, cross-wave exchanges through LDS);
+//   stop_pair: for every pair of slices, the number of words of one below
+//     each word of the other (searched in LDS), one count array per pair;
+//   stop_final: each word's rank = its index in its slice + those counts;
+//     mass and word stored in rank order;
+//   stop_cut: one workgroup per unit sums the block gains (ties count at
+//     T's mass), scans them, finds the stop and writes the last word kept.
 constexpr int kStopBlock = 64;
 constexpr int kStopMax = 16384;  // largest stratum that is truncated
+constexpr int kSlice = 1024;     // words sorted per wave
+constexpr int kSlices = kStopMax / kSlice;
+constexpr int kSortT = 256;                // threads per slice sort
+constexpr int kSE = kSlice / kSortT;      // words per thread in the sort
 
 // gain < tau * acc, exactly, for 0 < tau (tau >= 1 compares with acc).
 __device__ __forceinline__ bool gain_below(unsigned long long gain, unsigned long long acc,
@@ -413,223 +451,321 @@ __device__ __forceinline__ bool gain_below(unsigned long long gain, unsigned lon
   return ((unsigned __int128)gain << D) < rhs;
 }
 
-// First chunk c with pre[c + 1] > f (pre: exclusive prefix of per-chunk counts,
-// nc + 1 entries, in LDS).
-__device__ __forceinline__ int chunk_of(const int* pre, int nc, int f) {
-  int lo = 0, hi = nc - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pre[mid] <= f) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// Whether early stopping can cut this unit's stratum (uniform per unit).
+__device__ __forceinline__ bool stop_applies(const UnitState& st) {
+  if (st.flags & (kFlagEmpty | kFlagDense | kFlagNoTopk)) return false;
+  return st.k_eff > kStopBlock && st.k_eff <= kStopMax;
 }
 
-__global__ __launch_bounds__(kRT) void stop_kernel(SelectArgs a) {
-  __shared__ unsigned long long buf[kStopMax];  // ((~key) << 32) | position, sorted ascending
-  __shared__ int pre[kMaxResolveChunks + 1];    // exclusive prefix of per-chunk list counts
-  __shared__ unsigned long long scan_m[kRW];
-  __shared__ int scan_scr[kRW];
-  __shared__ int first_sh;
-  __shared__ int n_sh;
-  __shared__ int strad_sh;
-  const int u = blockIdx.x;
-  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
-  const int tid = threadIdx.x;
-  if (st.flags & (kFlagEmpty | kFlagDense | kFlagNoTopk)) return;  // uniform
-  if (st.k_eff <= kStopBlock || st.k_eff > kStopMax) return;       // nothing to cut
-  const int nc = (st.L + kChunk - 1) / kChunk;
-  const size_t cu = (size_t)u * a.nchunk;
-  const float* srow = a.scores + (size_t)u * a.score_ld;
-  const size_t seg = (size_t)u * a.seg_ld;
-  if (tid == 0) first_sh = 0x7fffffff;
-  // The stratum, in the flattened (chunk, list position) order: first every
-  // listed token above the threshold digit (all in the stratum), then the
-  // candidates above the threshold key or within the tie quota (a tie's rank
-  // is its position among the ties in this order, i.e. in index order).
-  auto prefix = [&](bool cand) {
-    int run = 0;
-    for (int c0 = 0; c0 < nc; c0 += kRT) {
-      const int c = c0 + tid;
-      const int v = c < nc ? clamp_count(cand ? a.cand_cnt[cu + c] : a.list_cnt[2 * (cu + c)],
-                                         kChunk)
-                           : 0;
-      int tot;
-      const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
-      if (c < nc) pre[c] = run + ex;
-      run += tot;
+__device__ __forceinline__ unsigned long long stratum_word(uint32_t key, int pos) {
+  return ((unsigned long long)~key << 32) | (uint32_t)pos;
+}
+
+// The value of lane ^ L, for a compile-time L < 64: lane distances 1 and 2
+// are quad permutations and 8 a rotation by 8 within a row of 16 (DPP, plain
+// VALU moves); 4 and 16 are swizzles within 32 lanes; 32 goes through the LDS
+// crossbar.
+template <int L>
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16 || L == 32, "lane distance");
+  if constexpr (L == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  } else if constexpr (L == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  } else if constexpr (L == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  } else if constexpr (L == 4 || L == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (L << 10));  // xor within 32
+  } else {
+    return (uint32_t)__shfl_xor((int)x, L);
+  }
+}
+
+template <int L>
+__device__ __forceinline__ unsigned long long lane_xor64(unsigned long long x) {
+  const uint32_t lo = lane_xor32<L>((uint32_t)x);
+  const uint32_t hi = lane_xor32<L>((uint32_t)(x >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// One bitonic stage (merge size K, partner distance J) on N = NT * E words
+// held E per thread in registers (element i = E * tid + e).  K and J are
+// compile-time constants, so every branch below folds: pairs closer than E
+// are exchanged inside a thread, pairs closer than 64 E across the lanes of a
+// wave by shuffle, the rest through LDS (buf: element E t + e at e * NT + t,
+// consecutive words per wave: no bank conflicts).
+template <int NT, int E, int K, int J>
+__device__ __forceinline__ void bitonic_stage(unsigned long long (&v)[E], unsigned long long* buf,
+                                              int tid) {
+  if constexpr (J < E) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & J) != 0) continue;
+      // ascending iff bit K of the element index is clear
+      const bool asc = K >= E ? ((E * tid) & K) == 0 : (e & K) == 0;
+      const unsigned long long x = v[e], y = v[e + J];
+      const bool swap = asc == (x > y);
+      v[e] = swap ? y : x;
+      v[e + J] = swap ? x : y;
     }
-    if (tid == 0) pre[nc] = run;
-    __syncthreads();
-    return run;
-  };
-  int n = min(prefix(false), kStopMax);
-  for (int f = tid; f < n; f += kRT) {
-    const int c = chunk_of(pre, nc, f);
-    const int pos = min(max(a.list_idx[seg + (size_t)c * kChunk + (f - pre[c])], 0), st.L - 1);
-    buf[f] = ((unsigned long long)~order_key(srow[pos]) << 32) | (uint32_t)pos;
-  }
-  __syncthreads();
-  // Candidates: the slot order is free (the buffer is sorted next), so slots
-  // come from a wave-aggregated LDS counter.  A tie (key == T) is in the
-  // stratum iff its global tie rank is below the quota: all ties of a chunk
-  // are in when the chunk's ties end within the quota, none when they start
-  // past it; only the one chunk straddling the quota ranks its ties (one wave,
-  // in index order).
-  const int ncand = prefix(true);
-  if (tid == 0) n_sh = n;
-  if (tid == 0) strad_sh = -1;
-  __syncthreads();
-  for (int c = tid; c < nc; c += kRT) {
-    const int tb = a.ties_before[cu + c];
-    const int tc = a.tiecnt[cu + c];
-    if (tb < st.ties_needed && st.ties_needed < tb + tc) strad_sh = c;
-  }
-  __syncthreads();
-  const int strad = strad_sh;
-  const int lane = tid & 63;
-  for (int f = tid; f - lane < ncand; f += kRT) {
-    bool in_s = false;
-    uint32_t key = 0u;
-    int pos = 0;
-    if (f < ncand) {
-      const int c = chunk_of(pre, nc, f);
-      const size_t at = seg + (size_t)c * kChunk + (f - pre[c]);
-      key = a.cand_key[at];
-      pos = min(max(a.cand_idx[at], 0), st.L - 1);
-      const int tb = a.ties_before[cu + c];
-      in_s = key > st.tkey ||
-             (key == st.tkey && c != strad && tb + a.tiecnt[cu + c] <= st.ties_needed);
-    }
-    const uint64_t m = __ballot(in_s);
-    int base = 0;
-    if (lane == 0 && m) base = atomicAdd(&n_sh, __popcll(m));
-    base = __shfl(base, 0);
-    const int slot = base + __popcll(m & ((1ull << lane) - 1ull));
-    if (in_s && slot < kStopMax) buf[slot] = ((unsigned long long)~key << 32) | (uint32_t)pos;
-  }
-  __syncthreads();
-  if (strad >= 0 && tid < 64) {  // the straddling chunk's ties, in index order
-    const int nca = pre[strad + 1] - pre[strad];
-    const size_t at0 = seg + (size_t)strad * kChunk;
-    int rank = a.ties_before[cu + strad];
-    for (int i0 = 0; i0 < nca; i0 += 64) {
-      const int i = i0 + tid;
-      const uint32_t key = i < nca ? a.cand_key[at0 + i] : 0u;
-      const bool tie = i < nca && key == st.tkey;
-      const uint64_t tm = __ballot(tie);
-      const int r = rank + __popcll(tm & ((1ull << tid) - 1ull));
-      const bool in_s = tie && r < st.ties_needed;
-      const uint64_t m = __ballot(in_s);
-      int base = 0;
-      if (tid == 0 && m) base = atomicAdd(&n_sh, __popcll(m));
-      base = __shfl(base, 0);
-      const int slot = base + __popcll(m & ((1ull << tid) - 1ull));
-      if (in_s && slot < kStopMax)
-        buf[slot] = ((unsigned long long)~key << 32) |
-                    (uint32_t)min(max(a.cand_idx[at0 + i], 0), st.L - 1);
-      rank += __popcll(tm);
-    }
-  }
-  __syncthreads();
-  n = min(n_sh, kStopMax);
-  __syncthreads();
-  // Bitonic sort of kStopMax elements, ascending (padding sorts last).  Thread
-  // t holds elements 16t .. 16t + 15 in registers: pairs closer than 16 are
-  // exchanged inside a thread, pairs closer than 1024 across the lanes of a
-  // wave, the rest through LDS.  In LDS, element 16t + e sits at e * 1024 + t,
-  // so a wave's accesses are 64 consecutive words (no bank conflicts); the
-  // unsorted slots are taken in that same order (the start order is free).
-  constexpr int E = kStopMax / kRT;  // 16
-  static_assert(E == 16, "16 elements per thread");
-  unsigned long long v[E];
+  } else {
+    // J >= E: the partner is element i ^ J, in thread tid ^ (J / E), same
+    // register; this thread keeps the minimum iff bit J and bit K of its
+    // element indices agree (both depend on tid only).
+    const bool keep_min = (((E * tid) & J) == 0) == (((E * tid) & K) == 0);
+    if constexpr (J >= E * 64) {
+      __syncthreads();
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int slot = e * kRT + tid;
-    v[e] = slot < n ? buf[slot] : ~0ull;
-  }
-  for (int k = 2; k <= kStopMax; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 1024) {
-        __syncthreads();
+      for (int e = 0; e < E; ++e) buf[e * NT + tid] = v[e];
+      __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) buf[e * kRT + tid] = v[e];
-        __syncthreads();
-        const int pt = tid ^ (j / E);  // partner thread, same register
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long o = buf[e * NT + (tid ^ (J / E))];
+        v[e] = keep_min == (o < v[e]) ? o : v[e];
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = E * tid + e;
-          const unsigned long long o = buf[e * kRT + pt];
-          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
-          v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
-        }
-      } else if (j >= E) {
-        const int lx = j / E;  // partner lane offset, < 64
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int i = E * tid + e;
-          const unsigned long long o = __shfl_xor(v[e], lx);
-          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
-          v[e] = keep_min ? (o < v[e] ? o : v[e]) : (o > v[e] ? o : v[e]);
-        }
-      } else {
-        auto cx = [&](int e0, int e1) {  // e0 < e1 = e0 + j inside this thread
-          const int i = E * tid + e0;
-          const bool asc = (i & k) == 0;
-          const unsigned long long x = v[e0], y = v[e1];
-          const bool swap = asc ? x > y : x < y;
-          v[e0] = swap ? y : x;
-          v[e1] = swap ? x : y;
-        };
-        switch (j) {
-          case 8:
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cx(e, e + 8);
-            break;
-          case 4:
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-              if ((e & 4) == 0) cx(e, e + 4);
-            break;
-          case 2:
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-              if ((e & 2) == 0) cx(e, e + 2);
-            break;
-          default:
-#pragma unroll
-            for (int e = 0; e < E; e += 2) cx(e, e + 1);
-            break;
-        }
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long o = lane_xor64<J / E>(v[e]);
+        v[e] = keep_min == (o < v[e]) ? o : v[e];
       }
     }
   }
-  // Block gains: a 64-token block is 4 consecutive threads' elements.
-  unsigned long long part = 0ull;
+}
+
+template <int NT, int E, int K, int J>
+__device__ __forceinline__ void bitonic_merge(unsigned long long (&v)[E], unsigned long long* buf,
+                                              int tid) {
+  bitonic_stage<NT, E, K, J>(v, buf, tid);
+  if constexpr (J > 1) bitonic_merge<NT, E, K, J / 2>(v, buf, tid);
+}
+
+// Bitonic sort, ascending, of NT * E words (element i = E * tid + e).
+template <int NT, int E, int K = 2>
+__device__ __forceinline__ void bitonic_sort(unsigned long long (&v)[E], unsigned long long* buf,
+                                             int tid) {
+  bitonic_merge<NT, E, K, K / 2>(v, buf, tid);
+  if constexpr (K < NT * E) bitonic_sort<NT, E, K * 2>(v, buf, tid);
+}
+
+// Grid: (chunks, units) x kNT threads.
+__global__ __launch_bounds__(kNT) void stop_gather_kernel(SelectArgs a) {
+  __shared__ int scan_scr[kNT / 64];
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int c0 = c * kChunk;
+  if (c0 >= st.L) return;  // uniform
+  const int n_words = min(max(a.stop_n[u], 0), kStopMax);
+  const size_t ci = (size_t)u * a.nchunk + c;
+  const size_t seg = (size_t)u * a.seg_ld + c0;
+  const int off = a.stop_off[ci];
+  const int n_above = clamp_count(a.list_cnt[2 * ci], kChunk);
+  const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
+  const int nvalid = min(kChunk, st.L - c0);
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  unsigned long long* out = a.stop_words + (size_t)u * kStopMax;
+  for (int i = threadIdx.x; i < n_above; i += kNT) {
+    const int pos = c0 + min(max(a.list_idx[seg + i] - c0, 0), nvalid - 1);
+    const int at = off + i;
+    if (at >= 0 && at < n_words) out[at] = stratum_word(order_key(srow[pos]), pos);
+  }
+  // Candidates above T, compacted in list (position) order.
+  int run = off + n_above;
+  for (int base = 0; base < ncand; base += kNT) {
+    const int i = base + threadIdx.x;
+    const uint32_t key = i < ncand ? a.cand_key[seg + i] : 0u;
+    const bool in = i < ncand && key > st.tkey;
+    int tot;
+    const int at = run + block_exclusive_scan<kNT>(in ? 1 : 0, scan_scr, &tot);
+    if (in && at >= 0 && at < n_words) {
+      const int pos = c0 + min(max(a.cand_idx[seg + i] - c0, 0), nvalid - 1);
+      out[at] = stratum_word(key, pos);
+    }
+    run += tot;
+  }
+}
+
+// Grid: (kSlices, units) x kSortT threads.
+__global__ __launch_bounds__(kSortT) void stop_sort_kernel(SelectArgs a) {
+  __shared__ unsigned long long buf[kSlice];
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int n_words = min(max(a.stop_n[u], 0), kStopMax);
+  const int f0 = blockIdx.x * kSlice;
+  if (f0 >= n_words) return;  // uniform
+  const int tid = threadIdx.x;
+  unsigned long long* w = a.stop_words + (size_t)u * kStopMax + f0;
+  unsigned long long v[kSE];
+#pragma unroll
+  for (int e = 0; e < kSE; ++e) {  // the start order is free: coalesced loads
+    const int f = e * kSortT + tid;
+    v[e] = f0 + f < n_words ? w[f] : ~0ull;  // padding sorts last
+  }
+  bitonic_sort<kSortT, kSE>(v, buf, tid);
+#pragma unroll
+  for (int e = 0; e < kSE; ++e) w[kSE * tid + e] = v[e];
+}
+
+// Grid: (kSlices * kSlices, units) x kNT threads: block (s, o) counts, for
+// each word of slice o, the words of slice s below it.
+__global__ __launch_bounds__(kNT) void stop_pair_kernel(SelectArgs a) {
+  constexpr int E = kSlice / kNT;
+  __shared__ unsigned long long sw[kSlice];
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int n_words = min(max(a.stop_n[u], 0), kStopMax);
+  const int ns = (n_words + kSlice - 1) / kSlice;
+  const int s = blockIdx.x % kSlices;
+  const int o = blockIdx.x / kSlices;
+  if (s >= ns || o >= ns || s == o) return;  // uniform
+  const unsigned long long* words = a.stop_words + (size_t)u * kStopMax;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sw[e * kNT + tid] = words[s * kSlice + e * kNT + tid];
+  unsigned long long x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = words[o * kSlice + E * tid + e];
+  __syncthreads();
+  // branchless binary searches, the thread's E searches stepping together
+  int lb[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) lb[e] = 0;
+#pragma unroll
+  for (int step = kSlice / 2; step >= 1; step >>= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) lb[e] += sw[lb[e] + step - 1] < x[e] ? step : 0;
+  }
+  uint16_t* cnt = a.stop_pair + (((size_t)u * kSlices + o) * kSlices + s) * kSlice + E * tid;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt[e] = (uint16_t)(lb[e] + (sw[lb[e]] < x[e] ? 1 : 0));
+}
+
+// Grid: (kSlices, units) x kNT threads.
+__global__ __launch_bounds__(kNT) void stop_final_kernel(SelectArgs a) {
+  constexpr int E = kSlice / kNT;
+  static_assert(E == 4, "four 16-bit counts per 8-byte load");
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int n_words = min(max(a.stop_n[u], 0), kStopMax);
+  const int ns = (n_words + kSlice - 1) / kSlice;
+  const int o = blockIdx.x;
+  if (o >= ns) return;  // uniform
+  const int tid = threadIdx.x;
+  const unsigned long long* words = a.stop_words + (size_t)u * kStopMax + o * kSlice;
+  unsigned long long x[E];
+  int rank[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    if (E * tid + e < n) {
-      const uint32_t key = ~(uint32_t)(v[e] >> 32);
-      part += mass_units(sexp(key_to_float(key) - st.M));
+    x[e] = words[E * tid + e];
+    rank[e] = E * tid + e;  // words of its own slice below it
+  }
+#pragma unroll
+  for (int s = 0; s < kSlices; ++s) {  // fixed trip count: all count loads in flight
+    if (s < ns && s != o) {
+      const uint16_t* cnt =
+          a.stop_pair + (((size_t)u * kSlices + o) * kSlices + s) * kSlice + E * tid;
+      const uint2 c4 = *reinterpret_cast<const uint2*>(cnt);  // E = 4 counts
+      rank[0] += c4.x & 0xffffu;
+      rank[1] += c4.x >> 16;
+      rank[2] += c4.y & 0xffffu;
+      rank[3] += c4.y >> 16;
     }
   }
-  part += __shfl_xor(part, 1);
-  part += __shfl_xor(part, 2);
-  const bool leader = (tid & 3) == 0 && E * tid < n;  // first thread of block tid / 4
-  const unsigned long long gain = leader ? part : 0ull;
+  unsigned long long* mass = a.stop_mass + (size_t)u * kStopMax;
+  unsigned long long* rword = a.stop_rword + (size_t)u * kStopMax;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    // words are distinct, so ranks are: a permutation of [0, n_words)
+    if (x[e] != ~0ull && rank[e] < n_words) {
+      const uint32_t key = ~(uint32_t)(x[e] >> 32);
+      mass[rank[e]] = mass_units(sexp(key_to_float(key) - st.M));
+      rword[rank[e]] = x[e];
+    }
+  }
+}
+
+// Grid: units x kNT threads (one per 64-token block of the largest stratum).
+__global__ __launch_bounds__(kNT) void stop_cut_kernel(SelectArgs a) {
+  constexpr int kNB = kStopMax / kStopBlock;
+  static_assert(kNB == kNT, "one thread per block of the largest stratum");
+  __shared__ unsigned long long scan_m[kNT / 64];
+  __shared__ int scan_scr[kNT / 64];
+  __shared__ int first_sh;
+  __shared__ int tie_pos_sh;
+  const int u = blockIdx.x;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  const int tid = threadIdx.x;
+  if (!stop_applies(st)) {  // uniform
+    if (tid == 0) a.stop_cut[u] = ~0ull;
+    return;
+  }
+  const int n = st.k_eff;
+  const int n_words = min(min(max(a.stop_n[u], 0), kStopMax), n);  // ranks below: words above T
+  const unsigned long long qT = mass_units(sexp(key_to_float(st.tkey) - st.M));
+  const int nb = (n + kStopBlock - 1) / kStopBlock;
+  if (tid == 0) {
+    first_sh = 0x7fffffff;
+    tie_pos_sh = 0;
+  }
+  unsigned long long g = 0ull;
+  if (tid < nb) {
+    // The block's masses: 32 16-byte loads, all in flight together.
+    const unsigned long long* mass = a.stop_mass + (size_t)u * kStopMax;
+    const int r0 = tid * kStopBlock;
+    const int r1 = min(r0 + kStopBlock, n);
+#pragma unroll
+    for (int q = 0; q < kStopBlock / 2; ++q) {
+      const int r = r0 + 2 * q;
+      if (r < n_words) {
+        const ulonglong2 m2 = *reinterpret_cast<const ulonglong2*>(mass + r);
+        g += m2.x + (r + 1 < n_words ? m2.y : 0ull);
+      }
+    }
+    if (r1 > n_words) g += (unsigned long long)(r1 - max(r0, n_words)) * qT;  // ties on T
+  }
   unsigned long long tot;
-  const unsigned long long acc = block_exclusive_scan<kRT>(gain, scan_m, &tot) + gain;
-  if (leader && gain_below(gain, acc, a.stop_tau)) atomicMin(&first_sh, tid >> 2);
+  const unsigned long long acc = block_exclusive_scan<kNT>(g, scan_m, &tot) + g;
+  if (tid < nb && gain_below(g, acc, a.stop_tau)) atomicMin(&first_sh, tid);
   __syncthreads();
   const int kept = first_sh == 0x7fffffff ? n : min(n, (first_sh + 1) * kStopBlock);
-  uint32_t* bits = a.stop_bits + (size_t)u * (a.seg_ld / 32);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int r = E * tid + e;
-    if (r >= kept && r < n) {
-      const uint32_t pos = (uint32_t)v[e];
-      atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+  unsigned long long cut = ~0ull;  // nothing cut
+  if (kept < n) {
+    if (kept <= n_words) {
+      cut = a.stop_rword[(size_t)u * kStopMax + kept - 1];
+    } else {
+      // The cut falls among the ties on T: tie number t (in position order)
+      // is the last one kept.  Find its chunk, then its place in the chunk's
+      // candidate list (position order).
+      const int t = kept - n_words - 1;
+      const size_t cu = (size_t)u * a.nchunk;
+      const int nc = (st.L + kChunk - 1) / kChunk;
+      for (int c = 0; c < nc; ++c) {  // uniform loop; each chunk's test is uniform
+        const int tb = a.ties_before[cu + c];
+        const int tc = a.tiecnt[cu + c];
+        if (t < tb || t >= tb + tc) continue;
+        const int ncand = clamp_count(a.cand_cnt[cu + c], kChunk);
+        const size_t seg = (size_t)u * a.seg_ld + (size_t)c * kChunk;
+        int run = tb;
+        for (int base = 0; base < ncand; base += kNT) {
+          const int i = base + tid;
+          const bool tie = i < ncand && a.cand_key[seg + i] == st.tkey;
+          int ntie;
+          const int r = run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &ntie);
+          if (tie && r == t) tie_pos_sh = min(max(a.cand_idx[seg + i], 0), st.L - 1);
+          run += ntie;
+        }
+        break;
+      }
+      __syncthreads();
+      cut = stratum_word(st.tkey, tie_pos_sh);
     }
   }
+  if (tid == 0) a.stop_cut[u] = cut;
 }
 
 // ------------------------------------------------------------------ sample
@@ -691,13 +827,18 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     blk_sh[threadIdx.x] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
   }
   for (int i = threadIdx.x; i < kChunk; i += kNT) flag[i] = (dense && i < nvalid) ? 1 : 0;
+  // Early stopping: the last stratum word kept (~0: the whole stratum).
+  const unsigned long long cut = a.stop_cut && !dense ? a.stop_cut[u] : ~0ull;
   __syncthreads();
   if (!dense) {
     const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
     const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
+    const float* srow = a.scores + (size_t)u * a.score_ld;
     for (int i = threadIdx.x; i < n_above; i += kNT) {
       const int t = lidx[i];
-      if ((unsigned)(t - c0) < (unsigned)nvalid) flag[t - c0] = 1;
+      if ((unsigned)(t - c0) < (unsigned)nvalid &&
+          (cut == ~0ull || stratum_word(order_key(srow[t]), t) <= cut))
+        flag[t - c0] = 1;
     }
     if (sampling)
       for (int i = threadIdx.x; i < n_samp; i += kNT)
@@ -720,7 +861,9 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
         if (v) {
           const int t = cidx[i];
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
-            if ((unsigned)(t - c0) < (unsigned)nvalid) flag[t - c0] = 1;
+            // stratum tokens past the early stop are neither read nor sampled
+            if ((unsigned)(t - c0) < (unsigned)nvalid && stratum_word(key, t) <= cut)
+              flag[t - c0] = 1;
           } else if (sampling) {
             sample_one(st, seed, b, h, ui.grp, t, sexp(key_to_float(key) - st.M), c0, nvalid,
                        flag, lwsh);
@@ -738,10 +881,6 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     const uint8_t f = flag[tb + i];
     smask |= (uint32_t)(f == 1) << i;
     rmask |= (uint32_t)(f == 2) << i;
-  }
-  if (a.stop_bits && !dense) {  // positions cut from the stratum by early stopping
-    const uint32_t word = a.stop_bits[(size_t)u * (a.seg_ld / 32) + ((c0 + tb) >> 5)];
-    smask &= ~((word >> ((c0 + tb) & 31)) & 0xffffu);
   }
   // One scan for both counts: deterministic count in the low 16 bits,
   // sampled count in the high 16 bits (each at most 4096).
@@ -816,7 +955,11 @@ hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream) {
 }
 
 hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream) {
-  stop_kernel<<<units, kRT, 0, stream>>>(a);
+  stop_gather_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);
+  stop_sort_kernel<<<dim3(kSlices, units), kSortT, 0, stream>>>(a);
+  stop_pair_kernel<<<dim3(kSlices * kSlices, units), kNT, 0, stream>>>(a);
+  stop_final_kernel<<<dim3(kSlices, units), kNT, 0, stream>>>(a);
+  stop_cut_kernel<<<units, kNT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -62,7 +62,10 @@ struct Dims {
   int B, Hq, Hkv, G, d, T, g, NG, U, NC, NS;
   int64_t SEG;
   float scale;
+  bool stop;  // early stopping on (its buffers are part of the workspace)
 };
+
+constexpr int kStopMaxStratum = 16384;  // the early-stopping kernels' largest stratum
 
 Dims dims_of(const ssa_params* p) {
   Dims d;
@@ -79,13 +82,15 @@ Dims dims_of(const ssa_params* p) {
   d.SEG = (int64_t)d.NC * SSA_CHUNK_TOKENS;
   d.NS = p->num_splits == 0 ? d.NC : (p->num_splits < d.NC ? p->num_splits : d.NC);
   d.scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  d.stop = p->early_stop > 0.0f;  // NaN compares false
   return d;
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, stop_bits, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
+  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
       list_cnt, wpart, tiecnt,
-      ties_before, state, sel_idx, sel_logw, sel_cnt, part, total;
+      ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
+      stop_words, stop_pair, stop_mass, stop_rword, total;
 };
 
 Layout layout_of(const Dims& d) {
@@ -103,7 +108,6 @@ Layout layout_of(const Dims& d) {
   l.hist1m = take(U * kBins * 8);
   l.hist2m = take(U * kBins * 8);
   l.maxkey = take(U * 4);
-  l.stop_bits = take(U * (SEG / 32) * 4);
   l.thresh = take(U * sizeof(ssa::Thresh1));
   l.cand_idx = take(U * SEG * 4);
   l.cand_key = take(U * SEG * 4);
@@ -119,6 +123,15 @@ Layout layout_of(const Dims& d) {
   l.sel_logw = take(U * SEG * 4);
   l.sel_cnt = take(U * NC * 2 * 4);
   l.part = take((size_t)d.B * d.T * d.Hq * d.NS * (d.d + 2) * 4);
+  const size_t SU = d.stop ? U : 0;  // early stopping's buffers only when it is on
+  const size_t KS = kStopMaxStratum;
+  l.stop_cut = take(SU * 8);
+  l.stop_off = take(SU * NC * 4);
+  l.stop_n = take(SU * 4);
+  l.stop_words = take(SU * KS * 8);
+  l.stop_pair = take(SU * (KS / 1024) * (KS / 1024) * 1024 * 2);
+  l.stop_mass = take(SU * KS * 8);
+  l.stop_rword = take(SU * KS * 8);
   l.total = off;
   return l;
 }
@@ -227,7 +240,13 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.norm_out = norm_out;
   // early stopping is on for tau > 0 (NaN compares false)
   a.stop_tau = p->early_stop > 1.0f ? 1.0f : p->early_stop;
-  a.stop_bits = p->early_stop > 0.0f ? at<uint32_t>(ws, l.stop_bits) : nullptr;
+  a.stop_cut = d.stop ? at<unsigned long long>(ws, l.stop_cut) : nullptr;
+  a.stop_off = d.stop ? at<int32_t>(ws, l.stop_off) : nullptr;
+  a.stop_n = d.stop ? at<int32_t>(ws, l.stop_n) : nullptr;
+  a.stop_words = d.stop ? at<unsigned long long>(ws, l.stop_words) : nullptr;
+  a.stop_pair = d.stop ? at<uint16_t>(ws, l.stop_pair) : nullptr;
+  a.stop_mass = d.stop ? at<unsigned long long>(ws, l.stop_mass) : nullptr;
+  a.stop_rword = d.stop ? at<unsigned long long>(ws, l.stop_rword) : nullptr;
   a.T = d.T;
   a.g = d.g;
   a.NG = d.NG;
@@ -300,13 +319,13 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, K
 hipError_t launch_init_for(const ssa::SelectArgs& a, int units, hipStream_t s) {
   const bool topp = a.top_p != nullptr;
   return ssa::launch_init(a.hist1, a.hist2, a.maxkey, topp ? a.hist1m : nullptr,
-                          topp ? a.hist2m : nullptr, a.stop_bits, a.seg_ld / 32, units, s);
+                          topp ? a.hist2m : nullptr, units, s);
 }
 
 // The resolve stage, then the early-stopping cut when it is on.
 hipError_t launch_resolve_for(const ssa::SelectArgs& a, int units, hipStream_t s) {
   const hipError_t e = ssa::launch_resolve(a, units, s);
-  if (e != hipSuccess || !a.stop_bits) return e;
+  if (e != hipSuccess || !a.stop_cut) return e;
   return ssa::launch_stop(a, units, s);
 }
 
@@ -470,7 +489,7 @@ int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int
   const ssa::IndexArgs ia = index_args(p, d, q, k_cache, block_table, seq_lens, scores,
                                        p->max_seq_len, workspace, l);
   SSA_TRY(ssa::launch_init(ia.hist1, at<uint32_t>(workspace, l.hist2), ia.maxkey, nullptr,
-                           nullptr, nullptr, 0, d.U, s));
+                           nullptr, d.U, s));
   SSA_TRY(ssa::launch_indexer(ia, d.U, s));
   return SSA_OK;
 }

@@ -82,8 +82,17 @@ struct SelectArgs {
   float* sel_logw;            // [U, seg_ld]
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
-  uint32_t* stop_bits;        // [U, seg_ld / 32] positions skipped by early stopping, or null
-  float stop_tau;             // early-stopping threshold (used when stop_bits is set)
+  // Early stopping (all null when it is off).  A stratum word is
+  // ((~key) << 32) | position: ascending words are the stratum's order.
+  float stop_tau;                 // the threshold tau, clamped to 1
+  unsigned long long* stop_cut;   // [U] the last word kept (~0: nothing cut)
+  int32_t* stop_off;              // [U, nchunk] offset of each chunk's words above the
+                                  //   threshold key in stop_words
+  int32_t* stop_n;                // [U] words above the threshold key (<= 16384 when cut)
+  unsigned long long* stop_words; // [U, 16384] those words, then sorted per 1024-word slice
+  uint16_t* stop_pair;            // [U, 16, 16, 1024] words of slice s below word i of slice o
+  unsigned long long* stop_mass;  // [U, 16384] mass units in stratum order
+  unsigned long long* stop_rword; // [U, 16384] words in stratum order
   int T, g, NG;
   int Hkv, max_seq_len, nchunk, max_blocks, num_blocks, emit_rows;
   int64_t seg_ld;             // nchunk * 4096
@@ -125,11 +134,10 @@ struct AppendArgs {
 int indexer_tokens_per_iteration(int pair_count);
 int indexer_max_tokens_per_wg();
 int indexer_resident_workgroups(int pair_count);  // 0 if unknown
-// Clears the histograms and maxima; the mass histograms and the early-stopping
-// bitmap (stop_words words per unit) only when non-null.
+// Clears the histograms and maxima; the mass histograms only when non-null.
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
-                       unsigned long long* hist1m, unsigned long long* hist2m,
-                       uint32_t* stop_bits, int64_t stop_words, int units, hipStream_t stream);
+                       unsigned long long* hist1m, unsigned long long* hist2m, int units,
+                       hipStream_t stream);
 hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream);
 hipError_t launch_score_hist(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_mass(const SelectArgs& a, int units, hipStream_t stream);
