@@ -137,3 +137,22 @@ def test_end_to_end_with_early_stopping():
         err = float(np.abs(got[b, h * G:(h + 1) * G] - ref[b, h * G:(h + 1) * G]).max())
         assert err <= 2e-3 * vmax_unit(V), f"early-stop e2e out of tolerance at {(b, h)}"
         say(f"[stop] e2e unit {(b, h)}: |S| {inf['S'].size} of {inf['S_full'].size}")
+
+
+def test_cut_inside_the_threshold_ties():
+    """The stop falls among the tokens tied on the stratum's last key, whose
+    order is by position across chunks: 100 high scores, then 5000 equal ones
+    spread over several chunks; top-k 3000 ends the stratum inside the tie run
+    and the stop lands a few blocks later, still inside it."""
+    rng = np.random.default_rng(10)
+    L = 20000
+    s = (rng.standard_normal((2, 1, L)) * 0.3 - 2.0).astype(np.float32)
+    for b in range(2):
+        pos = rng.permutation(L)
+        s[b, 0, pos[:100]] = np.float32(5.0)
+        s[b, 0, pos[100:5100]] = np.float32(1.0)
+    sels, cut = check_select(s, [L, L - 3001], [3000, 2500], [40, 40], [3, 4], 0.05, "tie cut")
+    for sel in sels.values():
+        S, full = sel["S"], sel["S_full"]
+        assert 100 < S.size < full.size, (S.size, full.size)  # the cut is inside the ties
+    assert cut > 0
