@@ -35,14 +35,16 @@ def unit_host(wl, b, h):
     return qg, orc.gather_rows(kc, bt, 0, L), orc.gather_rows(vc, bt, 0, L)
 
 
-def check_fullsize(name, units, top_p=None):
+def check_fullsize(name, units, top_p=None, early_stop=None):
     wl = synth.make_workload(name, DEV)
     say(f"[full] workload={name} B={wl.B} L={wl.lens[:4]}{'...' if wl.B > 4 else ''} "
-        f"units={units} top_p={top_p}")
+        f"units={units} top_p={top_p} early_stop={early_stop}")
+    tau = None if early_stop is None else np.float32(early_stop)
     tp = None if top_p is None else torch.full((wl.B,), top_p, dtype=torch.float32, device=DEV)
     tp32 = None if top_p is None else np.float32(top_p)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
-                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count,
+                       early_stop=0.0 if early_stop is None else float(early_stop))
     scale = 1.0 / math.sqrt(wl.d)
     G = wl.Hq // wl.Hkv
     ws = ssa.alloc_workspace(p, DEV)
@@ -67,7 +69,8 @@ def check_fullsize(name, units, top_p=None):
         ok, ratio = score_tolerance_ok(sc[b, h, :s64.size].cpu().numpy(), s64)
         assert ok, f"scores out of tolerance at {(b, h)} ({ratio})"
         sel = orc.select_unit(s64.astype(np.float32), int(wl.topk[b]), int(wl.sample_budget[b]),
-                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h, top_p=tp32)
+                              int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h, top_p=tp32,
+                              stop_tau=tau)
         sels[(b, h)] = sel
         s32[b, h, :s64.size] = torch.from_numpy(s64.astype(np.float32))
         w_in[b, h] = float(sel["W"])
@@ -107,6 +110,12 @@ def test_fullsize_1m_top_p():
     """Top-p 0.02 capped at the top-k budget: the mass bound ends the stratum
     (about 8k of the 10486 tokens) on this workload."""
     check_fullsize("1m", [(0, 0), (0, 5)], top_p=0.02)
+
+
+def test_fullsize_1m_early_stop():
+    """Early stopping at tau = 0.01 (the bench's variant): the stratum of
+    10486 tokens per kv head is cut to about 5.5k."""
+    check_fullsize("1m", [(0, 0), (0, 5)], early_stop=0.01)
 
 
 def test_fullsize_128k():
