@@ -7,8 +7,11 @@ sampling, gather attention and merge, with inputs already resident in HBM.
 Prints one JSON line: KV-tokens/s/layer (sum of sequence lengths / step
 time), the indexer's roofline against MI355X's 8 TB/s HBM peak (HIP events
 around the indexer launch inside the timed region), per-stage times from a
-separate event-bracketed pass, the same workload with a top-p capped
-deterministic stratum, and the CPU oracle timed on a bounded sample of the
+separate event-bracketed pass, the 128K workload, and variants of the main
+workload: a top-p capped deterministic stratum, early stopping over it, split
+keys (on the device and with the rest of the keys and the values in pinned
+host memory) with the cache append, and multi-token decode with shared and
+per-query selections; then the CPU oracle timed on a bounded sample of the
 same workload.
 """
 

@@ -18,8 +18,10 @@
 //   tail:   w_j = sexp(s_j - M), W = sum over the tail, computed directly in
 //           fp64 (never as total minus top-k, which cancels);
 //   sample: include j iff fl(u_j * W) < fl(m * w_j), u_j from Philox4x32-10
-//           keyed by the sequence's seed with counter (j >> 2, h, b, 0);
-//           pi_j = min(1, fl(m * w_j) / W); the logit bias is -log(pi_j).
+//           keyed by the sequence's seed with counter (j >> 2, h, b, group);
+//           pi_j = min(1, fl(m * w_j) / W); the logit bias is -log(pi_j);
+//   stop:   optionally the stratum is cut by the early-stopping rule (the
+//           section of that name below).
 //
 // A sequence is processed in 4096-token chunks.  Each chunk's selected tokens
 // are written to its own segment in index order, so no grid-wide ordering is
