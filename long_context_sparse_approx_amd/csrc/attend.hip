@@ -82,7 +82,10 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   __shared__ float lw_sh[kBatch + 32];
   __shared__ int pos_sh[kBatch + 32];
 
-  const int s = blockIdx.x;
+  const int slot = blockIdx.x;  // partial state written by this wave
+  const int s = slot / a.nsub;   // split: a range of chunks
+  const int sub = slot - s * a.nsub;  // share of each chunk's items
+  const int nslot = a.nsplit * a.nsub;
   const int u = blockIdx.y / a.mblocks;  // selection unit (b, grp, h)
   const int mb = blockIdx.y - u * a.mblocks;
   const int bg = u / a.Hkv;
@@ -155,11 +158,13 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
     // rows to the cache; positions at or past the member's span are masked:
     // no value can address outside the buffers.
     const int cnt = min(max(cntp[0], 0) + max(cntp[1], 0), kChunk);
+    const int i_lo = (int)((int64_t)sub * cnt / a.nsub);  // this wave's share
+    const int i_hi = (int)((int64_t)(sub + 1) * cnt / a.nsub);
     const int32_t* idxp = a.sel_idx + seg + (size_t)c * kChunk;
     const float* lwp = a.sel_logw + seg + (size_t)c * kChunk;
-    for (int b0 = 0; b0 < cnt; b0 += kBatch) {
+    for (int b0 = i_lo; b0 < i_hi; b0 += kBatch) {
       // Resolve up to kBatch items to cache rows (independent loads), into LDS.
-      const int nb = min(kBatch, cnt - b0);
+      const int nb = min(kBatch, i_hi - b0);
 #pragma unroll
       for (int k = 0; k < kBatch / 64; ++k) {
         const int i = lane + 64 * k;
@@ -289,14 +294,14 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
     const int col = 4 * q4 + r;
     if (col < nmem * a.G) {
       const int qrow = (b * a.T + t_a + col / a.G) * a.Hq + h * a.G + col % a.G;
-      float* dst = a.part + ((size_t)qrow * a.nsplit + s) * stride + n16 * DPL;
+      float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + n16 * DPL;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
     }
   }
   if (q4 == 0 && col_valid) {
     const int qrow = (b * a.T + col_t) * a.Hq + h * a.G + col_g;
-    float* dst = a.part + ((size_t)qrow * a.nsplit + s) * stride + D;
+    float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + D;
     dst[0] = m_run;
     dst[1] = l_run;
   }
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int dim = blockIdx.y * 64 + lane;
-  const int ns = a.nsplit;
+  const int ns = a.nsplit * a.nsub;
   const float* base = a.part + (size_t)bh * ns * (D + 2);
   float mx = -INFINITY;
   for (int s = threadIdx.x; s < ns; s += kMT) {
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
-  dim3 grid(a.nsplit, a.B * a.NG * a.Hkv * a.mblocks);
+  dim3 grid(a.nsplit * a.nsub, a.B * a.NG * a.Hkv * a.mblocks);
   // Split keys whose scored dims cover the whole head (no rest array) are
   // addressed exactly like whole keys.
   const bool split = a.k_rest != nullptr;

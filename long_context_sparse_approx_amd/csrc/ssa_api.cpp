@@ -60,12 +60,22 @@ bool params_ok(const ssa_params* p) {
 
 struct Dims {
   int B, Hq, Hkv, G, d, T, g, NG, U, NC, NS;
+  int NSUB;  // attention waves per split (NS * NSUB <= the merge's 4096 states)
   int64_t SEG;
   float scale;
   bool stop;  // early stopping on (its buffers are part of the workspace)
 };
 
 constexpr int kStopMaxStratum = 16384;  // the early-stopping kernels' largest stratum
+// Attention waves per split: each takes an equal share of every chunk's
+// selected items (a chunk holds about 82 of them at 50x sparsity, 3 tiles of
+// 32), which shortens each wave's chain of dependent loads, and the merge
+// reads that many more partial states.  Measured: more waves help while the
+// launch has fewer than about 2048 (128K x 4: 1024 waves -> 2 per split, the
+// attention 18.7 -> 15.6 us) and cost beyond (1M: 2048 waves; 2 per split
+// 23.7 -> 26.4 us).
+constexpr int kAttendWaves = 2048;
+constexpr int kAttendMaxSub = 4;
 
 Dims dims_of(const ssa_params* p) {
   Dims d;
@@ -81,6 +91,14 @@ Dims dims_of(const ssa_params* p) {
   d.NC = (p->max_seq_len + SSA_CHUNK_TOKENS - 1) / SSA_CHUNK_TOKENS;
   d.SEG = (int64_t)d.NC * SSA_CHUNK_TOKENS;
   d.NS = p->num_splits == 0 ? d.NC : (p->num_splits < d.NC ? p->num_splits : d.NC);
+  {
+    const int mpw = 16 / d.G;  // query columns per attention wave: members x heads
+    const int64_t waves = (int64_t)d.NS * d.U * ((d.g + mpw - 1) / mpw);
+    d.NSUB = 1;
+    while (d.NSUB < kAttendMaxSub && waves * d.NSUB * 2 <= kAttendWaves &&
+           (int64_t)d.NS * d.NSUB * 2 <= SSA_MAX_SEQ_LEN / SSA_CHUNK_TOKENS)
+      d.NSUB *= 2;
+  }
   d.scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
   d.stop = p->early_stop > 0.0f;  // NaN compares false
   return d;
@@ -122,7 +140,7 @@ Layout layout_of(const Dims& d) {
   l.sel_idx = take(U * SEG * 4);
   l.sel_logw = take(U * SEG * 4);
   l.sel_cnt = take(U * NC * 2 * 4);
-  l.part = take((size_t)d.B * d.T * d.Hq * d.NS * (d.d + 2) * 4);
+  l.part = take((size_t)d.B * d.T * d.Hq * d.NS * d.NSUB * (d.d + 2) * 4);
   const size_t SU = d.stop ? U : 0;  // early stopping's buffers only when it is on
   const size_t KS = kStopMaxStratum;
   l.stop_cut = take(SU * 8);
@@ -299,6 +317,7 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, K
   a.max_seq_len = p->max_seq_len;
   a.nchunk = d.NC;
   a.nsplit = d.NS;
+  a.nsub = d.NSUB;
   a.out_dtype = p->out_dtype;
   a.idx_are_rows = idx_are_rows;
   a.pair_begin = p->pair_begin;

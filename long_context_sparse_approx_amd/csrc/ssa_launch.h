@@ -108,11 +108,13 @@ struct AttendArgs {
   const int32_t* sel_idx;     // positions, or cache rows when idx_are_rows
   const float* sel_logw;
   const int32_t* sel_cnt;
-  float* part;                // [B*T*Hq, nsplit, d + 2]: acc[d], m, l
+  float* part;                // [B*T*Hq, nsplit * nsub, d + 2]: acc[d], m, l
   void* out;                  // [B, T, Hq, d]
   int T, g, NG;
   int mpw, mblocks;           // members per attention wave (16 / G), waves per group
   int B, Hq, Hkv, G, d, max_blocks, num_blocks, max_seq_len, nchunk, nsplit, out_dtype;
+  int nsub;                   // waves per split, each taking an equal share of every chunk's
+                              //   items; partial states per query row: nsplit * nsub
   int idx_are_rows;
   int pair_begin, pair_count; // the scored dims, for split keys
   int64_t seg_ld;
