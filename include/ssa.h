@@ -21,9 +21,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Memory.   Every array argument is a DEVICE pointer, owned by the caller, on
- *           the device current at the call.  The library allocates nothing
- *           and keeps no mutable global state.  q, k_cache, k_rest, v_cache,
- *           k_new and v_new must be 16-byte aligned.
+ *           the device current at the call.  The library allocates nothing;
+ *           its only global state is a per-device cache of one occupancy
+ *           query (a constant of the device, filled on first use, atomically).
+ *           q, k_cache, k_rest, v_cache, k_new and v_new must be 16-byte
+ *           aligned.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
  *           Calls enqueue work and return; nothing is synchronised.
  * Errors.   0 on success, a negative SSA_ERR_* code otherwise; no partial
