@@ -228,6 +228,36 @@ def test_run_twice_bitwise_identical():
     assert torch.equal(a, b)
 
 
+def test_concurrent_calls_on_two_streams():
+    """Calls are reentrant: two decode steps (different workloads, own
+    workspaces) enqueued on two streams at once give their sequential results
+    bitwise."""
+    say("[inv] two streams")
+    wa, wb = make_case("ragged_b2"), make_case("g8_d64")
+    pa, pb = params_of(wa), params_of(wb)
+    wsa, wsb = ssa.alloc_workspace(pa, DEV), ssa.alloc_workspace(pb, DEV)
+
+    def step(wl, p, ws, out=None, stream=None):
+        return ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens,
+                          wl.topk, wl.sample_budget, wl.seed, out=out, workspace=ws,
+                          stream=stream)
+
+    ref_a = step(wa, pa, wsa).clone()
+    ref_b = step(wb, pb, wsb).clone()
+    torch.cuda.synchronize()
+    oa, ob = torch.zeros_like(ref_a), torch.zeros_like(ref_b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            step(wa, pa, wsa, out=oa, stream=s1)
+        with torch.cuda.stream(s2):
+            step(wb, pb, wsb, out=ob, stream=s2)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ref_a) and torch.equal(ob, ref_b)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3])
 def test_split_count_changes_rounding_only(splits):
     wl = make_case("ragged_b2")
