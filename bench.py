@@ -7,7 +7,8 @@ sampling, gather attention and merge, with inputs already resident in HBM.
 Prints one JSON line: KV-tokens/s/layer (sum of sequence lengths / step
 time), the indexer's roofline against MI355X's 8 TB/s HBM peak (HIP events
 around the indexer launch inside the timed region), per-stage times from a
-separate event-bracketed pass, the 128K workload, and variants of the main
+separate event-bracketed pass, per-step medians with and without a 512 MiB
+cache-evicting read before each step, the 128K workload, and variants of the main
 workload: a top-p capped deterministic stratum, early stopping over it, split
 keys (on the device and with the rest of the keys and the values in pinned
 host memory) with the cache append, and multi-token decode with shared and
@@ -214,6 +215,34 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     for arr in idx_arrs or []:
         hip.destroy(arr[2 * ix])
         hip.destroy(arr[2 * ix + 1])
+    # Per-step medians (events from the first stage's start to the last
+    # stage's end), cold: a 512 MiB buffer read before every step evicts L2
+    # and the 256 MiB Infinity Cache (a read leaves no dirty lines whose
+    # write-back would land inside the step); warm: the same steps back to back.
+    cache = None
+    if args.cold_steps > 0 and graphs is None:
+        scrub = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+        scrub_sum = torch.empty((), dtype=torch.float32, device=dev)
+        arrs = event_arrays(args.cold_steps, [0, nst - 1])
+
+        def per_step_median_us(cold):
+            torch.cuda.synchronize()
+            for arr in arrs:
+                if cold:
+                    torch.sum(scrub, dim=0, out=scrub_sum)
+                step(*call, out=out, workspace=ws, stream=stream, top_p=tp,
+                     events=ctypes.addressof(arr))
+            torch.cuda.synchronize()
+            ts = sorted(hip.elapsed_ms(a[0], a[2 * nst - 1]) for a in arrs)
+            return round(ts[len(ts) // 2] * 1e3, 2)
+
+        cache = dict(steps=args.cold_steps, scrub_mib=512,
+                     cold_median_us=per_step_median_us(True),
+                     warm_median_us=per_step_median_us(False))
+        for arr in arrs:
+            hip.destroy(arr[0])
+            hip.destroy(arr[2 * nst - 1])
+        del scrub, scrub_sum
     del graphs
 
     # Selected-set sizes of this step (deterministic: same kernels, same inputs).
@@ -236,7 +265,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     res = dict(wl=wl, p=p, ms_step=ms_step, idx_ms=idx_ms, gpu_ms=gpu_ms, stage_ms=stage_ms,
                tokens=tokens,
                idx_bytes=idx_bytes, gather_bytes=gather_bytes, score_bytes=score_bytes,
-               n_det=n_det, n_smp=n_smp, t_gen=t_gen)
+               n_det=n_det, n_smp=n_smp, t_gen=t_gen, cache=cache)
     return res
 
 
@@ -392,6 +421,9 @@ def main():
                          "step, one shared selection vs one per query (0 = skip)")
     ap.add_argument("--no-split-keys", dest="split_keys", action="store_false",
                     help="skip the split-key (device and host-offloaded) and append timings")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="per-step medians over this many steps with and without a 512 MiB "
+                         "cache-evicting read before each (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -422,7 +454,8 @@ def main():
         also[name] = dict(workload=WORKLOADS[name], value=s2["value"], unit="KV-tokens/s/layer",
                           ms_per_step=s2["ms_per_step"], roofline=s2["roofline"],
                           stages_us=s2["stages_us"],
-                          hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"])
+                          hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"],
+                          per_step_cache=r2["cache"])
         del r2
         torch.cuda.empty_cache()
     variants = {}
@@ -511,6 +544,7 @@ def main():
         "cpu_baseline": cpu,
         "stages_us": main_sum["stages_us"],
         "gpu_step_us": main_sum["gpu_step_us"],
+        "per_step_cache": res["cache"],
         "hbm_gbps_algorithmic_step": main_sum["hbm_gbps_algorithmic_step"],
         "gather_gbps_algorithmic": main_sum["gather_gbps_algorithmic"],
         "selected": main_sum["selected"],

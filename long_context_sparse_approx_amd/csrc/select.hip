@@ -242,6 +242,9 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       st.flags = kFlagDense;
     } else {
       const int nc = (p.L + kChunk - 1) / kChunk;
+      // The chunks' tail sums do not depend on anything below: load them first.
+      double acc = 0.0;
+      for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
       const int tpc = threads_per_chunk(nc);
       const int cstep = kRT / tpc;
       const int csub = threadIdx.x % tpc;
@@ -382,8 +385,6 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         total_ties = run;
         if (a.stop_off) stop_offsets(a, u, cu, nc, ties_sh, scan_scr);
       }
-      double acc = 0.0;
-      for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
       W = block_sum_f64<kRT>(acc, dscr) + ctail;
       if (t1.mode != 0) {
         const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
