@@ -180,6 +180,7 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
 constexpr int kRT = 1024;
 constexpr int kRW = kRT / 64;
 constexpr int kMaxResolveChunks = SSA_MAX_SEQ_LEN / kChunk;
+static_assert(kBins % kRT == 0, "each resolve thread loads kBins / kRT histogram entries");
 
 // Candidate passes: thread t serves chunk (t / tpc) + k * (kRT / tpc) and,
 // inside it, items (t % tpc) + i * tpc.  Every load is independent and every
@@ -218,9 +219,39 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ double dscr[kRW];
 
   const int u = blockIdx.x;
+  // Every load that depends on the unit only is issued first, together: the
+  // sequence's parameters, the first-digit threshold and the maximum, the
+  // second-digit histogram, and this thread's candidate count and first
+  // candidate keys (read whole within the chunk's segment; entries past the
+  // count are never used).  Candidate passes give tpc threads to each chunk,
+  // fixed by the launch's chunk count, so every thread's items and every sum
+  // have a fixed order.
+  constexpr int kKeep = 16;
+  constexpr int kHist = kBins / kRT;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  const Thresh1 t1 = a.thresh[u];
+  const uint32_t maxkey = a.maxkey[u];
+  uint32_t hv[kHist];
+#pragma unroll
+  for (int j = 0; j < kHist; ++j) hv[j] = a.hist2[(size_t)u * kBins + threadIdx.x + j * kRT];
+  const size_t cu = (size_t)u * a.nchunk;
+  const uint32_t* ckeys = a.cand_key + (size_t)u * a.seg_ld;
+  const int tpc = threads_per_chunk(a.nchunk);
+  const int cstep = kRT / tpc;
+  const int csub = threadIdx.x % tpc;
+  const bool one_chunk = a.nchunk <= cstep;  // each thread serves at most one chunk
+  const int cm = threadIdx.x / tpc;
+  const bool has_cm = one_chunk && cm < a.nchunk;
+  const int cnt_m = has_cm ? a.cand_cnt[cu + cm] : 0;
+  const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
+  uint32_t kr[kKeep];
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    const int i = csub + k * tpc;
+    kr[k] = (has_cm && i < kChunk) ? ckm[i] : 0u;
+  }
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -230,14 +261,12 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   st.k_eff = p.k_eff;
   st.m = p.m;
   st.L = p.L;
-  const size_t cu = (size_t)u * a.nchunk;
-  const uint32_t* ckeys = a.cand_key + (size_t)u * a.seg_ld;
   double W = 0.0;
 
   if (p.L == 0) {
     st.flags = kFlagEmpty;
   } else {
-    st.M = key_to_float(a.maxkey[u]);
+    st.M = key_to_float(maxkey);
     if (p.dense) {
       st.flags = kFlagDense;
     } else {
@@ -245,36 +274,18 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       // The chunks' tail sums do not depend on anything below: load them first.
       double acc = 0.0;
       for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
-      const int tpc = threads_per_chunk(nc);
-      const int cstep = kRT / tpc;
-      const int csub = threadIdx.x % tpc;
       double ctail = 0.0;
       int total_ties = 0;
-      const Thresh1 t1 = a.thresh[u];
       if (t1.mode == 0) {
         st.flags = kFlagNoTopk;
         st.k_eff = 0;
       } else {
-        // Loads that do not depend on the second digit are issued first: the
-        // histograms, this thread's candidate count and (below) its keys.
-        constexpr int kKeep = 16;
-        const bool one_chunk = nc <= cstep;
-        const int cm = threadIdx.x / tpc;
-        const int nm = (one_chunk && cm < nc) ? clamp_count(a.cand_cnt[cu + cm], kChunk) : 0;
-        const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
-        uint32_t kr[kKeep];
-        for (int i = threadIdx.x; i < kBins; i += kRT) {
-          hist[i] = a.hist2[(size_t)u * kBins + i];
-          if (t1.mode & kBoundMass) mh[i] = a.hist2m[(size_t)u * kBins + i];
-        }
-        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
-        if (one_chunk) {
+        const int nm = (has_cm && cm < nc) ? clamp_count(cnt_m, kChunk) : 0;
 #pragma unroll
-          for (int k = 0; k < kKeep; ++k) {
-            const int i = csub + k * tpc;
-            kr[k] = i < nm ? ckm[i] : 0u;
-          }
-        }
+        for (int j = 0; j < kHist; ++j) hist[threadIdx.x + j * kRT] = hv[j];
+        if (t1.mode & kBoundMass)
+          for (int i = threadIdx.x; i < kBins; i += kRT) mh[i] = a.hist2m[(size_t)u * kBins + i];
+        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         __syncthreads();
         // Second digit.
         DigitBound d2;
