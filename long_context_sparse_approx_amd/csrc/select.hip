@@ -52,19 +52,22 @@ __global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
   __shared__ unsigned long long mh[kBins];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
-  const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   const int c0 = c * kChunk;
-  if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
-  const float M = key_to_float(a.maxkey[u]);
+  // The chunk's scores (up to the end of the row) and the maximum go out
+  // together with the sequence's parameters; entries at or past L are ignored.
   const float* srow = a.scores + (size_t)u * a.score_ld;
   float v[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     const int t = c0 + threadIdx.x + k * kNT;
-    v[k] = t < p.L ? srow[t] : 0.0f;
+    v[k] = t < a.score_ld ? srow[t] : 0.0f;
   }
+  const uint32_t maxkey = a.maxkey[u];
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
+  const float M = key_to_float(maxkey);
   for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = 0ull;
   __syncthreads();
 #pragma unroll
@@ -99,6 +102,13 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ unsigned long long pair_m[2];
   __shared__ double dscr[kNT / 64];
   const int u = blockIdx.x;
+  // The histogram and the maximum depend on the unit only: their loads go
+  // out together with the sequence's parameters.
+  constexpr int kH = kBins / kNT;
+  uint32_t hv[kH];
+#pragma unroll
+  for (int j = 0; j < kH; ++j) hv[j] = a.hist1[(size_t)u * kBins + threadIdx.x + j * kNT];
+  const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
@@ -107,10 +117,10 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
     return;
   }
   const bool topp = p.topp && p.k_eff > 0;
-  for (int i = threadIdx.x; i < kBins; i += kNT) {
-    hist[i] = a.hist1[(size_t)u * kBins + i];
-    if (topp) mh[i] = a.hist1m[(size_t)u * kBins + i];
-  }
+#pragma unroll
+  for (int j = 0; j < kH; ++j) hist[threadIdx.x + j * kNT] = hv[j];
+  if (topp)
+    for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = a.hist1m[(size_t)u * kBins + i];
   __syncthreads();
   DigitBound d{kBins, 0, 0ull, 0};
   if (p.k_eff > 0) {
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   }
   const int b1 = d.bin;
   const int above = count_above<kNT>(hist, kBins, b1, scan_scr);
-  const float M = key_to_float(a.maxkey[u]);
+  const float M = key_to_float(maxkey);
   double lb = 0.0;
   for (int bin = threadIdx.x; bin < b1; bin += kNT) {
     const uint32_t n = hist[bin];
@@ -158,15 +168,29 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
+  const int c0 = c * kChunk;
+  // The chunk's scores, the threshold and the maximum depend on the unit and
+  // chunk only: their loads go out together with the sequence's parameters.
+  // Scores are read up to the end of the row (score_ld entries); entries at
+  // or past L are ignored.
+  float v[kPer];
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int t = c0 + threadIdx.x + k * kNT;
+    v[k] = t < a.score_ld ? srow[t] : 0.0f;
+  }
+  const Thresh1 t1 = a.thresh[u];
+  const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const int h = ui.h;
   const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
-  const int c0 = c * kChunk;
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
-  const Thresh1 t1 = a.thresh[u];
-  const float M = key_to_float(a.maxkey[u]);
-  stage_chunk_scores(a.scores + (size_t)u * a.score_ld, c0, p.L, sh);
+  const float M = key_to_float(maxkey);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
+  __syncthreads();
   filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, sh, scan_scr, dscr);
 }
 

@@ -9,20 +9,6 @@ namespace ssa {
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 
-// Coalesced copy of the chunk's scores into LDS (entries past L are unused).
-// All of a thread's loads are issued before the first LDS store.
-__device__ __forceinline__ void stage_chunk_scores(const float* srow, int c0, int L, float* sh) {
-  float v[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int t = c0 + threadIdx.x + k * kNT;
-    v[k] = t < L ? srow[t] : 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
-  __syncthreads();
-}
-
 // Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  `sh` holds the
 // chunk's scores (entries at or past L are ignored); t1 is the unit's
 // first-digit threshold and M its maximum score.  Writes the chunk's
