@@ -10,14 +10,19 @@
 // contributes one contiguous 2*pair_count*2-byte slice of its key row (128 B
 // for 32 pairs at d = 128).  LPT lanes cover one token with one 16-byte
 // streaming load each; a wave instruction therefore reads 64/LPT token slices
-// and every lane keeps 8 independent loads (8 consecutive tokens) in flight.  The scaled proxy query
-// lives in registers as bf16 hi + lo parts and the slices are dotted with
-// v_dot2_f32_bf16 straight from the loaded words.  A DPP reduce-scatter
+// and every lane keeps 8 independent loads (8 consecutive tokens) in flight.
+// The scaled proxy query lives in registers as bf16 hi + lo parts and the
+// slices are dotted with v_dot2_f32_bf16 straight from the loaded words.  A DPP reduce-scatter
 // across the LPT lanes leaves each lane with complete token scores, so the
 // score stores are coalesced.  The epilogue counts each score's first radix
 // digit (top 11 bits of the order key) in an LDS histogram and tracks the
 // maximum order key; both are flushed with integer atomics, so the result is
 // independent of scheduling.
+//
+// Work split.  The grid is the number of workgroups the device holds at once,
+// and the units' tokens, laid end to end, are split evenly among them (below),
+// so the whole layer streams in one round whatever the mix of sequence
+// lengths.
 #include <atomic>
 
 #include "ssa_device.h"
@@ -28,9 +33,9 @@ namespace ssa {
 namespace {
 
 // Largest token tile of one indexer workgroup (its block ids and its scores
-// are staged in LDS: 8192 tokens keep four workgroups per CU resident, so a
-// 1M-token, 8-head layer runs as a single round of workgroups and every
-// workgroup writes its scores in one burst at its end).
+// are staged in LDS: 8192 tokens keep four workgroups per CU resident, and
+// the tile's scores are written in one burst at its end).  A 1M-token,
+// 8-head layer gives each of the 1024 resident workgroups one full tile.
 constexpr int kMaxTileTokens = 8192;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -146,34 +151,39 @@ __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uin
   }
 }
 
+// One tile [t0, t_end) of unit u (at most kMaxTileTokens tokens, t0 a
+// multiple of 16): proxy query, block ids, the key stream, then the tile's
+// histogram, maximum and scores.  Called by all threads of the workgroup.
 template <int LPT>
-__global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
+__device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, int t_end,
+                                           uint32_t* hist, uint32_t* blk_sh, float* sbuf,
+                                           uint32_t* wmax) {
   constexpr int TPI = kWave / LPT;           // tokens per wave-wide load
   constexpr int UNR = 8;                     // loads in flight per lane
   constexpr int WAVE_TOK = TPI * UNR;        // tokens per wave per iteration
   constexpr int WG_TOK = 4 * WAVE_TOK;       // tokens per workgroup per iteration
   // The query group's scored slice (at most 16 x 128 floats) is staged in the
   // score tile buffer before the first score lands there.
-  __shared__ uint32_t hist[kBins / 2];
-  __shared__ uint32_t blk_sh[kMaxTileTokens / kBlockTokens];
-  __shared__ float sbuf[kMaxTileTokens];
-  __shared__ uint32_t wmax[4];
   static_assert(16 * 128 <= kMaxTileTokens, "query slice fits the tile buffer");
   float* qsh = sbuf;
 
-  const int u = blockIdx.y;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const int h = ui.h;
-  const int L = ui.L;
-  const int t0 = blockIdx.x * a.tokens_per_wg;
-  if (t0 >= L) return;  // uniform over the workgroup
-  const int t_end = min(L, t0 + a.tokens_per_wg);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nd = 2 * a.pair_count;
   const int sub = lane % LPT;
+  // The tile's block ids (their loads go out with the query's).
+  const int blk0 = t0 / kBlockTokens;
+  const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
+  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.key_ld;
+  for (int i = tid; i < nblk; i += 256) {
+    const int blk = btrow[blk0 + i];
+    blk_sh[i] = (uint32_t)(blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk));
+  }
   // Proxy query: the mean over the group's members (consecutive query
   // positions) and their G query heads, accumulated member by member.
   const int t_first = ui.grp * a.g;
@@ -198,15 +208,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
     }
     __syncthreads();
   }
-  const int blk0 = t0 / kBlockTokens;
-  const int nblk = (t_end - t0 + kBlockTokens - 1) / kBlockTokens;
-  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
-  const uint64_t blk_stride = (uint64_t)a.Hkv * kBlockTokens * a.key_ld;
-  for (int i = tid; i < nblk; i += 256) {
-    const int blk = btrow[blk0 + i];
-    blk_sh[i] = (uint32_t)(blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk));
-  }
-  __syncthreads();
   // Per-lane proxy query over this lane's 8 dims, qbar = (scale / (G n)) *
   // sum over the n members and G heads, split into bf16 hi and lo parts
   // packed two dims per word.
@@ -230,10 +231,31 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
   const uint16_t* kbase = a.k_cache + (size_t)h * kBlockTokens * a.key_ld + a.key_off + sub * 8;
   float* srow = a.scores + (size_t)u * a.score_ld;
   uint32_t kmax = 0u;
+  // A CU serves its oldest waves first, so workgroups that share a CU would
+  // stream at very different rates and the late ones would finish alone with
+  // few loads in flight.  Each wave therefore lowers its priority as it
+  // advances (3 over its first quarter of the tile ... 0 over the last): a
+  // wave that is ahead yields to those behind, and the CU's workgroups finish
+  // together.
   int base = t0 + wave * WAVE_TOK;
-  for (; base + WAVE_TOK <= t_end; base += WG_TOK)
+  const int n_full = base + WAVE_TOK <= t_end ? (t_end - WAVE_TOK - base) / WG_TOK + 1 : 0;
+  __builtin_amdgcn_s_setprio(3);
+  int level = 0;  // quarter of the tile reached
+  for (int it = 0; it < n_full; ++it, base += WG_TOK) {
+    const int q = 4 * it / n_full;
+    if (q != level) {
+      level = q;
+      if (q == 1)
+        __builtin_amdgcn_s_setprio(2);
+      else if (q == 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
                                hist, kmax, lane);
+  }
+  __builtin_amdgcn_s_setprio(0);
   if (base < t_end)
     index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
                                 hist, kmax, lane);
@@ -262,6 +284,110 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
     }
   } else {
     for (int i = tid; i < n; i += 256) dst[i] = sbuf[i];
+  }
+  __syncthreads();  // the tile buffer and histogram are reused by the next tile
+}
+
+// Work split.  Every unit's token range, rounded up to kFlatAlign tokens, is
+// laid end to end in unit order; workgroup w takes the w-th of gridDim.x
+// equal shares of that space (whole multiples of kFlatAlign), so any mix of
+// sequence lengths keeps the workgroups equally busy, and equal lengths give
+// each workgroup one contiguous tile.  A share is processed as tiles of at
+// most kMaxTileTokens tokens of one unit; padding past a unit's length is
+// skipped.  Every workgroup derives the split from seq_lens itself.
+constexpr int kFlatAlign = 256;
+
+__device__ __forceinline__ int unit_len(const IndexArgs& a, int u) {
+  return unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len).L;
+}
+
+__device__ __forceinline__ unsigned long long padded(int L) {
+  return (unsigned long long)((L + kFlatAlign - 1) / kFlatAlign) * kFlatAlign;
+}
+
+__device__ __forceinline__ unsigned long long padded_len(const IndexArgs& a, int u) {
+  return u < a.units ? padded(unit_len(a, u)) : 0ull;
+}
+
+// A value the whole wave holds, moved to scalar registers.
+__device__ __forceinline__ unsigned long long uniform_u64(unsigned long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Both halves of a 64-bit value from lane l.
+__device__ __forceinline__ unsigned long long shfl_u64(unsigned long long v, int l) {
+  const uint32_t lo = __shfl((uint32_t)v, l);
+  const uint32_t hi = __shfl((uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+template <int LPT>
+__global__ __launch_bounds__(256) void indexer_kernel(IndexArgs a) {
+  __shared__ uint32_t hist[kBins / 2];
+  __shared__ uint32_t blk_sh[kMaxTileTokens / kBlockTokens];
+  __shared__ float sbuf[kMaxTileTokens];
+  __shared__ uint32_t wmax[4];
+  // This workgroup's share [r0, r1) of the flattened space, the units that
+  // hold its first and last token (the units in between are consecutive),
+  // and the first one's flattened start; derived by the first wave.
+  __shared__ unsigned long long span_r[2];
+  __shared__ unsigned long long span_off;
+  __shared__ int span_u[2];
+  __shared__ int span_len;  // length of the first unit
+  using u64 = unsigned long long;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    u64 total = 0ull;
+    for (int ub = 0; ub < a.units; ub += 64) total += wave_sum(padded_len(a, ub + lane));
+    const u64 step = (u64)gridDim.x * kFlatAlign;
+    const u64 share = (total + step - 1) / step * kFlatAlign;
+    const u64 r0 = share * blockIdx.x;
+    const u64 r1 = min(total, r0 + share);
+    int uf = -1, ul = -1, len_f = 0;
+    u64 off_f = 0ull;
+    u64 run = 0ull;  // flattened start of unit ub
+    for (int ub = 0; r0 < r1 && ub < a.units && ul < 0; ub += 64) {
+      const int L = ub + lane < a.units ? unit_len(a, ub + lane) : 0;
+      const u64 lp = padded(L);
+      const u64 inc = wave_inclusive_scan(lp);
+      const u64 off = run + inc - lp;
+      const u64 m0 = __ballot(lp > 0ull && off <= r0 && r0 < off + lp);
+      const u64 m1 = __ballot(lp > 0ull && off < r1 && r1 - 1 < off + lp);
+      if (m0) {
+        const int l = __ffsll((long long)m0) - 1;
+        uf = ub + l;
+        off_f = shfl_u64(off, l);
+        len_f = __shfl(L, l);
+      }
+      if (m1) ul = ub + __ffsll((long long)m1) - 1;
+      run += shfl_u64(inc, 63);
+    }
+    if (lane == 0) {
+      span_r[0] = r0;
+      span_r[1] = r1;
+      span_off = off_f;
+      span_u[0] = uf;
+      span_u[1] = ul;
+      span_len = len_f;
+    }
+  }
+  __syncthreads();
+  const u64 r0 = uniform_u64(span_r[0]);
+  const u64 r1 = uniform_u64(span_r[1]);
+  const int u_first = __builtin_amdgcn_readfirstlane(span_u[0]);
+  const int u_last = __builtin_amdgcn_readfirstlane(span_u[1]);
+  if (r0 >= r1 || u_first < 0) return;  // uniform over the workgroup
+  u64 uoff = uniform_u64(span_off);
+  for (int v = u_first; v <= u_last; ++v) {
+    const int L = __builtin_amdgcn_readfirstlane(v == u_first ? span_len : unit_len(a, v));
+    const u64 vlp = padded(L);
+    const int lo = (int)((r0 > uoff ? r0 : uoff) - uoff);
+    const int hi = min((int)((uoff + vlp < r1 ? uoff + vlp : r1) - uoff), L);
+    for (int t0 = lo; t0 < hi; t0 += kMaxTileTokens)
+      index_tile<LPT>(a, v, t0, min(hi, t0 + kMaxTileTokens), hist, blk_sh, sbuf, wmax);
+    uoff += vlp;
   }
 }
 
@@ -317,8 +443,6 @@ __global__ __launch_bounds__(256) void score_hist_kernel(SelectArgs a) {
 
 }  // namespace
 
-int indexer_tokens_per_iteration(int pair_count) { return 4 * (kWave / (pair_count / 4)) * 8; }
-int indexer_max_tokens_per_wg() { return kMaxTileTokens; }
 
 // Workgroups of the indexer instance for `pair_count` that the current device
 // holds at once (CUs x resident workgroups per CU), cached per device.
@@ -359,8 +483,8 @@ hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
 }
 
 hipError_t launch_indexer(const IndexArgs& a, int units, hipStream_t stream) {
-  const int tiles = (a.max_seq_len + a.tokens_per_wg - 1) / a.tokens_per_wg;
-  dim3 grid(tiles, units);
+  if (units != a.units || a.workgroups < 1) return hipErrorInvalidValue;
+  const dim3 grid(a.workgroups);
   switch (a.pair_count / 4) {
     case 1: indexer_kernel<1><<<grid, 256, 0, stream>>>(a); break;
     case 2: indexer_kernel<2><<<grid, 256, 0, stream>>>(a); break;

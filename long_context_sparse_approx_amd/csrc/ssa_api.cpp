@@ -170,21 +170,11 @@ struct Recorder {
   }
 };
 
-// Indexer tile: every unit gets an equal share of the workgroups the device
-// holds at once, so a layer that fits runs as one round (no tail round) and
-// each workgroup streams one large tile; at least one iteration, at most the
-// kernel's tile capacity.
-int tokens_per_wg(const ssa_params* p, const Dims& d) {
-  const int it = ssa::indexer_tokens_per_iteration(p->pair_count);
-  const int cap = ssa::indexer_max_tokens_per_wg() / it * it;
-  int resident = ssa::indexer_resident_workgroups(p->pair_count);
-  if (resident <= 0) resident = 1024;
-  const int per_unit = resident / d.U > 0 ? resident / d.U : 1;
-  int64_t tpw = ((int64_t)p->max_seq_len + per_unit - 1) / per_unit;
-  tpw = (tpw + it - 1) / it * it;
-  if (tpw > cap) tpw = cap;
-  if (tpw < it) tpw = it;
-  return (int)tpw;
+// The indexer's grid: as many workgroups as the device holds at once, so the
+// layer's tokens (split evenly among them) stream in a single round.
+int indexer_workgroups(const ssa_params* p) {
+  const int resident = ssa::indexer_resident_workgroups(p->pair_count);
+  return resident > 0 ? resident : 1024;
 }
 
 ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
@@ -211,7 +201,8 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
   a.max_blocks = p->max_blocks_per_seq;
   a.num_blocks = p->num_blocks;
   a.max_seq_len = p->max_seq_len;
-  a.tokens_per_wg = tokens_per_wg(p, d);
+  a.units = d.U;
+  a.workgroups = indexer_workgroups(p);
   const bool split = p->key_layout == SSA_KEYS_SPLIT;
   a.key_ld = split ? 2 * p->pair_count : d.d;
   a.key_off = split ? 0 : 2 * p->pair_begin;

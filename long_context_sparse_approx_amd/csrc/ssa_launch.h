@@ -43,7 +43,9 @@ struct IndexArgs {
   uint32_t* maxkey;           // [U]
   int T, g, NG;               // queries per sequence, queries per group, groups
   int Hq, Hkv, G, d, pair_begin, pair_count;
-  int max_blocks, num_blocks, max_seq_len, tokens_per_wg;
+  int max_blocks, num_blocks, max_seq_len;
+  int units;                  // selection units (score rows)
+  int workgroups;             // grid size: the units' tokens are split evenly among them
   int key_ld;                 // elements per key row: d (whole keys) or 2 * pair_count
   int key_off;                // first scored element of a row: 2 * pair_begin or 0
   float scale;
@@ -133,8 +135,6 @@ struct AppendArgs {
   int B, T, Hkv, d, pair_begin, pair_count, max_blocks, num_blocks, max_seq_len;
 };
 
-int indexer_tokens_per_iteration(int pair_count);
-int indexer_max_tokens_per_wg();
 int indexer_resident_workgroups(int pair_count);  // 0 if unknown
 // Clears the histograms and maxima; the mass histograms only when non-null.
 hipError_t launch_init(uint32_t* hist1, uint32_t* hist2, uint32_t* maxkey,
