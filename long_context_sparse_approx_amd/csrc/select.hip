@@ -814,24 +814,27 @@ __global__ __launch_bounds__(kNT) void stop_cut_kernel(SelectArgs a) {
 // written from an LDS membership map: deterministic tokens ascending, then
 // sampled tokens ascending.  With emit_rows the segment holds cache row
 // numbers (for the fused attention stage) instead of positions.
+// Membership of a chunk position: not selected, deterministic, or sampled
+// with its logit bias -log(pi) stored as the word itself (a finite float,
+// never one of the two marks, which are NaN patterns).
+constexpr uint32_t kMarkNone = 0xffffffffu;
+constexpr uint32_t kMarkDet = 0xfffffffeu;
+
 __device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, int b, int h,
                                            int grp, int t, float w, int c0, int nvalid,
-                                           uint8_t* flag, float* lwsh) {
+                                           uint32_t* mark) {
   if ((unsigned)(t - c0) >= (unsigned)nvalid) return;  // not a position of this chunk
   const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, grp);
   const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
   const float mw = (float)st.m * w;
-  if (uniform24(words[t & 3]) * st.W < mw) {
-    flag[t - c0] = 2;
-    lwsh[t - c0] = -logf(fminf(1.0f, mw / st.W));
-  }
+  if (uniform24(words[t & 3]) * st.W < mw)
+    mark[t - c0] = __float_as_uint(-logf(fminf(1.0f, mw / st.W)));
 }
 
 __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
-  __shared__ uint8_t flag[kChunk];  // 0 none, 1 deterministic, 2 sampled
-  __shared__ float lwsh[kChunk];
-  __shared__ int blk_sh[kChunk / kBlockTokens];
+  __shared__ uint32_t mark[kChunk];  // kMarkNone, kMarkDet or a sampled token's bias
   __shared__ int scan_scr[kNT / 64];
+  static_assert(kPer == kBlockTokens, "a thread's positions are one cache block");
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -860,11 +863,14 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   const int nvalid = min(kChunk, st.L - c0);
   const bool dense = st.flags & kFlagDense;
   const bool sampling = st.flags & kFlagSample;
+  // This thread's positions are one cache block: its id, for emitted rows.
+  int blk = 0;
   if (a.emit_rows && threadIdx.x < (nvalid + kBlockTokens - 1) / kBlockTokens) {
-    int blk = a.block_table[(size_t)b * a.max_blocks + c0 / kBlockTokens + threadIdx.x];
-    blk_sh[threadIdx.x] = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    blk = a.block_table[(size_t)b * a.max_blocks + c0 / kBlockTokens + threadIdx.x];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
   }
-  for (int i = threadIdx.x; i < kChunk; i += kNT) flag[i] = (dense && i < nvalid) ? 1 : 0;
+  for (int i = threadIdx.x; i < kChunk; i += kNT)
+    mark[i] = (dense && i < nvalid) ? kMarkDet : kMarkNone;
   // Early stopping: the last stratum word kept (~0: the whole stratum).
   const unsigned long long cut = a.stop_cut && !dense ? a.stop_cut[u] : ~0ull;
   __syncthreads();
@@ -876,12 +882,11 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
       const int t = lidx[i];
       if ((unsigned)(t - c0) < (unsigned)nvalid &&
           (cut == ~0ull || stratum_word(order_key(srow[t]), t) <= cut))
-        flag[t - c0] = 1;
+        mark[t - c0] = kMarkDet;
     }
     if (sampling)
       for (int i = threadIdx.x; i < n_samp; i += kNT)
-        sample_one(st, seed, b, h, ui.grp, lidx[n_above + i], lw[n_above + i], c0, nvalid, flag,
-                   lwsh);
+        sample_one(st, seed, b, h, ui.grp, lidx[n_above + i], lw[n_above + i], c0, nvalid, mark);
     if (!(st.flags & kFlagNoTopk)) {
       // Threshold-digit candidates, in index order: key above T -> S; key == T
       // -> S while the tie quota lasts; otherwise a tail token.
@@ -901,10 +906,10 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
             // stratum tokens past the early stop are neither read nor sampled
             if ((unsigned)(t - c0) < (unsigned)nvalid && stratum_word(key, t) <= cut)
-              flag[t - c0] = 1;
+              mark[t - c0] = kMarkDet;
           } else if (sampling) {
             sample_one(st, seed, b, h, ui.grp, t, sexp(key_to_float(key) - st.M), c0, nvalid,
-                       flag, lwsh);
+                       mark);
           }
         }
       }
@@ -916,9 +921,9 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   uint32_t smask = 0u, rmask = 0u;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const uint8_t f = flag[tb + i];
-    smask |= (uint32_t)(f == 1) << i;
-    rmask |= (uint32_t)(f == 2) << i;
+    const uint32_t m = mark[tb + i];
+    smask |= (uint32_t)(m == kMarkDet) << i;
+    rmask |= (uint32_t)(m < kMarkDet) << i;
   }
   // One scan for both counts: deterministic count in the low 16 bits,
   // sampled count in the high 16 bits (each at most 4096).
@@ -935,14 +940,14 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
     const uint32_t bit = 1u << i;
     if ((smask | rmask) & bit) {
       const int t = c0 + tb + i;
-      const int v = a.emit_rows ? (blk_sh[(tb + i) >> 4] * a.Hkv + h) * kBlockTokens + (t & 15) : t;
+      const int v = a.emit_rows ? (blk * a.Hkv + h) * kBlockTokens + (t & 15) : t;
       if (smask & bit) {
         sidx[ws] = v;
         slw[ws] = 0.0f;
         ++ws;
       } else {
         sidx[wr] = v;
-        slw[wr] = lwsh[tb + i];
+        slw[wr] = __uint_as_float(mark[tb + i]);
         ++wr;
       }
     }
