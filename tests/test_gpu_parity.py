@@ -54,6 +54,19 @@ CASES = {
     "budget_equals_length": dict(cfg=dict(B=1, Hq=4, Hkv=1, d=64, L=[2000], theta=1e4,
                                           kdist="normal", planted=0, pair_count=16, topk=1500,
                                           m=500, seeds=[25], data_seed=19)),
+    # Empty sequences between non-empty ones (their outputs are zero).
+    "empty_seqs": dict(cfg=dict(B=4, Hq=8, Hkv=2, d=128, L=[5000, 0, 300, 0], theta=1e6,
+                                kdist="normal", planted=4, pair_count=32, topk=40, m=30,
+                                seeds=[31, 32, 33, 34], data_seed=20)),
+    # 96 units of mixed lengths (empty, one token, ragged, several chunks): the
+    # indexer's split of the units' tokens crosses groups of 64 units.
+    "many_units": dict(cfg=dict(B=48, Hq=4, Hkv=2, d=64,
+                                L=[4100, 300, 1500, 4100, 300, 1500, 4100, 1, 0, 1, 1, 4100,
+                                   4100, 0, 17, 1500, 0, 1500, 0, 17, 1500, 1, 17, 1, 1500, 1,
+                                   4100, 17, 17, 300, 300, 300, 300, 4100, 1500, 1500, 1500,
+                                   300, 17, 4100, 17, 1, 4100, 0, 4100, 300, 0, 0],
+                                theta=1e4, kdist="normal", planted=0, pair_count=16, topk=20,
+                                m=15, seeds=list(range(100, 148)), data_seed=21)),
 }
 
 
@@ -142,7 +155,7 @@ def test_staged_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged_b2", "g8_d64", "mixture_edges",
-                                  "pure_sampling", "dense"])
+                                  "pure_sampling", "dense", "empty_seqs", "many_units"])
 def test_end_to_end(name):
     wl = make_case(name)
     say(f"[e2e] case={name} L={wl.lens}")
