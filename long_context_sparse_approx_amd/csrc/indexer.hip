@@ -234,15 +234,15 @@ __device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, in
   // A CU serves its oldest waves first, so workgroups that share a CU would
   // stream at very different rates and the late ones would finish alone with
   // few loads in flight.  Each wave therefore lowers its priority as it
-  // advances (3 over its first quarter of the tile ... 0 over the last): a
+  // advances (3 up to 60% of its tile, then 2, 1 from 85%, 0 from 95%): a
   // wave that is ahead yields to those behind, and the CU's workgroups finish
-  // together.
+  // together.  The bands narrow towards the end, where the spread matters.
   int base = t0 + wave * WAVE_TOK;
   const int n_full = base + WAVE_TOK <= t_end ? (t_end - WAVE_TOK - base) / WG_TOK + 1 : 0;
   __builtin_amdgcn_s_setprio(3);
-  int level = 0;  // quarter of the tile reached
+  int level = 0;  // priority bands passed
   for (int it = 0; it < n_full; ++it, base += WG_TOK) {
-    const int q = 4 * it / n_full;
+    const int q = (it * 20 >= 12 * n_full) + (it * 20 >= 17 * n_full) + (it * 20 >= 19 * n_full);
     if (q != level) {
       level = q;
       if (q == 1)
