@@ -123,8 +123,8 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
     for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = a.hist1m[(size_t)u * kBins + i];
   __syncthreads();
   DigitBound d{kBins, 0, 0ull, 0};
+  int bc = kBins, rc = 0;  // where the count bound ends (its rank search)
   if (p.k_eff > 0) {
-    int bc, rc;
     find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &bc, &rc);
     d = DigitBound{bc, rc, 0ull, kBoundCount};
     if (topp) {
@@ -142,7 +142,10 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
     }
   }
   const int b1 = d.bin;
-  const int above = count_above<kNT>(hist, kBins, b1, scan_scr);
+  // Tokens above b1: the rank search already counted them when it chose b1.
+  const int above = b1 == kBins ? 0
+                    : (b1 == bc && (d.mode & kBoundCount)) ? p.k_eff - rc
+                                                            : count_above<kNT>(hist, kBins, b1, scan_scr);
   const float M = key_to_float(maxkey);
   double lb = 0.0;
   for (int bin = threadIdx.x; bin < b1; bin += kNT) {
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       // The chunks' tail sums do not depend on anything below: load them first.
       double acc = 0.0;
       for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
-      double ctail = 0.0;
+      double cs = 0.0;  // this thread's candidates below the threshold key
       int total_ties = 0;
       if (t1.mode == 0) {
         st.flags = kFlagNoTopk;
@@ -312,15 +315,20 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         __syncthreads();
         // Second digit.
+        // The candidates above the chosen bin: counted by the rank search when
+        // the count bound chose it.
         DigitBound d2;
+        int above2;
         {
           int bc = 0, rc = 0, bm = 0;
           unsigned long long rm = 0ull;
           if (t1.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &bc, &rc);
           if (t1.mode & kBoundMass) find_bin<kRT>(mh, kBins, t1.rem_mass, scan_m, pair_m, &bm, &rm);
           d2 = combine_bounds(t1.mode, bc, rc, bm, rm);
+          above2 = ((d2.mode & kBoundCount) && d2.bin == bc)
+                       ? t1.rem - rc
+                       : count_above<kRT>(hist, kBins, d2.bin, scan_scr);
         }
-        const int above2 = count_above<kRT>(hist, kBins, d2.bin, scan_scr);
         const bool mass3 = d2.mode & kBoundMass;
         const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)d2.bin;
         for (int i = threadIdx.x; i < kBins3; i += kRT) {
@@ -351,14 +359,17 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         }
         __syncthreads();
         DigitBound d3;
+        int above3;
         {
           int bc = 0, rc = 0, bm = 0;
           unsigned long long rm = 0ull;
           if (d2.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins3, d2.rem, scan_scr, pair, &bc, &rc);
           if (mass3) find_bin<kRT>(mh, kBins3, d2.rem_mass, scan_m, pair_m, &bm, &rm);
           d3 = combine_bounds(d2.mode, bc, rc, bm, rm);
+          above3 = ((d3.mode & kBoundCount) && d3.bin == bc)
+                       ? d2.rem - rc
+                       : count_above<kRT>(hist, kBins3, d3.bin, scan_scr);
         }
-        const int above3 = count_above<kRT>(hist, kBins3, d3.bin, scan_scr);
         st.tkey = (prefix << kDigit2Shift) | (uint32_t)d3.bin;
         // Tokens on the last key all carry the same mass: the mass bound needs
         // ceil(remaining units / units per token) of them.
@@ -373,8 +384,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         // Ties on the threshold key per chunk and candidates above it
         // (integer, packed as ties + (above << 16): each at most 4096), and
         // the weight of the candidates strictly below it (each thread over
-        // its fixed items, in order, then a fixed tree).
-        double cs = 0.0;
+        // its fixed items, in order; summed with the chunk sums below).
         if (one_chunk) {
           int ties = 0;
 #pragma unroll
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
             if (ties) atomicAdd(&ties_sh[c], ties);
           }
         }
-        ctail = block_sum_f64<kRT>(cs, dscr);
+        __syncthreads();  // the chunks' tie counts are complete
         int run = 0;
         for (int c0 = 0; c0 < nc; c0 += kRT) {
           const int c = c0 + threadIdx.x;
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         total_ties = run;
         if (a.stop_off) stop_offsets(a, u, cu, nc, ties_sh, scan_scr);
       }
-      W = block_sum_f64<kRT>(acc, dscr) + ctail;
+      W = block_sum_f64<kRT>(acc + cs, dscr);  // every thread's share, one fixed tree
       if (t1.mode != 0) {
         const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
         W += (double)(total_ties - st.ties_needed) * wT;
