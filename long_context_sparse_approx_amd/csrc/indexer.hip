@@ -295,7 +295,7 @@ __device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, in
 // each workgroup one contiguous tile.  A share is processed as tiles of at
 // most kMaxTileTokens tokens of one unit; padding past a unit's length is
 // skipped.  Every workgroup derives the split from seq_lens itself.
-constexpr int kFlatAlign = 256;
+constexpr int kFlatAlign = kIndexAlign;
 
 __device__ __forceinline__ int unit_len(const IndexArgs& a, int u) {
   return unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len).L;

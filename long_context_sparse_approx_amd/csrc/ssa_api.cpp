@@ -171,10 +171,14 @@ struct Recorder {
 };
 
 // The indexer's grid: as many workgroups as the device holds at once, so the
-// layer's tokens (split evenly among them) stream in a single round.
-int indexer_workgroups(const ssa_params* p) {
+// layer's tokens (split evenly among them) stream in a single round; never
+// more than the units' longest possible token ranges have aligned blocks.
+int indexer_workgroups(const ssa_params* p, const Dims& d) {
   const int resident = ssa::indexer_resident_workgroups(p->pair_count);
-  return resident > 0 ? resident : 1024;
+  const int64_t blocks =
+      (int64_t)d.U * ((p->max_seq_len + ssa::kIndexAlign - 1) / ssa::kIndexAlign);
+  const int64_t g = resident > 0 ? resident : 1024;
+  return (int)(blocks < 1 ? 1 : (blocks < g ? blocks : g));
 }
 
 ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, const void* k_cache,
@@ -202,7 +206,7 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
   a.num_blocks = p->num_blocks;
   a.max_seq_len = p->max_seq_len;
   a.units = d.U;
-  a.workgroups = indexer_workgroups(p);
+  a.workgroups = indexer_workgroups(p, d);
   const bool split = p->key_layout == SSA_KEYS_SPLIT;
   a.key_ld = split ? 2 * p->pair_count : d.d;
   a.key_off = split ? 0 : 2 * p->pair_begin;

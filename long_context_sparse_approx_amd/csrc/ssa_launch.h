@@ -32,6 +32,10 @@ struct Thresh1 {
 };
 static_assert(sizeof(Thresh1) == 32, "one 32-byte record per unit");
 
+// The indexer splits the units' token ranges, each rounded up to this many
+// tokens, evenly over its workgroups.
+constexpr int kIndexAlign = 256;
+
 struct IndexArgs {
   const uint16_t* q;          // [B, T, Hq, d] bf16
   const uint16_t* k_cache;    // [num_blocks, Hkv, 16, key_ld] bf16
