@@ -380,11 +380,15 @@ def summarize(res, workload):
     roof = None
     if res["idx_ms"]:
         achieved = res["idx_bytes"] / (res["idx_ms"] * 1e-3) / 1e9
+        traffic = measured_traffic(workload)
         roof = dict(bound="hbm", kernel="indexer", achieved=round(achieved, 1),
                     peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBPS, 4),
-                    traffic=measured_traffic(workload),
+                    traffic=traffic,
                     algorithmic_bytes_per_launch=res["idx_bytes"],
-                    launch_us=round(res["idx_ms"] * 1e3, 2))
+                    launch_us=round(res["idx_ms"] * 1e3, 2),
+                    # the same launch's rate in measured HBM bytes (read + written)
+                    measured_gbps=(round(traffic / (res["idx_ms"] * 1e-3) / 1e9, 1)
+                                   if traffic else None))
     step_s = res["ms_step"] * 1e-3
     algo_total = res["idx_bytes"] + res["gather_bytes"]
     return dict(
