@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
 // set); tokens on b1 become candidates (index order, second-digit histogram);
 // tokens below b1 are tail tokens: their weights are summed in fp64 for W and
 // those passing the necessary inclusion test are listed with their weight.
-__global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
+// At most 64 VGPRs: eight waves per SIMD, so a 1M-token layer's chunk
+// workgroups are all resident at once.
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void filter_kernel(
+    SelectArgs a) {
   __shared__ float sh[kChunk];
   __shared__ int scan_scr[kNT / 64];
   __shared__ double dscr[kNT / 64];
@@ -175,13 +178,22 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   // The chunk's scores, the threshold and the maximum depend on the unit and
   // chunk only: their loads go out together with the sequence's parameters.
   // Scores are read up to the end of the row (score_ld entries); entries at
-  // or past L are ignored.
-  float v[kPer];
+  // or past L are ignored.  Each thread takes its 16 consecutive scores as
+  // four 16-byte loads when the rows allow it (the fused path's always do);
+  // otherwise they go through the LDS buffer with coalesced 4-byte loads
+  // after the checks.
   const float* srow = a.scores + (size_t)u * a.score_ld;
+  const bool direct = ((reinterpret_cast<uintptr_t>(srow) & 15u) | (a.score_ld & 3)) == 0;
+  const int tb = threadIdx.x * kPer;
+  float4 s4[kPer / 4];
+  if (direct) {
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int t = c0 + threadIdx.x + k * kNT;
-    v[k] = t < a.score_ld ? srow[t] : 0.0f;
+    for (int g = 0; g < kPer / 4; ++g) {
+      // Unconditional loads (clamped into the row) keep the four in flight
+      // together; a row holds at least 4 entries here.
+      const int t = c0 + tb + 4 * g;
+      s4[g] = *reinterpret_cast<const float4*>(srow + (t < a.score_ld ? t : 0));
+    }
   }
   const Thresh1 t1 = a.thresh[u];
   const uint32_t maxkey = a.maxkey[u];
@@ -191,10 +203,17 @@ __global__ __launch_bounds__(kNT) void filter_kernel(SelectArgs a) {
   const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const float M = key_to_float(maxkey);
+  if (!direct) {
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) sh[threadIdx.x + k * kNT] = v[k];
-  __syncthreads();
-  filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, sh, scan_scr, dscr);
+    for (int k = 0; k < kPer; ++k) {
+      const int t = c0 + threadIdx.x + k * kNT;
+      sh[threadIdx.x + k * kNT] = srow[t < a.score_ld ? t : a.score_ld - 1];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < kPer / 4; ++g) s4[g] = *reinterpret_cast<const float4*>(sh + tb + 4 * g);
+  }
+  filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, s4, sh, scan_scr, dscr);
 }
 
 // ------------------------------------------------------------------ resolve

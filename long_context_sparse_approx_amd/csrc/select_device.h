@@ -9,19 +9,25 @@ namespace ssa {
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 
-// Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  `sh` holds the
-// chunk's scores (entries at or past L are ignored); t1 is the unit's
+// Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  s4 holds the
+// thread's 16 consecutive scores (entries at or past L are ignored) and sh
+// the chunk's score buffer in LDS, of which the thread uses its own 16
+// entries; t1 is the unit's
 // first-digit threshold and M its maximum score.  Writes the chunk's
 // candidates (positions and keys, second-digit histogram), its lists (tokens
 // above the threshold digit, then tail tokens passing the necessary
 // inclusion test fl(u * W_lb) < fl(m * w) with their weights), its
 // candidate and list counts and its fp64 tail weight sum.
-// Branch-free: every token's weight and every group's uniforms are computed;
-// masks select what counts.
+// Two passes over the thread's 16 tokens: the first computes every token's
+// class, weight and inclusion test in groups of four (one Philox block each)
+// and keeps only bit masks and the fp64 tail sum; after the scans the second
+// visits the set bits only, recomputing the key and weight of the few tokens
+// it writes.  Keeping no per-token arrays holds the kernel to 64 VGPRs, so a
+// 1M-token layer's chunk workgroups are all resident at once.
 __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParams& p,
                                              const Thresh1& t1, float M, int u, int b, int h,
-                                             int grp, int c, const float* sh, int* scan_scr,
-                                             double* dscr) {
+                                             int grp, int c, const float4 (&s4)[kPer / 4],
+                                             float* sh, int* scan_scr, double* dscr) {
   const int c0 = c * kChunk;
   const int b1 = t1.b1;  // 2048 when there is no deterministic set
   // With top-p the stratum size is not known yet: list sampling candidates
@@ -32,36 +38,35 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   const uint64_t seed = a.seed[b];
   const int tb = threadIdx.x * kPer;
   const int nv = p.L - (c0 + tb);  // valid tokens of this thread: min(16, max(nv, 0))
-  uint32_t candmask = 0u, abovemask = 0u, tailmask = 0u, sampmask = 0u;
+  uint32_t candmask = 0u, abovemask = 0u, sampmask = 0u;
   double wsum = 0.0;
-  uint32_t keys[kPer];
-  float w[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const float s = sh[tb + i];
-    const uint32_t key = order_key(s);
-    keys[i] = key;
-    const int bin = (int)(key >> kDigit1Shift);
-    const bool valid = i < nv;
-    abovemask |= (uint32_t)(valid && bin > b1) << i;
-    candmask |= (uint32_t)(valid && bin == b1) << i;
-    const bool tail = valid && bin < b1;
-    tailmask |= (uint32_t)tail << i;
-    w[i] = sexp(s - M);
-    wsum += tail ? (double)w[i] : 0.0;
-  }
-  if (sampling) {
+  for (int g = 0; g < kPer / 4; ++g) {
+    // One group at a time: its loads may still be in flight while the
+    // previous group is computed.
+    // The empty asm ties the group's Philox counter to the previous group's
+    // result, so the four blocks are not computed at once (they would not
+    // fit 64 VGPRs).
+    uint32_t jq = (uint32_t)(c0 + tb + 4 * g) >> 2;
+    asm volatile("" : "+v"(jq) : "v"(sampmask));
+    const float s[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
+    // Kept for the second pass (no other thread reads this thread's entries).
+    *reinterpret_cast<float4*>(sh + tb + 4 * g) = s4[g];
+    uint4 wd = make_uint4(0u, 0u, 0u, 0u);
+    if (sampling) wd = philox_block(seed, b, h, jq, grp);
+    const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
 #pragma unroll
-    for (int g = 0; g < kPer / 4; ++g) {
-      const uint4 wd = philox_block(seed, b, h, (uint32_t)(c0 + tb + 4 * g) >> 2, grp);
-      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * g + r;
-        sampmask |= (uint32_t)(uniform24(words[r]) * t1.wlb < mf * w[i]) << i;
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g + r;
+      const int bin = (int)(order_key(s[r]) >> kDigit1Shift);
+      const bool valid = i < nv;
+      abovemask |= (uint32_t)(valid && bin > b1) << i;
+      candmask |= (uint32_t)(valid && bin == b1) << i;
+      const bool tail = valid && bin < b1;
+      const float w = sexp(s[r] - M);
+      wsum += tail ? (double)w : 0.0;
+      sampmask |= (uint32_t)(sampling && tail && uniform24(words[r]) * t1.wlb < mf * w) << i;
     }
-    sampmask &= tailmask;
   }
   int total;
   const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
@@ -74,21 +79,25 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
   float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
   int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
+  // The classes are disjoint; ascending bits keep every list in index order.
+  for (uint32_t rest = candmask | abovemask | sampmask; rest != 0u; rest &= rest - 1u) {
+    const int i = __builtin_ctz(rest);
+    const uint32_t bit = 1u << i;
     const int t = c0 + tb + i;
-    if (candmask & (1u << i)) {
+    const float s = sh[tb + i];
+    if (candmask & bit) {
+      const uint32_t key = order_key(s);
       cidx[wc] = t;
-      ckey[wc] = keys[i];
+      ckey[wc] = key;
       ++wc;
-      const int d2 = (keys[i] >> kDigit2Shift) & (kBins - 1);
+      const int d2 = (key >> kDigit2Shift) & (kBins - 1);
       atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
-      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w[i]));
-    }
-    if (abovemask & (1u << i)) lidx[wa++] = t;
-    if (sampmask & (1u << i)) {
+      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(sexp(s - M)));
+    } else if (abovemask & bit) {
+      lidx[wa++] = t;
+    } else {
       lidx[ws] = t;
-      lw[ws] = w[i];
+      lw[ws] = sexp(s - M);
       ++ws;
     }
   }

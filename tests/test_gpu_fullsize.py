@@ -215,3 +215,37 @@ def test_fullsize_1m_split_keys():
     out_h = ssa.decode_split(ps, wl.q, k_dom, k_rest_h, v_h, *args, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(ref, out_h)
+
+
+@pytest.mark.parametrize("name", ["1m", "128k"])
+def test_fullsize_fused_equals_staged(name):
+    """At full size, in the indexer's one-round split: every token's score
+    lands where it belongs (a NaN-filled score array is fully overwritten, the
+    same on a second run), and the fused step's own histogram and maximum
+    select what the staged path selects from those scores (the fused output
+    equals attention over the staged selection, bit for bit)."""
+    wl = synth.make_workload(name, DEV)
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    ws = ssa.alloc_workspace(p, DEV)
+    shape = (wl.B, wl.Hkv, wl.max_seq_len)
+    runs = []
+    for _ in range(2):
+        sc = torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+        ssa.score(p, wl.q, wl.k_cache, wl.block_table, wl.seq_lens, scores=sc, workspace=ws)
+        runs.append(sc)
+    torch.cuda.synchronize()
+    for b in range(wl.B):
+        L = wl.lens[b]
+        assert not torch.isnan(runs[0][b, :, :L]).any(), f"scores missing in sequence {b}"
+        assert torch.equal(runs[0][b, :, :L], runs[1][b, :, :L]), f"scores differ in sequence {b}"
+    out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                     wl.sample_budget, wl.seed, workspace=ws).clone()
+    si, sl, sn, _ = ssa.select(p, runs[0], wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                               workspace=ws)
+    att = ssa.attend(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, si, sl, sn,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    say(f"[full] {name} fused vs staged: max |diff| "
+        f"{float((out.double() - att.double()).abs().max()):.3g}")
+    assert torch.equal(out, att)
