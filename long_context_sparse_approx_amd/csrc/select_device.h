@@ -9,11 +9,11 @@ namespace ssa {
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 
-// Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  s4 holds the
-// thread's 16 consecutive scores (entries at or past L are ignored) and sh
-// the chunk's score buffer in LDS, of which the thread uses its own 16
-// entries; t1 is the unit's
-// first-digit threshold and M its maximum score.  Writes the chunk's
+// Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  s4
+// holds the thread's 16 consecutive scores (entries at or past L are
+// ignored); sh is the chunk's score buffer in LDS, of which the thread uses
+// its own 16 entries; t1 is the unit's first-digit threshold and M its
+// maximum score.  Writes the chunk's
 // candidates (positions and keys, second-digit histogram), its lists (tokens
 // above the threshold digit, then tail tokens passing the necessary
 // inclusion test fl(u * W_lb) < fl(m * w) with their weights), its
@@ -43,10 +43,9 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
 #pragma unroll
   for (int g = 0; g < kPer / 4; ++g) {
     // One group at a time: its loads may still be in flight while the
-    // previous group is computed.
-    // The empty asm ties the group's Philox counter to the previous group's
-    // result, so the four blocks are not computed at once (they would not
-    // fit 64 VGPRs).
+    // previous group is computed.  The empty asm ties the group's Philox
+    // counter to the previous group's result, so the four blocks are not
+    // computed at once (they would not fit 64 VGPRs).
     uint32_t jq = (uint32_t)(c0 + tb + 4 * g) >> 2;
     asm volatile("" : "+v"(jq) : "v"(sampmask));
     const float s[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
