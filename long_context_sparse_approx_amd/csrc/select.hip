@@ -872,7 +872,20 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   const int h = ui.h;
   const int c0 = c * kChunk;
   const size_t ci = (size_t)u * a.nchunk + c;
-  // Independent loads first: unit state, per-chunk counts, the chunk's block ids.
+  const int tid = threadIdx.x;
+  // Independent loads first: unit state, per-chunk counts, the chunk's block
+  // ids, and this thread's first entry of each list (the lists are read
+  // whole within the chunk's segment; entries past a count are never used),
+  // so the common chunk, with fewer than kNT entries per list, needs no
+  // further round trip.
+  const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
+  const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
+  const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
+  const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+  const int l_first = lidx[tid];
+  const float w_first = lw[tid];
+  const int c_first = cidx[tid];
+  const uint32_t k_first = ckey[tid];
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   // Counts are clamped to the segment and positions checked against the
   // chunk, so no value in the workspace can address outside it.
@@ -904,34 +917,34 @@ __global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
   const unsigned long long cut = a.stop_cut && !dense ? a.stop_cut[u] : ~0ull;
   __syncthreads();
   if (!dense) {
-    const int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
-    const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
     const float* srow = a.scores + (size_t)u * a.score_ld;
-    for (int i = threadIdx.x; i < n_above; i += kNT) {
-      const int t = lidx[i];
-      if ((unsigned)(t - c0) < (unsigned)nvalid &&
-          (cut == ~0ull || stratum_word(order_key(srow[t]), t) <= cut))
-        mark[t - c0] = kMarkDet;
+    // The chunk's list: tokens above the threshold digit, then the listed
+    // sampling candidates with their weights.
+    const int n_list = n_above + (sampling ? n_samp : 0);
+    for (int i = tid; i < n_list; i += kNT) {
+      const int t = i == tid ? l_first : lidx[i];
+      if (i < n_above) {
+        if ((unsigned)(t - c0) < (unsigned)nvalid &&
+            (cut == ~0ull || stratum_word(order_key(srow[t]), t) <= cut))
+          mark[t - c0] = kMarkDet;
+      } else {
+        sample_one(st, seed, b, h, ui.grp, t, i == tid ? w_first : lw[i], c0, nvalid, mark);
+      }
     }
-    if (sampling)
-      for (int i = threadIdx.x; i < n_samp; i += kNT)
-        sample_one(st, seed, b, h, ui.grp, lidx[n_above + i], lw[n_above + i], c0, nvalid, mark);
     if (!(st.flags & kFlagNoTopk)) {
       // Threshold-digit candidates, in index order: key above T -> S; key == T
       // -> S while the tie quota lasts; otherwise a tail token.
-      const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
-      const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
       int run = 0;  // ties seen in earlier rounds of this loop
       for (int base = 0; base < ncand; base += kNT) {
-        const int i = base + threadIdx.x;
+        const int i = base + tid;
         const bool v = i < ncand;
-        const uint32_t key = v ? ckey[i] : 0u;
+        const uint32_t key = v ? (base == 0 ? k_first : ckey[i]) : 0u;
+        const int t = v ? (base == 0 ? c_first : cidx[i]) : 0;
         const bool tie = v && key == st.tkey;
         int tot;
         const int rank = before + run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &tot);
         run += tot;
         if (v) {
-          const int t = cidx[i];
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
             // stratum tokens past the early stop are neither read nor sampled
             if ((unsigned)(t - c0) < (unsigned)nvalid && stratum_word(key, t) <= cut)
