@@ -152,12 +152,27 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
   const size_t seg = (size_t)u * a.seg_ld;
+  // The split's first chunk when the span covers every chunk: its counts and
+  // first batch of items are read together with the query, ahead of the
+  // sequence length that decides the chunk range (used only if it matches).
+  const int c_guess = (int)((int64_t)s * a.nchunk / a.nsplit);
+  const int32_t* cnt_guess = a.sel_cnt + ((size_t)u * a.nchunk + c_guess) * 2;
+  const int pf_cnt0 = cnt_guess[0], pf_cnt1 = cnt_guess[1];
+  int pf_idx[kBatch / 64];
+  float pf_lw[kBatch / 64];
+#pragma unroll
+  for (int k = 0; k < kBatch / 64; ++k) {
+    pf_idx[k] = a.sel_idx[seg + (size_t)c_guess * kChunk + lane + 64 * k];
+    pf_lw[k] = a.sel_logw[seg + (size_t)c_guess * kChunk + lane + 64 * k];
+  }
   for (int c = c_begin; c < c_end; ++c) {
+    const bool guessed = c == c_guess;
     const int32_t* cntp = a.sel_cnt + ((size_t)u * a.nchunk + c) * 2;
     // Counts of a caller-provided selection are clamped to the segment and
     // rows to the cache; positions at or past the member's span are masked:
     // no value can address outside the buffers.
-    const int cnt = min(max(cntp[0], 0) + max(cntp[1], 0), kChunk);
+    const int cnt = min(max(guessed ? pf_cnt0 : cntp[0], 0) + max(guessed ? pf_cnt1 : cntp[1], 0),
+                        kChunk);
     const int i_lo = (int)((int64_t)sub * cnt / a.nsub);  // this wave's share
     const int i_hi = (int)((int64_t)(sub + 1) * cnt / a.nsub);
     const int32_t* idxp = a.sel_idx + seg + (size_t)c * kChunk;
@@ -171,8 +186,9 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
         int row = -1, pos = 0;  // rows given directly carry no position
         float lw = -INFINITY;
         if (i < nb) {
-          const int v = idxp[b0 + i];
-          lw = lwp[b0 + i];
+          const bool pre = guessed && b0 == 0;  // items 0 .. kBatch - 1 of the guessed chunk
+          const int v = pre ? pf_idx[k] : idxp[b0 + i];
+          lw = pre ? pf_lw[k] : lwp[b0 + i];
           if (a.idx_are_rows) {
             row = min(max(v, 0), max_row);
           } else if (v < L) {  // positions past every member's span are dropped
