@@ -11,8 +11,9 @@
 // for 32 pairs at d = 128).  LPT lanes cover one token with one 16-byte
 // streaming load each; a wave instruction therefore reads 64/LPT token slices
 // and every lane keeps 8 independent loads (8 consecutive tokens) in flight.
-// The scaled proxy query lives in registers as bf16 hi + lo parts and the
-// slices are dotted with v_dot2_f32_bf16 straight from the loaded words.  A DPP reduce-scatter
+// The scaled proxy query lives in registers as three bf16 parts (hi + mid +
+// lo, float32 precision) and the slices are dotted with v_dot2_f32_bf16
+// straight from the loaded words.  A DPP reduce-scatter
 // across the LPT lanes leaves each lane with complete token scores, so the
 // score stores are coalesced.  The epilogue counts each score's first radix
 // digit (top 11 bits of the order key) in an LDS histogram and tracks the
@@ -52,14 +53,21 @@ __device__ __forceinline__ float dot2(uint32_t k2, uint32_t q2, float acc) {
                                          __builtin_bit_cast(bf16x2, q2), acc, false);
 }
 
-// Partial score of one 8-dim key slice: the proxy query is held as two bf16
-// parts (hi + lo, ~16 significant bits); bf16 x bf16 products are exact and
-// accumulate in fp32.
-__device__ __forceinline__ float slice_dot(const uint32_t* qh, const uint32_t* ql, u32x4 k) {
+// Partial score of one 8-dim key slice: the proxy query is held as three
+// bf16 parts (hi + mid + lo: 24 significant bits, float32's precision);
+// bf16 x bf16 products are exact and accumulate in fp32.  The key words are
+// already in registers, so the third part costs VALU only (the kernel is
+// bound by HBM).
+__device__ __forceinline__ float slice_dot(const uint32_t* qh, const uint32_t* qm,
+                                           const uint32_t* ql, u32x4 k) {
   float s = dot2(k.x, qh[0], 0.0f);
   s = dot2(k.y, qh[1], s);
   s = dot2(k.z, qh[2], s);
   s = dot2(k.w, qh[3], s);
+  s = dot2(k.x, qm[0], s);
+  s = dot2(k.y, qm[1], s);
+  s = dot2(k.z, qm[2], s);
+  s = dot2(k.w, qm[3], s);
   s = dot2(k.x, ql[0], s);
   s = dot2(k.y, ql[1], s);
   s = dot2(k.z, ql[2], s);
@@ -118,8 +126,9 @@ template <int LPT, bool FULL>
 __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uint32_t* blk_sh,
                                                 uint64_t blk_stride, int d, int t0, int base,
                                                 int t_end,
-                                                const uint32_t* qh, const uint32_t* ql,
-                                                float* sbuf, uint32_t* hist, uint32_t& kmax,
+                                                const uint32_t* qh, const uint32_t* qm,
+                                                const uint32_t* ql, float* sbuf, uint32_t* hist,
+                                                uint32_t& kmax,
                                                 int lane) {
   constexpr int UNR = 8;
   constexpr int LG = LPT < 8 ? LPT : 8;
@@ -128,15 +137,18 @@ __device__ __forceinline__ void index_iteration(const uint16_t* kbase, const uin
   const int pos = (lane % LPT) % LG;
   const bool writer = LPT <= 8 || (lane & 8) == 0;
   const int tg = base + UNR * grp;  // first token of this lane's group (a multiple of 8)
+  // A group past the tile's end (ragged iteration only) loads nothing; it
+  // takes block 0's id so that its LDS read stays inside the tile's ids.
+  const int bi = (FULL || tg < t_end) ? (tg - t0) >> 4 : 0;
   const uint16_t* row0 =
-      kbase + (uint64_t)blk_sh[(tg - t0) >> 4] * blk_stride + (uint64_t)(tg & 15) * d;
+      kbase + (uint64_t)blk_sh[bi] * blk_stride + (uint64_t)(tg & 15) * d;
   u32x4 kv[UNR];
 #pragma unroll
   for (int r = 0; r < UNR; ++r)
     kv[r] = (FULL || tg + r < t_end) ? load_stream(row0 + (size_t)r * d) : u32x4{0u, 0u, 0u, 0u};
   float v[UNR];
 #pragma unroll
-  for (int r = 0; r < UNR; ++r) v[r] = slice_dot(qh, ql, kv[r]);
+  for (int r = 0; r < UNR; ++r) v[r] = slice_dot(qh, qm, ql, kv[r]);
   reduce_scatter<LPT>(v, lane);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -209,20 +221,29 @@ __device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, in
     __syncthreads();
   }
   // Per-lane proxy query over this lane's 8 dims, qbar = (scale / (G n)) *
-  // sum over the n members and G heads, split into bf16 hi and lo parts
-  // packed two dims per word.
-  uint32_t qh[4], ql[4];
+  // sum over the n members and G heads, split into bf16 hi, mid and lo parts
+  // (each the rounding of what the previous parts leave) packed two dims per
+  // word.
+  uint32_t qh[4], qm[4], ql[4];
   {
     const float qscale = a.scale / (float)(a.G * (t_last - t_first));
 #pragma unroll
     for (int i = 0; i < 8; ++i) qf[i] *= qscale;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t h0 = f32_to_bf16_bits(qf[2 * i]), h1 = f32_to_bf16_bits(qf[2 * i + 1]);
-      const uint32_t l0 = f32_to_bf16_bits(qf[2 * i] - __uint_as_float(h0 << 16));
-      const uint32_t l1 = f32_to_bf16_bits(qf[2 * i + 1] - __uint_as_float(h1 << 16));
-      qh[i] = h0 | (h1 << 16);
-      ql[i] = l0 | (l1 << 16);
+      uint32_t part[3][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float r = qf[2 * i + j];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          part[k][j] = f32_to_bf16_bits(r);
+          r -= __uint_as_float(part[k][j] << 16);
+        }
+      }
+      qh[i] = part[0][0] | (part[0][1] << 16);
+      qm[i] = part[1][0] | (part[1][1] << 16);
+      ql[i] = part[2][0] | (part[2][1] << 16);
     }
   }
   for (int i = tid; i < kBins / 2; i += 256) hist[i] = 0u;
@@ -252,13 +273,13 @@ __device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, in
       else
         __builtin_amdgcn_s_setprio(0);
     }
-    index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
-                               hist, kmax, lane);
+    index_iteration<LPT, true>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, qm, ql,
+                               sbuf, hist, kmax, lane);
   }
   __builtin_amdgcn_s_setprio(0);
   if (base < t_end)
-    index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, ql, sbuf,
-                                hist, kmax, lane);
+    index_iteration<LPT, false>(kbase, blk_sh, blk_stride, a.key_ld, t0, base, t_end, qh, qm, ql,
+                                sbuf, hist, kmax, lane);
 
   kmax = wave_max_u32(kmax);
   if (lane == 0) wmax[wave] = kmax;
