@@ -95,9 +95,16 @@ def jaccard(a, b):
 
 
 def score_tolerance_ok(gpu, ref):
+    """|gpu - ref| <= 1e-3 * max(|ref|, 1e-2 * rms(ref)) for every token: 1e-3
+    relative, with a floor at a hundredth of the unit's typical score (a pure
+    relative bound is ill-posed at a score of 0).  Returns (ok, worst
+    error / bound)."""
+    if ref.size == 0:
+        return True, 0.0
     err = np.abs(gpu.astype(np.float64) - ref)
-    bound = 1e-3 * np.maximum(np.abs(ref), 1.0)
-    return bool(np.all(err <= bound)), float((err / bound).max()) if err.size else 0.0
+    rms = float(np.sqrt(np.mean(np.square(ref))))
+    bound = 1e-3 * np.maximum(np.abs(ref), 1e-2 * rms)
+    return bool(np.all(err <= bound)), float((err / bound).max())
 
 
 def default_scale(d):

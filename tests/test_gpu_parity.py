@@ -1,7 +1,8 @@
 """GPU parity of the HIP path with the CPU oracle, through the C ABI.
 
 Bars (from the method's contract):
-  * scores:     |s_gpu - s_oracle| <= 1e-3 * max(|s_oracle|, 1) per token;
+  * scores:     |s_gpu - s_oracle| <= 1e-3 * max(|s_oracle|, 1e-2 * rms(s_oracle))
+                per token (rms over the unit);
   * selection:  bit-exact S and R (as index sets) when the library's
                 selection stage is fed the oracle's float32 scores and W;
   * output:     max |o_gpu - o_oracle| <= 2e-3 * max|V| (per unit, fp32 out)
