@@ -342,12 +342,13 @@ def cpu_baseline(wl, budget_s=15.0):
     """The oracle as it stands, on a bounded sample of the workload's units."""
     import numpy as np
 
+    from threadpoolctl import threadpool_limits
+
     from oracle import ssa_oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    # The oracle is plain numpy: sorts, Philox, the specified exp and the row
+    # gathers run on one thread; its two small matrix products are held to
+    # one BLAS thread too, so the core count below is the one it used.
+    limiter = threadpool_limits(limits=1)
     scale = 1.0 / math.sqrt(wl.d)
     units = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
     done, tokens, elapsed = 0, 0, 0.0
@@ -367,12 +368,14 @@ def cpu_baseline(wl, budget_s=15.0):
         del K, V, kc, vc
         if elapsed >= budget_s:
             break
+    limiter.unregister()
     # One unit is one kv head of one sequence; a layer has Hkv heads per token.
     value = tokens / wl.Hkv / elapsed
-    return dict(value=value, unit="KV-tokens/s/layer", cores=int(threads), kind="oracle",
+    return dict(value=value, unit="KV-tokens/s/layer", cores=1, kind="oracle",
+                host_cores=len(os.sched_getaffinity(0)),
                 sample=f"{done} of {len(units)} (sequence, kv head) units of the same workload, "
-                       f"{tokens} token-heads in {elapsed:.1f} s; layer rate = token-heads / "
-                       f"{wl.Hkv} / time")
+                       f"{tokens} token-heads in {elapsed:.1f} s on one thread (numpy, BLAS "
+                       f"limited to 1 thread); layer rate = token-heads / {wl.Hkv} / time")
 
 
 def summarize(res, workload):
@@ -391,11 +394,27 @@ def summarize(res, workload):
                                    if traffic else None))
     step_s = res["ms_step"] * 1e-3
     algo_total = res["idx_bytes"] + res["gather_bytes"]
-    return dict(
+    # The two HBM-bound kernels together (the path's >= 70% target): their
+    # algorithmic bytes over their summed event times from the breakdown pass.
+    pair_s = (st["index"] + st["attend"]) * 1e-3
+    index_gather = None
+    if pair_s > 0:
+        gbps = algo_total / pair_s / 1e9
+        index_gather = dict(bytes=algo_total, us=round(pair_s * 1e6, 2), gbps=round(gbps, 1),
+                            frac=round(gbps / HBM_PEAK_GBPS, 4))
+    cold = None
+    if res["cache"]:
+        c = res["cache"]
+        cold = dict(value=res["tokens"] / (c["cold_median_us"] * 1e-6),
+                    us=c["cold_median_us"],
+                    hbm_frac_algorithmic=round(algo_total / (c["cold_median_us"] * 1e-6) / 1e9
+                                               / HBM_PEAK_GBPS, 4))
+    return dict(index_gather=index_gather, cold=cold,
         value=res["tokens"] / step_s, ms_per_step=res["ms_step"], roofline=roof,
         stages_us={k: round(v * 1e3, 2) for k, v in st.items()},
         gpu_step_us=round(res["gpu_ms"] * 1e3, 2),
         hbm_gbps_algorithmic_step=round(algo_total / step_s / 1e9, 1),
+        hbm_frac_algorithmic_step=round(algo_total / step_s / 1e9 / HBM_PEAK_GBPS, 4),
         gather_gbps_algorithmic=(round(res["gather_bytes"] / (st["attend"] * 1e-3) / 1e9, 1)
                                  if st["attend"] > 0 else None),
         selected=dict(deterministic=res["n_det"], sampled=res["n_smp"]),
@@ -459,6 +478,9 @@ def main():
                           ms_per_step=s2["ms_per_step"], roofline=s2["roofline"],
                           stages_us=s2["stages_us"],
                           hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"],
+                          hbm_frac_algorithmic_step=s2["hbm_frac_algorithmic_step"],
+                          index_gather=s2["index_gather"],
+                          value_cache_flushed=s2["cold"],
                           per_step_cache=r2["cache"])
         del r2
         torch.cuda.empty_cache()
@@ -549,7 +571,10 @@ def main():
         "stages_us": main_sum["stages_us"],
         "gpu_step_us": main_sum["gpu_step_us"],
         "per_step_cache": res["cache"],
+        "value_cache_flushed": main_sum["cold"],
+        "index_gather": main_sum["index_gather"],
         "hbm_gbps_algorithmic_step": main_sum["hbm_gbps_algorithmic_step"],
+        "hbm_frac_algorithmic_step": main_sum["hbm_frac_algorithmic_step"],
         "gather_gbps_algorithmic": main_sum["gather_gbps_algorithmic"],
         "selected": main_sum["selected"],
         "also": also,
