@@ -22,8 +22,10 @@
  * ---------------------------------------
  * Memory.   Every array argument is a DEVICE pointer, owned by the caller, on
  *           the device current at the call.  The library allocates nothing;
- *           its only global state is a per-device cache of one occupancy
- *           query (a constant of the device, filled on first use, atomically).
+ *           its global state is a per-device cache of one occupancy query (a
+ *           constant of the device, filled on first use, atomically) and the
+ *           per-device static workspace of ssa_decode_static (a device array
+ *           of SSA_STATIC_WORKSPACE_BYTES, with its address looked up once).
  *           q, k_cache, k_rest, v_cache, k_new and v_new must be 16-byte
  *           aligned.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = null stream).
@@ -100,6 +102,8 @@ extern "C" {
 #define SSA_ERR_INVALID (-1)   /* bad params, null or misaligned pointer, bad size */
 #define SSA_ERR_WORKSPACE (-2) /* workspace smaller than ssa_workspace_bytes()     */
 #define SSA_ERR_HIP (-3)       /* a HIP call or kernel launch failed               */
+#define SSA_ERR_STATIC_LIMIT (-4) /* the step needs more workspace than             */
+                                  /* SSA_STATIC_WORKSPACE_BYTES (ssa_decode_static) */
 
 /* Output element types. */
 #define SSA_F32 0
@@ -184,6 +188,25 @@ int ssa_decode(const ssa_params* p, const void* q, const void* k_cache, const vo
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* topk,
                const float* top_p, const int32_t* sample_budget, const uint64_t* seed, void* out,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the device array that ssa_decode_static uses as its workspace:
+ * 128 MiB, held by every device the library runs on until the process ends.
+ * It covers, for example, a 128K-token layer of batch 4 with 8 kv heads. */
+#define SSA_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+/* ssa_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step, bitwise the same output, with the workspace taken from a device
+ * array of SSA_STATIC_WORKSPACE_BYTES that the library holds per device
+ * (its address is looked up once per device, on the first call with that
+ * device current).  Allocates nothing.  Returns SSA_ERR_STATIC_LIMIT, before
+ * any launch, when ssa_workspace_bytes(p) exceeds that size.  Every call on a
+ * device shares that device's array, so calls that overlap on one device
+ * (other streams or threads) race; calls in one stream are ordered. */
+int ssa_decode_static(const ssa_params* p, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* topk, const float* top_p, const int32_t* sample_budget,
+                      const uint64_t* seed, void* out, void* stream);
 
 /* ssa_decode, recording hipEvent_t events[2*s] before and events[2*s+1] after
  * the kernel(s) of stage s (SSA_STAGE_*); NULL entries are skipped, and a

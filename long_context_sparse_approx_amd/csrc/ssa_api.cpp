@@ -625,6 +625,7 @@ const char* ssa_error_string(int code) {
     case SSA_ERR_INVALID: return "invalid argument";
     case SSA_ERR_WORKSPACE: return "workspace too small";
     case SSA_ERR_HIP: return "HIP launch or runtime error";
+    case SSA_ERR_STATIC_LIMIT: return "step needs more than the static workspace (SSA_STATIC_WORKSPACE_BYTES)";
     default: return "unknown status";
   }
 }

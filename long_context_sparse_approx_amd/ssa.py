@@ -20,6 +20,8 @@ SSA_OK = 0
 SSA_ERR_INVALID = -1
 SSA_ERR_WORKSPACE = -2
 SSA_ERR_HIP = -3
+SSA_ERR_STATIC_LIMIT = -4
+STATIC_WORKSPACE_BYTES = 128 << 20
 SSA_F32 = 0
 SSA_BF16 = 1
 SSA_KEYS_WHOLE = 0
@@ -27,7 +29,8 @@ SSA_KEYS_SPLIT = 1
 BLOCK_TOKENS = 16
 CHUNK_TOKENS = 4096
 STAGES = ("init", "index", "filter", "resolve", "sample", "attend", "merge")
-EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_timed",
+EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_static",
+           "ssa_decode_timed",
            "ssa_decode_split", "ssa_score", "ssa_select", "ssa_attend", "ssa_attend_split",
            "ssa_append_kv", "ssa_host_device_address", "ssa_debug_philox", "ssa_debug_sexp",
            "ssa_error_string")
@@ -71,6 +74,8 @@ def lib() -> ctypes.CDLL:
         common = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_decode.argtypes = common
         L.ssa_decode.restype = ctypes.c_int
+        L.ssa_decode_static.argtypes = common[:11] + [_P]
+        L.ssa_decode_static.restype = ctypes.c_int
         L.ssa_decode_timed.argtypes = common + [_P]
         L.ssa_decode_timed.restype = ctypes.c_int
         L.ssa_decode_split.argtypes = ([_PP, _P, _P, _P] + common[3:] + [_P])
@@ -213,6 +218,23 @@ def decode(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk, sampl
         _check(lib().ssa_decode(*args), "ssa_decode")
     else:
         _check(lib().ssa_decode_timed(*args, ctypes.c_void_p(events)), "ssa_decode_timed")
+    return out
+
+
+def decode_static(p: SsaParams, q, k_cache, v_cache, block_table, seq_lens, topk,
+                  sample_budget, seed, out=None, stream=None, top_p=None):
+    """decode() with the library's own static device workspace (no
+    workspace argument; the library allocates nothing).  Raises SsaError
+    with SSA_ERR_STATIC_LIMIT when the step needs more than
+    STATIC_WORKSPACE_BYTES."""
+    _check_top_p(top_p, p.batch)
+    if out is None:
+        dt = torch.float32 if p.out_dtype == SSA_F32 else torch.bfloat16
+        out = torch.empty(q.shape, dtype=dt, device=q.device)
+    _check(lib().ssa_decode_static(
+        ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(topk), _ptr(top_p), _ptr(sample_budget), _ptr(seed), _ptr(out),
+        _stream(stream)), "ssa_decode_static")
     return out
 
 

@@ -1,0 +1,66 @@
+"""ssa_decode_static (the allocation-free decode entry point) against
+ssa_decode with a caller-allocated workspace, through the C ABI.
+
+Two calls in a row on the static workspace, the second with a smaller
+problem than the first (different batch, heads, head size and lengths), each
+bitwise equal to ssa_decode on the same inputs; then the same first problem
+again; and a problem whose workspace exceeds SSA_STATIC_WORKSPACE_BYTES is
+refused before any launch.
+"""
+
+import pytest
+import torch
+
+from long_context_sparse_approx_amd import ssa, synth
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+BIG = dict(B=3, Hq=32, Hkv=8, d=128, L=[20000, 4097, 9000], theta=1e6, kdist="normal",
+           planted=8, pair_count=32, topk="rule", m="rule", seeds=[41, 42, 43], data_seed=61)
+SMALL = dict(B=1, Hq=8, Hkv=1, d=64, L=[5000], theta=1e4, kdist="normal", planted=4,
+             pair_count=16, topk=40, m=30, seeds=[44], data_seed=62)
+
+
+def run_pair(cfg, label):
+    wl = synth.make_workload(dict(cfg), DEV)
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    need = ssa.workspace_bytes(p)
+    assert need <= ssa.STATIC_WORKSPACE_BYTES
+    args = (p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+            wl.sample_budget, wl.seed)
+    say(f"[no-alloc] {label}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} L={wl.lens} "
+        f"workspace {need} B")
+    got = ssa.decode_static(*args).clone()
+    torch.cuda.synchronize()
+    ref = ssa.decode(*args)
+    torch.cuda.synchronize()
+    assert torch.isfinite(got).all()
+    assert torch.equal(got, ref), f"{label}: max |diff| {float((got - ref).abs().max())}"
+    say(f"[no-alloc] {label}: bitwise equal to ssa_decode")
+    return wl
+
+
+def test_static_workspace_decode_matches_decode():
+    run_pair(BIG, "first call")
+    run_pair(SMALL, "second call, smaller")
+    run_pair(BIG, "third call, the first problem again")
+
+
+def test_static_workspace_limit_refused():
+    wl = synth.make_workload(dict(SMALL), DEV)
+    # A 1M-token sequence capacity with 8 kv heads needs far more than 128 MiB.
+    p = ssa.make_params(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                        max_blocks_per_seq=65536, num_blocks=wl.k_cache.shape[0],
+                        max_seq_len=1 << 20, pair_count=32)
+    assert ssa.workspace_bytes(p) > ssa.STATIC_WORKSPACE_BYTES
+    out = torch.zeros((1, 32, 128), dtype=torch.float32, device=DEV)
+    with pytest.raises(ssa.SsaError) as e:
+        ssa.decode_static(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                          wl.sample_budget, wl.seed, out=out)
+    assert e.value.code == ssa.SSA_ERR_STATIC_LIMIT
+    torch.cuda.synchronize()
+    assert float(out.abs().max()) == 0.0  # nothing was launched
