@@ -140,7 +140,8 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
                        query_group=query_group, early_stop=early_stop,
-                       key_layout=ssa.SSA_KEYS_SPLIT if split else ssa.SSA_KEYS_WHOLE)
+                       key_layout=ssa.SSA_KEYS_SPLIT if split else ssa.SSA_KEYS_WHOLE,
+                       max_topk=int(wl.topk.max()))
     ws = ssa.alloc_workspace(p, dev)
     out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -248,7 +249,8 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     # Selected-set sizes of this step (deterministic: same kernels, same inputs).
     sc = ssa.score(p, wl.q, call[2], wl.block_table, wl.seq_lens, workspace=ws)
     _, _, cnt, _ = ssa.select(p, sc, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
-                              workspace=ws, top_p=tp)
+                              workspace=ws, top_p=tp, q=wl.q, k_cache=call[2],
+                              k_rest=call[3] if split else None, block_table=wl.block_table)
     cnt = cnt.sum(dim=2).cpu()
     n_det, n_smp = int(cnt[..., 0].sum()), int(cnt[..., 1].sum())
     del sc
@@ -501,8 +503,9 @@ def main():
         s5 = summarize(r5, args.workload)
         variants["early_stop"] = dict(
             policy=f"deterministic stratum visited in 64-token blocks of its order, stopping "
-                   f"after the first block whose gain is below {args.early_stop} of the mass "
-                   "so far; same tail sample",
+                   f"after the first block at which every query head's gain in exact "
+                   f"attention mass is below {args.early_stop} of its mass so far; same tail "
+                   "sample",
             value=s5["value"], unit="KV-tokens/s/layer", ms_per_step=s5["ms_per_step"],
             stages_us=s5["stages_us"], selected=s5["selected"])
         del r5

@@ -34,7 +34,8 @@
  *           work is enqueued when argument validation fails.  Host-visible
  *           arguments (params, pointers, sizes) are validated; device-resident
  *           values are not: seq_lens are clamped to [0, max_seq_len],
- *           negative topk / sample_budget act as 0, and block_table entries
+ *           negative topk / sample_budget act as 0, topk above a positive
+ *           params.max_topk acts as max_topk, and block_table entries
  *           are clamped to [0, num_blocks) (a wrong entry reads a wrong block,
  *           never out of bounds).
  * Determinism. No floating-point atomics are used: identical inputs and
@@ -148,7 +149,16 @@ typedef struct ssa_params {
   int32_t query_group;        /* g >= 1 consecutive queries sharing one selection        */
   float early_stop;           /* tau of the early-stopping rule below; <= 0 or NaN = off */
   int32_t key_layout;         /* SSA_KEYS_WHOLE or SSA_KEYS_SPLIT                         */
+  int32_t max_topk;           /* >= 0: an upper bound of topk[b] (larger device values    */
+                              /*   act as it); 0 = max_seq_len.  Early stopping needs     */
+                              /*   it (or max_seq_len) <= SSA_STOP_MAX_STRATUM            */
 } ssa_params;
+
+/* Largest deterministic stratum the early-stopping kernels order (tokens). */
+#define SSA_STOP_MAX_STRATUM 16384
+/* Largest number of query rows (members x query heads) of one selection unit
+ * that early stopping weighs. */
+#define SSA_STOP_MAX_ROWS 16
 
 /* Bytes of device workspace that ssa_decode / ssa_score / ssa_select /
  * ssa_attend need for these params (0 if params are invalid).  The workspace
@@ -172,13 +182,26 @@ int32_t ssa_num_chunks(const ssa_params* p);
  * To use top-p alone pass topk[b] >= L_b.
  *
  * Early stopping ("S2O: Early Stopping for Sparse Attention via Online
- * Permutation", methodology part 2).  With params.early_stop = tau > 0 the
- * stratum, in its order, is visited in blocks of 64 tokens; a block's gain is
- * its mass in the units above and the visit stops after the first block whose
- * gain is below tau times the mass of the blocks visited so far (exact
- * comparison; tau above 1 acts as 1).  The rest of the stratum is skipped:
- * neither read nor sampled; the tail sample is unchanged.  A stratum of more
- * than 16384 tokens is visited whole.
+ * Permutation", methodology parts 2 and 3).  With params.early_stop = tau > 0
+ * the stratum, in its order, is visited in blocks of 64 tokens while the
+ * online-softmax state of every query row of the unit (each query head of
+ * each member of the query group; a row sees only tokens inside its member's
+ * span) takes in the block's exact attention mass; the visit stops after the
+ * first block at which, for every row, the block's gain in the row's softmax
+ * denominator l is 0 or below tau times the row's l so far (tau above 1 acts
+ * as 1).  The rest of the stratum is skipped: neither read nor sampled; the
+ * tail sample is unchanged.  The decision is exact and reproducible: the
+ * logit is fl32(scale * dot), the dot of bf16 values summed in float32 (each
+ * 8-dim slice in dim order, then the slices pairwise), and gains are counted
+ * in the integer units above, floor(2^38 exp(l - M_row)) with the specified
+ * exp and M_row the row's largest logit over the stratum.  Requires the
+ * stratum bound (params.max_topk, or max_seq_len when it is 0) to be at most
+ * SSA_STOP_MAX_STRATUM and the unit's query rows (min(query_group,
+ * num_queries) x Hq / Hkv) at most SSA_STOP_MAX_ROWS; otherwise every entry
+ * point returns SSA_ERR_INVALID.  Cost: ordering the stratum and weighing it
+ * takes six short kernels (about 40 us for a 1M-token layer of 8 kv heads
+ * with a 10486-token stratum), more than the attention it saves at 50x
+ * sparsity; it pays only where attention over the stratum dominates.
  *
  * Tail.  sample_budget[b] (m) is the expected number of tail samples.  If
  * k + m >= L_b every token is read with weight 1 (dense attention).
@@ -229,34 +252,59 @@ int ssa_decode_split(const ssa_params* p, const void* q, const void* k_dom, cons
                      const uint64_t* seed, void* out, void* workspace, size_t workspace_bytes,
                      void* stream, void* const* events);
 
-/* Stage 1 alone: approximate scores, scores[u * max_seq_len + j] (f32) of
+/* Stage 1 alone ("FASA: Frequency-aware Sparse Attention", section 3 stage 1
+ * TIP: a token's online score sums the contributions of a fixed subset of
+ * RoPE frequency chunks; the query group is averaged into one proxy query as
+ * in "PIVOT slashes sparse-attention indexer cost", "The two observations
+ * behind PIVOT"): approximate scores, scores[u * max_seq_len + j] (f32) of
  * selection unit u = (b * NG + group) * Hkv + h, for j below the group's span
  * (its last member's causal length); later entries are left untouched.
  *   s_j = (1/(n G)) sum over the group's n members and G heads of
  *         scale * sum_{p in pairs} (q[2p] k_j[2p] + q[2p+1] k_j[2p+1]).
- * k_cache holds whole keys or, with SSA_KEYS_SPLIT, the scored dims only. */
+ * k_cache holds whole keys or, with SSA_KEYS_SPLIT, the scored dims only.
+ * Errors as for ssa_decode. */
 int ssa_score(const ssa_params* p, const void* q, const void* k_cache,
               const int32_t* block_table, const int32_t* seq_lens, float* scores,
               void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stages 2-4 alone, from a caller-provided score array laid out as ssa_score
- * writes it (one row per selection unit, valid over the unit's span); topk,
- * top_p (may be NULL) and sample_budget as for ssa_decode.  Sampling for
- * (b, group, h, token j) uses counter (j >> 2, h, b, group).
- * If w_in is non-NULL, w_in[b*Hkv + h] replaces the computed tail normaliser
- * W.  Writes the selection (layout above) and norm_out [B, Hkv, 2] = (M, W):
- * the maximum score and the normaliser actually used. */
+/* Stages 2-4 alone ("Stratified Sparse Attention speeds up decoding 2.96x
+ * at 1M context", sections "Where sparse attention loses quality" and "How
+ * SSA stratifies the cache": the top-k or top-p stratum read
+ * deterministically, the tail Poisson-sampled with probability proportional
+ * to exp(score) and weighted by the inverse inclusion probability), from a
+ * caller-provided score array laid out as ssa_score writes it (one row per
+ * selection unit, valid over the unit's span); topk, top_p (may be NULL) and
+ * sample_budget as for ssa_decode.  Sampling for (b, group, h, token j) uses
+ * counter (j >> 2, h, b, group).  If w_in is non-NULL, w_in[u] replaces the
+ * computed tail normaliser W of unit u.  Writes the selection (layout above)
+ * and norm_out [B, NG, Hkv, 2] = (M, W): the maximum score and the normaliser
+ * actually used.  q, k_cache, k_rest and block_table are read only by early
+ * stopping (params.early_stop > 0), which weighs the stratum by exact
+ * attention (k_rest as for ssa_decode_split with SSA_KEYS_SPLIT, else NULL);
+ * they may be NULL when it is off.  Errors as for ssa_decode; the score
+ * array is not validated (non-finite scores select arbitrarily but stay in
+ * bounds). */
 int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
                const int32_t* topk, const float* top_p, const int32_t* sample_budget,
-               const uint64_t* seed, const float* w_in, int32_t* sel_idx, float* sel_logw,
+               const uint64_t* seed, const float* w_in, const void* q, const void* k_cache,
+               const void* k_rest, const int32_t* block_table, int32_t* sel_idx, float* sel_logw,
                int32_t* sel_count, float* norm_out, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* Stages 5-6 alone: attention over a caller-provided selection (one per
- * selection unit), for every query position t and head g of the unit's group:
+/* Stages 5-6 alone ("FASA: Frequency-aware Sparse Attention", section 3
+ * stage 2 FAC: full-precision attention on the selected tokens at their
+ * original positions; the inverse-inclusion-probability weights of "How SSA
+ * stratifies the cache" enter as logit biases; split partial states
+ * (m, l, acc) are merged as in "S2O: Early Stopping for Sparse Attention via
+ * Online Permutation", methodology part 3): attention over a caller-provided
+ * selection (one per selection unit), for every query position t and head g
+ * of the unit's group:
  *   out_g = sum_A e^{l_gj + logw_j} v_j / sum_A e^{l_gj + logw_j},
  *   l_gj = scale * q_g . k_j over the full head dimension, A = the unit's
- *   selected positions below the query's span (later ones are ignored). */
+ *   selected positions below the query's span (later ones are ignored).
+ * Counts are clamped to a chunk's segment and positions to the span, so a
+ * malformed selection reads wrong rows, never out of bounds.  Errors as for
+ * ssa_decode. */
 int ssa_attend(const ssa_params* p, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_table, const int32_t* seq_lens, const int32_t* sel_idx,
                const float* sel_logw, const int32_t* sel_count, void* out, void* workspace,

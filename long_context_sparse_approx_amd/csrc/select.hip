@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
   const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
   if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
   const float M = key_to_float(maxkey);
   for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = 0ull;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
   if (p.dense || p.L == 0) {
     if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0, 0ull, 0, 0};
     return;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void f
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const int h = ui.h;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const float M = key_to_float(maxkey);
   if (!direct) {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   constexpr int kHist = kBins / kRT;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
   const Thresh1 t1 = a.thresh[u];
   const uint32_t maxkey = a.maxkey[u];
   uint32_t hv[kHist];
@@ -475,31 +475,39 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 
 // ------------------------------------------------------------------ early stopping
 // "S2O: Early Stopping for Sparse Attention via Online Permutation",
-// methodology part 2.  The deterministic stratum, in its order (key
-// descending, position ascending), is cut into 64-token blocks whose gains are
-// their mass units; the visit stops after the first block whose gain is below
-// tau times the mass so far (exact integer arithmetic).  A token's word is
-// ((~key) << 32) | position, so ascending words are the stratum's order, and
-// the cut is published as the last word kept: the sample kernel drops every
-// deterministic token whose word is larger.  The stratum is the tokens above
-// the threshold key T (at most 16384 when a cut applies) followed by the
-// first ties on T (one mass value, ranked by position), so only the former
-// are ordered, in five steps that spread over the device and use no global
-// atomics:
-//   stop_gather: each chunk writes its words above T (its listed tokens
-//     above the threshold digit, then its candidates above T) at the offset
-//     the resolve kernel computed for it;
+// methodology parts 2 and 3.  The deterministic stratum, in its order (key
+// descending, position ascending), is visited in 64-token blocks while the
+// online-softmax state of every query row of the unit (each query head of each
+// member of its query group) takes in the block's exact attention mass; the
+// visit stops after the first block at which every row's gain in its softmax
+// denominator l is 0 or below tau times the row's l so far.  Gains are counted
+// in integer units floor(2^38 sexp(l - M_row)) of exact logits computed in a
+// specified float32 order, so the cut is exact and reproducible.  A token's
+// word is ((~key) << 32) | position, so ascending words are the stratum's
+// order, and the cut is published as the last word kept: the sample kernel
+// drops every deterministic token whose word is larger.  The stratum is the
+// tokens above the threshold key T followed by the first ties on T (ranked by
+// position); only the former need sorting.  Six kernels, none with a global
+// atomic:
+//   stop_gather: each chunk writes its words above T (its listed tokens above
+//     the threshold digit, then its candidates above T) at the offset the
+//     resolve kernel computed for it, and its ties within the quota straight
+//     to their ranks (after every word above T);
 //   stop_sort: one workgroup sorts each 1024-word slice (4 words per thread
 //     in registers, cross-wave exchanges through LDS);
 //   stop_pair: for every pair of slices, the number of words of one below
 //     each word of the other (searched in LDS), one count array per pair;
 //   stop_final: each word's rank = its index in its slice + those counts;
-//     mass and word stored in rank order;
-//   stop_cut: one workgroup per unit sums the block gains (ties count at
-//     T's mass), scans them, finds the stop and writes the last word kept.
+//     the words stored in rank order;
+//   stop_logit: one wave per 64-token block of the order computes every
+//     row's exact logit of its tokens (key rows through the block table);
+//   stop_cut: one workgroup per unit takes each row's maximum, the block
+//     gains, their prefix sums and the first block where every row agrees,
+//     and writes the last word kept.
 constexpr int kStopBlock = 64;
-constexpr int kStopMax = 16384;  // largest stratum that is truncated
-constexpr int kSlice = 1024;     // words sorted per wave
+constexpr int kStopMax = SSA_STOP_MAX_STRATUM;  // largest stratum that is ordered
+constexpr int kStopRows = SSA_STOP_MAX_ROWS;    // query rows per unit, at most
+constexpr int kSlice = 1024;     // words sorted per workgroup
 constexpr int kSlices = kStopMax / kSlice;
 constexpr int kSortT = 256;                // threads per slice sort
 constexpr int kSE = kSlice / kSortT;      // words per thread in the sort
@@ -511,10 +519,10 @@ __device__ __forceinline__ bool gain_below(unsigned long long gain, unsigned lon
   int e;
   const float f = __builtin_frexpf(tau, &e);
   const unsigned long long mant = (unsigned long long)(f * 0x1.0p24f);  // tau = mant 2^(e-24)
-  const unsigned __int128 rhs = (unsigned __int128)mant * acc;          // < 2^86
+  const unsigned __int128 rhs = (unsigned __int128)mant * acc;          // < 2^88
   const int D = 24 - e;                                                 // >= 24
   if (gain == 0ull) return rhs != 0;
-  if (D >= 86 || (64 - __builtin_clzll(gain)) + D > 127) return false;  // lhs >= 2^86 > rhs
+  if (D >= 88 || (64 - __builtin_clzll(gain)) + D > 127) return false;  // lhs >= 2^88 > rhs
   return ((unsigned __int128)gain << D) < rhs;
 }
 
@@ -630,27 +638,37 @@ __global__ __launch_bounds__(kNT) void stop_gather_kernel(SelectArgs a) {
   const int off = a.stop_off[ci];
   const int n_above = clamp_count(a.list_cnt[2 * ci], kChunk);
   const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
+  const int tie0 = a.ties_before[ci];  // ties on T in earlier chunks
   const int nvalid = min(kChunk, st.L - c0);
   const float* srow = a.scores + (size_t)u * a.score_ld;
   unsigned long long* out = a.stop_words + (size_t)u * kStopMax;
+  unsigned long long* rword = a.stop_rword + (size_t)u * kStopMax;
   for (int i = threadIdx.x; i < n_above; i += kNT) {
     const int pos = c0 + min(max(a.list_idx[seg + i] - c0, 0), nvalid - 1);
     const int at = off + i;
     if (at >= 0 && at < n_words) out[at] = stratum_word(order_key(srow[pos]), pos);
   }
-  // Candidates above T, compacted in list (position) order.
+  // Candidates above T, compacted in list (position) order, and the ties on
+  // T within the quota, at ranks n_words + (their rank among the ties).
   int run = off + n_above;
+  int tie_run = tie0;
   for (int base = 0; base < ncand; base += kNT) {
     const int i = base + threadIdx.x;
     const uint32_t key = i < ncand ? a.cand_key[seg + i] : 0u;
     const bool in = i < ncand && key > st.tkey;
+    const bool tie = i < ncand && key == st.tkey;
     int tot;
-    const int at = run + block_exclusive_scan<kNT>(in ? 1 : 0, scan_scr, &tot);
-    if (in && at >= 0 && at < n_words) {
-      const int pos = c0 + min(max(a.cand_idx[seg + i] - c0, 0), nvalid - 1);
-      out[at] = stratum_word(key, pos);
+    const int ex = block_exclusive_scan<kNT>((in ? 1 : 0) | (tie ? 0x10000 : 0), scan_scr, &tot);
+    const int pos = c0 + min(max((i < ncand ? a.cand_idx[seg + i] : c0) - c0, 0), nvalid - 1);
+    const int at = run + (ex & 0xffff);
+    if (in && at >= 0 && at < n_words) out[at] = stratum_word(key, pos);
+    const int tr = tie_run + (ex >> 16);
+    if (tie && tr >= 0 && tr < st.ties_needed) {
+      const int rank = n_words + tr;
+      if (rank < kStopMax) rword[rank] = stratum_word(key, pos);
     }
-    run += tot;
+    run += tot & 0xffff;
+    tie_run += tot >> 16;
   }
 }
 
@@ -743,27 +761,105 @@ __global__ __launch_bounds__(kNT) void stop_final_kernel(SelectArgs a) {
       rank[3] += c4.y >> 16;
     }
   }
-  unsigned long long* mass = a.stop_mass + (size_t)u * kStopMax;
   unsigned long long* rword = a.stop_rword + (size_t)u * kStopMax;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     // words are distinct, so ranks are: a permutation of [0, n_words)
-    if (x[e] != ~0ull && rank[e] < n_words) {
-      const uint32_t key = ~(uint32_t)(x[e] >> 32);
-      mass[rank[e]] = mass_units(sexp(key_to_float(key) - st.M));
-      rword[rank[e]] = x[e];
+    if (x[e] != ~0ull && rank[e] < n_words) rword[rank[e]] = x[e];
+  }
+}
+
+// The exact logit of each (rank, query row) of a unit's stratum, in the
+// specified float32 order: lane c of a token's D/8 lanes holds its 8-dim
+// slice c, sums the 8 exact bf16 products in dim order, and the slices are
+// combined pairwise by butterfly exchanges (lane c and its partner add the
+// same two values, so every lane ends with the same sum); then one multiply
+// by the softmax scale.  Rows whose member's span excludes the token get
+// -inf.  Grid: (kStopMax / 64, units) x 64 threads, one wave per block.
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(64) void stop_logit_kernel(SelectArgs a) {
+  constexpr int LPT = D / 8;     // lanes per token
+  constexpr int TPI = 64 / LPT;  // tokens per iteration
+  __shared__ float qsh[kStopRows * D];
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int n = min(st.k_eff, kStopMax);
+  const int r0 = blockIdx.x * kStopBlock;
+  if (r0 >= n) return;  // uniform
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const int h = ui.h;
+  const int lane = threadIdx.x;
+  const int t0 = ui.grp * a.g;                 // the group's first member
+  const int nmem = min(a.g, a.T - t0);
+  const int rows = min(nmem * a.G, kStopRows);  // the host guarantees nmem * G <= kStopRows
+  const int P = clamp_len(a.seq_lens[b], a.max_seq_len);
+  for (int i = lane; i < rows * D; i += 64) {
+    const int r = i / D;
+    const int e = i - r * D;
+    const int t = t0 + r / a.G;
+    const uint16_t bits = a.q[((size_t)(b * a.T + t) * a.Hq + h * a.G + r % a.G) * D + e];
+    qsh[i] = __uint_as_float((uint32_t)bits << 16);
+  }
+  __syncthreads();
+  const int sl = lane % LPT;  // this lane's slice
+  const int tk = lane / LPT;
+  // This lane's key slice: dims sl*8 .. +8 of row r are at kb + r * kld.
+  const uint16_t* kb;
+  uint32_t kld;
+  {
+    const int dim = sl * 8;
+    if (!SPLIT) {
+      kb = a.k_cache + dim;
+      kld = D;
+    } else {
+      const int lo = 2 * a.pair_begin;
+      const int nd = 2 * a.pair_count;
+      const bool scored = dim >= lo && dim < lo + nd;
+      kb = scored ? a.k_cache + (dim - lo) : a.k_rest + (dim < lo ? dim : dim - nd);
+      kld = scored ? nd : D - nd;
+    }
+  }
+  const unsigned long long* rword = a.stop_rword + (size_t)u * kStopMax;
+  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  float* out = a.stop_logit + (size_t)u * kStopMax * kStopRows;
+  const int L = ui.L;
+  for (int it = 0; it < kStopBlock / TPI; ++it) {
+    const int rank = r0 + it * TPI + tk;
+    const bool valid = rank < n;
+    const int pos = valid ? min(max((int)(uint32_t)rword[rank], 0), max(L - 1, 0)) : 0;
+    int blk = btrow[pos >> 4];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    const uint32_t row = (uint32_t)((blk * a.Hkv + h) * kBlockTokens + (pos & 15));
+    const uint4 kv = *reinterpret_cast<const uint4*>(kb + (size_t)row * kld);
+    const float kf[8] = {bf16_lo(kv.x), bf16_hi(kv.x), bf16_lo(kv.y), bf16_hi(kv.y),
+                         bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
+#pragma unroll
+    for (int r = 0; r < kStopRows; ++r) {
+      if (r >= rows) break;  // uniform
+      const float* qr = qsh + r * D + sl * 8;
+      float acc = qr[0] * kf[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) acc = acc + qr[i] * kf[i];  // exact products
+#pragma unroll
+      for (int x = 1; x < LPT; x <<= 1) acc = acc + __shfl_xor(acc, x);
+      const float l = acc * a.scale;
+      const bool vis = pos < member_span(P, a.T, t0 + r / a.G);
+      if (valid && sl == r % LPT) out[(size_t)rank * kStopRows + r] = vis ? l : -INFINITY;
     }
   }
 }
 
-// Grid: units x kNT threads (one per 64-token block of the largest stratum).
-__global__ __launch_bounds__(kNT) void stop_cut_kernel(SelectArgs a) {
+// Grid: units x kCutT threads.
+constexpr int kCutT = 1024;
+constexpr int kCutW = kCutT / 64;
+__global__ __launch_bounds__(kCutT) void stop_cut_kernel(SelectArgs a) {
   constexpr int kNB = kStopMax / kStopBlock;
-  static_assert(kNB == kNT, "one thread per block of the largest stratum");
-  __shared__ unsigned long long scan_m[kNT / 64];
-  __shared__ int scan_scr[kNT / 64];
+  __shared__ uint32_t mkey[kStopRows];                // each row's largest logit (order key)
+  __shared__ unsigned long long gain[kNB][kStopRows];  // block gains in units
+  __shared__ unsigned long long scan_m[kCutW];
   __shared__ int first_sh;
-  __shared__ int tie_pos_sh;
   const int u = blockIdx.x;
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   const int tid = threadIdx.x;
@@ -771,68 +867,67 @@ __global__ __launch_bounds__(kNT) void stop_cut_kernel(SelectArgs a) {
     if (tid == 0) a.stop_cut[u] = ~0ull;
     return;
   }
-  const int n = st.k_eff;
-  const int n_words = min(min(max(a.stop_n[u], 0), kStopMax), n);  // ranks below: words above T
-  const unsigned long long qT = mass_units(sexp(key_to_float(st.tkey) - st.M));
+  const int n = min(st.k_eff, kStopMax);
   const int nb = (n + kStopBlock - 1) / kStopBlock;
-  if (tid == 0) {
-    first_sh = 0x7fffffff;
-    tie_pos_sh = 0;
-  }
-  unsigned long long g = 0ull;
-  if (tid < nb) {
-    // The block's masses: 32 16-byte loads, all in flight together.
-    const unsigned long long* mass = a.stop_mass + (size_t)u * kStopMax;
-    const int r0 = tid * kStopBlock;
-    const int r1 = min(r0 + kStopBlock, n);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int rows = min(min(a.g, a.T - ui.grp * a.g) * a.G, kStopRows);
+  const float* lg = a.stop_logit + (size_t)u * kStopMax * kStopRows;
+  if (tid < kStopRows) mkey[tid] = 0u;
+  if (tid == 0) first_sh = 0x7fffffff;
+  __syncthreads();
+  // 1. Each row's maximum over the stratum (-inf entries never count).
+  {
+    uint32_t mk[kStopRows];
 #pragma unroll
-    for (int q = 0; q < kStopBlock / 2; ++q) {
-      const int r = r0 + 2 * q;
-      if (r < n_words) {
-        const ulonglong2 m2 = *reinterpret_cast<const ulonglong2*>(mass + r);
-        g += m2.x + (r + 1 < n_words ? m2.y : 0ull);
+    for (int r = 0; r < kStopRows; ++r) mk[r] = 0u;
+    for (int rank = tid; rank < n; rank += kCutT) {
+#pragma unroll
+      for (int r = 0; r < kStopRows; ++r) {
+        if (r < rows) {
+          const float l = lg[(size_t)rank * kStopRows + r];
+          const uint32_t k = l > -INFINITY ? order_key(l) : 0u;
+          mk[r] = k > mk[r] ? k : mk[r];
+        }
       }
     }
-    if (r1 > n_words) g += (unsigned long long)(r1 - max(r0, n_words)) * qT;  // ties on T
+#pragma unroll
+    for (int r = 0; r < kStopRows; ++r) {
+      if (r < rows) {
+        const uint32_t v = wave_max_u32(mk[r]);
+        if ((tid & 63) == 0 && v) atomicMax(&mkey[r], v);
+      }
+    }
   }
-  unsigned long long tot;
-  const unsigned long long acc = block_exclusive_scan<kNT>(g, scan_m, &tot) + g;
-  if (tid < nb && gain_below(g, acc, a.stop_tau)) atomicMin(&first_sh, tid);
+  __syncthreads();
+  // 2. Block gains: wave w takes blocks w, w + kCutW, ...; lane = token.
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int i = wave; i < nb; i += kCutW) {
+      const int rank = i * kStopBlock + lane;
+      for (int r = 0; r < rows; ++r) {
+        const float l = rank < n ? lg[(size_t)rank * kStopRows + r] : -INFINITY;
+        const unsigned long long q =
+            (l > -INFINITY && mkey[r]) ? mass_units(sexp(l - key_to_float(mkey[r]))) : 0ull;
+        const unsigned long long g = wave_sum(q);
+        if (lane == 0) gain[i][r] = g;
+      }
+    }
+  }
+  __syncthreads();
+  // 3. Per row, the mass so far; block i agrees when every row's gain is 0
+  //    or below tau times its mass so far.
+  bool agree = tid < nb;
+  for (int r = 0; r < rows; ++r) {  // uniform
+    const unsigned long long g = tid < nb ? gain[tid][r] : 0ull;
+    unsigned long long tot;
+    const unsigned long long acc = block_exclusive_scan<kCutT>(g, scan_m, &tot) + g;
+    if (g != 0ull && !gain_below(g, acc, a.stop_tau)) agree = false;
+  }
+  if (agree) atomicMin(&first_sh, tid);
   __syncthreads();
   const int kept = first_sh == 0x7fffffff ? n : min(n, (first_sh + 1) * kStopBlock);
-  unsigned long long cut = ~0ull;  // nothing cut
-  if (kept < n) {
-    if (kept <= n_words) {
-      cut = a.stop_rword[(size_t)u * kStopMax + kept - 1];
-    } else {
-      // The cut falls among the ties on T: tie number t (in position order)
-      // is the last one kept.  Find its chunk, then its place in the chunk's
-      // candidate list (position order).
-      const int t = kept - n_words - 1;
-      const size_t cu = (size_t)u * a.nchunk;
-      const int nc = (st.L + kChunk - 1) / kChunk;
-      for (int c = 0; c < nc; ++c) {  // uniform loop; each chunk's test is uniform
-        const int tb = a.ties_before[cu + c];
-        const int tc = a.tiecnt[cu + c];
-        if (t < tb || t >= tb + tc) continue;
-        const int ncand = clamp_count(a.cand_cnt[cu + c], kChunk);
-        const size_t seg = (size_t)u * a.seg_ld + (size_t)c * kChunk;
-        int run = tb;
-        for (int base = 0; base < ncand; base += kNT) {
-          const int i = base + tid;
-          const bool tie = i < ncand && a.cand_key[seg + i] == st.tkey;
-          int ntie;
-          const int r = run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &ntie);
-          if (tie && r == t) tie_pos_sh = min(max(a.cand_idx[seg + i], 0), st.L - 1);
-          run += ntie;
-        }
-        break;
-      }
-      __syncthreads();
-      cut = stratum_word(st.tkey, tie_pos_sh);
-    }
-  }
-  if (tid == 0) a.stop_cut[u] = cut;
+  if (tid == 0)
+    a.stop_cut[u] = kept < n ? a.stop_rword[(size_t)u * kStopMax + kept - 1] : ~0ull;
 }
 
 // ------------------------------------------------------------------ sample
@@ -1040,11 +1135,22 @@ hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream) {
 }
 
 hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream) {
+  if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
   stop_gather_kernel<<<dim3(a.nchunk, units), kNT, 0, stream>>>(a);
   stop_sort_kernel<<<dim3(kSlices, units), kSortT, 0, stream>>>(a);
   stop_pair_kernel<<<dim3(kSlices * kSlices, units), kNT, 0, stream>>>(a);
   stop_final_kernel<<<dim3(kSlices, units), kNT, 0, stream>>>(a);
-  stop_cut_kernel<<<units, kNT, 0, stream>>>(a);
+  const dim3 lg(kStopMax / kStopBlock, units);
+  const bool split = a.k_rest != nullptr;
+  if (a.d == 128 && !split)
+    stop_logit_kernel<128, false><<<lg, 64, 0, stream>>>(a);
+  else if (a.d == 128)
+    stop_logit_kernel<128, true><<<lg, 64, 0, stream>>>(a);
+  else if (!split)
+    stop_logit_kernel<64, false><<<lg, 64, 0, stream>>>(a);
+  else
+    stop_logit_kernel<64, true><<<lg, 64, 0, stream>>>(a);
+  stop_cut_kernel<<<units, kCutT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -45,6 +45,14 @@ bool params_ok(const ssa_params* p) {
   if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale)) return false;
   if (p->num_queries < 1 || p->num_queries > 256 || p->query_group < 1) return false;
   if (p->key_layout != SSA_KEYS_WHOLE && p->key_layout != SSA_KEYS_SPLIT) return false;
+  if (p->max_topk < 0) return false;
+  if (p->early_stop > 0.0f) {  // NaN compares false: off
+    // the stratum must fit the early-stopping kernels, and so must the rows
+    const int bound = p->max_topk > 0 ? p->max_topk : p->max_seq_len;
+    if (bound > SSA_STOP_MAX_STRATUM) return false;
+    const int g = p->query_group < p->num_queries ? p->query_group : p->num_queries;
+    if ((int64_t)g * G > SSA_STOP_MAX_ROWS) return false;
+  }
   const int64_t ng = (p->num_queries + p->query_group - 1) / p->query_group;
   // grid.y of the per-unit and per-(query position, kv head) launches
   if ((int64_t)p->batch * ng * p->num_kv_heads > 65535) return false;
@@ -66,7 +74,6 @@ struct Dims {
   bool stop;  // early stopping on (its buffers are part of the workspace)
 };
 
-constexpr int kStopMaxStratum = 16384;  // the early-stopping kernels' largest stratum
 // Attention waves per split: each takes an equal share of every chunk's
 // selected items (a chunk holds about 82 of them at 50x sparsity, 3 tiles of
 // 32), which shortens each wave's chain of dependent loads, and the merge
@@ -99,7 +106,8 @@ Dims dims_of(const ssa_params* p) {
            (int64_t)d.NS * d.NSUB * 2 <= SSA_MAX_SEQ_LEN / SSA_CHUNK_TOKENS)
       d.NSUB *= 2;
   }
-  d.scale = p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / std::sqrt((float)p->head_dim);
+  d.scale = p->softmax_scale > 0.0f ? p->softmax_scale
+                                     : (float)(1.0 / std::sqrt((double)p->head_dim));
   d.stop = p->early_stop > 0.0f;  // NaN compares false
   return d;
 }
@@ -108,7 +116,7 @@ struct Layout {
   size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
-      stop_words, stop_pair, stop_mass, stop_rword, total;
+      stop_words, stop_pair, stop_rword, stop_logit, total;
 };
 
 Layout layout_of(const Dims& d) {
@@ -142,14 +150,14 @@ Layout layout_of(const Dims& d) {
   l.sel_cnt = take(U * NC * 2 * 4);
   l.part = take((size_t)d.B * d.T * d.Hq * d.NS * d.NSUB * (d.d + 2) * 4);
   const size_t SU = d.stop ? U : 0;  // early stopping's buffers only when it is on
-  const size_t KS = kStopMaxStratum;
+  const size_t KS = SSA_STOP_MAX_STRATUM;
   l.stop_cut = take(SU * 8);
   l.stop_off = take(SU * NC * 4);
   l.stop_n = take(SU * 4);
   l.stop_words = take(SU * KS * 8);
   l.stop_pair = take(SU * (KS / 1024) * (KS / 1024) * 1024 * 2);
-  l.stop_mass = take(SU * KS * 8);
   l.stop_rword = take(SU * KS * 8);
+  l.stop_logit = take(SU * KS * SSA_STOP_MAX_ROWS * 4);
   l.total = off;
   return l;
 }
@@ -214,10 +222,17 @@ ssa::IndexArgs index_args(const ssa_params* p, const Dims& d, const void* q, con
   return a;
 }
 
+// Keys as the kernels take them: whole rows (rest null), or the scored dims
+// and the others.
+struct Keys {
+  const void* main;
+  const void* rest;
+};
+
 ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* scores,
                             int64_t score_ld, const int32_t* seq_lens, const int32_t* topk,
                             const float* top_p, const int32_t* sample_budget,
-                            const uint64_t* seed, const float* w_in,
+                            const uint64_t* seed, const float* w_in, const void* q, Keys keys,
                             const int32_t* block_table, int emit_rows, int32_t* sel_idx,
                             float* sel_logw, int32_t* sel_cnt, float* norm_out, void* ws,
                             const Layout& l) {
@@ -258,8 +273,18 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.stop_n = d.stop ? at<int32_t>(ws, l.stop_n) : nullptr;
   a.stop_words = d.stop ? at<unsigned long long>(ws, l.stop_words) : nullptr;
   a.stop_pair = d.stop ? at<uint16_t>(ws, l.stop_pair) : nullptr;
-  a.stop_mass = d.stop ? at<unsigned long long>(ws, l.stop_mass) : nullptr;
   a.stop_rword = d.stop ? at<unsigned long long>(ws, l.stop_rword) : nullptr;
+  a.stop_logit = d.stop ? at<float>(ws, l.stop_logit) : nullptr;
+  a.max_topk = p->max_topk > 0 ? p->max_topk : INT32_MAX;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint16_t*>(keys.main);
+  a.k_rest = static_cast<const uint16_t*>(keys.rest);
+  a.Hq = d.Hq;
+  a.G = d.G;
+  a.d = d.d;
+  a.pair_begin = p->pair_begin;
+  a.pair_count = p->pair_count;
+  a.scale = d.scale;
   a.T = d.T;
   a.g = d.g;
   a.NG = d.NG;
@@ -272,13 +297,6 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.seg_ld = d.SEG;
   return a;
 }
-
-// Keys as the kernels take them: whole rows (rest null), or the scored dims
-// and the others.
-struct Keys {
-  const void* main;
-  const void* rest;
-};
 
 ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, Keys keys,
                             const void* v_cache, const int32_t* block_table,
@@ -399,8 +417,8 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
   // applies its own causal span.
   const int rows = d.T == 1 ? 1 : 0;
   const ssa::SelectArgs sa =
-      select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr,
-                  block_table, rows, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
+      select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr, q,
+                  keys, block_table, rows, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
   const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, sel_idx,
                                          sel_logw, sel_cnt, rows, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
@@ -510,7 +528,8 @@ int ssa_score(const ssa_params* p, const void* q, const void* k_cache, const int
 
 int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens,
                const int32_t* topk, const float* top_p, const int32_t* sample_budget,
-               const uint64_t* seed, const float* w_in, int32_t* sel_idx, float* sel_logw,
+               const uint64_t* seed, const float* w_in, const void* q, const void* k_cache,
+               const void* k_rest, const int32_t* block_table, int32_t* sel_idx, float* sel_logw,
                int32_t* sel_count, float* norm_out, void* workspace, size_t workspace_bytes,
                void* stream) {
   Layout l;
@@ -520,10 +539,22 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
       !sel_count || !norm_out)
     return SSA_ERR_INVALID;
   const Dims d = dims_of(p);
+  Keys keys{nullptr, nullptr};
+  if (d.stop) {  // early stopping weighs the stratum by exact attention
+    if (!q || !aligned16(q) || !block_table) return SSA_ERR_INVALID;
+    if (p->key_layout == SSA_KEYS_SPLIT) {
+      if (!split_keys_ok(p, k_cache, k_rest)) return SSA_ERR_INVALID;
+      keys = Keys{k_cache, rest_of(p, k_rest)};
+    } else {
+      if (!k_cache || !aligned16(k_cache) || k_rest) return SSA_ERR_INVALID;
+      keys = Keys{k_cache, nullptr};
+    }
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const ssa::SelectArgs sa =
       select_args(p, d, scores, p->max_seq_len, seq_lens, topk, top_p, sample_budget, seed, w_in,
-                  nullptr, /*emit_rows=*/0, sel_idx, sel_logw, sel_count, norm_out, workspace, l);
+                  q, keys, block_table, /*emit_rows=*/0, sel_idx, sel_logw, sel_count, norm_out,
+                  workspace, l);
   SSA_TRY(launch_init_for(sa, d.U, s));
   SSA_TRY(ssa::launch_score_hist(sa, d.U, s));
   SSA_TRY(launch_first_digit(sa, d.U, s));

@@ -369,10 +369,11 @@ struct SeqParams {
 };
 
 __device__ __forceinline__ SeqParams seq_params(int L, const int32_t* topk, const float* top_p,
-                                                const int32_t* sample_budget, int b) {
+                                                const int32_t* sample_budget, int b,
+                                                int max_topk) {
   SeqParams p;
   p.L = L;
-  const int k = max(topk[b], 0);
+  const int k = min(max(topk[b], 0), max_topk);
   p.m = max(sample_budget[b], 0);
   p.topp = top_p != nullptr;
   p.p = p.topp ? top_p[b] : 1.0f;

@@ -88,6 +88,7 @@ struct SelectArgs {
   float* sel_logw;            // [U, seg_ld]
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
+  int max_topk;               // topk[b] above it acts as it (INT_MAX: no bound)
   // Early stopping (all null when it is off).  A stratum word is
   // ((~key) << 32) | position: ascending words are the stratum's order.
   float stop_tau;                 // the threshold tau, clamped to 1
@@ -97,8 +98,16 @@ struct SelectArgs {
   int32_t* stop_n;                // [U] words above the threshold key (<= 16384 when cut)
   unsigned long long* stop_words; // [U, 16384] those words, then sorted per 1024-word slice
   uint16_t* stop_pair;            // [U, 16, 16, 1024] words of slice s below word i of slice o
-  unsigned long long* stop_mass;  // [U, 16384] mass units in stratum order
-  unsigned long long* stop_rword; // [U, 16384] words in stratum order
+  unsigned long long* stop_rword; // [U, 16384] the stratum's words in its order (ties too)
+  float* stop_logit;              // [U, 16384, 16] exact logit of (rank, query row);
+                                  //   -inf outside the row's span
+  // What the exact logits read: the unit's query rows (each member's G
+  // heads) and its keys, whole or split, through the block table.
+  const uint16_t* q;              // [B, T, Hq, d]
+  const uint16_t* k_cache;        // whole keys [rows, d], or the scored dims [rows, 2 pc]
+  const uint16_t* k_rest;         // split keys: the other dims; else null
+  int Hq, G, d, pair_begin, pair_count;
+  float scale;
   int T, g, NG;
   int Hkv, max_seq_len, nchunk, max_blocks, num_blocks, emit_rows;
   int64_t seg_ld;             // nchunk * 4096

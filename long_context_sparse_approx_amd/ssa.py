@@ -26,6 +26,8 @@ SSA_F32 = 0
 SSA_BF16 = 1
 SSA_KEYS_WHOLE = 0
 SSA_KEYS_SPLIT = 1
+STOP_MAX_STRATUM = 16384
+STOP_MAX_ROWS = 16
 BLOCK_TOKENS = 16
 CHUNK_TOKENS = 4096
 STAGES = ("init", "index", "filter", "resolve", "sample", "attend", "merge")
@@ -45,7 +47,7 @@ class SsaParams(ctypes.Structure):
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("num_queries", ctypes.c_int32),
                 ("query_group", ctypes.c_int32), ("early_stop", ctypes.c_float),
-                ("key_layout", ctypes.c_int32)]
+                ("key_layout", ctypes.c_int32), ("max_topk", ctypes.c_int32)]
 
 
 class SsaError(RuntimeError):
@@ -82,8 +84,8 @@ def lib() -> ctypes.CDLL:
         L.ssa_decode_split.restype = ctypes.c_int
         L.ssa_score.argtypes = [_PP, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_score.restype = ctypes.c_int
-        L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                 ctypes.c_size_t, _P]
+        L.ssa_select.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _P, ctypes.c_size_t, _P]
         L.ssa_select.restype = ctypes.c_int
         L.ssa_attend.argtypes = [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.ssa_attend.restype = ctypes.c_int
@@ -147,13 +149,14 @@ def _stream(stream):
 def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, num_blocks,
                 max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
                 softmax_scale=0.0, block_size=BLOCK_TOKENS, num_queries=1,
-                query_group=1, early_stop=0.0, key_layout=SSA_KEYS_WHOLE) -> SsaParams:
+                query_group=1, early_stop=0.0, key_layout=SSA_KEYS_WHOLE,
+                max_topk=0) -> SsaParams:
     if pair_begin is None:
         pair_begin = head_dim // 2 - pair_count
     return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
                      float(softmax_scale), int(num_queries), int(query_group),
-                     float(early_stop), int(key_layout))
+                     float(early_stop), int(key_layout), int(max_topk))
 
 
 def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
@@ -286,9 +289,11 @@ def score(p: SsaParams, q, k_cache, block_table, seq_lens, scores=None, workspac
 
 
 def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None, workspace=None,
-           stream=None, top_p=None):
+           stream=None, top_p=None, q=None, k_cache=None, k_rest=None, block_table=None):
     """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out),
-    each [B, NG*Hkv, ...] (one row per selection unit)."""
+    each [B, NG*Hkv, ...] (one row per selection unit).  With early stopping
+    (p.early_stop > 0) the query, keys (k_rest for split keys) and block
+    table are needed too: the stratum is weighed by exact attention."""
     _check_top_p(top_p, p.batch)
     dev = scores.device
     nc = num_chunks(p)
@@ -301,7 +306,8 @@ def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None,
     workspace = _ws(p, workspace, dev)
     assert w_in is None or w_in.numel() == U
     _check(lib().ssa_select(ctypes.byref(p), _ptr(scores), _ptr(seq_lens), _ptr(topk),
-                            _ptr(top_p), _ptr(sample_budget), _ptr(seed), _ptr(w_in), _ptr(sel_idx),
+                            _ptr(top_p), _ptr(sample_budget), _ptr(seed), _ptr(w_in), _ptr(q),
+                            _kv_ptr(k_cache), _kv_ptr(k_rest), _ptr(block_table), _ptr(sel_idx),
                             _ptr(sel_logw), _ptr(sel_count), _ptr(norm), _ptr(workspace),
                             ctypes.c_size_t(workspace.numel()), _stream(stream)), "ssa_select")
     return sel_idx, sel_logw, sel_count, norm

@@ -85,13 +85,21 @@ R16 Multi-query decode (PIVOT reuse): a step may carry T query positions per
     the population stays unbiased for that subset).
 R17 Early stopping (S2O): with a gain threshold tau > 0 the deterministic
     stratum S, in its order (key descending, index ascending), is visited in
-    blocks of 64 consecutive tokens; block i's gain D_i is its mass in R15's
-    integer units and C_i the mass of blocks 0..i; the visit stops after the
-    first block with D_i < tau * C_i (exact), and S's later blocks are
-    skipped: neither read exactly nor sampled.  The tail sample (over the
-    complement of the whole S, normaliser W over it) is unchanged.  tau is
-    clamped to 1 (NaN and tau <= 0: no stopping); a stratum of more than
-    16384 tokens is not truncated.
+    blocks of 64 consecutive tokens while the online-softmax state of every
+    query row of the unit (each query head of each member; a row only sees
+    tokens inside its member's span) accumulates the block's exact attention
+    mass.  Block i's marginal gain for row r is D_i^r = the increment of that
+    row's l, and C_i^r = the row's l after the block; the visit stops after
+    the first block at which every row has D_i^r < tau * C_i^r or D_i^r = 0,
+    and S's later blocks are skipped: neither read nor sampled.  The tail
+    sample (over the complement of the whole S, normaliser W over it) is
+    unchanged.  The decision is taken in the kernel's precision: the exact
+    logit is l = fl32(scale * dot), the dot of bf16 values summed in float32
+    (each 8-dim slice in dim order, then the slices pairwise); the gain is
+    counted in R15's integer units of sexp(l - M_r), M_r the row's largest
+    logit over S, so the sums and the comparison are exact.  tau is clamped
+    to 1 (NaN and tau <= 0: no stopping).  The rule applies at every
+    stratum size.
 R18 Split keys (FASA-M): a key row is held as two rows under the same row
     number: the scored dims [2 pair_begin, 2 (pair_begin + pair_count)) in
     one array and the remaining dims, in their order ([0, 2 pair_begin) then
@@ -131,7 +139,8 @@ __all__ = [
     "attend_unit",
     "decode",
     "STOP_BLOCK",
-    "STOP_MAX_STRATUM",
+    "stop_logits",
+    "stop_gains",
     "stop_count",
     "member_span",
     "group_span",
@@ -288,28 +297,71 @@ def topp_count(s32: np.ndarray, p) -> int:
 
 
 # ---------------------------------------------------------------------------
-# Early stopping over the deterministic stratum ([S2O] methodology part 2) --
-# reading R17
+# Early stopping over the deterministic stratum ([S2O] methodology parts 2
+# and 3) -- reading R17
 # ---------------------------------------------------------------------------
 
 STOP_BLOCK = 64
-STOP_MAX_STRATUM = 16384
 
 
-def stop_count(q_ordered, tau) -> int:
-    """Tokens of the stratum kept by the early-stopping rule: q_ordered are the
-    stratum's mass units in its order; blocks of 64, stop after the first
-    block whose gain D_i < tau * C_i (C_i = mass of blocks 0..i)."""
-    n = len(q_ordered)
+def stop_logits(q_rows: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """Exact logits l = fl32(scale * dot) in the decision precision of R17,
+    float32 [R, n] for query rows q_rows [R, d] and keys K [n, d] (both
+    holding bf16 values): products of bf16 values are exact in float32; each
+    8-dim slice is summed in dim order, then the d/8 slice sums pairwise
+    (neighbours first), all in float32."""
+    q = np.asarray(q_rows, dtype=_F32)
+    k = np.asarray(K, dtype=_F32)
+    R, d = q.shape
+    n = k.shape[0]
+    prod = q[:, None, :] * k[None, :, :]  # exact
+    prod = prod.reshape(R, n, d // 8, 8)
+    acc = prod[..., 0]
+    for i in range(1, 8):
+        acc = np.add(acc, prod[..., i], dtype=_F32)
+    while acc.shape[-1] > 1:
+        acc = np.add(acc[..., 0::2], acc[..., 1::2], dtype=_F32)
+    return np.multiply(acc[..., 0], _F32(scale), dtype=_F32)
+
+
+def stop_gains(logits: np.ndarray, visible: np.ndarray) -> np.ndarray:
+    """Per-row block gains in integer units, uint64 [R, nblocks]: the stratum's
+    logits [R, n] in stratum order, visible [R, n] = the token lies in the
+    row's span.  A row's units are floor(2^38 sexp(l - M_r)) with M_r its
+    largest visible logit; invisible tokens add nothing."""
+    R, n = logits.shape
+    nb = -(-n // STOP_BLOCK)
+    gains = np.zeros((R, nb), np.uint64)
+    for r in range(R):
+        vis = np.asarray(visible[r], bool)
+        if not vis.any():
+            continue
+        M = _F32(logits[r][vis].max())
+        units = mass_units(sexp(np.subtract(logits[r], M, dtype=_F32)))
+        units[~vis] = 0
+        for i in range(nb):
+            gains[r, i] = sum(int(x) for x in units[i * STOP_BLOCK:(i + 1) * STOP_BLOCK])
+    return gains
+
+
+def stop_count(gains: np.ndarray, n: int, tau) -> int:
+    """Tokens of the stratum (n of them) kept by the rule: the visit stops
+    after the first block at which every row's gain D is 0 or below tau times
+    the row's mass C of blocks 0..i (exact rationals)."""
     tau = float(np.float32(tau))
-    if not tau > 0.0 or n > STOP_MAX_STRATUM:
+    if not tau > 0.0 or n == 0:
         return n
     tau = Fraction(min(tau, 1.0))
-    acc = 0
-    for i in range(-(-n // STOP_BLOCK)):
-        gain = sum(int(x) for x in q_ordered[i * STOP_BLOCK:(i + 1) * STOP_BLOCK])
-        acc += gain
-        if gain < tau * acc:
+    gains = np.atleast_2d(gains)
+    acc = [0] * gains.shape[0]
+    for i in range(gains.shape[1]):
+        agree = True
+        for r in range(gains.shape[0]):
+            g = int(gains[r, i])
+            acc[r] += g
+            if g != 0 and not g < tau * acc[r]:
+                agree = False
+        if agree:
             return min((i + 1) * STOP_BLOCK, n)
     return n
 
@@ -418,18 +470,25 @@ def sample_tail(strata: dict, m: int, seed: int, b: int, h: int, grp: int = 0):
 
 
 def select_unit(s32: np.ndarray, topk: int, m: int, seed: int, b: int, h: int, W_in=None,
-                top_p=None, grp: int = 0, stop_tau=None):
+                top_p=None, grp: int = 0, stop_tau=None, stop_rows=None):
     """Full selection of one (batch, [query group,] kv head): dict with S, R,
-    pi_R, M, W, dense (and S_full, the stratum before early stopping)."""
+    pi_R, M, W, dense (and S_full, the stratum before early stopping).
+
+    Early stopping (R17) needs ``stop_tau`` and ``stop_rows`` = (q_rows
+    [R, d], K [L, d], spans [R], scale): the unit's query rows, its key rows
+    and each row's causal length."""
     st = tail_stratum(s32, topk, m, W_in, top_p)
     R, pi_R = sample_tail(st, m, seed, b, h, grp)
     S = st["S"]
     S_full = S
     if stop_tau is not None and not st["dense"] and S.size:
         s32 = np.asarray(s32, dtype=_F32)
-        order = np.lexsort((S, ~order_key(s32[S])))  # key descending, index ascending
-        q = mass_units(sexp(np.subtract(s32[S[order]], st["M"], dtype=_F32)))
-        S = np.sort(S[order[:stop_count(q, stop_tau)]])
+        order = S[np.lexsort((S, ~order_key(s32[S])))]  # key descending, index ascending
+        q_rows, K, spans, scale = stop_rows
+        logits = stop_logits(q_rows, K[order], scale)
+        visible = order[None, :] < np.asarray(spans)[:, None]
+        kept = stop_count(stop_gains(logits, visible), order.size, stop_tau)
+        S = np.sort(order[:kept])
     return dict(S=S, R=R, pi_R=pi_R, M=st["M"], W=st["W"], dense=st["dense"], S_full=S_full)
 
 
@@ -503,7 +562,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed
         s32 = s64.astype(_F32)
         tp = None if top_p is None else np.float32(top_p[b])
         sel = select_unit(s32, int(topk[b]), int(sample_budget[b]), int(seed[b]), b, h,
-                          top_p=tp, stop_tau=stop_tau)
+                          top_p=tp, stop_tau=stop_tau, stop_rows=(qg, K, [L] * G, scale))
         out[b, h * G:(h + 1) * G, :] = attend_unit(qg, K, V, sel["S"], sel["R"], sel["pi_R"], scale)
         info[(b, h)] = dict(scores=s64, **sel)
     return out, info
@@ -556,8 +615,10 @@ def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget
         qstack = np.concatenate([q[b, t, h * G:(h + 1) * G, :] for t in members]).astype(np.float64)
         s64 = approx_scores(qstack, K, pair_begin, pair_count, scale)
         tp = None if top_p is None else np.float32(top_p[b])
+        spans = [member_span(P, T, t) for t in members for _ in range(G)]
         sel = select_unit(s64.astype(_F32), int(topk[b]), int(sample_budget[b]), int(seed[b]),
-                          b, h, top_p=tp, grp=c, stop_tau=stop_tau)
+                          b, h, top_p=tp, grp=c, stop_tau=stop_tau,
+                          stop_rows=(qstack, K, spans, scale))
         for t in members:
             Lt = member_span(P, T, t)
             S = sel["S"][sel["S"] < Lt]

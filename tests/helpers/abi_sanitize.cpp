@@ -67,6 +67,7 @@ static ssa_params valid() {
   p.query_group = 1;
   p.early_stop = 0.0f;
   p.key_layout = SSA_KEYS_WHOLE;
+  p.max_topk = 0;
   return p;
 }
 
@@ -122,7 +123,39 @@ int main() {
                      nullptr) != SSA_OK);
     CHECK(ssa_score(&p, dev, dev, i32, i32, nullptr, w, need, nullptr) != SSA_OK);
     CHECK(ssa_select(&p, nullptr, i32, i32, nullptr, i32, u64, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, w, need, nullptr) != SSA_OK);
+                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, w, need,
+                     nullptr) != SSA_OK);
+    // early stopping: the stratum bound and the rows must fit its kernels, and
+    // the selection needs the query and keys
+    {
+      ssa_params es = valid();
+      es.early_stop = 0.1f;
+      CHECK(ssa_workspace_bytes(&es) > 0);  // max_seq_len 1000 bounds the stratum
+      es.max_seq_len = 16385;
+      es.max_blocks_per_seq = 1025;
+      CHECK(ssa_workspace_bytes(&es) == 0);
+      es.max_topk = SSA_STOP_MAX_STRATUM;
+      CHECK(ssa_workspace_bytes(&es) > 0);
+      es.max_topk = -1;
+      CHECK(ssa_workspace_bytes(&es) == 0);
+      es.max_topk = 100;
+      es.num_queries = 8;
+      es.query_group = 8;  // 8 members x 4 heads > SSA_STOP_MAX_ROWS
+      CHECK(ssa_workspace_bytes(&es) == 0);
+      es.query_group = 4;
+      const size_t need_es = ssa_workspace_bytes(&es);
+      CHECK(need_es > 0);
+      std::vector<unsigned char> wes(need_es + 256);
+      float* sc = reinterpret_cast<float*>(buf);
+      int32_t* o32 = reinterpret_cast<int32_t*>(buf);
+      float* of = reinterpret_cast<float*>(buf);
+      CHECK(ssa_select(&es, sc, i32, i32, nullptr, i32, u64, nullptr, nullptr, dev, nullptr, i32,
+                       o32, of, o32, of, wes.data(), need_es, nullptr) == SSA_ERR_INVALID);
+      CHECK(ssa_select(&es, sc, i32, i32, nullptr, i32, u64, nullptr, dev, nullptr, nullptr, i32,
+                       o32, of, o32, of, wes.data(), need_es, nullptr) == SSA_ERR_INVALID);
+      CHECK(ssa_select(&es, sc, i32, i32, nullptr, i32, u64, nullptr, dev, dev, nullptr, nullptr,
+                       o32, of, o32, of, wes.data(), need_es, nullptr) == SSA_ERR_INVALID);
+    }
     CHECK(ssa_attend(&p, dev, dev, dev, i32, i32, nullptr, f32, i32, dev, w, need, nullptr) !=
           SSA_OK);
     // split-key entry points reject whole-key params, and the reverse

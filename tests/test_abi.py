@@ -101,7 +101,7 @@ def test_small_workspace_rejected(lib):
     assert rc == ssa.SSA_ERR_WORKSPACE
     rc = lib.ssa_score(ctypes.byref(p), fake, fake, fake, fake, fake, fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
-    rc = lib.ssa_select(ctypes.byref(p), *([fake] * 11), fake, ctypes.c_size_t(16), None)
+    rc = lib.ssa_select(ctypes.byref(p), *([fake] * 15), fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
     rc = lib.ssa_attend(ctypes.byref(p), *([fake] * 9), fake, ctypes.c_size_t(16), None)
     assert rc == ssa.SSA_ERR_WORKSPACE
@@ -170,3 +170,39 @@ def test_key_layouts_checked(lib):
     assert append(ps, 0, fake) == ssa.SSA_OK
     assert lib.ssa_host_device_address(None, ctypes.byref(ctypes.c_void_p())) == ssa.SSA_ERR_INVALID
     assert lib.ssa_host_device_address(fake, None) == ssa.SSA_ERR_INVALID
+
+
+@pytest.mark.parametrize("bad", [
+    dict(max_seq_len=20000, max_blocks_per_seq=1250),           # stratum bound above 16384
+    dict(max_seq_len=20000, max_blocks_per_seq=1250, max_topk=16385),
+    dict(num_queries=8, query_group=8),                         # 8 members x 4 heads > 16 rows
+    dict(max_topk=-1),
+])
+def test_early_stop_limits_rejected(lib, bad):
+    """Early stopping is refused before any launch when the stratum could
+    exceed its kernels' capacity or the unit has too many query rows."""
+    p = good(early_stop=0.05, **bad)
+    assert lib.ssa_workspace_bytes(ctypes.byref(p)) == 0
+    fake = ctypes.c_void_p(4096)
+    rc = lib.ssa_decode(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+                        fake, fake, ctypes.c_size_t(1 << 40), None)
+    assert rc == ssa.SSA_ERR_INVALID
+
+
+def test_early_stop_within_limits_accepted(lib):
+    for kw in (dict(), dict(max_seq_len=20000, max_blocks_per_seq=1250, max_topk=16384),
+               dict(num_queries=8, query_group=4)):
+        assert lib.ssa_workspace_bytes(ctypes.byref(good(early_stop=0.05, **kw))) > 0
+    # without early stopping the bound is free
+    assert lib.ssa_workspace_bytes(ctypes.byref(good(max_seq_len=20000,
+                                                     max_blocks_per_seq=1250))) > 0
+
+
+def test_early_stop_selection_needs_query_and_keys(lib):
+    p = good(early_stop=0.05)
+    n = ssa.workspace_bytes(p)
+    fake = ctypes.c_void_p(4096)
+    for q, k, bt in ((None, fake, fake), (fake, None, fake), (fake, fake, None)):
+        rc = lib.ssa_select(ctypes.byref(p), fake, fake, fake, None, fake, fake, None, q, k,
+                            None, bt, fake, fake, fake, fake, fake, ctypes.c_size_t(n), None)
+        assert rc == ssa.SSA_ERR_INVALID

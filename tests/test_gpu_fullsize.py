@@ -54,10 +54,13 @@ def check_fullsize(name, units=None, top_p=None, early_stop=None):
     tp32 = None if top_p is None else np.float32(top_p)
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
-                       early_stop=0.0 if early_stop is None else float(early_stop))
+                       early_stop=0.0 if early_stop is None else float(early_stop),
+                       max_topk=int(wl.topk.max()))
     scale = 1.0 / math.sqrt(wl.d)
     G = wl.Hq // wl.Hkv
     ws = ssa.alloc_workspace(p, DEV)
+    # what early stopping's exact gains read (ignored when it is off)
+    exact = dict(q=wl.q, k_cache=wl.k_cache, block_table=wl.block_table)
     out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
                      wl.sample_budget, wl.seed, workspace=ws, top_p=tp).clone()
     out2 = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
@@ -79,13 +82,13 @@ def check_fullsize(name, units=None, top_p=None, early_stop=None):
     for b, h in units:
         qg, K, _ = unit_host(wl, b, h, values=False)
         s64 = orc.approx_scores(qg, K, wl.pair_begin, wl.pair_count, scale)
-        del K
         ok, ratio = score_tolerance_ok(sc[b, h, :s64.size], s64)
         worst = max(worst, ratio)
         assert ok, f"scores out of tolerance at {(b, h)} ({ratio})"
         sel = orc.select_unit(s64.astype(np.float32), int(wl.topk[b]), int(wl.sample_budget[b]),
                               int(wl.seed[b]) & 0xFFFFFFFFFFFFFFFF, b, h, top_p=tp32,
-                              stop_tau=tau)
+                              stop_tau=tau, stop_rows=(qg, K, [wl.lens[b]] * G, scale))
+        del K
         sels[(b, h)] = sel
         s32[b, h, :s64.size] = torch.from_numpy(s64.astype(np.float32))
         w_in[b, h] = float(sel["W"])
@@ -97,7 +100,7 @@ def check_fullsize(name, units=None, top_p=None, early_stop=None):
     s32d = s32.to(DEV)
     # Selection fed the oracle's scores and normaliser: bit-exact.
     si, sl, sn, _ = ssa.select(p, s32d, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
-                               w_in=w_in.to(DEV), workspace=ws, top_p=tp)
+                               w_in=w_in.to(DEV), workspace=ws, top_p=tp, **exact)
     torch.cuda.synchronize()
     si, sl, sn = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy()
     for (b, h), sel in sels.items():
@@ -106,7 +109,7 @@ def check_fullsize(name, units=None, top_p=None, early_stop=None):
     say(f"[full] {name} selection bit-exact on {len(units)} units")
     # The library's own maximum and normaliser (no injected W).
     si, sl, sn, nm = ssa.select(p, s32d, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
-                                workspace=ws, top_p=tp)
+                                workspace=ws, top_p=tp, **exact)
     torch.cuda.synchronize()
     si, sl, sn, nm = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy(), nm.cpu().numpy()
     worst_w, same_w = 0.0, 0
@@ -157,8 +160,8 @@ def test_fullsize_1m_top_p():
 
 
 def test_fullsize_1m_early_stop():
-    """Early stopping at tau = 0.01 (the bench's variant)."""
-    check_fullsize("1m", [(0, 0), (0, 5)], early_stop=0.01)
+    """Early stopping at tau = 0.01 (the bench's variant), every unit."""
+    check_fullsize("1m", early_stop=0.01)
 
 
 def test_fullsize_128k():

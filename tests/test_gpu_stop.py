@@ -2,11 +2,13 @@
 C ABI.
 
 "S2O: Early Stopping for Sparse Attention via Online Permutation",
-methodology part 2: the stratum is visited in 64-token blocks of its order and
-the visit ends after the first block whose gain is below tau times the mass
-visited so far.  Gains are integer mass units, so the cut is bit-exact against
-the oracle given the same float32 scores; sampling is compared with the
-oracle's normaliser injected.
+methodology parts 2 and 3: the stratum is visited in 64-token blocks of its
+order while every query row's online-softmax l takes in the block's exact
+attention mass, and the visit ends after the first block at which every
+row's gain is 0 or below tau times its l so far.  The decision logits are
+float32 in a specified order and the gains integer units, so the cut is
+bit-exact against the oracle given the same float32 scores; the sample is
+compared with the oracle's normaliser injected.
 """
 
 import math
@@ -18,35 +20,72 @@ import torch
 from long_context_sparse_approx_amd import ssa, synth
 from oracle import ssa_oracle as orc
 
-from gpu_helpers import default_scale, gpu_sets, oracle_scores, say, unit_rows, vmax_unit
+from gpu_helpers import default_scale, gpu_sets, say, unit_rows, vmax_unit
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def check_select(s32, lens, topk, m, seeds, tau, label, top_p=None, T=1, g=1, Hkv=None):
-    """Stratum cut and sample bit-exact for scores s32 [B, units per sequence, Lmax]."""
-    B, UH, Lmax = s32.shape
-    Hkv = Hkv or UH
-    p = ssa.make_params(batch=B, num_q_heads=Hkv, num_kv_heads=Hkv, head_dim=128,
-                        max_blocks_per_seq=(Lmax + 15) // 16, num_blocks=1, max_seq_len=Lmax,
-                        num_queries=T, query_group=g, early_stop=float(tau))
+def oracle_selection(wl, tau, topk, m, top_p=None, g=1):
+    """The oracle's scores and early-stopped selection of every unit
+    (b, group, h): (s32 [B, NG*Hkv, Lmax], w_in [B, NG*Hkv], sels)."""
+    hs = wl.host()
+    scale = default_scale(wl.d)
+    q = hs["q"]
+    T = 1 if q.ndim == 3 else q.shape[1]
+    g = min(g, T)
+    NG = -(-T // g)
+    G = wl.Hq // wl.Hkv
+    s32 = np.zeros((wl.B, NG * wl.Hkv, wl.max_seq_len), np.float32)
+    w_in = np.zeros((wl.B, NG * wl.Hkv), np.float32)
+    sels = {}
+    for b in range(wl.B):
+        P = wl.lens[b]
+        for c in range(NG):
+            members = list(range(c * g, min((c + 1) * g, T)))
+            Lg = orc.group_span(P, T, g, c)
+            for h in range(wl.Hkv):
+                K, _ = unit_rows(hs, b, h, Lg)
+                if T == 1:
+                    qs = q[b, h * G:(h + 1) * G].astype(np.float64)
+                else:
+                    qs = np.concatenate([q[b, t, h * G:(h + 1) * G] for t in members]).astype(
+                        np.float64)
+                s64 = orc.approx_scores(qs, K, wl.pair_begin, wl.pair_count, scale)
+                spans = [orc.member_span(P, T, t) for t in members for _ in range(G)]
+                tp = None if top_p is None else np.float32(top_p[b])
+                sel = orc.select_unit(s64.astype(np.float32), int(topk[b]), int(m[b]),
+                                      int(hs["seed"][b]), b, h, top_p=tp, grp=c,
+                                      stop_tau=np.float32(tau), stop_rows=(qs, K, spans, scale))
+                r = c * wl.Hkv + h
+                s32[b, r, :s64.size] = s64.astype(np.float32)
+                w_in[b, r] = sel["W"]
+                sels[(b, r)] = sel
+    return s32, w_in, sels
+
+
+def check_stop(wl, tau, label, topk=None, m=None, top_p=None, g=1, max_topk=0, split=False):
+    """Stratum cut and sample bit-exact against the oracle; returns the sels
+    and the number of tokens cut."""
+    topk = [int(x) for x in (wl.topk.cpu() if topk is None else topk)]
+    m = [int(x) for x in (wl.sample_budget.cpu() if m is None else m)]
+    s32, w_in, sels = oracle_selection(wl, tau, topk, m, top_p, g)
+    kw = dict(early_stop=float(tau), query_group=g, max_topk=max_topk or max(topk))
+    if split:
+        kw["key_layout"] = ssa.SSA_KEYS_SPLIT
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count, **kw)
     i32 = lambda xs: torch.tensor(xs, dtype=torch.int32, device=DEV)
-    seed_t = torch.tensor([int(x) for x in seeds], dtype=torch.int64, device=DEV)
     tp = None if top_p is None else torch.tensor(np.asarray(top_p, np.float32), device=DEV)
-    sels, w_in = {}, np.zeros((B, UH), np.float32)
-    ng = UH // Hkv
-    for b in range(B):
-        for r in range(UH):
-            c, h = divmod(r, Hkv)
-            span = orc.group_span(lens[b], T, min(g, T), c)
-            sel = orc.select_unit(s32[b, r, :span], int(topk[b]), int(m[b]), int(seeds[b]), b, h,
-                                  top_p=None if top_p is None else np.float32(top_p[b]), grp=c,
-                                  stop_tau=np.float32(tau))
-            sels[(b, r)] = sel
-            w_in[b, r] = sel["W"]
-    si, sl, sn, _ = ssa.select(p, torch.from_numpy(s32).to(DEV), i32(lens), i32(topk), i32(m),
-                               seed_t, w_in=torch.from_numpy(w_in).to(DEV), top_p=tp)
+    keys = dict(k_cache=wl.k_cache)
+    if split:
+        lo, hi = 2 * wl.pair_begin, 2 * (wl.pair_begin + wl.pair_count)
+        keys = dict(k_cache=wl.k_cache[..., lo:hi].contiguous(),
+                    k_rest=torch.cat([wl.k_cache[..., :lo], wl.k_cache[..., hi:]],
+                                     dim=-1).contiguous())
+    si, sl, sn, _ = ssa.select(p, torch.from_numpy(s32).to(DEV), wl.seq_lens, i32(topk), i32(m),
+                               wl.seed, w_in=torch.from_numpy(w_in).to(DEV), top_p=tp, q=wl.q,
+                               block_table=wl.block_table, **keys)
     torch.cuda.synchronize()
     si, sl, sn = (t.cpu().numpy() for t in (si, sl, sn))
     cut = 0
@@ -61,62 +100,94 @@ def check_select(s32, lens, topk, m, seeds, tau, label, top_p=None, T=1, g=1, Hk
     return sels, cut
 
 
-def model_scores(wl):
-    hs = wl.host()
-    ref = oracle_scores(wl, hs, default_scale(wl.d))
-    s32 = np.zeros((wl.B, wl.Hkv, wl.max_seq_len), np.float32)
-    for (b, h), s64 in ref.items():
-        s32[b, h, :s64.size] = s64.astype(np.float32)
-    return s32
-
-
 RAGGED = dict(B=2, Hq=8, Hkv=2, d=128, L=[9000, 4097], theta=1e6, kdist="normal", planted=16,
               pair_count=32, topk=700, m=40, seeds=[5, 6], data_seed=11)
 
 
-def test_cut_on_model_scores():
-    wl = synth.make_workload(dict(RAGGED), "cpu")
-    s32 = model_scores(wl)
+def test_cut_on_model_caches():
+    wl = synth.make_workload(dict(RAGGED), DEV)
     total = 0
     for tau in (0.02, 0.1, 0.3, 1.0):
-        _, cut = check_select(s32, wl.lens, [700, 700], [40, 40], [5, 6], tau, f"tau={tau}")
+        _, cut = check_stop(wl, tau, f"tau={tau}")
         total += cut
     assert total > 0
 
 
-def test_cut_among_equal_keys():
-    """Coarse scores: the cut falls inside runs of equal keys, ordered by position."""
-    rng = np.random.default_rng(7)
-    L = 12000
-    s = (np.round(rng.standard_normal((2, 1, L)) * 3) / 3).astype(np.float32)
-    for tau in (0.05, 0.2):
-        check_select(s, [L, L - 777], [3000, 5000], [60, 60], [1, 2], tau, f"ties tau={tau}")
+def test_cut_head_dim_64_and_many_heads():
+    wl = synth.make_workload(dict(B=1, Hq=16, Hkv=1, d=64, L=[12289], theta=1e4,
+                                  kdist="normal", planted=8, pair_count=16, topk=3000, m=50,
+                                  seeds=[7], data_seed=12), DEV)
+    _, cut = check_stop(wl, 0.05, "d=64, 16 heads")
+    assert cut > 0
+
+
+def tied_workload(L, n_ties, rank):
+    """A cache in which n_ties tokens share the scored dims of the token
+    ranked `rank` (so their proxy scores tie exactly) while their other dims
+    differ (so their exact logits differ)."""
+    wl = synth.make_workload(dict(B=2, Hq=8, Hkv=2, d=128, L=[L, L - 777], theta=1e6,
+                                  kdist="normal", planted=0, pair_count=32, topk=100, m=60,
+                                  seeds=[1, 2], data_seed=13), DEV)
+    hs = wl.host()
+    lo, hi = 2 * wl.pair_begin, 2 * (wl.pair_begin + wl.pair_count)
+    G = wl.Hq // wl.Hkv
+    gen = np.random.default_rng(14)
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            K, _ = unit_rows(hs, b, h, wl.lens[b])
+            s = orc.approx_scores(hs["q"][b, h * G:(h + 1) * G], K, wl.pair_begin,
+                                  wl.pair_count, default_scale(wl.d))
+            src = int(np.argsort(-s, kind="stable")[rank])
+            dst = gen.choice(wl.lens[b], n_ties, replace=False)
+            bt = wl.block_table[b].long()
+            src_row = wl.k_cache[bt[src // 16], h, src % 16, lo:hi].clone()
+            dst_t = torch.from_numpy(dst).to(DEV)
+            wl.k_cache[bt[dst_t // 16], h, dst_t % 16, lo:hi] = src_row
+    return wl
+
+
+def test_cut_inside_the_threshold_ties():
+    """The stratum ends inside a run of 5000 tokens tied on its last key
+    (ranked by position across chunks, each with its own exact logit) and
+    the stop lands inside that run."""
+    wl = tied_workload(20000, 5000, 40)
+    sels, cut = check_stop(wl, 0.05, "tie cut", topk=[3000, 2500], m=[40, 40])
+    assert cut > 0
+    for sel in sels.values():
+        assert sel["S"].size < sel["S_full"].size
 
 
 def test_stratum_limits():
-    """At most 64 tokens: nothing to cut; more than 16384: visited whole; dense."""
-    rng = np.random.default_rng(8)
-    L = 40000
-    s = (rng.standard_normal((3, 1, L)) * 2).astype(np.float32)
-    sels, cut = check_select(s, [L, L, 600], [60, 16385, 500], [30, 30, 300], [1, 2, 3], 0.5,
-                             "limits")
-    assert cut == 0
+    """At most 64 tokens: nothing to cut; the largest stratum (16384 tokens,
+    max_topk 16384): cut; dense: nothing to cut."""
+    wl = synth.make_workload(dict(B=3, Hq=8, Hkv=2, d=128, L=[40000, 40000, 600], theta=1e6,
+                                  kdist="normal", planted=0, pair_count=32, topk=100, m=60,
+                                  seeds=[1, 2, 3], data_seed=15), DEV)
+    sels, cut = check_stop(wl, 0.5, "limits", topk=[60, 16384, 500], m=[30, 30, 300],
+                           max_topk=16384)
+    assert cut > 0
+    for (b, r), sel in sels.items():
+        if b != 1:
+            assert sel["S"].size == sel["S_full"].size
+        else:
+            assert sel["S"].size < sel["S_full"].size
 
 
-def test_cut_with_top_p_and_groups():
-    wl = synth.make_workload(dict(RAGGED), "cpu")
-    s32 = model_scores(wl)
-    check_select(s32, wl.lens, [4000, 4000], [40, 40], [5, 6], 0.05, "top-p", top_p=[0.5, 0.3])
-    # two query groups per sequence: rows are (group, head)
-    rng = np.random.default_rng(9)
-    s = (rng.standard_normal((2, 4, 9000)) * 1.5).astype(np.float32)
-    check_select(s, [9000, 7000], [900, 900], [50, 50], [3, 4], 0.1, "groups", T=4, g=2, Hkv=2)
+def test_cut_with_top_p_query_groups_and_split_keys():
+    wl = synth.make_workload(dict(RAGGED), DEV)
+    check_stop(wl, 0.05, "top-p", topk=[4000, 4000], m=[40, 40], top_p=[0.5, 0.3])
+    check_stop(wl, 0.05, "split keys", topk=[2000, 2000], split=True)
+    # four query positions, groups of 2 and of 4 members (8 and 16 query rows
+    # per unit, each row with its own span)
+    wq = synth.make_workload(dict(RAGGED), DEV, num_queries=4)
+    check_stop(wq, 0.1, "groups of 2", topk=[900, 900], m=[50, 50], g=2)
+    check_stop(wq, 0.1, "groups of 4", topk=[900, 900], m=[50, 50], g=4)
 
 
 def test_end_to_end_with_early_stopping():
     cfg = dict(RAGGED)
     wl = synth.make_workload(cfg, DEV)
-    tau = 0.05
+    tau = 0.3
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count, early_stop=tau)
     out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
@@ -137,22 +208,4 @@ def test_end_to_end_with_early_stopping():
         err = float(np.abs(got[b, h * G:(h + 1) * G] - ref[b, h * G:(h + 1) * G]).max())
         assert err <= 2e-3 * vmax_unit(V), f"early-stop e2e out of tolerance at {(b, h)}"
         say(f"[stop] e2e unit {(b, h)}: |S| {inf['S'].size} of {inf['S_full'].size}")
-
-
-def test_cut_inside_the_threshold_ties():
-    """The stop falls among the tokens tied on the stratum's last key, whose
-    order is by position across chunks: 100 high scores, then 5000 equal ones
-    spread over several chunks; top-k 3000 ends the stratum inside the tie run
-    and the stop lands a few blocks later, still inside it."""
-    rng = np.random.default_rng(10)
-    L = 20000
-    s = (rng.standard_normal((2, 1, L)) * 0.3 - 2.0).astype(np.float32)
-    for b in range(2):
-        pos = rng.permutation(L)
-        s[b, 0, pos[:100]] = np.float32(5.0)
-        s[b, 0, pos[100:5100]] = np.float32(1.0)
-    sels, cut = check_select(s, [L, L - 3001], [3000, 2500], [40, 40], [3, 4], 0.05, "tie cut")
-    for sel in sels.values():
-        S, full = sel["S"], sel["S_full"]
-        assert 100 < S.size < full.size, (S.size, full.size)  # the cut is inside the ties
-    assert cut > 0
+    assert any(i["S"].size < i["S_full"].size for i in info.values())
