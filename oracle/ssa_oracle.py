@@ -109,6 +109,23 @@ R18 Split keys (FASA-M): a key row is held as two rows under the same row
     pos mod 16 of block block_table[b][pos // 16]; negative positions are
     skipped.  A step over split keys computes what it computes over the
     whole keys they hold.
+R19 Query groups, refine mode (PIVOT "Two operating modes": each member
+    refines the proxy's candidate list): with a refine factor r >= 1 the
+    group's proxy selection (R16) runs with a deterministic stratum of r * k
+    tokens -- the candidate list C -- and each member t then scores C's
+    tokens inside its span with its own query (the mean of its G heads'
+    partial logits over the scored pairs) and takes the first
+    k_t = min(k, |C inside its span|) of them in the order (own score
+    descending, index ascending) as its own deterministic stratum S_t
+    (dense when k_t + m >= its span).  Its tail is the group's span minus
+    S_t, sampled with the proxy's weights w_j = sexp(s_j - M) (M the group's
+    maximum proxy score) and its own normaliser W_t = sum of w_j over that
+    tail (float64 sum rounded to float32), with the group's uniforms (Philox
+    counter (j >> 2, h, b, group)); pi_j = min(1, fl(fl(m w_j) / W_t)).  The
+    member attends over S_t and its samples inside its span.  The own score
+    is ranked in the decision precision: per head the float32 dot over the
+    scored dims (8-dim slices in dim order, then the slices pairwise, as in
+    R17), the heads summed in head order, times fl32(fl32(scale) / G).
 """
 
 from __future__ import annotations
@@ -145,6 +162,8 @@ __all__ = [
     "member_span",
     "group_span",
     "decode_multi",
+    "member_scores",
+    "refine_member",
     "split_keys",
     "join_keys",
     "append_kv",
@@ -583,15 +602,67 @@ def group_span(P: int, T: int, g: int, grp: int) -> int:
     return max(P - T + min((grp + 1) * g, T), 0)
 
 
+def member_scores(q_member: np.ndarray, K: np.ndarray, pair_begin: int, pair_count: int,
+                  scale: float) -> np.ndarray:
+    """A member's own approximate score of each key row, float32 [n], in the
+    decision precision of R19: per head the float32 dot over the scored dims
+    (R17's summation order), summed over the G heads in head order, times
+    fl32(fl32(scale) / G)."""
+    dims = np.arange(2 * pair_begin, 2 * (pair_begin + pair_count))
+    q = np.asarray(q_member)[:, dims]
+    dots = stop_logits(q, np.asarray(K)[:, dims], 1.0)  # [G, n]
+    acc = dots[0]
+    for g in range(1, dots.shape[0]):
+        acc = np.add(acc, dots[g], dtype=_F32)
+    c = np.divide(_F32(scale), _F32(dots.shape[0]), dtype=_F32)
+    return np.multiply(acc, c, dtype=_F32)
+
+
+def refine_member(sel_group: dict, s32_group: np.ndarray, q_member: np.ndarray, K: np.ndarray,
+                  Lt: int, topk: int, m: int, seed: int, b: int, h: int, grp: int,
+                  pair_begin: int, pair_count: int, scale: float, W_in=None) -> dict:
+    """Refine mode (R19): member t's own selection from the group's
+    selection with candidate list C = sel_group["S"] (r * k tokens of the
+    proxy order).  K holds the group span's key rows.  Returns a dict with
+    S, R (samples inside the member's span), pi_R, W, dense."""
+    Lg = s32_group.size
+    C = np.asarray(sel_group["S"], np.int64)
+    cand = C[C < Lt]
+    own = member_scores(q_member, K[cand], pair_begin, pair_count, scale)
+    kt = min(topk, cand.size)
+    e = np.zeros(0, np.int64)
+    if kt + m >= Lt:  # reading R5 for the member
+        return dict(S=np.arange(Lt, dtype=np.int64), R=e, pi_R=np.zeros(0, _F32), W=_F32(0),
+                    dense=True)
+    order = np.lexsort((cand, ~order_key(own)))  # own score descending, index ascending
+    S = np.sort(cand[order[:kt]])
+    in_s = np.zeros(Lg, bool)
+    in_s[S] = True
+    T = np.nonzero(~in_s)[0].astype(np.int64)  # the group's span minus S_t
+    w = sexp(np.subtract(np.asarray(s32_group, _F32)[T], sel_group["M"], dtype=_F32))
+    W = _F32(w.astype(np.float64).sum()) if W_in is None else _F32(W_in)
+    if m == 0 or T.size == 0 or not W > 0:
+        return dict(S=S, R=e, pi_R=np.zeros(0, _F32), W=W, dense=False)
+    mw = np.multiply(_F32(m), w, dtype=_F32)
+    pi = np.minimum(_F32(1.0), np.divide(mw, W, dtype=_F32)).astype(_F32)
+    u = uniforms(seed, b, h, T, grp)
+    keep = (np.multiply(u, W, dtype=_F32) < mw) & (T < Lt)
+    return dict(S=S, R=T[keep], pi_R=pi[keep], W=W, dense=False)
+
+
 def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget, seed,
                  pair_begin: int, pair_count: int, query_group: int,
-                 scale: float | None = None, units=None, top_p=None, stop_tau=None):
+                 scale: float | None = None, units=None, top_p=None, stop_tau=None,
+                 refine: int = 0):
     """T query positions per sequence, g = query_group per shared selection.
 
     q [B, T, Hq, d]; seq_lens are the cache lengths P_b (the T new tokens
     included).  ``units`` optionally restricts the work to (b, grp, h)
-    triples.  Returns (out [B, T, Hq, d] float64, info keyed by (b, grp, h)
-    with the group's scores and selection).
+    triples.  With ``refine`` = r >= 1 every member refines the group's
+    candidate list of r * k tokens (R19) instead of reusing its selection.
+    Returns (out [B, T, Hq, d] float64, info keyed by (b, grp, h) with the
+    group's scores and selection, and with refine a "members" dict keyed by
+    t with each member's selection).
     """
     q = np.asarray(q)
     B, T, Hq, d = q.shape
@@ -615,6 +686,21 @@ def decode_multi(q, k_cache, v_cache, block_table, seq_lens, topk, sample_budget
         qstack = np.concatenate([q[b, t, h * G:(h + 1) * G, :] for t in members]).astype(np.float64)
         s64 = approx_scores(qstack, K, pair_begin, pair_count, scale)
         tp = None if top_p is None else np.float32(top_p[b])
+        if refine:
+            s32 = s64.astype(_F32)
+            k, m = int(topk[b]), int(sample_budget[b])
+            sel = select_unit(s32, int(refine) * k, m, int(seed[b]), b, h, grp=c)
+            mem = {}
+            for t in members:
+                Lt = member_span(P, T, t)
+                qg = q[b, t, h * G:(h + 1) * G, :].astype(np.float64)
+                ms = refine_member(sel, s32, qg, K, Lt, k, m, int(seed[b]), b, h, c,
+                                   pair_begin, pair_count, scale)
+                mem[t] = ms
+                out[b, t, h * G:(h + 1) * G, :] = attend_unit(qg, K[:Lt], V[:Lt], ms["S"],
+                                                              ms["R"], ms["pi_R"], scale)
+            info[(b, c, h)] = dict(scores=s64, span=Lg, members=mem, **sel)
+            continue
         spans = [member_span(P, T, t) for t in members for _ in range(G)]
         sel = select_unit(s64.astype(_F32), int(topk[b]), int(sample_budget[b]), int(seed[b]),
                           b, h, top_p=tp, grp=c, stop_tau=stop_tau,
