@@ -50,8 +50,9 @@
  *   members' queries ("PIVOT slashes sparse-attention indexer cost", "The two
  *   observations behind PIVOT"), and its one selection serves every member,
  *   each restricted to its own span.  NG = ceil(T / g) groups per sequence.
- *   Selection units are u = (b * NG + group) * Hkv + h.  T = g = 1 is plain
- *   one-token decode.
+ *   Selection units are u = (b * NG + group) * Hkv + h (with params.refine,
+ *   every member's own: see "Refine mode").  T = g = 1 is plain one-token
+ *   decode.
  *
  * Layouts (row-major, innermost last)
  *   q            [B, T, Hq, d]                   bf16 (post-RoPE queries)
@@ -152,6 +153,9 @@ typedef struct ssa_params {
   int32_t max_topk;           /* >= 0: an upper bound of topk[b] (larger device values    */
                               /*   act as it); 0 = max_seq_len.  Early stopping needs     */
                               /*   it (or max_seq_len) <= SSA_STOP_MAX_STRATUM            */
+  int32_t refine;             /* >= 0: 0 = query groups reuse the group's selection;     */
+                              /*   r >= 1 = every member refines a candidate list of      */
+                              /*   r * topk tokens (see "Refine mode" below)              */
 } ssa_params;
 
 /* Largest deterministic stratum the early-stopping kernels order (tokens). */
@@ -202,6 +206,25 @@ int32_t ssa_num_chunks(const ssa_params* p);
  * takes six short kernels (about 40 us for a 1M-token layer of 8 kv heads
  * with a 10486-token stratum), more than the attention it saves at 50x
  * sparsity; it pays only where attention over the stratum dominates.
+ *
+ * Refine mode ("PIVOT slashes sparse-attention indexer cost", "The two
+ * observations behind PIVOT" and "Two operating modes": the proxy's
+ * candidate list is refined for each member).  With params.refine = r >= 1
+ * the group's selection runs with a stratum of r * topk tokens, the
+ * candidate list C; each member t (query position) then scores C's tokens
+ * inside its span with its own query -- per head the float32 dot over the
+ * scored dims (8-dim slices in dim order, then the slices pairwise), the
+ * heads summed in head order, times fl32(fl32(scale) / G) -- and keeps the
+ * first k_t = min(topk, |C inside its span|) of them in the order (own score
+ * descending, position ascending); it is dense when k_t + m reaches its span.
+ * Its tail is the group's span minus its stratum, sampled with the proxy's
+ * weights exp(s_j - M), the group's Philox stream and its own normaliser
+ * W_t (the sum of those weights over its tail).  Every member then has its
+ * own selection: ssa_select writes, ssa_attend reads and w_in / norm_out
+ * hold one selection unit per (b, t, h), u = (b * T + t) * Hkv + h, in the
+ * layout below with NG = T.  Not combined with top_p or early stopping
+ * (SSA_ERR_INVALID); the group's staged query slices, min(query_group,
+ * num_queries) * Hq / Hkv * 2 * pair_count floats, must be at most 8192.
  *
  * Tail.  sample_budget[b] (m) is the expected number of tail samples.  If
  * k + m >= L_b every token is read with weight 1 (dense attention).

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
   const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   if (c0 >= p.L || p.dense || p.k_eff == 0) return;  // uniform over the workgroup
   const float M = key_to_float(maxkey);
   for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = 0ull;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   const uint32_t maxkey = a.maxkey[u];
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   if (p.dense || p.L == 0) {
     if (threadIdx.x == 0) a.thresh[u] = Thresh1{kBins, 0, 0.0f, 0, 0ull, 0, 0};
     return;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void f
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const int h = ui.h;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   if (c0 >= p.L || p.dense) return;  // uniform over the workgroup
   const float M = key_to_float(maxkey);
   if (!direct) {
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   constexpr int kHist = kBins / kRT;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk);
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   const Thresh1 t1 = a.thresh[u];
   const uint32_t maxkey = a.maxkey[u];
   uint32_t hv[kHist];
@@ -462,6 +462,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
     }
   }
   st.W = a.w_in ? a.w_in[u] : (float)W;
+  if (a.w64 && threadIdx.x == 0) a.w64[u] = W;
   if (!(st.flags & (kFlagEmpty | kFlagDense)) && p.m > 0 && p.L - st.k_eff > 0 && st.W > 0.0f)
     st.flags |= kFlagSample;
   if (threadIdx.x == 0) {

@@ -45,7 +45,13 @@ bool params_ok(const ssa_params* p) {
   if (!(p->softmax_scale >= 0.0f) || !std::isfinite(p->softmax_scale)) return false;
   if (p->num_queries < 1 || p->num_queries > 256 || p->query_group < 1) return false;
   if (p->key_layout != SSA_KEYS_WHOLE && p->key_layout != SSA_KEYS_SPLIT) return false;
-  if (p->max_topk < 0) return false;
+  if (p->max_topk < 0 || p->refine < 0) return false;
+  if (p->refine > 0) {
+    if (p->early_stop > 0.0f) return false;  // not combined with early stopping
+    // the refine kernels stage the group's scored query slices in LDS
+    const int g = p->query_group < p->num_queries ? p->query_group : p->num_queries;
+    if ((int64_t)g * G * 2 * p->pair_count > 8192) return false;
+  }
   if (p->early_stop > 0.0f) {  // NaN compares false: off
     // the stratum must fit the early-stopping kernels, and so must the rows
     const int bound = p->max_topk > 0 ? p->max_topk : p->max_seq_len;
@@ -68,6 +74,8 @@ bool params_ok(const ssa_params* p) {
 
 struct Dims {
   int B, Hq, Hkv, G, d, T, g, NG, U, NC, NS;
+  int refine;  // candidate list factor r of the refine mode (0: reuse)
+  int Um;      // member units B * T * Hkv (refine mode)
   int NSUB;  // attention waves per split (NS * NSUB <= the merge's 4096 states)
   int64_t SEG;
   float scale;
@@ -98,9 +106,15 @@ Dims dims_of(const ssa_params* p) {
   d.NC = (p->max_seq_len + SSA_CHUNK_TOKENS - 1) / SSA_CHUNK_TOKENS;
   d.SEG = (int64_t)d.NC * SSA_CHUNK_TOKENS;
   d.NS = p->num_splits == 0 ? d.NC : (p->num_splits < d.NC ? p->num_splits : d.NC);
+  d.refine = p->refine;
+  d.Um = d.B * d.T * d.Hkv;
   {
+    // Attention runs over the selection units, or with refine over the
+    // member units (one member each).
+    const int ag = d.refine > 0 ? 1 : d.g;
+    const int64_t au = d.refine > 0 ? d.Um : d.U;
     const int mpw = 16 / d.G;  // query columns per attention wave: members x heads
-    const int64_t waves = (int64_t)d.NS * d.U * ((d.g + mpw - 1) / mpw);
+    const int64_t waves = (int64_t)d.NS * au * ((ag + mpw - 1) / mpw);
     d.NSUB = 1;
     while (d.NSUB < kAttendMaxSub && waves * d.NSUB * 2 <= kAttendWaves &&
            (int64_t)d.NS * d.NSUB * 2 <= SSA_MAX_SEQ_LEN / SSA_CHUNK_TOKENS)
@@ -116,7 +130,8 @@ struct Layout {
   size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
-      stop_words, stop_pair, stop_rword, stop_logit, total;
+      stop_words, stop_pair, stop_rword, stop_logit, w64, own_key, mstate, msel_idx, msel_logw,
+      msel_cnt, total;
 };
 
 Layout layout_of(const Dims& d) {
@@ -158,6 +173,15 @@ Layout layout_of(const Dims& d) {
   l.stop_pair = take(SU * (KS / 1024) * (KS / 1024) * 1024 * 2);
   l.stop_rword = take(SU * KS * 8);
   l.stop_logit = take(SU * KS * SSA_STOP_MAX_ROWS * 4);
+  // refine mode's member selections (only when it is on)
+  const size_t RU = d.refine > 0 ? (size_t)d.U : 0;
+  const size_t RM = d.refine > 0 ? (size_t)d.Um : 0;
+  l.w64 = take(RU * 8);
+  l.own_key = take(RM * SEG * 4);
+  l.mstate = take(RM * 32);
+  l.msel_idx = take(RM * SEG * 4);
+  l.msel_logw = take(RM * SEG * 4);
+  l.msel_cnt = take(RM * NC * 2 * 4);
   l.total = off;
   return l;
 }
@@ -276,6 +300,8 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.stop_rword = d.stop ? at<unsigned long long>(ws, l.stop_rword) : nullptr;
   a.stop_logit = d.stop ? at<float>(ws, l.stop_logit) : nullptr;
   a.max_topk = p->max_topk > 0 ? p->max_topk : INT32_MAX;
+  a.kmult = d.refine > 0 ? d.refine : 1;
+  a.w64 = d.refine > 0 ? at<double>(ws, l.w64) : nullptr;
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint16_t*>(keys.main);
   a.k_rest = static_cast<const uint16_t*>(keys.rest);
@@ -298,6 +324,55 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   return a;
 }
 
+// The refine stage: the group selection (sel_*) is refined into member
+// selections (msel_*); norm_out and w_in are per member unit.
+ssa::RefineArgs refine_args(const ssa_params* p, const Dims& d, const ssa::SelectArgs& sa,
+                            const void* q, const void* k_main, const int32_t* block_table,
+                            const float* w_in, int32_t* msel_idx, float* msel_logw,
+                            int32_t* msel_cnt, float* norm_out, void* ws, const Layout& l) {
+  ssa::RefineArgs r;
+  r.scores = sa.scores;
+  r.score_ld = sa.score_ld;
+  r.gsel_idx = sa.sel_idx;
+  r.gsel_cnt = sa.sel_cnt;
+  r.gstate = sa.state;
+  r.gw64 = at<double>(ws, l.w64);
+  r.seq_lens = sa.seq_lens;
+  r.topk = sa.topk;
+  r.sample_budget = sa.sample_budget;
+  r.seed = sa.seed;
+  r.w_in = w_in;
+  r.q = static_cast<const uint16_t*>(q);
+  r.k_cache = static_cast<const uint16_t*>(k_main);
+  r.block_table = block_table;
+  r.own_key = at<uint32_t>(ws, l.own_key);
+  r.mstate = at<void>(ws, l.mstate);
+  r.msel_idx = msel_idx;
+  r.msel_logw = msel_logw;
+  r.msel_cnt = msel_cnt;
+  r.norm_out = norm_out;
+  r.T = d.T;
+  r.g = d.g;
+  r.NG = d.NG;
+  r.Hq = d.Hq;
+  r.Hkv = d.Hkv;
+  r.G = d.G;
+  r.d = d.d;
+  r.pair_begin = p->pair_begin;
+  r.pair_count = p->pair_count;
+  r.max_seq_len = p->max_seq_len;
+  r.nchunk = d.NC;
+  r.max_blocks = p->max_blocks_per_seq;
+  r.num_blocks = p->num_blocks;
+  r.max_topk = p->max_topk > 0 ? p->max_topk : INT32_MAX;
+  const bool split = p->key_layout == SSA_KEYS_SPLIT;
+  r.key_ld = split ? 2 * p->pair_count : d.d;
+  r.key_off = split ? 0 : 2 * p->pair_begin;
+  r.seg_ld = d.SEG;
+  r.own_scale = d.scale / (float)d.G;  // one float32 division
+  return r;
+}
+
 ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, Keys keys,
                             const void* v_cache, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* sel_idx, const float* sel_logw,
@@ -316,10 +391,11 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, K
   a.part = at<float>(ws, l.part);
   a.out = out;
   a.T = d.T;
-  a.g = d.g;
-  a.NG = d.NG;
+  // With refine every member has its own selection: one member per unit.
+  a.g = d.refine > 0 ? 1 : d.g;
+  a.NG = d.refine > 0 ? d.T : d.NG;
   a.mpw = 16 / d.G;  // G <= 16
-  a.mblocks = (d.g + a.mpw - 1) / a.mpw;
+  a.mblocks = (a.g + a.mpw - 1) / a.mpw;
   a.B = d.B;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -415,12 +491,25 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
   // One query per sequence: the selection can hold cache rows (one dependent
   // load less in the gather).  Several: positions, so that every member
   // applies its own causal span.
-  const int rows = d.T == 1 ? 1 : 0;
+  if (d.refine > 0 && top_p) return SSA_ERR_INVALID;  // refine ranks by count only
+  const int rows = d.T == 1 && d.refine == 0 ? 1 : 0;
   const ssa::SelectArgs sa =
       select_args(p, d, scores, d.SEG, seq_lens, topk, top_p, sample_budget, seed, nullptr, q,
                   keys, block_table, rows, sel_idx, sel_logw, sel_cnt, nullptr, workspace, l);
-  const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, sel_idx,
-                                         sel_logw, sel_cnt, rows, out, workspace, l);
+  // With refine, attention reads the member selections.
+  int32_t* a_idx = sel_idx;
+  float* a_logw = sel_logw;
+  int32_t* a_cnt = sel_cnt;
+  ssa::RefineArgs ra{};
+  if (d.refine > 0) {
+    a_idx = at<int32_t>(workspace, l.msel_idx);
+    a_logw = at<float>(workspace, l.msel_logw);
+    a_cnt = at<int32_t>(workspace, l.msel_cnt);
+    ra = refine_args(p, d, sa, q, keys.main, block_table, nullptr, a_idx, a_logw, a_cnt, nullptr,
+                     workspace, l);
+  }
+  const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, a_idx,
+                                         a_logw, a_cnt, rows, out, workspace, l);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(launch_init_for(sa, d.U, s));
   rec.end(SSA_STAGE_INIT);
@@ -435,6 +524,7 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
   rec.end(SSA_STAGE_RESOLVE);
   rec.begin(SSA_STAGE_SAMPLE);
   SSA_TRY(ssa::launch_sample(sa, d.U, s));
+  if (d.refine > 0) SSA_TRY(ssa::launch_refine(ra, d.U, d.Um, s));
   rec.end(SSA_STAGE_SAMPLE);
   rec.begin(SSA_STAGE_ATTEND);
   SSA_TRY(ssa::launch_attend(aa, s));
@@ -540,7 +630,8 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
     return SSA_ERR_INVALID;
   const Dims d = dims_of(p);
   Keys keys{nullptr, nullptr};
-  if (d.stop) {  // early stopping weighs the stratum by exact attention
+  if (d.refine > 0 && top_p) return SSA_ERR_INVALID;  // refine ranks by count only
+  if (d.stop || d.refine > 0) {  // exact gains and own scores read the query and keys
     if (!q || !aligned16(q) || !block_table) return SSA_ERR_INVALID;
     if (p->key_layout == SSA_KEYS_SPLIT) {
       if (!split_keys_ok(p, k_cache, k_rest)) return SSA_ERR_INVALID;
@@ -551,6 +642,23 @@ int ssa_select(const ssa_params* p, const float* scores, const int32_t* seq_lens
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.refine > 0) {
+    // The group selection goes to the workspace, the members' to the caller.
+    const ssa::SelectArgs sa = select_args(
+        p, d, scores, p->max_seq_len, seq_lens, topk, nullptr, sample_budget, seed, nullptr, q,
+        keys, block_table, /*emit_rows=*/0, at<int32_t>(workspace, l.sel_idx),
+        at<float>(workspace, l.sel_logw), at<int32_t>(workspace, l.sel_cnt), nullptr,
+        workspace, l);
+    const ssa::RefineArgs ra = refine_args(p, d, sa, q, keys.main, block_table, w_in, sel_idx,
+                                           sel_logw, sel_count, norm_out, workspace, l);
+    SSA_TRY(launch_init_for(sa, d.U, s));
+    SSA_TRY(ssa::launch_score_hist(sa, d.U, s));
+    SSA_TRY(launch_first_digit(sa, d.U, s));
+    SSA_TRY(launch_resolve_for(sa, d.U, s));
+    SSA_TRY(ssa::launch_sample(sa, d.U, s));
+    SSA_TRY(ssa::launch_refine(ra, d.U, d.Um, s));
+    return SSA_OK;
+  }
   const ssa::SelectArgs sa =
       select_args(p, d, scores, p->max_seq_len, seq_lens, topk, top_p, sample_budget, seed, w_in,
                   q, keys, block_table, /*emit_rows=*/0, sel_idx, sel_logw, sel_count, norm_out,

@@ -41,6 +41,19 @@ struct UnitState {
 };
 static_assert(sizeof(UnitState) == 32, "the host reserves 32 bytes per unit");
 
+// Refine mode: a member's selection state.  The member's stratum is the
+// candidates whose word ((~own key) << 24) | position is at most vstar.
+struct MemberState {
+  unsigned long long vstar;
+  float W;     // the member's tail normaliser
+  float M;     // the group's maximum proxy score
+  int32_t k;   // the member's stratum size
+  int32_t flags;
+  int32_t L;   // the member's span
+  int32_t m;
+};
+static_assert(sizeof(MemberState) == 32, "the host reserves 32 bytes per member unit");
+
 // ---------------------------------------------------------------- sizes
 
 __device__ __forceinline__ int clamp_len(int L, int max_seq_len) {
@@ -370,10 +383,11 @@ struct SeqParams {
 
 __device__ __forceinline__ SeqParams seq_params(int L, const int32_t* topk, const float* top_p,
                                                 const int32_t* sample_budget, int b,
-                                                int max_topk) {
+                                                int max_topk, int kmult = 1) {
   SeqParams p;
   p.L = L;
-  const int k = min(max(topk[b], 0), max_topk);
+  const int64_t k64 = (int64_t)min(max(topk[b], 0), max_topk) * kmult;
+  const int k = k64 > L ? L : (int)k64;
   p.m = max(sample_budget[b], 0);
   p.topp = top_p != nullptr;
   p.p = p.topp ? top_p[b] : 1.0f;

@@ -89,6 +89,8 @@ struct SelectArgs {
   int32_t* sel_cnt;           // [U, nchunk, 2]
   float* norm_out;            // [U, 2] or null
   int max_topk;               // topk[b] above it acts as it (INT_MAX: no bound)
+  int kmult;                  // the stratum holds kmult * topk tokens (refine mode's list)
+  double* w64;                // [U] the tail sum W in float64, or null
   // Early stopping (all null when it is off).  A stratum word is
   // ((~key) << 32) | position: ascending words are the stratum's order.
   float stop_tau;                 // the threshold tau, clamped to 1
@@ -136,6 +138,37 @@ struct AttendArgs {
   float scale;
 };
 
+// Refine mode of query groups: every member re-ranks the group's candidate
+// list (the group selection's deterministic entries) by its own score.
+// Member units are v = (b * T + t) * Hkv + h.
+struct RefineArgs {
+  const float* scores;        // the group's proxy scores, row u of stride score_ld
+  int64_t score_ld;
+  const int32_t* gsel_idx;    // [U, seg_ld] the group selection (positions)
+  const int32_t* gsel_cnt;    // [U, nchunk, 2]
+  const void* gstate;         // [U] UnitState of the group selection
+  const double* gw64;         // [U] the group's tail sum (its span minus C), float64
+  const int32_t* seq_lens;
+  const int32_t* topk;
+  const int32_t* sample_budget;
+  const uint64_t* seed;
+  const float* w_in;          // [Um] replaces each member's normaliser, or null
+  const uint16_t* q;          // [B, T, Hq, d]
+  const uint16_t* k_cache;    // the scored dims of row r at k_cache + r * key_ld + key_off
+  const int32_t* block_table;
+  uint32_t* own_key;          // [Um, seg_ld] member's order key of each group entry
+  void* mstate;               // [Um] MemberState
+  int32_t* msel_idx;          // [Um, seg_ld] member selections (positions)
+  float* msel_logw;           // [Um, seg_ld]
+  int32_t* msel_cnt;          // [Um, nchunk, 2]
+  float* norm_out;            // [Um, 2] (M, W_t) or null
+  int T, g, NG, Hq, Hkv, G, d, pair_begin, pair_count;
+  int max_seq_len, nchunk, max_blocks, num_blocks, max_topk;
+  int key_ld, key_off;
+  int64_t seg_ld;
+  float own_scale;            // fl32(fl32(scale) / G)
+};
+
 // Appending new tokens' keys and values to the cache (whole or split keys).
 struct AppendArgs {
   const uint16_t* k_new;      // [B, T, Hkv, d]
@@ -163,6 +196,8 @@ hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_refine(const RefineArgs& a, int group_units, int member_units,
+                         hipStream_t stream);
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int n,
                                uint32_t* words, hipStream_t stream);

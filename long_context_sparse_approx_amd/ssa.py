@@ -47,7 +47,8 @@ class SsaParams(ctypes.Structure):
                 ("num_splits", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("num_queries", ctypes.c_int32),
                 ("query_group", ctypes.c_int32), ("early_stop", ctypes.c_float),
-                ("key_layout", ctypes.c_int32), ("max_topk", ctypes.c_int32)]
+                ("key_layout", ctypes.c_int32), ("max_topk", ctypes.c_int32),
+                ("refine", ctypes.c_int32)]
 
 
 class SsaError(RuntimeError):
@@ -150,13 +151,13 @@ def make_params(*, batch, num_q_heads, num_kv_heads, head_dim, max_blocks_per_se
                 max_seq_len, pair_begin=None, pair_count=32, num_splits=0, out_dtype=SSA_F32,
                 softmax_scale=0.0, block_size=BLOCK_TOKENS, num_queries=1,
                 query_group=1, early_stop=0.0, key_layout=SSA_KEYS_WHOLE,
-                max_topk=0) -> SsaParams:
+                max_topk=0, refine=0) -> SsaParams:
     if pair_begin is None:
         pair_begin = head_dim // 2 - pair_count
     return SsaParams(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks, max_seq_len, pair_begin, pair_count, num_splits, out_dtype,
                      float(softmax_scale), int(num_queries), int(query_group),
-                     float(early_stop), int(key_layout), int(max_topk))
+                     float(early_stop), int(key_layout), int(max_topk), int(refine))
 
 
 def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
@@ -176,6 +177,12 @@ def params_for(q, k_cache, block_table, max_seq_len, **kw) -> SsaParams:
 def num_groups(p: SsaParams) -> int:
     g = min(p.query_group, p.num_queries)
     return -(-p.num_queries // g)
+
+
+def selection_rows(p: SsaParams) -> int:
+    """Selection units per sequence: groups x kv heads, or with refine one
+    per query position and kv head (every member has its own selection)."""
+    return (p.num_queries if p.refine > 0 else num_groups(p)) * p.num_kv_heads
 
 
 def workspace_bytes(p: SsaParams) -> int:
@@ -293,11 +300,14 @@ def select(p: SsaParams, scores, seq_lens, topk, sample_budget, seed, w_in=None,
     """Selection from a score array: (sel_idx, sel_logw, sel_count, norm_out),
     each [B, NG*Hkv, ...] (one row per selection unit).  With early stopping
     (p.early_stop > 0) the query, keys (k_rest for split keys) and block
-    table are needed too: the stratum is weighed by exact attention."""
+    table are needed too: the stratum is weighed by exact attention.  With
+    refine (p.refine > 0) they are needed as well (each member scores the
+    group's candidates), the selections are the members' ([B, T*Hkv, ...])
+    and w_in, norm_out are per member."""
     _check_top_p(top_p, p.batch)
     dev = scores.device
     nc = num_chunks(p)
-    UH = num_groups(p) * p.num_kv_heads
+    UH = selection_rows(p)
     U = p.batch * UH
     sel_idx = torch.empty((p.batch, UH, nc * CHUNK_TOKENS), dtype=torch.int32, device=dev)
     sel_logw = torch.empty((p.batch, UH, nc * CHUNK_TOKENS), dtype=torch.float32, device=dev)

@@ -229,8 +229,12 @@ def make_workload(name_or_cfg, device="cpu", *, L=None, B=None, topk=None, m=Non
             k_cache[blk, :, slot, :] = kz.to(torch.bfloat16)
             v_cache[blk, :, slot, :] = vz.to(torch.bfloat16)
     rule = [budget_rule(L_) for L_ in lens]
-    tk = [r[0] for r in rule] if cfg["topk"] == "rule" else [int(cfg["topk"])] * B
-    mm = [r[1] for r in rule] if cfg["m"] == "rule" else [int(cfg["m"])] * B
+    def per_seq(v, i):  # "rule", one value for every sequence, or one per sequence
+        if isinstance(v, str):
+            return [r[i] for r in rule]
+        return [int(x) for x in v] if isinstance(v, (list, tuple)) else [int(v)] * B
+
+    tk, mm = per_seq(cfg["topk"], 0), per_seq(cfg["m"], 1)
     seeds_ = list(cfg["seeds"])
     if len(seeds_) == 1 and B > 1:
         seeds_ = seeds_ * B

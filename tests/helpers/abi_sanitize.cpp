@@ -28,6 +28,7 @@ hipError_t launch_sample(const SelectArgs&, int, hipStream_t) { ++g_launches; re
 hipError_t launch_attend(const AttendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_append(const AppendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_merge(const AttendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+hipError_t launch_refine(const RefineArgs&, int, int, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_debug_philox(uint64_t, int, int, int, int, int, uint32_t*, hipStream_t) {
   ++g_launches;
   return hipErrorInvalidValue;
@@ -125,6 +126,37 @@ int main() {
     CHECK(ssa_select(&p, nullptr, i32, i32, nullptr, i32, u64, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, w, need,
                      nullptr) != SSA_OK);
+    // refine mode: not with early stopping, the staged query slices must fit,
+    // and the selection needs the query and keys
+    {
+      ssa_params rp = valid();
+      rp.num_queries = 4;
+      rp.query_group = 4;
+      rp.refine = 2;
+      CHECK(ssa_workspace_bytes(&rp) > ssa_workspace_bytes(&p));
+      rp.refine = -1;
+      CHECK(ssa_workspace_bytes(&rp) == 0);
+      rp.refine = 2;
+      rp.early_stop = 0.5f;
+      CHECK(ssa_workspace_bytes(&rp) == 0);
+      rp.early_stop = 0.0f;
+      rp.num_queries = 64;
+      rp.query_group = 64;  // 64 members x 4 heads x 64 scored dims > 8192 staged floats
+      CHECK(ssa_workspace_bytes(&rp) == 0);
+      rp.num_queries = 4;
+      rp.query_group = 4;
+      const size_t need_r = ssa_workspace_bytes(&rp);
+      std::vector<unsigned char> wr(need_r + 256);
+      float* sc = reinterpret_cast<float*>(buf);
+      int32_t* o32 = reinterpret_cast<int32_t*>(buf);
+      float* of = reinterpret_cast<float*>(buf);
+      CHECK(ssa_select(&rp, sc, i32, i32, nullptr, i32, u64, nullptr, nullptr, dev, nullptr, i32,
+                       o32, of, o32, of, wr.data(), need_r, nullptr) == SSA_ERR_INVALID);
+      CHECK(ssa_select(&rp, sc, i32, i32, f32, i32, u64, nullptr, dev, dev, nullptr, i32, o32,
+                       of, o32, of, wr.data(), need_r, nullptr) == SSA_ERR_INVALID);
+      CHECK(ssa_decode(&rp, dev, dev, dev, i32, i32, i32, f32, i32, u64, dev, wr.data(), need_r,
+                       nullptr) == SSA_ERR_INVALID);
+    }
     // early stopping: the stratum bound and the rows must fit its kernels, and
     // the selection needs the query and keys
     {
