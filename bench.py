@@ -117,7 +117,7 @@ def split_keys(wl, host):
 
 
 def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None,
-            num_queries=1, query_group=1, early_stop=0.0, keys="whole"):
+            num_queries=1, query_group=1, early_stop=0.0, keys="whole", refine=0):
     """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
     ``top_p`` (a float) caps every sequence's deterministic stratum at the
     top-p prefix; ``wl`` reuses an already generated workload; with
@@ -141,7 +141,7 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
                        pair_begin=wl.pair_begin, pair_count=wl.pair_count,
                        query_group=query_group, early_stop=early_stop,
                        key_layout=ssa.SSA_KEYS_SPLIT if split else ssa.SSA_KEYS_WHOLE,
-                       max_topk=int(wl.topk.max()))
+                       max_topk=int(wl.topk.max()), refine=refine)
     ws = ssa.alloc_workspace(p, dev)
     out = torch.empty(wl.q.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
@@ -533,18 +533,20 @@ def main():
         T = args.multi
         mq = dict(queries_per_step=T,
                   policy="T query positions per sequence (the last T cache positions); a group "
-                         "of g consecutive queries is scored once with its mean query and "
-                         "shares one selection; every query attends over it within its "
-                         "causal span",
+                         "of g consecutive queries is scored once with its mean query; reuse: "
+                         "the group's one selection serves every query within its causal "
+                         "span; refine_2: every query re-ranks the group's 2 x top-k "
+                         "candidates by its own score and samples the rest with its own "
+                         "normaliser; group_1: one selection per query",
                   unit="query-KV-tokens/s/layer")
         wl_m = None
-        for g in (T, 1):
+        for key, g, r in ((f"group_{T}", T, 0), (f"group_{T}_refine_2", T, 2), ("group_1", 1, 0)):
             r4 = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events,
-                         wl=wl_m, num_queries=T, query_group=g)
+                         wl=wl_m, num_queries=T, query_group=g, refine=r)
             wl_m = r4["wl"]
             s4 = summarize(r4, args.workload)
-            mq[f"group_{g}"] = dict(value=T * s4["value"], ms_per_step=s4["ms_per_step"],
-                                    stages_us=s4["stages_us"], selected=s4["selected"])
+            mq[key] = dict(value=T * s4["value"], ms_per_step=s4["ms_per_step"],
+                           stages_us=s4["stages_us"], selected=s4["selected"])
             del r4
         del wl_m
         torch.cuda.empty_cache()

@@ -36,7 +36,7 @@ namespace ssa {
 namespace {
 
 constexpr int kRS = 256;     // threads of a score or emit workgroup
-constexpr int kRT = 1024;    // threads of a member's select workgroup
+constexpr int kRT = 1024;    // threads of a member's select workgroup (one per member unit)
 constexpr int kRefineQ = 8192;  // floats of the group's staged query slices
 
 __device__ __forceinline__ void decode_member(const RefineArgs& a, int v, int* b, int* t, int* h,
@@ -52,12 +52,36 @@ __device__ __forceinline__ unsigned long long member_word(uint32_t own_key, int 
   return ((unsigned long long)(~own_key) << 24) | (uint32_t)pos;
 }
 
-// Grid: (chunks, group units) x kRS threads.  LPT lanes per candidate (one
-// 16-byte slice of its scored dims each); all the group's members are scored
-// from one load of the slice.
+// The partner lane across lane-index bit BIT of a 16-lane row (DPP: quad
+// permutations for bits 0 and 1, the half-row mirror for bit 2, a rotation
+// by 8 for bit 3).  Each pairing is an involution that joins the two halves
+// of the current group, so the butterfly sums neighbouring slices first.
+template <int BIT>
+__device__ __forceinline__ float dpp_partner(float x) {
+  constexpr int ctrl = BIT == 0 ? 0xB1 : (BIT == 1 ? 0x4E : (BIT == 2 ? 0x141 : 0x128));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               ctrl, 0xf, 0xf, false));
+}
+
+template <int LPT>
+__device__ __forceinline__ float butterfly(float p) {
+  if constexpr (LPT >= 2) p = p + dpp_partner<0>(p);
+  if constexpr (LPT >= 4) p = p + dpp_partner<1>(p);
+  if constexpr (LPT >= 8) p = p + dpp_partner<2>(p);
+  if constexpr (LPT >= 16) p = p + dpp_partner<3>(p);
+  return p;
+}
+
+// Grid: (chunks, group units) x kRS threads; dynamic LDS holds the group's
+// scored query slices (nmem * G * 2 * pair_count floats).  LPT lanes per
+// candidate (one 16-byte slice of its scored dims each); all the group's
+// members are scored from one load of the slice.  A thread's candidates
+// (kPass passes of kRS / LPT) have their positions, block ids and slices
+// loaded in three rounds, each round's loads all in flight together.
+constexpr int kPass = 4;
 template <int LPT>
 __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
-  __shared__ float qsh[kRefineQ];
+  extern __shared__ float qsh[];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
@@ -70,7 +94,7 @@ __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
   const int t0 = ui.grp * a.g;
   const int nmem = min(a.g, a.T - t0);
   const int nd = 2 * a.pair_count;
-  const int rowq = a.G * nd;  // floats per member (the host keeps nmem * rowq <= kRefineQ)
+  const int rowq = a.G * nd;  // floats per member
   for (int i = threadIdx.x; i < nmem * rowq; i += kRS) {
     const int mi = i / rowq;
     const int r = i - mi * rowq;
@@ -80,38 +104,51 @@ __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
         a.q[((size_t)(b * a.T + t0 + mi) * a.Hq + h * a.G + gh) * a.d + 2 * a.pair_begin + e];
     qsh[i] = __uint_as_float((uint32_t)bits << 16);
   }
-  __syncthreads();
   const int sl = threadIdx.x % LPT;
   const int tk = threadIdx.x / LPT;
   constexpr int TPP = kRS / LPT;  // candidates per pass
   const int32_t* pidx = a.gsel_idx + (size_t)u * a.seg_ld + c0;
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
-  for (int base = 0; base < n_det; base += TPP) {  // uniform trip count
-    const int i = base + tk;
-    const bool valid = i < n_det;
-    const int pos = valid ? min(max(pidx[i], 0), ui.L - 1) : 0;
-    int blk = btrow[pos >> 4];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    const size_t row = (size_t)(blk * a.Hkv + h) * kBlockTokens + (pos & 15);
-    const uint4 kv =
-        *reinterpret_cast<const uint4*>(a.k_cache + row * a.key_ld + a.key_off + sl * 8);
-    const float kf[8] = {bf16_lo(kv.x), bf16_hi(kv.x), bf16_lo(kv.y), bf16_hi(kv.y),
-                         bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
-    for (int mi = 0; mi < nmem; ++mi) {  // uniform
-      float acc = 0.0f;
-      for (int gh = 0; gh < a.G; ++gh) {  // uniform
-        const float* qs = qsh + mi * rowq + gh * nd + sl * 8;
-        float p = qs[0] * kf[0];
+  __syncthreads();
+  for (int base = 0; base < n_det; base += kPass * TPP) {  // uniform trip count
+    int pos[kPass];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) p = p + qs[e] * kf[e];  // exact products, dim order
+    for (int p = 0; p < kPass; ++p) {
+      const int i = base + p * TPP + tk;
+      pos[p] = i < n_det ? min(max(pidx[i], 0), ui.L - 1) : 0;
+    }
+    int blk[kPass];
 #pragma unroll
-        for (int x = 1; x < LPT; x <<= 1) p = p + __shfl_xor(p, x);
-        acc = gh == 0 ? p : acc + p;
-      }
-      const float s = acc * a.own_scale;
-      if (valid && sl == 0) {
-        const int v = (b * a.T + t0 + mi) * a.Hkv + h;
-        a.own_key[(size_t)v * a.seg_ld + c0 + i] = order_key(s);
+    for (int p = 0; p < kPass; ++p) blk[p] = btrow[pos[p] >> 4];
+    uint4 kv[kPass];
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int bk = blk[p] < 0 ? 0 : (blk[p] >= a.num_blocks ? a.num_blocks - 1 : blk[p]);
+      const size_t row = (size_t)(bk * a.Hkv + h) * kBlockTokens + (pos[p] & 15);
+      kv[p] = *reinterpret_cast<const uint4*>(a.k_cache + row * a.key_ld + a.key_off + sl * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int i = base + p * TPP + tk;
+      if (base + p * TPP >= n_det) break;  // uniform
+      const float kf[8] = {bf16_lo(kv[p].x), bf16_hi(kv[p].x), bf16_lo(kv[p].y),
+                           bf16_hi(kv[p].y), bf16_lo(kv[p].z), bf16_hi(kv[p].z),
+                           bf16_lo(kv[p].w), bf16_hi(kv[p].w)};
+      for (int mi = 0; mi < nmem; ++mi) {  // uniform
+        float acc = 0.0f;
+        for (int gh = 0; gh < a.G; ++gh) {  // uniform
+          const float* qs = qsh + mi * rowq + gh * nd + sl * 8;
+          float d = qs[0] * kf[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) d = d + qs[e] * kf[e];  // exact products, dim order
+          d = butterfly<LPT>(d);
+          acc = gh == 0 ? d : acc + d;
+        }
+        const float s = acc * a.own_scale;
+        if (i < n_det && sl == 0) {
+          const int v = (b * a.T + t0 + mi) * a.Hkv + h;
+          a.own_key[(size_t)v * a.seg_ld + c0 + i] = order_key(s);
+        }
       }
     }
   }
@@ -146,10 +183,18 @@ __device__ __forceinline__ void find_bin_up(const uint32_t* hist, int nbins, int
   __syncthreads();
 }
 
-// Grid: member units x kRT threads.
+// Grid: member units x kRT threads.  The group's candidates are flattened
+// over its chunks (a prefix of the chunks' counts in LDS) and thread t takes
+// items t, t + kRT, ...: the first kKeep of them are read once into
+// registers as words, so the radix passes touch only registers and LDS (a
+// thread's further items, when the list exceeds kRT * kKeep, are read again
+// on every pass).
+constexpr int kKeep = 24;
+constexpr int kMaxChunks = SSA_MAX_SEQ_LEN / SSA_CHUNK_TOKENS;
 __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
-  constexpr int kDig = 4096;
+  constexpr int kDig = 8192;
   __shared__ uint32_t hist[kDig];
+  __shared__ int cpre[kMaxChunks + 1];  // candidates in chunks before c
   __shared__ int scan[kRT / 64];
   __shared__ int pair[2];
   __shared__ double dscr[kRT / 64];
@@ -164,26 +209,63 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
   const int k = min(max(a.topk[b], 0), a.max_topk);
   const int m = max(a.sample_budget[b], 0);
   const int nc = (Lg + kChunk - 1) / kChunk;
-  // Candidate passes: thread t serves chunk (t / tpc) + j * (kRT / tpc) and,
-  // inside it, entries (t % tpc) + i * tpc: fixed items, fixed sum orders.
-  int tpc = kRT;
-  while (tpc > 1 && tpc * nc > kRT) tpc >>= 1;
-  const int cstep = kRT / tpc;
-  const int csub = threadIdx.x % tpc;
   const size_t cu = (size_t)u * a.nchunk;
   const int32_t* gidx = a.gsel_idx + (size_t)u * a.seg_ld;
   const uint32_t* okey = a.own_key + (size_t)v * a.seg_ld;
-  auto each = [&](auto&& f) {
-    for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-      const int n = clamp_count(a.gsel_cnt[2 * (cu + c)], kChunk);
-      for (int i = csub; i < n; i += tpc) {
-        const size_t at = (size_t)c * kChunk + i;
-        f(min(max(gidx[at], 0), max(Lg - 1, 0)), at);
-      }
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  if (threadIdx.x < 2) hist[threadIdx.x] = 0u;
+  // Prefix of the chunks' candidate counts.
+  {
+    int run = 0;
+    for (int c0 = 0; c0 < nc; c0 += kRT) {
+      const int c = c0 + threadIdx.x;
+      const int n = c < nc ? clamp_count(a.gsel_cnt[2 * (cu + c)], kChunk) : 0;
+      int tot;
+      const int ex = block_exclusive_scan<kRT>(n, scan, &tot);
+      if (c < nc) cpre[c] = run + ex;
+      run += tot;
     }
+    if (threadIdx.x == 0) cpre[nc] = run;
+    __syncthreads();
+  }
+  const int N = cpre[nc];
+  // Item j's place in the group's segments: its chunk by binary search.
+  auto at_of = [&](int j) -> int {  // < nchunk * 4096 <= 2^24
+    int lo = 0, hi = nc;  // cpre[lo] <= j < cpre[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cpre[mid] <= j) lo = mid; else hi = mid;
+    }
+    return lo * kChunk + (j - cpre[lo]);
   };
+  auto word_of = [&](int j) -> unsigned long long {
+    const int at = at_of(j);
+    return member_word(okey[at], min(max(gidx[at], 0), max(Lg - 1, 0)));
+  };
+  unsigned long long wv[kKeep];
+  {
+    int at[kKeep];
+#pragma unroll
+    for (int e = 0; e < kKeep; ++e) {
+      const int j = threadIdx.x + e * kRT;
+      at[e] = j < N ? at_of(j) : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kKeep; ++e) {  // every load of the thread's items in flight
+      const int j = threadIdx.x + e * kRT;
+      wv[e] = j < N ? member_word(okey[at[e]], min(max(gidx[at[e]], 0), max(Lg - 1, 0))) : ~0ull;
+    }
+  }
+  // Every item of this thread (registers first, then memory), with f(word).
+  auto each = [&](auto&& f) {
+#pragma unroll
+    for (int e = 0; e < kKeep; ++e)
+      if (threadIdx.x + e * kRT < N) f(wv[e]);
+    for (int j = threadIdx.x + kKeep * kRT; j < N; j += kRT) f(word_of(j));
+  };
+  auto pos_of = [](unsigned long long w) { return (int)(w & 0xffffffull); };
   int ncand = 0;
-  each([&](int pos, size_t) { ncand += pos < Lt ? 1 : 0; });
+  each([&](unsigned long long w) { ncand += pos_of(w) < Lt ? 1 : 0; });
   ncand = block_sum_i32<kRT>(ncand, scan);
   const int kt = min(k, ncand);
   int flags = 0;
@@ -193,38 +275,93 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
   double W = 0.0;
   if (!(flags & (kFlagEmpty | kFlagDense))) {
     if (kt > 0) {
-      // Radix select of the kt-th smallest 56-bit word: the inverted own key
-      // as digits of 11, 11 and 10 bits, then the position as 12 and 12.
-      const int shifts[5] = {45, 34, 24, 12, 0};
-      const int widths[5] = {11, 11, 10, 12, 12};
+      // Radix select of the kt-th smallest word.  The candidates' inverted
+      // keys span [lo, lo + 2^kb), so the word's key part is taken relative
+      // to lo: 12-bit digits then cover the part of the key that differs
+      // (the top bits of the order key, sign and exponent, are shared by
+      // most candidates and would send them all to a few bins).
+      uint32_t lo = 0xffffffffu, hi = 0u;
+      each([&](unsigned long long w) {
+        if (pos_of(w) < Lt) {
+          const uint32_t ik = (uint32_t)(w >> 24);
+          lo = ik < lo ? ik : lo;
+          hi = ik > hi ? ik : hi;
+        }
+      });
+      lo = ~wave_max_u32(~lo);
+      hi = wave_max_u32(hi);
+      if ((threadIdx.x & 63) == 0) {
+        atomicMax(&hist[0], ~lo);  // hist[0..1] as scratch: both start at 0
+        atomicMax(&hist[1], hi);
+      }
+      __syncthreads();
+      lo = ~hist[0];
+      const int kb = 32 - __builtin_clz((hist[1] - lo) | 1u);  // bits of the key part
+      __syncthreads();
+      const int nbits = kb + 24;
+      auto rel = [&](unsigned long long w) {
+        return ((unsigned long long)((uint32_t)(w >> 24) - lo) << 24) | (w & 0xffffffull);
+      };
       unsigned long long prefix = 0ull;
       int rank = kt;
-      for (int d = 0; d < 5; ++d) {
-        const int sh = shifts[d], wd = widths[d];
+      // Digits of at most 13 bits, the key part split evenly (two passes for
+      // the usual range of up to 26 bits); then the position's two 12-bit
+      // digits, only when the candidates tied on the threshold key are not
+      // all taken.
+      const int kpass = (kb + 12) / 13;
+      int top = nbits;
+      for (int d = 0; d < kpass + 2; ++d) {
+        const int key_bits_left = top - 24;
+        const int wd = d < kpass ? (key_bits_left + (kpass - d) - 1) / (kpass - d) : 12;
+        const int sh = top - wd;
         for (int i = threadIdx.x; i < kDig; i += kRT) hist[i] = 0u;
         __syncthreads();
-        each([&](int pos, size_t at) {
-          if (pos >= Lt) return;
-          const unsigned long long w = member_word(okey[at], pos);
-          if ((w >> (sh + wd)) == prefix)
-            atomicAdd(&hist[(w >> sh) & ((1u << wd) - 1u)], 1u);
+        each([&](unsigned long long w) {
+          const unsigned long long r = rel(w);
+          if (pos_of(w) < Lt && (r >> top) == prefix)
+            atomicAdd(&hist[(r >> sh) & ((1u << wd) - 1u)], 1u);
         });
         __syncthreads();
         int bin, rem;
         find_bin_up(hist, kDig, rank, scan, pair, &bin, &rem);
+        const bool whole = hist[bin] == (uint32_t)rem;  // every tie on the key taken
+        __syncthreads();
         prefix = (prefix << wd) | (unsigned long long)bin;
         rank = rem;
+        top = sh;
+        if (top == 24 && whole) {  // the key part is resolved and its ties all fit
+          prefix = (prefix << 24) | 0xffffffull;
+          top = 0;
+          break;
+        }
       }
-      vstar = prefix;
+      // back to the absolute word
+      vstar = ((unsigned long long)((uint32_t)(prefix >> 24) + lo) << 24) | (prefix & 0xffffffull);
     }
     // W_t: the group's tail sum plus the proxy weight of every candidate the
-    // member does not keep (those outside its span included).
+    // member does not keep (those outside its span included).  The score
+    // loads of the register items go out together.
     double ws = 0.0;
-    const float* srow = a.scores + (size_t)u * a.score_ld;
-    each([&](int pos, size_t at) {
-      const bool kept = kt > 0 && pos < Lt && member_word(okey[at], pos) <= vstar;
-      if (!kept) ws += (double)sexp(srow[pos] - gs.M);
-    });
+    constexpr int kBatch = 8;  // score loads in flight together
+    static_assert(kKeep % kBatch == 0, "whole batches");
+#pragma unroll
+    for (int e0 = 0; e0 < kKeep; e0 += kBatch) {
+      float sv[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e)
+        sv[e] = threadIdx.x + (e0 + e) * kRT < N ? srow[pos_of(wv[e0 + e])] : 0.0f;
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const unsigned long long w = wv[e0 + e];
+        const bool kept = kt > 0 && pos_of(w) < Lt && w <= vstar;
+        if (threadIdx.x + (e0 + e) * kRT < N && !kept) ws += (double)sexp(sv[e] - gs.M);
+      }
+    }
+    for (int j = threadIdx.x + kKeep * kRT; j < N; j += kRT) {
+      const unsigned long long w = word_of(j);
+      const bool kept = kt > 0 && pos_of(w) < Lt && w <= vstar;
+      if (!kept) ws += (double)sexp(srow[pos_of(w)] - gs.M);
+    }
     W = gw + block_sum_f64<kRT>(ws, dscr);
   }
   const float Wt = a.w_in ? a.w_in[v] : (float)W;
@@ -251,92 +388,135 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
 constexpr uint32_t kMarkNone = 0xffffffffu;
 constexpr uint32_t kMarkDet = 0xfffffffeu;
 
-// Grid: (chunks, member units) x kRS threads.
+// Grid: (chunks, group units) x kRS threads.  The chunk's group entries
+// (candidates, then the group's samples), their proxy weights and uniforms
+// are loaded and drawn once; then each member in turn marks its stratum and
+// samples in an LDS map of the chunk and writes its segment from it.
 __global__ __launch_bounds__(kRS) void refine_emit_kernel(RefineArgs a) {
   __shared__ uint32_t mark[kChunk];
   __shared__ int scan_scr[kRS / 64];
-  constexpr int kPerT = kChunk / kRS;
+  constexpr int kPerT = kChunk / kRS;  // 16: also the most group entries per thread
   const int c = blockIdx.x;
-  const int v = blockIdx.y;
-  int b, t, h, u;
-  decode_member(a, v, &b, &t, &h, &u);
-  const MemberState ms = reinterpret_cast<const MemberState*>(a.mstate)[v];
+  const int u = blockIdx.y;
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b, h = ui.h;
+  const int t0 = ui.grp * a.g;
+  const int nmem = min(a.g, a.T - t0);
   const int c0 = c * kChunk;
-  int32_t* cnt = a.msel_cnt + ((size_t)v * a.nchunk + c) * 2;
-  if (c0 >= ms.L || (ms.flags & kFlagEmpty)) {
-    if (threadIdx.x == 0) {
-      cnt[0] = 0;
-      cnt[1] = 0;
+  const size_t ci = (size_t)u * a.nchunk + c;
+  const int n_det = c0 < ui.L ? clamp_count(a.gsel_cnt[2 * ci], kChunk) : 0;
+  const int n_smp = c0 < ui.L ? clamp_count(a.gsel_cnt[2 * ci + 1], kChunk - n_det) : 0;
+  const int n_all = n_det + n_smp;
+  const int32_t* gidx = a.gsel_idx + (size_t)u * a.seg_ld + c0;
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  const float M = reinterpret_cast<const UnitState*>(a.gstate)[u].M;
+  const uint64_t seed = a.seed[b];
+  // Entry i's position (-1 outside the chunk or span), proxy weight and
+  // uniform.  A thread keeps its first kFast entries (i = threadIdx.x +
+  // e * kRS) in registers; a chunk rarely holds more than kRS * kFast
+  // entries, and further ones are computed again for every member.
+  constexpr int kFast = 2;
+  auto entry = [&](int i, int& p, float& w, float& un) {
+    p = i < n_all ? gidx[i] : -1;
+    const bool in = (unsigned)(p - c0) < (unsigned)kChunk && p < ui.L;
+    if (!in) p = -1;
+    w = in ? sexp(srow[p] - M) : 0.0f;
+    un = 0.0f;
+    if (in) {
+      const uint4 wd = philox_block(seed, b, h, (uint32_t)p >> 2, ui.grp);
+      const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+      un = uniform24(words[p & 3]);
     }
-    return;
-  }
-  const int nvalid = min(kChunk, ms.L - c0);
-  const bool dense = ms.flags & kFlagDense;
-  const bool sampling = ms.flags & kFlagSample;
-  for (int i = threadIdx.x; i < kChunk; i += kRS)
-    mark[i] = (dense && i < nvalid) ? kMarkDet : kMarkNone;
-  __syncthreads();
-  if (!dense) {
-    const size_t ci = (size_t)u * a.nchunk + c;
-    const int n_det = clamp_count(a.gsel_cnt[2 * ci], kChunk);
-    const int n_smp = clamp_count(a.gsel_cnt[2 * ci + 1], kChunk - n_det);
-    const int32_t* gidx = a.gsel_idx + (size_t)u * a.seg_ld + c0;
+  };
+  int pos[kFast];
+  float wgt[kFast], uni[kFast];
+#pragma unroll
+  for (int e = 0; e < kFast; ++e) entry(threadIdx.x + e * kRS, pos[e], wgt[e], uni[e]);
+  for (int mi = 0; mi < nmem; ++mi) {  // uniform
+    const int v = (b * a.T + t0 + mi) * a.Hkv + h;
+    const MemberState ms = reinterpret_cast<const MemberState*>(a.mstate)[v];
+    int32_t* cnt = a.msel_cnt + ((size_t)v * a.nchunk + c) * 2;
+    if (c0 >= ms.L || (ms.flags & kFlagEmpty)) {  // uniform
+      if (threadIdx.x == 0) {
+        cnt[0] = 0;
+        cnt[1] = 0;
+      }
+      continue;
+    }
+    const int nvalid = min(kChunk, ms.L - c0);
+    const bool dense = ms.flags & kFlagDense;
+    const bool sampling = ms.flags & kFlagSample;
+    const bool notopk = ms.flags & kFlagNoTopk;
     const uint32_t* okey = a.own_key + (size_t)v * a.seg_ld + c0;
-    const float* srow = a.scores + (size_t)u * a.score_ld;
-    const uint64_t seed = a.seed[b];
-    const int grp = t / a.g;
-    const float mf = (float)ms.m;
-    for (int i = threadIdx.x; i < n_det + n_smp; i += kRS) {
-      const int pos = gidx[i];
-      if ((unsigned)(pos - c0) >= (unsigned)nvalid) continue;  // outside the member's span
-      if (i < n_det && !(ms.flags & kFlagNoTopk) && member_word(okey[i], pos) <= ms.vstar) {
-        mark[pos - c0] = kMarkDet;
-      } else if (sampling) {
-        const uint4 wd = philox_block(seed, b, h, (uint32_t)pos >> 2, grp);
-        const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
-        const float mw = mf * sexp(srow[pos] - ms.M);
-        if (uniform24(words[pos & 3]) * ms.W < mw)
-          mark[pos - c0] = __float_as_uint(-logf(fminf(1.0f, mw / ms.W)));
+    uint32_t ok[kFast];
+#pragma unroll
+    for (int e = 0; e < kFast; ++e) {
+      const int i = threadIdx.x + e * kRS;
+      ok[e] = (!dense && i < n_det) ? okey[i] : 0u;
+    }
+    __syncthreads();  // the previous member's map has been read
+    for (int i = threadIdx.x; i < kChunk; i += kRS)
+      mark[i] = (dense && i < nvalid) ? kMarkDet : kMarkNone;
+    __syncthreads();
+    if (!dense) {
+      const float mf = (float)ms.m;
+      auto place = [&](int i, int p, float w, float un, uint32_t key) {
+        if (p < 0 || p - c0 >= nvalid) return;  // not in the member's span
+        if (i < n_det && !notopk && member_word(key, p) <= ms.vstar) {
+          mark[p - c0] = kMarkDet;
+        } else if (sampling) {
+          const float mw = mf * w;
+          if (un * ms.W < mw) mark[p - c0] = __float_as_uint(-logf(fminf(1.0f, mw / ms.W)));
+        }
+      };
+#pragma unroll
+      for (int e = 0; e < kFast; ++e)
+        place(threadIdx.x + e * kRS, pos[e], wgt[e], uni[e], ok[e]);
+      for (int i = threadIdx.x + kFast * kRS; i < n_all; i += kRS) {
+        int p;
+        float w, un;
+        entry(i, p, w, un);
+        place(i, p, w, un, i < n_det ? okey[i] : 0u);
       }
     }
-  }
-  __syncthreads();
-  // Compaction from the membership map (16 consecutive positions per thread).
-  const int tb = threadIdx.x * kPerT;
-  uint32_t smask = 0u, rmask = 0u;
+    __syncthreads();
+    // Compaction from the membership map (16 consecutive positions per thread).
+    const int tb = threadIdx.x * kPerT;
+    uint32_t smask = 0u, rmask = 0u;
 #pragma unroll
-  for (int i = 0; i < kPerT; ++i) {
-    const uint32_t mk = mark[tb + i];
-    smask |= (uint32_t)(mk == kMarkDet) << i;
-    rmask |= (uint32_t)(mk < kMarkDet) << i;
-  }
-  int packed_tot;
-  const int packed = block_exclusive_scan<kRS>(__popc(smask) | (__popc(rmask) << 16), scan_scr,
-                                               &packed_tot);
-  const int totS = packed_tot & 0xffff;
-  const int totR = packed_tot >> 16;
-  int32_t* sidx = a.msel_idx + (size_t)v * a.seg_ld + c0;
-  float* slw = a.msel_logw + (size_t)v * a.seg_ld + c0;
-  int ws = packed & 0xffff, wr = totS + (packed >> 16);
+    for (int i = 0; i < kPerT; ++i) {
+      const uint32_t mk = mark[tb + i];
+      smask |= (uint32_t)(mk == kMarkDet) << i;
+      rmask |= (uint32_t)(mk < kMarkDet) << i;
+    }
+    int packed_tot;
+    const int packed = block_exclusive_scan<kRS>(__popc(smask) | (__popc(rmask) << 16),
+                                                 scan_scr, &packed_tot);
+    const int totS = packed_tot & 0xffff;
+    const int totR = packed_tot >> 16;
+    int32_t* sidx = a.msel_idx + (size_t)v * a.seg_ld + c0;
+    float* slw = a.msel_logw + (size_t)v * a.seg_ld + c0;
+    int ws = packed & 0xffff, wr = totS + (packed >> 16);
 #pragma unroll
-  for (int i = 0; i < kPerT; ++i) {
-    const uint32_t bit = 1u << i;
-    if ((smask | rmask) & bit) {
-      const int pos = c0 + tb + i;
-      if (smask & bit) {
-        sidx[ws] = pos;
-        slw[ws] = 0.0f;
-        ++ws;
-      } else {
-        sidx[wr] = pos;
-        slw[wr] = __uint_as_float(mark[tb + i]);
-        ++wr;
+    for (int i = 0; i < kPerT; ++i) {
+      const uint32_t bit = 1u << i;
+      if ((smask | rmask) & bit) {
+        const int p = c0 + tb + i;
+        if (smask & bit) {
+          sidx[ws] = p;
+          slw[ws] = 0.0f;
+          ++ws;
+        } else {
+          sidx[wr] = p;
+          slw[wr] = __uint_as_float(mark[tb + i]);
+          ++wr;
+        }
       }
     }
-  }
-  if (threadIdx.x == 0) {
-    cnt[0] = totS;
-    cnt[1] = totR;
+    if (threadIdx.x == 0) {
+      cnt[0] = totS;
+      cnt[1] = totR;
+    }
   }
 }
 
@@ -347,16 +527,17 @@ hipError_t launch_refine(const RefineArgs& a, int group_units, int member_units,
   const int nmem = a.g < a.T ? a.g : a.T;
   if (nmem * a.G * 2 * a.pair_count > kRefineQ) return hipErrorInvalidValue;
   const dim3 sg(a.nchunk, group_units);
+  const size_t qbytes = (size_t)nmem * a.G * 2 * a.pair_count * sizeof(float);
   switch (a.pair_count / 4) {  // lanes per candidate: 2 * pair_count / 8
-    case 1: refine_score_kernel<1><<<sg, kRS, 0, stream>>>(a); break;
-    case 2: refine_score_kernel<2><<<sg, kRS, 0, stream>>>(a); break;
-    case 4: refine_score_kernel<4><<<sg, kRS, 0, stream>>>(a); break;
-    case 8: refine_score_kernel<8><<<sg, kRS, 0, stream>>>(a); break;
-    case 16: refine_score_kernel<16><<<sg, kRS, 0, stream>>>(a); break;
+    case 1: refine_score_kernel<1><<<sg, kRS, qbytes, stream>>>(a); break;
+    case 2: refine_score_kernel<2><<<sg, kRS, qbytes, stream>>>(a); break;
+    case 4: refine_score_kernel<4><<<sg, kRS, qbytes, stream>>>(a); break;
+    case 8: refine_score_kernel<8><<<sg, kRS, qbytes, stream>>>(a); break;
+    case 16: refine_score_kernel<16><<<sg, kRS, qbytes, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   refine_select_kernel<<<member_units, kRT, 0, stream>>>(a);
-  refine_emit_kernel<<<dim3(a.nchunk, member_units), kRS, 0, stream>>>(a);
+  refine_emit_kernel<<<dim3(a.nchunk, group_units), kRS, 0, stream>>>(a);
   return hipGetLastError();
 }
 

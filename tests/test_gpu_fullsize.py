@@ -296,3 +296,80 @@ def test_fullsize_fused_equals_staged(name):
     say(f"[full] {name} fused vs staged: max |diff| "
         f"{float((out.double() - att.double()).abs().max()):.3g}")
     assert torch.equal(out, att)
+
+
+def test_fullsize_1m_refine():
+    """The 1M workload with 4 query positions per step in one group, refine
+    mode with a candidate list of 2 x 10486 tokens: every (group, kv head)
+    unit and member; member selections bit-exact given the oracle's group
+    scores and member normalisers, the library's own member normalisers
+    within 1e-6, and the fused output within the bound."""
+    T, g, r = 4, 4, 2
+    wl = synth.make_workload("1m", DEV, num_queries=T)
+    say(f"[full] 1m refine T={T} g={g} r={r}")
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count, query_group=g,
+                       refine=r)
+    scale = 1.0 / math.sqrt(wl.d)
+    G = wl.Hq // wl.Hkv
+    ws = ssa.alloc_workspace(p, DEV)
+    out = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+                     wl.sample_budget, wl.seed, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    got = out.double().cpu().numpy()
+    P = wl.lens[0]
+    k, m, seed = int(wl.topk[0]), int(wl.sample_budget[0]), int(wl.seed[0]) & 0xFFFFFFFFFFFFFFFF
+    s32 = torch.zeros((1, wl.Hkv, wl.max_seq_len), dtype=torch.float32)
+    w_in = torch.zeros((1, T * wl.Hkv), dtype=torch.float32)
+    members = {}
+    qh = wl.q.float().cpu().numpy().astype(np.float64)
+    bt = wl.block_table[0].cpu().numpy().astype(np.int64)
+    for h in range(wl.Hkv):
+        K = orc.gather_rows(wl.k_cache[:, h:h + 1].float().cpu().numpy(), bt, 0, P)
+        qs = qh[0, :, h * G:(h + 1) * G].reshape(-1, wl.d)
+        s = orc.approx_scores(qs, K, wl.pair_begin, wl.pair_count, scale).astype(np.float32)
+        s32[0, h, :P] = torch.from_numpy(s)
+        sel = orc.select_unit(s, r * k, m, seed, 0, h, grp=0)
+        for t in range(T):
+            ms = orc.refine_member(sel, s, qh[0, t, h * G:(h + 1) * G], K,
+                                   orc.member_span(P, T, t), k, m, seed, 0, h, 0,
+                                   wl.pair_begin, wl.pair_count, scale)
+            members[(t, h)] = ms
+            w_in[0, t * wl.Hkv + h] = float(ms["W"])
+        del K
+        say(f"[full] 1m refine kv head {h}: oracle member strata "
+            f"{[members[(t, h)]['S'].size for t in range(T)]}, samples "
+            f"{[members[(t, h)]['R'].size for t in range(T)]}")
+    exact = dict(q=wl.q, k_cache=wl.k_cache, block_table=wl.block_table)
+    sd = s32.to(DEV)
+    si, sl, sn, _ = ssa.select(p, sd, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                               w_in=w_in.to(DEV), workspace=ws, **exact)
+    _, _, _, nm = ssa.select(p, sd, wl.seq_lens, wl.topk, wl.sample_budget, wl.seed,
+                             workspace=ws, **exact)
+    torch.cuda.synchronize()
+    si, sl, sn, nm = si.cpu().numpy(), sl.cpu().numpy(), sn.cpu().numpy(), nm.cpu().numpy()
+    worst_w = 0.0
+    for (t, h), ms in members.items():
+        S, R, _ = gpu_sets(si, sl, sn, 0, t * wl.Hkv + h)
+        assert np.array_equal(S, ms["S"]) and np.array_equal(R, ms["R"]), (t, h)
+        W = float(ms["W"])
+        rel = abs(float(nm[0, t * wl.Hkv + h, 1]) - W) / W
+        worst_w = max(worst_w, rel)
+        assert rel <= 1e-6, (t, h, rel)
+    say(f"[full] 1m refine: member selections bit-exact, own W worst rel err {worst_w:.3g}")
+    worst = 0.0
+    for h in range(wl.Hkv):
+        K = orc.gather_rows(wl.k_cache[:, h:h + 1].float().cpu().numpy(), bt, 0, P)
+        V = orc.gather_rows(wl.v_cache[:, h:h + 1].float().cpu().numpy(), bt, 0, P)
+        bound = 2e-3 * float(np.abs(V).max())
+        for t in range(T):
+            ms = members[(t, h)]
+            Lt = orc.member_span(P, T, t)
+            o = orc.attend_unit(qh[0, t, h * G:(h + 1) * G], K[:Lt], V[:Lt], ms["S"], ms["R"],
+                                ms["pi_R"], scale)
+            err = float(np.abs(got[0, t, h * G:(h + 1) * G] - o).max())
+            worst = max(worst, err / bound)
+            assert err <= bound, f"member {t} of kv head {h}: {err} > {bound}"
+        del K, V
+    say(f"[full] 1m refine: fused output worst err/bound {worst:.3g}")
