@@ -284,6 +284,7 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   for (int j = 0; j < kHist; ++j) hv[j] = a.hist2[(size_t)u * kBins + threadIdx.x + j * kRT];
   const size_t cu = (size_t)u * a.nchunk;
   const uint32_t* ckeys = a.cand_key + (size_t)u * a.seg_ld;
+  const float* cws = a.cand_w + (size_t)u * a.seg_ld;
   const int tpc = threads_per_chunk(a.nchunk);
   const int cstep = kRT / tpc;
   const int csub = threadIdx.x % tpc;
@@ -292,12 +293,18 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   const bool has_cm = one_chunk && cm < a.nchunk;
   const int cnt_m = has_cm ? a.cand_cnt[cu + cm] : 0;
   const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
+  const float* cwm = cws + (size_t)cm * kChunk;
   uint32_t kr[kKeep];
+  float wr[kKeep];  // the candidates' tail weights, computed by the filter
 #pragma unroll
   for (int k = 0; k < kKeep; ++k) {
     const int i = csub + k * tpc;
     kr[k] = (has_cm && i < kChunk) ? ckm[i] : 0u;
+    wr[k] = (has_cm && i < kChunk) ? cwm[i] : 0.0f;
   }
+  // This thread's chunk tail sum, with the first loads when every chunk has
+  // its own thread (entries past the sequence's chunks are ignored).
+  const double wp = (a.nchunk <= kRT && (int)threadIdx.x < a.nchunk) ? a.wpart[cu + threadIdx.x] : 0.0;
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -317,9 +324,9 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
       st.flags = kFlagDense;
     } else {
       const int nc = (p.L + kChunk - 1) / kChunk;
-      // The chunks' tail sums do not depend on anything below: load them first.
-      double acc = 0.0;
-      for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
+      double acc = (a.nchunk <= kRT && (int)threadIdx.x < nc) ? wp : 0.0;
+      if (a.nchunk > kRT)
+        for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
       double cs = 0.0;  // this thread's candidates below the threshold key
       int total_ties = 0;
       if (t1.mode == 0) {
@@ -356,24 +363,25 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         }
         __syncthreads();
         // Third digit: LDS histograms of the candidates that share the prefix.
-        auto add3 = [&](uint32_t key) {
+        auto add3 = [&](uint32_t key, float w) {
           if ((key >> kDigit2Shift) == prefix) {
             atomicAdd(&hist[key & (kBins3 - 1)], 1u);
-            if (mass3) atomicAdd(&mh[key & (kBins3 - 1)], mass_units(sexp(key_to_float(key) - st.M)));
+            if (mass3) atomicAdd(&mh[key & (kBins3 - 1)], mass_units(w));
           }
         };
         if (one_chunk) {
 #pragma unroll
           for (int k = 0; k < kKeep; ++k) {
             const int i = csub + k * tpc;
-            if (i < nm) add3(kr[k]);
+            if (i < nm) add3(kr[k], wr[k]);
           }
-          for (int i = csub + kKeep * tpc; i < nm; i += tpc) add3(ckm[i]);
+          for (int i = csub + kKeep * tpc; i < nm; i += tpc) add3(ckm[i], cwm[i]);
         } else {
           for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
             const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
             const uint32_t* ck = ckeys + (size_t)c * kChunk;
-            for (int i = csub; i < n; i += tpc) add3(ck[i]);
+            const float* cw = cws + (size_t)c * kChunk;
+            for (int i = csub; i < n; i += tpc) add3(ck[i], cw[i]);
           }
         }
         __syncthreads();
@@ -411,24 +419,25 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
             const int i = csub + k * tpc;
             if (i < nm) {
               ties += kr[k] == st.tkey ? 1 : (kr[k] > st.tkey ? 0x10000 : 0);
-              if (kr[k] < st.tkey) cs += (double)sexp(key_to_float(kr[k]) - st.M);
+              if (kr[k] < st.tkey) cs += (double)wr[k];
             }
           }
           for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
             const uint32_t key = ckm[i];
             ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
-            if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
+            if (key < st.tkey) cs += (double)cwm[i];
           }
           if (ties) atomicAdd(&ties_sh[cm], ties);
         } else {
           for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
             const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
             const uint32_t* ck = ckeys + (size_t)c * kChunk;
+            const float* cw = cws + (size_t)c * kChunk;
             int ties = 0;
             for (int i = csub; i < n; i += tpc) {
               const uint32_t key = ck[i];
               ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
-              if (key < st.tkey) cs += (double)sexp(key_to_float(key) - st.M);
+              if (key < st.tkey) cs += (double)cw[i];
             }
             if (ties) atomicAdd(&ties_sh[c], ties);
           }

@@ -14,7 +14,8 @@ constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 // ignored); sh is the chunk's score buffer in LDS, of which the thread uses
 // its own 16 entries; t1 is the unit's first-digit threshold and M its
 // maximum score.  Writes the chunk's
-// candidates (positions and keys, second-digit histogram), its lists (tokens
+// candidates (positions, keys and tail weights, second-digit histogram), its
+// lists (tokens
 // above the threshold digit, then tail tokens passing the necessary
 // inclusion test fl(u * W_lb) < fl(m * w) with their weights), its
 // candidate and list counts and its fp64 tail weight sum.
@@ -75,6 +76,7 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   const int n_above = lst_tot & 0xffff;
   int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
   uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+  float* cw = a.cand_w + (size_t)u * a.seg_ld + c0;
   int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
   float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
   int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
@@ -86,12 +88,14 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
     const float s = sh[tb + i];
     if (candmask & bit) {
       const uint32_t key = order_key(s);
+      const float w = sexp(s - M);
       cidx[wc] = t;
       ckey[wc] = key;
+      cw[wc] = w;
       ++wc;
       const int d2 = (key >> kDigit2Shift) & (kBins - 1);
       atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
-      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(sexp(s - M)));
+      if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w));
     } else if (abovemask & bit) {
       lidx[wa++] = t;
     } else {

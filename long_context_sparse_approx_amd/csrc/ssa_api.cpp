@@ -127,7 +127,8 @@ Dims dims_of(const ssa_params* p) {
 }
 
 struct Layout {
-  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_cnt, list_idx, list_w,
+  size_t scores, hist1, hist2, hist1m, hist2m, maxkey, thresh, cand_idx, cand_key, cand_w, cand_cnt,
+      list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
       stop_words, stop_pair, stop_rword, stop_logit, w64, own_key, mstate, msel_idx, msel_logw,
@@ -152,6 +153,7 @@ Layout layout_of(const Dims& d) {
   l.thresh = take(U * sizeof(ssa::Thresh1));
   l.cand_idx = take(U * SEG * 4);
   l.cand_key = take(U * SEG * 4);
+  l.cand_w = take(U * SEG * 4);
   l.cand_cnt = take(U * NC * 4);
   l.list_idx = take(U * SEG * 4);
   l.list_w = take(U * SEG * 4);
@@ -278,6 +280,7 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.thresh = at<ssa::Thresh1>(ws, l.thresh);
   a.cand_idx = at<int32_t>(ws, l.cand_idx);
   a.cand_key = at<uint32_t>(ws, l.cand_key);
+  a.cand_w = at<float>(ws, l.cand_w);
   a.cand_cnt = at<int32_t>(ws, l.cand_cnt);
   a.list_idx = at<int32_t>(ws, l.list_idx);
   a.list_w = at<float>(ws, l.list_w);

@@ -186,13 +186,17 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Maximum over the wave: the running maximum of the DPP pattern below (the
+// same steps as the inclusive scan), read from the last lane.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t o = __shfl_xor(v, off);
-    v = o > v ? o : v;
-  }
-  return v;
+  auto step = [](uint32_t x, uint32_t o) { return o > x ? o : x; };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave (int or 64-bit unsigned).
@@ -204,6 +208,31 @@ __device__ __forceinline__ T wave_inclusive_scan(T v) {
     const T o = __shfl_up(v, off);
     if (lane >= off) v += o;
   }
+  return v;
+}
+
+template <>
+__device__ __forceinline__ int wave_inclusive_scan<int>(int v);
+
+// 32-bit integer sum over the wave: the DPP inclusive scan's last lane.
+template <>
+__device__ __forceinline__ int wave_sum<int>(int v) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan<int>(v), 63);
+}
+
+// 32-bit integers: six DPP adds in the VALU instead of six LDS-crossbar
+// shuffles.  Within each 16-lane row: add the value 1, 2, 4 and 8 lanes
+// below (lanes without one add 0); then row 1 and row 3 add the last lane of
+// the row below (row_bcast:15), rows 2 and 3 the last lane of row 1
+// (row_bcast:31).
+template <>
+__device__ __forceinline__ int wave_inclusive_scan<int>(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 

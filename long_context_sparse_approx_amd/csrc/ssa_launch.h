@@ -76,6 +76,7 @@ struct SelectArgs {
   Thresh1* thresh;            // [U]
   int32_t* cand_idx;          // [U, seg_ld] threshold-digit candidates per chunk
   uint32_t* cand_key;         // [U, seg_ld]
+  float* cand_w;              // [U, seg_ld] the candidates' tail weights sexp(s - M)
   int32_t* cand_cnt;          // [U, nchunk]
   int32_t* list_idx;          // [U, seg_ld] per chunk: above-threshold tokens, then
   float* list_w;              //   sampling candidates with their tail weights
