@@ -52,26 +52,6 @@ __device__ __forceinline__ unsigned long long member_word(uint32_t own_key, int 
   return ((unsigned long long)(~own_key) << 24) | (uint32_t)pos;
 }
 
-// The partner lane across lane-index bit BIT of a 16-lane row (DPP: quad
-// permutations for bits 0 and 1, the half-row mirror for bit 2, a rotation
-// by 8 for bit 3).  Each pairing is an involution that joins the two halves
-// of the current group, so the butterfly sums neighbouring slices first.
-template <int BIT>
-__device__ __forceinline__ float dpp_partner(float x) {
-  constexpr int ctrl = BIT == 0 ? 0xB1 : (BIT == 1 ? 0x4E : (BIT == 2 ? 0x141 : 0x128));
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               ctrl, 0xf, 0xf, false));
-}
-
-template <int LPT>
-__device__ __forceinline__ float butterfly(float p) {
-  if constexpr (LPT >= 2) p = p + dpp_partner<0>(p);
-  if constexpr (LPT >= 4) p = p + dpp_partner<1>(p);
-  if constexpr (LPT >= 8) p = p + dpp_partner<2>(p);
-  if constexpr (LPT >= 16) p = p + dpp_partner<3>(p);
-  return p;
-}
-
 // Grid: (chunks, group units) x kRS threads; dynamic LDS holds the group's
 // scored query slices (nmem * G * 2 * pair_count floats).  LPT lanes per
 // candidate (one 16-byte slice of its scored dims each); all the group's

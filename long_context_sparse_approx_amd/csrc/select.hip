@@ -497,8 +497,8 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 // order, and the cut is published as the last word kept: the sample kernel
 // drops every deterministic token whose word is larger.  The stratum is the
 // tokens above the threshold key T followed by the first ties on T (ranked by
-// position); only the former need sorting.  Six kernels, none with a global
-// atomic:
+// position); only the former need sorting.  Seven kernels, none with a
+// global atomic:
 //   stop_gather: each chunk writes its words above T (its listed tokens above
 //     the threshold digit, then its candidates above T) at the offset the
 //     resolve kernel computed for it, and its ties within the quota straight
@@ -510,10 +510,12 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
 //   stop_final: each word's rank = its index in its slice + those counts;
 //     the words stored in rank order;
 //   stop_logit: one wave per 64-token block of the order computes every
-//     row's exact logit of its tokens (key rows through the block table);
-//   stop_cut: one workgroup per unit takes each row's maximum, the block
-//     gains, their prefix sums and the first block where every row agrees,
-//     and writes the last word kept.
+//     row's exact logit of its tokens (key rows through the block table)
+//     and the block's maximum of each row;
+//   stop_gain: one wave per block sums its tokens' units for every row;
+//   stop_cut: one workgroup per unit takes the block gains' prefix sums
+//     and the first block where every row agrees, and writes the last word
+//     kept.
 constexpr int kStopBlock = 64;
 constexpr int kStopMax = SSA_STOP_MAX_STRATUM;  // largest stratum that is ordered
 constexpr int kStopRows = SSA_STOP_MAX_ROWS;    // query rows per unit, at most
@@ -782,15 +784,25 @@ __global__ __launch_bounds__(kNT) void stop_final_kernel(SelectArgs a) {
 // The exact logit of each (rank, query row) of a unit's stratum, in the
 // specified float32 order: lane c of a token's D/8 lanes holds its 8-dim
 // slice c, sums the 8 exact bf16 products in dim order, and the slices are
-// combined pairwise by butterfly exchanges (lane c and its partner add the
-// same two values, so every lane ends with the same sum); then one multiply
-// by the softmax scale.  Rows whose member's span excludes the token get
-// -inf.  Grid: (kStopMax / 64, units) x 64 threads, one wave per block.
+// combined pairwise by butterfly exchanges (every lane of the token ends with
+// the same sum); then one multiply by the softmax scale.  Rows whose member's
+// span excludes the token get -inf.  The block's largest order key of each
+// row goes to stop_mkey (0: none).  Grid: (kStopMax / 64, units) x 256
+// threads: wave w takes the block's tokens 16 w .. 16 w + 15, resolves them
+// to cache rows in one round of loads and loads all their key slices
+// together.
+constexpr int kLogitT = 256;
+constexpr int kLogitTok = kStopBlock / (kLogitT / 64);  // tokens per wave
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(64) void stop_logit_kernel(SelectArgs a) {
-  constexpr int LPT = D / 8;     // lanes per token
-  constexpr int TPI = 64 / LPT;  // tokens per iteration
+__global__ __launch_bounds__(kLogitT) void stop_logit_kernel(SelectArgs a) {
+  constexpr int LPT = D / 8;           // lanes per token
+  constexpr int TPI = 64 / LPT;        // tokens per step
+  constexpr int NIT = kLogitTok / TPI;  // steps per wave
+  static_assert(kStopRows * LPT <= kLogitT, "one 16-byte query slice per thread");
   __shared__ float qsh[kStopRows * D];
+  __shared__ uint32_t row_sh[kStopBlock];
+  __shared__ int pos_sh[kStopBlock];
+  __shared__ uint32_t mk_sh[kLogitT / 64][kStopRows];
   const int u = blockIdx.y;
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   if (!stop_applies(st)) return;  // uniform
@@ -800,17 +812,43 @@ __global__ __launch_bounds__(64) void stop_logit_kernel(SelectArgs a) {
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int b = ui.b;
   const int h = ui.h;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int t0 = ui.grp * a.g;                 // the group's first member
   const int nmem = min(a.g, a.T - t0);
   const int rows = min(nmem * a.G, kStopRows);  // the host guarantees nmem * G <= kStopRows
   const int P = clamp_len(a.seq_lens[b], a.max_seq_len);
-  for (int i = lane; i < rows * D; i += 64) {
-    const int r = i / D;
-    const int e = i - r * D;
-    const int t = t0 + r / a.G;
-    const uint16_t bits = a.q[((size_t)(b * a.T + t) * a.Hq + h * a.G + r % a.G) * D + e];
-    qsh[i] = __uint_as_float((uint32_t)bits << 16);
+  const int L = ui.L;
+  if (lane < kLogitTok) {
+    // Token j of the block (rank r0 + j < kStopMax: the load stays in the
+    // unit's word array; ranks past the stratum are masked below).
+    const int j = wave * kLogitTok + lane;
+    const unsigned long long w = a.stop_rword[(size_t)u * kStopMax + r0 + j];
+    const int pos = min(max((int)(uint32_t)w, 0), max(L - 1, 0));
+    int blk = a.block_table[(size_t)b * a.max_blocks + (pos >> 4)];
+    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
+    row_sh[j] = (uint32_t)((blk * a.Hkv + h) * kBlockTokens + (pos & 15));
+    pos_sh[j] = pos;
+  }
+  {
+    // The query rows in LDS as floats: thread (r, c) stages slice c of row r.
+    const int r = tid / LPT;
+    const int c = tid - r * LPT;
+    if (r < rows) {
+      const int t = t0 + r / a.G;
+      const uint4 v = *reinterpret_cast<const uint4*>(
+          a.q + ((size_t)(b * a.T + t) * a.Hq + h * a.G + r % a.G) * D + c * 8);
+      float* dst = qsh + r * D + c * 8;
+      dst[0] = bf16_lo(v.x);
+      dst[1] = bf16_hi(v.x);
+      dst[2] = bf16_lo(v.y);
+      dst[3] = bf16_hi(v.y);
+      dst[4] = bf16_lo(v.z);
+      dst[5] = bf16_hi(v.z);
+      dst[6] = bf16_lo(v.w);
+      dst[7] = bf16_hi(v.w);
+    }
   }
   __syncthreads();
   const int sl = lane % LPT;  // this lane's slice
@@ -831,43 +869,121 @@ __global__ __launch_bounds__(64) void stop_logit_kernel(SelectArgs a) {
       kld = scored ? nd : D - nd;
     }
   }
-  const unsigned long long* rword = a.stop_rword + (size_t)u * kStopMax;
-  const int* btrow = a.block_table + (size_t)b * a.max_blocks;
-  float* out = a.stop_logit + (size_t)u * kStopMax * kStopRows;
-  const int L = ui.L;
-  for (int it = 0; it < kStopBlock / TPI; ++it) {
-    const int rank = r0 + it * TPI + tk;
-    const bool valid = rank < n;
-    const int pos = valid ? min(max((int)(uint32_t)rword[rank], 0), max(L - 1, 0)) : 0;
-    int blk = btrow[pos >> 4];
-    blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-    const uint32_t row = (uint32_t)((blk * a.Hkv + h) * kBlockTokens + (pos & 15));
-    const uint4 kv = *reinterpret_cast<const uint4*>(kb + (size_t)row * kld);
-    const float kf[8] = {bf16_lo(kv.x), bf16_hi(kv.x), bf16_lo(kv.y), bf16_hi(kv.y),
-                         bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
+  uint4 kv[NIT];
 #pragma unroll
-    for (int r = 0; r < kStopRows; ++r) {
-      if (r >= rows) break;  // uniform
-      const float* qr = qsh + r * D + sl * 8;
+  for (int it = 0; it < NIT; ++it)
+    kv[it] = *reinterpret_cast<const uint4*>(
+        kb + (size_t)row_sh[wave * kLogitTok + it * TPI + tk] * kld);
+  float* out = a.stop_logit + (size_t)u * kStopMax * kStopRows;
+  // One query row at a time (a uniform runtime loop), the wave's tokens
+  // unrolled inside it, so every key slice stays in a fixed register.
+  for (int r = 0; r < rows; ++r) {
+    float qr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qr[i] = qsh[r * D + sl * 8 + i];
+    const int span = member_span(P, a.T, t0 + r / a.G);
+    uint32_t mk = 0u;  // this lane's largest order key of the row
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int j = wave * kLogitTok + it * TPI + tk;  // the token's index in the block
+      const int rank = r0 + j;
+      const float kf[8] = {bf16_lo(kv[it].x), bf16_hi(kv[it].x), bf16_lo(kv[it].y),
+                           bf16_hi(kv[it].y), bf16_lo(kv[it].z), bf16_hi(kv[it].z),
+                           bf16_lo(kv[it].w), bf16_hi(kv[it].w)};
       float acc = qr[0] * kf[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) acc = acc + qr[i] * kf[i];  // exact products
-#pragma unroll
-      for (int x = 1; x < LPT; x <<= 1) acc = acc + __shfl_xor(acc, x);
-      const float l = acc * a.scale;
-      const bool vis = pos < member_span(P, a.T, t0 + r / a.G);
+      const float l = butterfly<LPT>(acc) * a.scale;
+      const bool valid = rank < n;
+      const bool vis = pos_sh[j] < span;
       if (valid && sl == r % LPT) out[(size_t)rank * kStopRows + r] = vis ? l : -INFINITY;
+      const uint32_t k = (valid && vis && l > -INFINITY) ? order_key(l) : 0u;
+      mk = k > mk ? k : mk;
     }
+    const uint32_t v = wave_max_u32(mk);
+    if (lane == 0) mk_sh[wave][r] = v;
+  }
+  __syncthreads();
+  if (tid < rows) {
+    uint32_t v = mk_sh[0][tid];
+#pragma unroll
+    for (int w = 1; w < kLogitT / 64; ++w) v = mk_sh[w][tid] > v ? mk_sh[w][tid] : v;
+    a.stop_mkey[((size_t)u * (kStopMax / kStopBlock) + blockIdx.x) * kStopRows + tid] = v;
   }
 }
 
-// Grid: units x kCutT threads.
-constexpr int kCutT = 1024;
-constexpr int kCutW = kCutT / 64;
-__global__ __launch_bounds__(kCutT) void stop_cut_kernel(SelectArgs a) {
+// Gains of the 64-token blocks of the order: block i's gain for row r is the
+// sum over its tokens of floor(2^38 sexp(l - M_r)), M_r the row's largest
+// logit over the stratum (the maximum of the blocks' maxima; -inf entries
+// add nothing).  Grid: (kStopMax / 64, units) x 64 threads, lane = token;
+// the blocks' maxima and the lane's row logits are loaded together.
+__global__ __launch_bounds__(64) void stop_gain_kernel(SelectArgs a) {
   constexpr int kNB = kStopMax / kStopBlock;
-  __shared__ uint32_t mkey[kStopRows];                // each row's largest logit (order key)
-  __shared__ unsigned long long gain[kNB][kStopRows];  // block gains in units
+  const int u = blockIdx.y;
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  if (!stop_applies(st)) return;  // uniform
+  const int n = min(st.k_eff, kStopMax);
+  const int nb = (n + kStopBlock - 1) / kStopBlock;
+  const int i = blockIdx.x;
+  if (i >= nb) return;  // uniform
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int rows = min(min(a.g, a.T - ui.grp * a.g) * a.G, kStopRows);
+  const int lane = threadIdx.x;
+  const int rank = i * kStopBlock + lane;  // < kStopMax
+  const float4* lg4 =
+      reinterpret_cast<const float4*>(a.stop_logit + ((size_t)u * kStopMax + rank) * kStopRows);
+  float l[kStopRows];
+#pragma unroll
+  for (int k = 0; k < kStopRows / 4; ++k) {
+    const float4 v = lg4[k];
+    l[4 * k] = v.x;
+    l[4 * k + 1] = v.y;
+    l[4 * k + 2] = v.z;
+    l[4 * k + 3] = v.w;
+  }
+  // This lane's blocks lane, lane + 64, ...: their maxima of every row, the
+  // blocks past nb (not written by this call) counting as none.
+  uint32_t m[kStopRows];
+#pragma unroll
+  for (int r = 0; r < kStopRows; ++r) m[r] = 0u;
+  const uint4* mkb = reinterpret_cast<const uint4*>(a.stop_mkey + (size_t)u * kNB * kStopRows);
+#pragma unroll
+  for (int k = 0; k < kNB / 64; ++k) {
+    const int blk = lane + 64 * k;
+    uint4 v[kStopRows / 4];
+#pragma unroll
+    for (int c = 0; c < kStopRows / 4; ++c) v[c] = mkb[blk * (kStopRows / 4) + c];
+    if (blk < nb) {
+#pragma unroll
+      for (int c = 0; c < kStopRows / 4; ++c) {
+        m[4 * c] = v[c].x > m[4 * c] ? v[c].x : m[4 * c];
+        m[4 * c + 1] = v[c].y > m[4 * c + 1] ? v[c].y : m[4 * c + 1];
+        m[4 * c + 2] = v[c].z > m[4 * c + 2] ? v[c].z : m[4 * c + 2];
+        m[4 * c + 3] = v[c].w > m[4 * c + 3] ? v[c].w : m[4 * c + 3];
+      }
+    }
+  }
+  unsigned long long* gout = a.stop_gain + ((size_t)u * kNB + i) * kStopRows;
+#pragma unroll
+  for (int r = 0; r < kStopRows; ++r) {
+    if (r >= rows) break;  // uniform
+    const uint32_t mk = wave_max_u32(m[r]);
+    const unsigned long long q = (rank < n && l[r] > -INFINITY && mk)
+                                     ? mass_units(sexp(l[r] - key_to_float(mk)))
+                                     : 0ull;
+    const unsigned long long g = wave_sum(q);
+    if (lane == 0) gout[r] = g;
+  }
+}
+
+// Grid: units x kCutT threads.  Per row, the mass so far after each block
+// (prefix sums of the block gains); block i agrees when every row's gain is
+// 0 or below tau times its mass so far; the cut follows the first block
+// that agrees.
+constexpr int kCutT = 256;
+constexpr int kCutW = kCutT / 64;
+static_assert(kCutT == kStopMax / kStopBlock, "one thread per block of the order");
+__global__ __launch_bounds__(kCutT) void stop_cut_kernel(SelectArgs a) {
   __shared__ unsigned long long scan_m[kCutW];
   __shared__ int first_sh;
   const int u = blockIdx.x;
@@ -881,58 +997,29 @@ __global__ __launch_bounds__(kCutT) void stop_cut_kernel(SelectArgs a) {
   const int nb = (n + kStopBlock - 1) / kStopBlock;
   const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
   const int rows = min(min(a.g, a.T - ui.grp * a.g) * a.G, kStopRows);
-  const float* lg = a.stop_logit + (size_t)u * kStopMax * kStopRows;
-  if (tid < kStopRows) mkey[tid] = 0u;
+  // Thread tid holds block tid's gains (all 16 words loaded together; blocks
+  // at or past nb were not written and are ignored).
+  unsigned long long g[kStopRows];
+  {
+    const ulonglong2* gp = reinterpret_cast<const ulonglong2*>(
+        a.stop_gain + ((size_t)u * kCutT + tid) * kStopRows);
+#pragma unroll
+    for (int k = 0; k < kStopRows / 2; ++k) {
+      const ulonglong2 v = gp[k];
+      g[2 * k] = tid < nb ? v.x : 0ull;
+      g[2 * k + 1] = tid < nb ? v.y : 0ull;
+    }
+  }
   if (tid == 0) first_sh = 0x7fffffff;
-  __syncthreads();
-  // 1. Each row's maximum over the stratum (-inf entries never count).
-  {
-    uint32_t mk[kStopRows];
-#pragma unroll
-    for (int r = 0; r < kStopRows; ++r) mk[r] = 0u;
-    for (int rank = tid; rank < n; rank += kCutT) {
-#pragma unroll
-      for (int r = 0; r < kStopRows; ++r) {
-        if (r < rows) {
-          const float l = lg[(size_t)rank * kStopRows + r];
-          const uint32_t k = l > -INFINITY ? order_key(l) : 0u;
-          mk[r] = k > mk[r] ? k : mk[r];
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kStopRows; ++r) {
-      if (r < rows) {
-        const uint32_t v = wave_max_u32(mk[r]);
-        if ((tid & 63) == 0 && v) atomicMax(&mkey[r], v);
-      }
-    }
-  }
-  __syncthreads();
-  // 2. Block gains: wave w takes blocks w, w + kCutW, ...; lane = token.
-  {
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int i = wave; i < nb; i += kCutW) {
-      const int rank = i * kStopBlock + lane;
-      for (int r = 0; r < rows; ++r) {
-        const float l = rank < n ? lg[(size_t)rank * kStopRows + r] : -INFINITY;
-        const unsigned long long q =
-            (l > -INFINITY && mkey[r]) ? mass_units(sexp(l - key_to_float(mkey[r]))) : 0ull;
-        const unsigned long long g = wave_sum(q);
-        if (lane == 0) gain[i][r] = g;
-      }
-    }
-  }
-  __syncthreads();
-  // 3. Per row, the mass so far; block i agrees when every row's gain is 0
-  //    or below tau times its mass so far.
   bool agree = tid < nb;
-  for (int r = 0; r < rows; ++r) {  // uniform
-    const unsigned long long g = tid < nb ? gain[tid][r] : 0ull;
+#pragma unroll
+  for (int r = 0; r < kStopRows; ++r) {
+    if (r >= rows) break;  // uniform
     unsigned long long tot;
-    const unsigned long long acc = block_exclusive_scan<kCutT>(g, scan_m, &tot) + g;
-    if (g != 0ull && !gain_below(g, acc, a.stop_tau)) agree = false;
+    const unsigned long long acc = block_exclusive_scan<kCutT>(g[r], scan_m, &tot) + g[r];
+    if (g[r] != 0ull && !gain_below(g[r], acc, a.stop_tau)) agree = false;
   }
+  __syncthreads();
   if (agree) atomicMin(&first_sh, tid);
   __syncthreads();
   const int kept = first_sh == 0x7fffffff ? n : min(n, (first_sh + 1) * kStopBlock);
@@ -1153,13 +1240,14 @@ hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream) {
   const dim3 lg(kStopMax / kStopBlock, units);
   const bool split = a.k_rest != nullptr;
   if (a.d == 128 && !split)
-    stop_logit_kernel<128, false><<<lg, 64, 0, stream>>>(a);
+    stop_logit_kernel<128, false><<<lg, kLogitT, 0, stream>>>(a);
   else if (a.d == 128)
-    stop_logit_kernel<128, true><<<lg, 64, 0, stream>>>(a);
+    stop_logit_kernel<128, true><<<lg, kLogitT, 0, stream>>>(a);
   else if (!split)
-    stop_logit_kernel<64, false><<<lg, 64, 0, stream>>>(a);
+    stop_logit_kernel<64, false><<<lg, kLogitT, 0, stream>>>(a);
   else
-    stop_logit_kernel<64, true><<<lg, 64, 0, stream>>>(a);
+    stop_logit_kernel<64, true><<<lg, kLogitT, 0, stream>>>(a);
+  stop_gain_kernel<<<lg, 64, 0, stream>>>(a);
   stop_cut_kernel<<<units, kCutT, 0, stream>>>(a);
   return hipGetLastError();
 }

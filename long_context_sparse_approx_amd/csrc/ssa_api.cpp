@@ -131,7 +131,7 @@ struct Layout {
       list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
-      stop_words, stop_pair, stop_rword, stop_logit, w64, own_key, mstate, msel_idx, msel_logw,
+      stop_words, stop_pair, stop_rword, stop_logit, stop_mkey, stop_gain, w64, own_key, mstate, msel_idx, msel_logw,
       msel_cnt, total;
 };
 
@@ -175,6 +175,8 @@ Layout layout_of(const Dims& d) {
   l.stop_pair = take(SU * (KS / 1024) * (KS / 1024) * 1024 * 2);
   l.stop_rword = take(SU * KS * 8);
   l.stop_logit = take(SU * KS * SSA_STOP_MAX_ROWS * 4);
+  l.stop_mkey = take(SU * (KS / 64) * SSA_STOP_MAX_ROWS * 4);
+  l.stop_gain = take(SU * (KS / 64) * SSA_STOP_MAX_ROWS * 8);
   // refine mode's member selections (only when it is on)
   const size_t RU = d.refine > 0 ? (size_t)d.U : 0;
   const size_t RM = d.refine > 0 ? (size_t)d.Um : 0;
@@ -302,6 +304,8 @@ ssa::SelectArgs select_args(const ssa_params* p, const Dims& d, const float* sco
   a.stop_pair = d.stop ? at<uint16_t>(ws, l.stop_pair) : nullptr;
   a.stop_rword = d.stop ? at<unsigned long long>(ws, l.stop_rword) : nullptr;
   a.stop_logit = d.stop ? at<float>(ws, l.stop_logit) : nullptr;
+  a.stop_mkey = d.stop ? at<uint32_t>(ws, l.stop_mkey) : nullptr;
+  a.stop_gain = d.stop ? at<unsigned long long>(ws, l.stop_gain) : nullptr;
   a.max_topk = p->max_topk > 0 ? p->max_topk : INT32_MAX;
   a.kmult = d.refine > 0 ? d.refine : 1;
   a.w64 = d.refine > 0 ? at<double>(ws, l.w64) : nullptr;

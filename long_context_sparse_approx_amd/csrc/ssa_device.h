@@ -119,6 +119,31 @@ __device__ __forceinline__ float sexp(float x) {
   return low ? 0.0f : y;
 }
 
+// ---------------------------------------------------------------- lane butterflies
+
+// The partner lane across lane-index bit BIT of a 16-lane row (DPP: quad
+// permutations for bits 0 and 1, the half-row mirror for bit 2, a rotation
+// by 8 for bit 3).  Each pairing is an involution that joins the two halves
+// of the current group, so the butterfly sums neighbouring slices first.
+template <int BIT>
+__device__ __forceinline__ float dpp_partner(float x) {
+  constexpr int ctrl = BIT == 0 ? 0xB1 : (BIT == 1 ? 0x4E : (BIT == 2 ? 0x141 : 0x128));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                               ctrl, 0xf, 0xf, false));
+}
+
+// Sum of the LPT (<= 16, a power of two) lanes of an aligned lane group,
+// pairwise: neighbouring lanes first, then neighbouring pairs, and so on;
+// every lane of the group ends with the same sum.
+template <int LPT>
+__device__ __forceinline__ float butterfly(float p) {
+  if constexpr (LPT >= 2) p = p + dpp_partner<0>(p);
+  if constexpr (LPT >= 4) p = p + dpp_partner<1>(p);
+  if constexpr (LPT >= 8) p = p + dpp_partner<2>(p);
+  if constexpr (LPT >= 16) p = p + dpp_partner<3>(p);
+  return p;
+}
+
 // ---------------------------------------------------------------- top-p mass
 
 // Approximate mass of a token in integer units: floor(w * 2^38) for a weight

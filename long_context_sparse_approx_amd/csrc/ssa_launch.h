@@ -104,6 +104,9 @@ struct SelectArgs {
   unsigned long long* stop_rword; // [U, 16384] the stratum's words in its order (ties too)
   float* stop_logit;              // [U, 16384, 16] exact logit of (rank, query row);
                                   //   -inf outside the row's span
+  uint32_t* stop_mkey;            // [U, 256, 16] each 64-token block's largest logit per
+                                  //   row (order key; 0: none)
+  unsigned long long* stop_gain;  // [U, 256, 16] each 64-token block's gain per row, in units
   // What the exact logits read: the unit's query rows (each member's G
   // heads) and its keys, whole or split, through the block table.
   const uint16_t* q;              // [B, T, Hq, d]
