@@ -1052,7 +1052,8 @@ __device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, i
     mark[t - c0] = __float_as_uint(-logf(fminf(1.0f, mw / st.W)));
 }
 
-__global__ __launch_bounds__(kNT) void sample_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void sample_kernel(
+    SelectArgs a) {
   __shared__ uint32_t mark[kChunk];  // kMarkNone, kMarkDet or a sampled token's bias
   __shared__ int scan_scr[kNT / 64];
   static_assert(kPer == kBlockTokens, "a thread's positions are one cache block");
