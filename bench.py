@@ -117,7 +117,8 @@ def split_keys(wl, host):
 
 
 def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=None,
-            num_queries=1, query_group=1, early_stop=0.0, keys="whole", refine=0):
+            num_queries=1, query_group=1, early_stop=0.0, keys="whole", refine=0,
+            ceilings=False):
     """Times `steps` decode steps (after `warmup` untimed ones) of a workload.
     ``top_p`` (a float) caps every sequence's deterministic stratum at the
     top-p prefix; ``wl`` reuses an already generated workload; with
@@ -264,7 +265,9 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
     score_bytes = tokens * wl.Hkv * 4 * 4                       # 1 write + 3 reads
     if split:
         del call, k_dom, k_rest, v_split
+    ceil = measure_ceilings(wl, idx_bytes, 2 * (n_det + n_smp)) if ceilings else None
     res = dict(wl=wl, p=p, ms_step=ms_step, idx_ms=idx_ms, gpu_ms=gpu_ms, stage_ms=stage_ms,
+               ceilings=ceil,
                tokens=tokens,
                idx_bytes=idx_bytes, gather_bytes=gather_bytes, score_bytes=score_bytes,
                n_det=n_det, n_smp=n_smp, t_gen=t_gen, cache=cache)
@@ -380,6 +383,54 @@ def cpu_baseline(wl, budget_s=15.0):
                        f"limited to 1 thread); layer rate = token-heads / {wl.Hkv} / time")
 
 
+def measure_ceilings(wl, stream_bytes, gather_rows, reps=7):
+    """What HBM delivers on this device for the step's two bandwidth-bound
+    access patterns, with the library's measurement kernels: a contiguous read
+    of the indexer's byte count (from the key cache), and a gather of the
+    attention's K+V row count of d*2-byte rows scattered uniformly over the
+    value cache (seeded ids).  Each rep runs after a 512 MiB read that evicts
+    L2 and the Infinity Cache; medians of the reps, from HIP events on the
+    stream the kernels run on."""
+    import torch
+
+    from long_context_sparse_approx_amd import ssa
+
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(ssa.MEASURE_SINK_WORDS, dtype=torch.int32, device=dev)
+    scrub = torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    scrub_sum = torch.empty((), dtype=torch.float32, device=dev)
+    row_bytes = wl.d * 2
+    num_rows = wl.v_cache.numel() * 2 // row_bytes
+    g = torch.Generator(device=dev).manual_seed(20260)
+    rows = torch.randint(0, num_rows, (int(gather_rows),), generator=g, device=dev,
+                         dtype=torch.int32)
+    nbytes = min(int(stream_bytes), wl.k_cache.numel() * 2) // 16 * 16
+
+    def timed(launch):
+        ts = []
+        for _ in range(reps + 1):
+            torch.sum(scrub, dim=0, out=scrub_sum)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts = sorted(ts[1:])
+        return ts[len(ts) // 2]
+
+    us_s = timed(lambda: ssa.measure_stream(wl.k_cache, nbytes, sink, stream))
+    us_g = timed(lambda: ssa.measure_gather(wl.v_cache, row_bytes, rows, sink, stream))
+    del scrub, scrub_sum, rows
+    return dict(
+        stream_read=dict(bytes=nbytes, us=round(us_s, 2), gbps=round(nbytes / us_s / 1e3, 1)),
+        row_gather=dict(rows=int(gather_rows), row_bytes=row_bytes,
+                        bytes=int(gather_rows) * row_bytes, us=round(us_g, 2),
+                        gbps=round(int(gather_rows) * row_bytes / us_g / 1e3, 1)),
+        reps=reps, evict_mib=512)
+
+
 def summarize(res, workload):
     st = res["stage_ms"]
     roof = None
@@ -404,6 +455,19 @@ def summarize(res, workload):
         gbps = algo_total / pair_s / 1e9
         index_gather = dict(bytes=algo_total, us=round(pair_s * 1e6, 2), gbps=round(gbps, 1),
                             frac=round(gbps / HBM_PEAK_GBPS, 4))
+    ceil = res.get("ceilings")
+    if roof and ceil:
+        roof["measured_ceiling"] = dict(pattern="contiguous read", gbps=ceil["stream_read"]["gbps"])
+        roof["frac_of_measured_ceiling"] = round(roof["achieved"] / ceil["stream_read"]["gbps"], 4)
+    attention = None
+    if st["attend"] > 0:
+        gbps = res["gather_bytes"] / (st["attend"] * 1e-3) / 1e9
+        attention = dict(bytes=res["gather_bytes"], us=round(st["attend"] * 1e3, 2),
+                         gbps=round(gbps, 1), frac=round(gbps / HBM_PEAK_GBPS, 4))
+        if ceil:
+            attention["measured_ceiling"] = dict(pattern="scattered row gather",
+                                                 gbps=ceil["row_gather"]["gbps"])
+            attention["frac_of_measured_ceiling"] = round(gbps / ceil["row_gather"]["gbps"], 4)
     cold = None
     if res["cache"]:
         c = res["cache"]
@@ -411,7 +475,7 @@ def summarize(res, workload):
                     us=c["cold_median_us"],
                     hbm_frac_algorithmic=round(algo_total / (c["cold_median_us"] * 1e-6) / 1e9
                                                / HBM_PEAK_GBPS, 4))
-    return dict(index_gather=index_gather, cold=cold,
+    return dict(index_gather=index_gather, cold=cold, attention=attention, ceilings=ceil,
         value=res["tokens"] / step_s, ms_per_step=res["ms_step"], roofline=roof,
         stages_us={k: round(v * 1e3, 2) for k, v in st.items()},
         gpu_step_us=round(res["gpu_ms"] * 1e3, 2),
@@ -449,6 +513,9 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="per-step medians over this many steps with and without a 512 MiB "
                          "cache-evicting read before each (0 = skip)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip timing the measurement kernels (contiguous read and row gather "
+                         "of the step's byte and row counts)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -470,11 +537,13 @@ def main():
         print(f"copy calibration: {n} bytes read + {n} bytes written per launch", file=sys.stderr)
         del a, b
 
-    res = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events)
+    res = run_gpu(args, args.workload, args.steps, args.warmup, not args.no_stage_events,
+                  ceilings=not args.no_ceilings)
     main_sum = summarize(res, args.workload)
     also = {}
     for name in [w for w in args.also.split(",") if w and w not in ("none", args.workload)]:
-        r2 = run_gpu(args, name, args.steps, args.warmup, not args.no_stage_events)
+        r2 = run_gpu(args, name, args.steps, args.warmup, not args.no_stage_events,
+                     ceilings=not args.no_ceilings)
         s2 = summarize(r2, name)
         also[name] = dict(workload=WORKLOADS[name], value=s2["value"], unit="KV-tokens/s/layer",
                           ms_per_step=s2["ms_per_step"], roofline=s2["roofline"],
@@ -482,6 +551,7 @@ def main():
                           hbm_gbps_algorithmic_step=s2["hbm_gbps_algorithmic_step"],
                           hbm_frac_algorithmic_step=s2["hbm_frac_algorithmic_step"],
                           index_gather=s2["index_gather"],
+                          attention=s2["attention"], ceilings=s2["ceilings"],
                           value_cache_flushed=s2["cold"],
                           per_step_cache=r2["cache"])
         del r2
@@ -578,6 +648,8 @@ def main():
         "per_step_cache": res["cache"],
         "value_cache_flushed": main_sum["cold"],
         "index_gather": main_sum["index_gather"],
+        "attention": main_sum["attention"],
+        "ceilings": main_sum["ceilings"],
         "hbm_gbps_algorithmic_step": main_sum["hbm_gbps_algorithmic_step"],
         "hbm_frac_algorithmic_step": main_sum["hbm_frac_algorithmic_step"],
         "gather_gbps_algorithmic": main_sum["gather_gbps_algorithmic"],

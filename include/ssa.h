@@ -369,6 +369,27 @@ int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t group, int32_t
 /* Test hook: y[i] = the library's specified float32 exp of x[i], i < n. */
 int ssa_debug_sexp(const float* x, float* y, int32_t n, void* stream);
 
+/* Measurement aids, not steps of the decode: the HBM read rate this device
+ * delivers for the access patterns of the step's two bandwidth-bound
+ * kernels, so that their achieved rates can be set beside what the memory
+ * gives for the same pattern (the published peak is not reachable by any
+ * access pattern).  Each folds every 32-bit word it reads by XOR into the
+ * sink, an array of SSA_MEASURE_SINK_WORDS words (integer atomics spread over
+ * the array; the result does not depend on the order of the work): clear the
+ * sink first, and the XOR of its words afterwards is the XOR of the data.
+ *   ssa_measure_stream: bytes (a positive multiple of 16) read contiguously
+ *     from src, the indexer's pattern (a long stream).
+ *   ssa_measure_gather: n rows of row_bytes (a power of two, 16 to 1024) at
+ *     src + rows[i] * row_bytes, rows[i] clamped to [0, num_rows) -- src
+ *     must hold num_rows such rows -- the attention's pattern (selected K
+ *     and V rows, scattered over the cache).
+ * src must be 16-byte aligned.  SSA_ERR_INVALID on a null pointer or a size
+ * out of range; n = 0 enqueues nothing. */
+#define SSA_MEASURE_SINK_WORDS 4096
+int ssa_measure_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int ssa_measure_gather(const void* src, size_t row_bytes, int64_t num_rows, const int32_t* rows,
+                       int64_t n, uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* ssa_error_string(int code);
 

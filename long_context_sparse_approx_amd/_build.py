@@ -14,6 +14,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssa.so")
 
 SOURCES = ["indexer.hip", "select.hip", "refine.hip", "attend.hip", "append.hip", "static_ws.hip",
+           "measure.hip",
            "ssa_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for every HIP translation unit; contraction

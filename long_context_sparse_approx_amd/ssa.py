@@ -28,6 +28,7 @@ SSA_KEYS_WHOLE = 0
 SSA_KEYS_SPLIT = 1
 STOP_MAX_STRATUM = 16384
 STOP_MAX_ROWS = 16
+MEASURE_SINK_WORDS = 4096
 BLOCK_TOKENS = 16
 CHUNK_TOKENS = 4096
 STAGES = ("init", "index", "filter", "resolve", "sample", "attend", "merge")
@@ -35,7 +36,7 @@ EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_st
            "ssa_decode_timed",
            "ssa_decode_split", "ssa_score", "ssa_select", "ssa_attend", "ssa_attend_split",
            "ssa_append_kv", "ssa_host_device_address", "ssa_debug_philox", "ssa_debug_sexp",
-           "ssa_error_string")
+           "ssa_measure_stream", "ssa_measure_gather", "ssa_error_string")
 
 
 class SsaParams(ctypes.Structure):
@@ -102,6 +103,11 @@ def lib() -> ctypes.CDLL:
         L.ssa_debug_philox.restype = ctypes.c_int
         L.ssa_debug_sexp.argtypes = [_P, _P, ctypes.c_int32, _P]
         L.ssa_debug_sexp.restype = ctypes.c_int
+        L.ssa_measure_stream.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.ssa_measure_stream.restype = ctypes.c_int
+        L.ssa_measure_gather.argtypes = [_P, ctypes.c_size_t, ctypes.c_int64, _P, ctypes.c_int64,
+                                         _P, _P]
+        L.ssa_measure_gather.restype = ctypes.c_int
         L.ssa_error_string.argtypes = [ctypes.c_int]
         L.ssa_error_string.restype = ctypes.c_char_p
         _lib = L
@@ -363,6 +369,30 @@ def debug_sexp(x: torch.Tensor):
     y = torch.empty_like(x)
     _check(lib().ssa_debug_sexp(_ptr(x), _ptr(y), x.numel(), _stream(None)), "ssa_debug_sexp")
     return y
+
+
+def measure_stream(src: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None):
+    """Contiguous read of the first nbytes of src (measurement aid); XOR of its
+    32-bit words folded into sink (MEASURE_SINK_WORDS int32, cleared by the
+    caller; the XOR of sink's words is the XOR of the data)."""
+    if nbytes > src.numel() * src.element_size():
+        raise ValueError("nbytes exceeds the source tensor")
+    if sink.numel() < MEASURE_SINK_WORDS or sink.element_size() != 4:
+        raise ValueError("sink must hold MEASURE_SINK_WORDS 32-bit words")
+    _check(lib().ssa_measure_stream(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "ssa_measure_stream")
+
+
+def measure_gather(src: torch.Tensor, row_bytes: int, rows: torch.Tensor, sink: torch.Tensor,
+                   stream=None):
+    """Gather of the rows (int32 ids) of src viewed as rows of row_bytes
+    (measurement aid); XOR of their 32-bit words folded into sink as in
+    measure_stream."""
+    if sink.numel() < MEASURE_SINK_WORDS or sink.element_size() != 4:
+        raise ValueError("sink must hold MEASURE_SINK_WORDS 32-bit words")
+    num_rows = src.numel() * src.element_size() // row_bytes
+    _check(lib().ssa_measure_gather(_ptr(src), row_bytes, num_rows, _ptr(rows), rows.numel(),
+                                    _ptr(sink), _stream(stream)), "ssa_measure_gather")
 
 
 def decode_workload(wl, **kw):

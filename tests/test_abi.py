@@ -206,3 +206,27 @@ def test_early_stop_selection_needs_query_and_keys(lib):
         rc = lib.ssa_select(ctypes.byref(p), fake, fake, fake, None, fake, fake, None, q, k,
                             None, bt, fake, fake, fake, fake, fake, ctypes.c_size_t(n), None)
         assert rc == ssa.SSA_ERR_INVALID
+
+
+def test_measurement_aids_reject_bad_arguments_on_the_host(lib):
+    # validation comes before any HIP call, so these run without a GPU
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.ssa_measure_stream(None, 16, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_stream(fake, 24, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_stream(fake, 0, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_stream(ctypes.c_void_p((1 << 20) + 4), 16, fake, None) == \
+        ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_gather(fake, 256, 0, fake, 4, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_gather(fake, 256, 16, None, 4, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_gather(fake, 256, 16, fake, -1, fake, None) == ssa.SSA_ERR_INVALID
+    assert lib.ssa_measure_gather(fake, 256, 16, fake, 0, fake, None) == ssa.SSA_OK
+
+
+def test_binding_constants_match_the_header():
+    text = open(HEADER).read()
+    defines = dict(re.findall(r"#define (SSA_\w+) \(?(-?\d+)\)?", text))
+    assert int(defines["SSA_MEASURE_SINK_WORDS"]) == ssa.MEASURE_SINK_WORDS
+    assert int(defines["SSA_STOP_MAX_STRATUM"]) == ssa.STOP_MAX_STRATUM
+    assert int(defines["SSA_STOP_MAX_ROWS"]) == ssa.STOP_MAX_ROWS
+    assert int(defines["SSA_ERR_INVALID"]) == ssa.SSA_ERR_INVALID
+    assert int(defines["SSA_OK"]) == ssa.SSA_OK
