@@ -372,7 +372,7 @@ constexpr uint32_t kMarkDet = 0xfffffffeu;
 // (candidates, then the group's samples), their proxy weights and uniforms
 // are loaded and drawn once; then each member in turn marks its stratum and
 // samples in an LDS map of the chunk and writes its segment from it.
-__global__ __launch_bounds__(kRS) void refine_emit_kernel(RefineArgs a) {
+__global__ __launch_bounds__(kRS) __attribute__((amdgpu_waves_per_eu(8))) void refine_emit_kernel(RefineArgs a) {
   __shared__ uint32_t mark[kChunk];
   __shared__ int scan_scr[kRS / 64];
   constexpr int kPerT = kChunk / kRS;  // 16: also the most group entries per thread
