@@ -39,8 +39,14 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   const uint64_t seed = a.seed[b];
   const int tb = threadIdx.x * kPer;
   const int nv = p.L - (c0 + tb);  // valid tokens of this thread: min(16, max(nv, 0))
-  uint32_t candmask = 0u, abovemask = 0u, sampmask = 0u;
+  // Per-token class bits, formed arithmetically so that none of them is held
+  // as a lane mask across the loop: d = first digit - b1 has its sign bit set
+  // for a tail token (d < 0), and -d for a token above the threshold digit.
+  // Positions past the sequence are scored -inf (weight exactly 0, so the
+  // tail sum is unchanged) and their bits are cleared at the end.
+  uint32_t tailbits = 0u, abovebits = 0u, sampbits = 0u;
   double wsum = 0.0;
+  const uint32_t vmask = nv >= kPer ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
 #pragma unroll
   for (int g = 0; g < kPer / 4; ++g) {
     // One group at a time: its loads may still be in flight while the
@@ -48,26 +54,34 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
     // counter to the previous group's result, so the four blocks are not
     // computed at once (they would not fit 64 VGPRs).
     uint32_t jq = (uint32_t)(c0 + tb + 4 * g) >> 2;
-    asm volatile("" : "+v"(jq) : "v"(sampmask));
-    const float s[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
+    asm volatile("" : "+v"(jq) : "v"(sampbits));
+    float s[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
     // Kept for the second pass (no other thread reads this thread's entries).
     *reinterpret_cast<float4*>(sh + tb + 4 * g) = s4[g];
+    if (nv < kPer) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * g + r >= nv) s[r] = -INFINITY;
+    }
     uint4 wd = make_uint4(0u, 0u, 0u, 0u);
     if (sampling) wd = philox_block(seed, b, h, jq, grp);
     const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 4 * g + r;
-      const int bin = (int)(order_key(s[r]) >> kDigit1Shift);
-      const bool valid = i < nv;
-      abovemask |= (uint32_t)(valid && bin > b1) << i;
-      candmask |= (uint32_t)(valid && bin == b1) << i;
-      const bool tail = valid && bin < b1;
+      const int d = (int)(order_key(s[r]) >> kDigit1Shift) - b1;
+      const uint32_t tbit = (uint32_t)d >> 31;
+      tailbits |= tbit << i;
+      abovebits |= ((uint32_t)(-d) >> 31) << i;
       const float w = sexp(s[r] - M);
-      wsum += tail ? (double)w : 0.0;
-      sampmask |= (uint32_t)(sampling && tail && uniform24(words[r]) * t1.wlb < mf * w) << i;
+      wsum += (double)__uint_as_float(__float_as_uint(w) & (0u - tbit));
+      const uint32_t sbit = uniform24(words[r]) * t1.wlb < mf * w ? 1u : 0u;
+      sampbits |= (sbit & tbit) << i;
     }
   }
+  const uint32_t abovemask = abovebits & vmask;
+  const uint32_t candmask = ~(abovebits | tailbits) & vmask;
+  const uint32_t sampmask = sampling ? sampbits & vmask : 0u;
   int total;
   const int off = block_exclusive_scan<kNT>(__popc(candmask), scan_scr, &total);
   int lst_tot;
