@@ -30,15 +30,19 @@ __device__ __forceinline__ void wave_xor_to(uint32_t v, uint32_t* sink) {
 }
 
 constexpr int kMT = 256;         // threads per workgroup
-constexpr int kStreamWG = 2048;  // workgroups of the stream (measured best of 1024 - 16384)
+constexpr int kStreamWG = 2048;  // workgroups of the stream
 
-// n16 16-byte words of src, grid-stride: a wave's loads cover 1 KiB of
-// consecutive memory and consecutive waves the next ones.
+// n16 16-byte words of src, grid-stride, non-temporal loads: a wave's loads
+// cover 1 KiB of consecutive memory and consecutive waves the next ones.
+// The fastest of a sweep over 1024-4096 workgroups, 1 or 4 loads in flight
+// per thread, plain or non-temporal loads, and one contiguous range per
+// workgroup (1 GiB in 152-155 us).
 __global__ __launch_bounds__(kMT) void stream_kernel(const u32x4* __restrict__ src, size_t n16,
                                                      uint32_t* sink) {
   const size_t stride = (size_t)gridDim.x * kMT;
   uint32_t acc = 0u;
-  for (size_t i = (size_t)blockIdx.x * kMT + threadIdx.x; i < n16; i += stride) acc ^= fold(src[i]);
+  for (size_t i = (size_t)blockIdx.x * kMT + threadIdx.x; i < n16; i += stride)
+    acc ^= fold(__builtin_nontemporal_load(src + i));
   wave_xor_to(acc, sink);
 }
 
