@@ -74,7 +74,8 @@ constexpr int kBatch = 256;  // selected items resolved to cache rows at a time
 // dominant key components resident and moves the rest of the key and the
 // values elsewhere); a row is put back together from its 16-byte slices.
 template <int D, bool SPLIT>
-__global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(
+    AttendArgs a) {
   constexpr int KK = D / 32;   // QK steps over the head dim
   constexpr int DPL = D / 16;  // head dims per PV column = PV steps
   using VS = VSlice<D>;
@@ -212,32 +213,46 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
       __syncthreads();
       for (int t0 = 0; t0 < nb; t0 += 32) {
         // QK for the two 16-token halves: A = K rows (token n16 of the half).
-        f32x4 sc[2];
+        // Every K load of the tile is unconditional (a marked item reads row 0
+        // and is zeroed), so the eight loads are in flight together; the V
+        // loads follow the same way once the QK products are issued.
+        bf16x8 kf[2][KK];
+        bool kok[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int r = rows_sh[t0 + 16 * hh + n16];
-          bf16x8 kf[KK];
+          kok[hh] = r >= 0;
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (r >= 0) v = *reinterpret_cast<const uint4*>(kb[kk] + (size_t)r * kld[kk]);
-            kf[kk] = as_bf16x8(v);
+          for (int kk = 0; kk < KK; ++kk)
+            kf[hh][kk] =
+                as_bf16x8(*reinterpret_cast<const uint4*>(kb[kk] + (size_t)max(r, 0) * kld[kk]));
+        }
+        f32x4 sc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if (!kok[hh]) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) kf[hh][kk] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
           }
           f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hh][kk], qf[kk], d, 0, 0, 0);
           sc[hh] = d;
         }
-        // V rows of this lane's 8 k-slots (issued before the softmax math).
+        // V rows of this lane's 8 k-slots (issued before the softmax math, and
+        // kept after the QK products so that K and V registers are not live
+        // together).
+        __builtin_amdgcn_sched_barrier(0);
         typename VS::T vr[8];
+        bool vok[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
           const int r = rows_sh[t0 + tok];
-          vr[i] = VS::zero();
-          if (r >= 0)
-            vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)r * D + n16 * DPL);
+          vok[i] = r >= 0;
+          vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)max(r, 0) * D +
+                                                          n16 * DPL);
         }
         // Logits of (column n16, slot tokens), online softmax update; a
         // column ignores positions past its member's span.
@@ -282,6 +297,9 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
 #pragma unroll
           for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (!vok[i]) vr[i] = VS::zero();
         const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
         const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
 #pragma unroll
