@@ -440,11 +440,18 @@ __device__ __forceinline__ SeqParams seq_params(int L, const int32_t* topk, cons
                                                 int max_topk, int kmult = 1) {
   SeqParams p;
   p.L = L;
-  const int64_t k64 = (int64_t)min(max(topk[b], 0), max_topk) * kmult;
+  // The three loads are unconditional (without a top-p array the last one
+  // reads the budget's word and is discarded), so they go out together.
+  const int tk = topk[b];
+  const int mb = sample_budget[b];
+  float pv;
+  __builtin_memcpy(&pv, top_p ? static_cast<const void*>(top_p + b)
+                              : static_cast<const void*>(sample_budget + b), sizeof(float));
+  const int64_t k64 = (int64_t)min(max(tk, 0), max_topk) * kmult;
   const int k = k64 > L ? L : (int)k64;
-  p.m = max(sample_budget[b], 0);
+  p.m = max(mb, 0);
   p.topp = top_p != nullptr;
-  p.p = p.topp ? top_p[b] : 1.0f;
+  p.p = p.topp ? pv : 1.0f;
   p.dense = p.topp ? p.m >= p.L : (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
   p.k_eff = min(k, p.L);
   return p;
