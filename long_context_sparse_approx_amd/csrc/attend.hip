@@ -342,62 +342,83 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 }
 
 // Merge of the split states of one (query position, query head), for one
-// 64-dim slice of the head (grid: B*T*Hq x d/64):
+// 16-dim slice of the head (grid: B*T*Hq x d/16):
 //   m* = max_s m_s,  o = sum_s e^{m_s - m*} acc_s / sum_s e^{m_s - m*} l_s,
-// in a fixed order (deterministic).  The split weights e^{m_s - m*} are
-// computed once into LDS; each wave then takes every kMW-th split (lane =
-// dim, so one split's slice is one contiguous wave-wide load).
+// in a fixed order (deterministic).  Thread t takes dim t % 16 of the slice
+// for splits t / 16, t / 16 + 16, ...; the first kMSlots of its accumulator
+// values go out with the split maxima and sums, so the common merge (at most
+// 256 splits) is one round of loads and three barriers, and a head's slices
+// are read by d/16 workgroups side by side.  The split weights e^{m_s - m*}
+// are computed once into LDS.
 constexpr int kMT = 256;
 constexpr int kMW = kMT / 64;
+constexpr int kMSlice = 16;                // dims per workgroup
+constexpr int kMGroups = kMT / kMSlice;    // split groups per workgroup
+constexpr int kMSlots = 16;                // accumulator values per thread in the first loads
 constexpr int kMaxMergeSplits = SSA_MAX_SEQ_LEN / kChunk;
 
 __global__ __launch_bounds__(kMT) void merge_kernel(AttendArgs a) {
-  __shared__ float red[kMW];
+  __shared__ float red_m[kMW];
+  __shared__ float red_d[kMW];
   __shared__ float esh[kMaxMergeSplits];
-  __shared__ float accsh[kMW][64];
+  __shared__ float osh[kMGroups][kMSlice];
   const int bh = blockIdx.x;
   const int D = a.d;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int dim = blockIdx.y * 64 + lane;
+  const int grp = threadIdx.x / kMSlice;
+  const int sub = threadIdx.x % kMSlice;
+  const int dim = blockIdx.y * kMSlice + sub;
   const int ns = a.nsplit * a.nsub;
-  const float* base = a.part + (size_t)bh * ns * (D + 2);
-  float mx = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += kMT) {
-    const float m = base[(size_t)s * (D + 2) + D];
-    esh[s] = m;
-    mx = fmaxf(mx, m);
-  }
+  const size_t stride = (size_t)D + 2;
+  const float* base = a.part + (size_t)bh * ns * stride;
+  // Every load from a split clamped into range; values of splits past ns are
+  // never used.
+  const size_t s0 = (size_t)min((int)threadIdx.x, ns - 1);
+  const float m0 = base[s0 * stride + D];
+  const float l0 = base[s0 * stride + D + 1];
+  float av[kMSlots];
+#pragma unroll
+  for (int i = 0; i < kMSlots; ++i)
+    av[i] = base[(size_t)min(grp + kMGroups * i, ns - 1) * stride + dim];
+  float mx = (int)threadIdx.x < ns ? m0 : -INFINITY;
+  for (int s = threadIdx.x + kMT; s < ns; s += kMT) mx = fmaxf(mx, base[(size_t)s * stride + D]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) red[wave] = mx;
+  if (lane == 0) red_m[wave] = mx;
   __syncthreads();
-  float mstar = red[0];
+  float mstar = red_m[0];
 #pragma unroll
-  for (int w = 1; w < kMW; ++w) mstar = fmaxf(mstar, red[w]);
-  __syncthreads();
+  for (int w = 1; w < kMW; ++w) mstar = fmaxf(mstar, red_m[w]);
   float den = 0.0f;
   for (int s = threadIdx.x; s < ns; s += kMT) {
-    const float m = esh[s];
+    const bool first = s == (int)threadIdx.x;
+    const float m = first ? m0 : base[(size_t)s * stride + D];
+    const float l = first ? l0 : base[(size_t)s * stride + D + 1];
     const float e = (m != -INFINITY) ? __expf(m - mstar) : 0.0f;
     esh[s] = e;
-    den += e * base[(size_t)s * (D + 2) + D + 1];
+    den += e * l;
   }
   den = wave_sum(den);
-  if (lane == 0) red[wave] = den;
+  if (lane == 0) red_d[wave] = den;
   __syncthreads();
   float denom = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kMW; ++w) denom += red[w];
+  for (int w = 0; w < kMW; ++w) denom += red_d[w];
   float o = 0.0f;
-#pragma unroll 16
-  for (int s = wave; s < ns; s += kMW) o += esh[s] * base[(size_t)s * (D + 2) + dim];
-  accsh[wave][lane] = o;
+#pragma unroll
+  for (int i = 0; i < kMSlots; ++i) {
+    const int s = grp + kMGroups * i;
+    if (s < ns) o += esh[s] * av[i];
+  }
+  for (int s = grp + kMGroups * kMSlots; s < ns; s += kMGroups)
+    o += esh[s] * base[(size_t)s * stride + dim];
+  osh[grp][sub] = o;
   __syncthreads();
-  if (threadIdx.x < 64) {
+  if (threadIdx.x < kMSlice) {
     float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kMW; ++w) t += accsh[w][threadIdx.x];
+    for (int g = 0; g < kMGroups; ++g) t += osh[g][threadIdx.x];
     const float res = (mstar == -INFINITY || denom <= 0.0f) ? 0.0f : t / denom;
     if (a.out_dtype == SSA_BF16)
       reinterpret_cast<uint16_t*>(a.out)[(size_t)bh * D + dim] = (uint16_t)f32_to_bf16_bits(res);
@@ -428,7 +449,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const AttendArgs& a, hipStream_t stream) {
   if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
-  merge_kernel<<<dim3(a.B * a.T * a.Hq, a.d / 64), kMT, 0, stream>>>(a);
+  merge_kernel<<<dim3(a.B * a.T * a.Hq, a.d / kMSlice), kMT, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -96,10 +96,8 @@ __global__ __launch_bounds__(kNT) void mass_kernel(SelectArgs a) {
 __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ unsigned long long mh[kBins];
-  __shared__ int scan_scr[kNT / 64];
-  __shared__ int pair[2];
-  __shared__ unsigned long long scan_m[kNT / 64];
-  __shared__ unsigned long long pair_m[2];
+  __shared__ int dig_sh[4];  // the digit's bin, remainder, mode and count above
+  __shared__ unsigned long long dig_m;
   __shared__ double dscr[kNT / 64];
   const int u = blockIdx.x;
   // The histogram and the maximum depend on the unit only: their loads go
@@ -122,30 +120,43 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   if (topp)
     for (int i = threadIdx.x; i < kBins; i += kNT) mh[i] = a.hist1m[(size_t)u * kBins + i];
   __syncthreads();
-  DigitBound d{kBins, 0, 0ull, 0};
-  int bc = kBins, rc = 0;  // where the count bound ends (its rank search)
-  if (p.k_eff > 0) {
-    find_rank_bin<kNT>(hist, kBins, p.k_eff, scan_scr, pair, &bc, &rc);
-    d = DigitBound{bc, rc, 0ull, kBoundCount};
-    if (topp) {
-      unsigned long long qs = 0ull;
-      for (int i = threadIdx.x; i < kBins; i += kNT) qs += mh[i];
-      const unsigned long long tau = mass_target(p.p, block_sum_u64<kNT>(qs, scan_m));
-      if (tau == 0ull) {
-        d = DigitBound{kBins, 0, 0ull, 0};
-      } else {
-        int bm;
-        unsigned long long rm;
-        find_bin<kNT>(mh, kBins, tau, scan_m, pair_m, &bm, &rm);
-        d = combine_bounds(kBoundCount | kBoundMass, bc, rc, bm, rm);
+  // The digit is searched by one wave; the others wait at the barrier.
+  if (threadIdx.x < 64) {
+    DigitBound d{kBins, 0, 0ull, 0};
+    int above = 0;
+    if (p.k_eff > 0) {
+      int bc, rc;  // where the count bound ends (its rank search)
+      wave_find_bin<int>(hist, kBins, p.k_eff, &bc, &rc);
+      d = DigitBound{bc, rc, 0ull, kBoundCount};
+      if (topp) {
+        unsigned long long qs = 0ull;
+        for (int i = threadIdx.x; i < kBins; i += 64) qs += mh[i];
+        const unsigned long long tau = mass_target(p.p, wave_sum(qs));
+        if (tau == 0ull) {
+          d = DigitBound{kBins, 0, 0ull, 0};
+        } else {
+          int bm;
+          unsigned long long rm;
+          wave_find_bin<unsigned long long>(mh, kBins, tau, &bm, &rm);
+          d = combine_bounds(kBoundCount | kBoundMass, bc, rc, bm, rm);
+        }
       }
+      // Tokens above the digit: the rank search already counted them when it
+      // chose the digit.
+      above = d.bin == kBins ? 0
+              : (d.bin == bc && (d.mode & kBoundCount)) ? p.k_eff - rc
+                                                        : wave_count_above(hist, kBins, d.bin);
+    }
+    if (threadIdx.x == 0) {
+      dig_sh[0] = d.bin;
+      dig_sh[1] = d.rem;
+      dig_sh[2] = d.mode;
+      dig_sh[3] = above;
+      dig_m = d.rem_mass;
     }
   }
-  const int b1 = d.bin;
-  // Tokens above b1: the rank search already counted them when it chose b1.
-  const int above = b1 == kBins ? 0
-                    : (b1 == bc && (d.mode & kBoundCount)) ? p.k_eff - rc
-                                                            : count_above<kNT>(hist, kBins, b1, scan_scr);
+  __syncthreads();
+  const int b1 = dig_sh[0];
   const float M = key_to_float(maxkey);
   double lb = 0.0;
   for (int bin = threadIdx.x; bin < b1; bin += kNT) {
@@ -156,7 +167,8 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
   lb = block_sum_f64<kNT>(lb, dscr);
   float wlb = (float)(lb * (1.0 - 0x1.0p-10));
   if (a.w_in) wlb = fminf(wlb, a.w_in[u]);
-  if (threadIdx.x == 0) a.thresh[u] = Thresh1{b1, d.rem, wlb, d.mode, d.rem_mass, above, 0};
+  if (threadIdx.x == 0)
+    a.thresh[u] = Thresh1{b1, dig_sh[1], wlb, dig_sh[2], dig_m, dig_sh[3], 0};
 }
 
 // ------------------------------------------------------------------ filter
@@ -220,22 +232,23 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void f
 // One workgroup per unit: finish the radix select on the candidates (second
 // digit from the histogram, third digit from an LDS histogram of the
 // candidates sharing the first two digits), then the per-chunk tie counts,
-// the tie quota offsets and the tail normaliser W.  Candidate passes run over
-// the flattened candidate list, every thread on a fixed stride, so loads are
-// independent and every sum has a fixed order.
+// the tie quota offsets and the tail normaliser W.
+//
+// Wave w serves the unit's chunks w, w + 16, w + 32, ...; in each, lane l
+// takes candidates l, l + 64, ..., so every load reads 256 contiguous bytes
+// of a chunk's segment.  The first 64 candidates of the wave's first 16
+// chunks stay in registers between the passes (at 50x sparsity a chunk holds
+// about 40); the rest are read again in each pass.  The digit searches and
+// the scan over the chunks run in one wave between two barriers, and the
+// per-chunk counts are wave ballots, so no pass needs an LDS atomic but the
+// third-digit histogram's.  Every thread's items are fixed by the chunk
+// count, so every sum has a fixed order.
 constexpr int kRT = 1024;
 constexpr int kRW = kRT / 64;
+constexpr int kRSlots = 16;  // chunks per wave whose first 64 candidates stay in registers
 constexpr int kMaxResolveChunks = SSA_MAX_SEQ_LEN / kChunk;
 static_assert(kBins % kRT == 0, "each resolve thread loads kBins / kRT histogram entries");
-
-// Candidate passes: thread t serves chunk (t / tpc) + k * (kRT / tpc) and,
-// inside it, items (t % tpc) + i * tpc.  Every load is independent and every
-// thread's items are fixed by (nc, t): sums over them have a fixed order.
-__device__ __forceinline__ int threads_per_chunk(int nc) {
-  int tpc = kRT;
-  while (tpc > 1 && tpc * nc > kRT) tpc >>= 1;
-  return tpc;
-}
+static_assert(kRSlots <= 64, "one lane per slot holds the slot's candidate count");
 
 // Early stopping: where each chunk's words above the threshold key (its
 // listed tokens above the threshold digit, then its candidates above the key;
@@ -254,29 +267,42 @@ __device__ __forceinline__ void stop_offsets(const SelectArgs& a, int u, size_t 
   if (threadIdx.x == 0) a.stop_n[u] = run;
 }
 
+// One radix digit of the stratum's end, searched by one wave over the LDS
+// count (and, with the mass bound open, mass) histograms: where the open
+// bounds end (the one reached first decides) and how many candidates lie
+// above that bin.
+__device__ __forceinline__ void wave_digit(const uint32_t* hist, const unsigned long long* mh,
+                                           int nbins, int mode, int rem,
+                                           unsigned long long rem_mass, DigitBound* d,
+                                           int* above) {
+  int bc = 0, rc = 0, bm = 0;
+  unsigned long long rm = 0ull;
+  if (mode & kBoundCount) wave_find_bin<int>(hist, nbins, rem, &bc, &rc);
+  if (mode & kBoundMass) wave_find_bin<unsigned long long>(mh, nbins, rem_mass, &bm, &rm);
+  *d = combine_bounds(mode, bc, rc, bm, rm);
+  *above = ((d->mode & kBoundCount) && d->bin == bc) ? rem - rc
+                                                     : wave_count_above(hist, nbins, d->bin);
+}
+
 __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   __shared__ uint32_t hist[kBins];
   __shared__ unsigned long long mh[kBins];  // mass units per digit (top-p)
   __shared__ int ties_sh[kMaxResolveChunks];  // ties + (candidates above the key << 16)
+  __shared__ int dig_sh[4];                   // a digit's bin, remainder, mode, count above
+  __shared__ unsigned long long dig_m;        // and its mass remainder
   __shared__ int scan_scr[kRW];
-  __shared__ int pair[2];
-  __shared__ unsigned long long scan_m[kRW];
-  __shared__ unsigned long long pair_m[2];
   __shared__ double dscr[kRW];
 
   const int u = blockIdx.x;
-  // Every load that depends on the unit only is issued first, together: the
-  // sequence's parameters, the first-digit threshold and the maximum, the
-  // second-digit histogram, and this thread's candidate count and first
-  // candidate keys (read whole within the chunk's segment; entries past the
-  // count are never used).  Candidate passes give tpc threads to each chunk,
-  // fixed by the launch's chunk count, so every thread's items and every sum
-  // have a fixed order.
-  constexpr int kKeep = 16;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // The loads that need no sequence parameter come first: the first-digit
+  // threshold and the maximum, the second-digit histogram, the wave's chunk
+  // counts (lane j: slot j), the first 64 candidate keys and weights of its
+  // chunks (read whole within each chunk's segment, from a chunk clamped into
+  // the launch's range; entries past a count are never used) and the chunk
+  // tail sums.
   constexpr int kHist = kBins / kRT;
-  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
-  const int b = ui.b;
-  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   const Thresh1 t1 = a.thresh[u];
   const uint32_t maxkey = a.maxkey[u];
   uint32_t hv[kHist];
@@ -285,26 +311,27 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
   const size_t cu = (size_t)u * a.nchunk;
   const uint32_t* ckeys = a.cand_key + (size_t)u * a.seg_ld;
   const float* cws = a.cand_w + (size_t)u * a.seg_ld;
-  const int tpc = threads_per_chunk(a.nchunk);
-  const int cstep = kRT / tpc;
-  const int csub = threadIdx.x % tpc;
-  const bool one_chunk = a.nchunk <= cstep;  // each thread serves at most one chunk
-  const int cm = threadIdx.x / tpc;
-  const bool has_cm = one_chunk && cm < a.nchunk;
-  const int cnt_m = has_cm ? a.cand_cnt[cu + cm] : 0;
-  const uint32_t* ckm = ckeys + (size_t)cm * kChunk;
-  const float* cwm = cws + (size_t)cm * kChunk;
-  uint32_t kr[kKeep];
-  float wr[kKeep];  // the candidates' tail weights, computed by the filter
+  const int last = a.nchunk - 1;
+  const int cnt_l = a.cand_cnt[cu + min(wave + kRW * min(lane, kRSlots - 1), last)];
+  uint32_t kr[kRSlots];
+  float wr[kRSlots];  // the candidates' tail weights, computed by the filter
 #pragma unroll
-  for (int k = 0; k < kKeep; ++k) {
-    const int i = csub + k * tpc;
-    kr[k] = (has_cm && i < kChunk) ? ckm[i] : 0u;
-    wr[k] = (has_cm && i < kChunk) ? cwm[i] : 0.0f;
+  for (int j = 0; j < kRSlots; ++j) {
+    const size_t at = (size_t)min(wave + kRW * j, last) * kChunk + lane;
+    kr[j] = ckeys[at];
+    wr[j] = cws[at];
   }
   // This thread's chunk tail sum, with the first loads when every chunk has
   // its own thread (entries past the sequence's chunks are ignored).
-  const double wp = (a.nchunk <= kRT && (int)threadIdx.x < a.nchunk) ? a.wpart[cu + threadIdx.x] : 0.0;
+  const double wp = a.wpart[cu + min((int)threadIdx.x, last)];
+  // The scalar loads of the sequence's parameters go out after these (a
+  // scheduling barrier), so their dependent round trips overlap the vector
+  // loads in flight, and the vector loads stay here instead of sinking into
+  // the branch that uses them.
+  __builtin_amdgcn_sched_barrier(0);
+  const UnitInfo ui = unit_info(u, a.Hkv, a.NG, a.T, a.g, a.seq_lens, a.max_seq_len);
+  const int b = ui.b;
+  const SeqParams p = seq_params(ui.L, a.topk, a.top_p, a.sample_budget, b, a.max_topk, a.kmult);
   UnitState st;
   st.tkey = 0u;
   st.ties_needed = 0;
@@ -323,38 +350,36 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
     if (p.dense) {
       st.flags = kFlagDense;
     } else {
-      const int nc = (p.L + kChunk - 1) / kChunk;
-      double acc = (a.nchunk <= kRT && (int)threadIdx.x < nc) ? wp : 0.0;
-      if (a.nchunk > kRT)
-        for (int c = threadIdx.x; c < nc; c += kRT) acc += a.wpart[cu + c];
+      const int nc = (p.L + kChunk - 1) / kChunk;  // at most a.nchunk
+      double acc = (int)threadIdx.x < nc ? wp : 0.0;
+      for (int c = threadIdx.x + kRT; c < nc; c += kRT) acc += a.wpart[cu + c];
       double cs = 0.0;  // this thread's candidates below the threshold key
-      int total_ties = 0;
+      int total_ties = 0;  // wave 0 only
       if (t1.mode == 0) {
         st.flags = kFlagNoTopk;
         st.k_eff = 0;
       } else {
-        const int nm = (has_cm && cm < nc) ? clamp_count(cnt_m, kChunk) : 0;
 #pragma unroll
         for (int j = 0; j < kHist; ++j) hist[threadIdx.x + j * kRT] = hv[j];
         if (t1.mode & kBoundMass)
           for (int i = threadIdx.x; i < kBins; i += kRT) mh[i] = a.hist2m[(size_t)u * kBins + i];
-        for (int c = threadIdx.x; c < nc; c += kRT) ties_sh[c] = 0;
         __syncthreads();
         // Second digit.
-        // The candidates above the chosen bin: counted by the rank search when
-        // the count bound chose it.
-        DigitBound d2;
-        int above2;
-        {
-          int bc = 0, rc = 0, bm = 0;
-          unsigned long long rm = 0ull;
-          if (t1.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins, t1.rem, scan_scr, pair, &bc, &rc);
-          if (t1.mode & kBoundMass) find_bin<kRT>(mh, kBins, t1.rem_mass, scan_m, pair_m, &bm, &rm);
-          d2 = combine_bounds(t1.mode, bc, rc, bm, rm);
-          above2 = ((d2.mode & kBoundCount) && d2.bin == bc)
-                       ? t1.rem - rc
-                       : count_above<kRT>(hist, kBins, d2.bin, scan_scr);
+        if (wave == 0) {
+          DigitBound d;
+          int above;
+          wave_digit(hist, mh, kBins, t1.mode, t1.rem, t1.rem_mass, &d, &above);
+          if (lane == 0) {
+            dig_sh[0] = d.bin;
+            dig_sh[1] = d.rem;
+            dig_sh[2] = d.mode;
+            dig_sh[3] = above;
+            dig_m = d.rem_mass;
+          }
         }
+        __syncthreads();
+        const DigitBound d2{dig_sh[0], dig_sh[1], dig_m, dig_sh[2]};
+        const int above2 = dig_sh[3];
         const bool mass3 = d2.mode & kBoundMass;
         const uint32_t prefix = ((uint32_t)t1.b1 << 11) | (uint32_t)d2.bin;
         for (int i = threadIdx.x; i < kBins3; i += kRT) {
@@ -369,34 +394,37 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
             if (mass3) atomicAdd(&mh[key & (kBins3 - 1)], mass_units(w));
           }
         };
-        if (one_chunk) {
 #pragma unroll
-          for (int k = 0; k < kKeep; ++k) {
-            const int i = csub + k * tpc;
-            if (i < nm) add3(kr[k], wr[k]);
+        for (int j = 0; j < kRSlots; ++j) {
+          const int c = wave + kRW * j;
+          if (c < nc) {  // uniform over the wave
+            const int n = clamp_count(__builtin_amdgcn_readlane(cnt_l, j), kChunk);
+            if (lane < n) add3(kr[j], wr[j]);
+            for (int i = lane + 64; i < n; i += 64) add3(ckeys[(size_t)c * kChunk + i],
+                                                          cws[(size_t)c * kChunk + i]);
           }
-          for (int i = csub + kKeep * tpc; i < nm; i += tpc) add3(ckm[i], cwm[i]);
-        } else {
-          for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-            const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
-            const uint32_t* ck = ckeys + (size_t)c * kChunk;
-            const float* cw = cws + (size_t)c * kChunk;
-            for (int i = csub; i < n; i += tpc) add3(ck[i], cw[i]);
+        }
+        for (int c = wave + kRW * kRSlots; c < nc; c += kRW) {
+          const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
+          for (int i = lane; i < n; i += 64) add3(ckeys[(size_t)c * kChunk + i],
+                                                   cws[(size_t)c * kChunk + i]);
+        }
+        __syncthreads();
+        if (wave == 0) {
+          DigitBound d;
+          int above;
+          wave_digit(hist, mh, kBins3, d2.mode, d2.rem, d2.rem_mass, &d, &above);
+          if (lane == 0) {
+            dig_sh[0] = d.bin;
+            dig_sh[1] = d.rem;
+            dig_sh[2] = d.mode;
+            dig_sh[3] = above;
+            dig_m = d.rem_mass;
           }
         }
         __syncthreads();
-        DigitBound d3;
-        int above3;
-        {
-          int bc = 0, rc = 0, bm = 0;
-          unsigned long long rm = 0ull;
-          if (d2.mode & kBoundCount) find_rank_bin<kRT>(hist, kBins3, d2.rem, scan_scr, pair, &bc, &rc);
-          if (mass3) find_bin<kRT>(mh, kBins3, d2.rem_mass, scan_m, pair_m, &bm, &rm);
-          d3 = combine_bounds(d2.mode, bc, rc, bm, rm);
-          above3 = ((d3.mode & kBoundCount) && d3.bin == bc)
-                       ? d2.rem - rc
-                       : count_above<kRT>(hist, kBins3, d3.bin, scan_scr);
-        }
+        const DigitBound d3{dig_sh[0], dig_sh[1], dig_m, dig_sh[2]};
+        const int above3 = dig_sh[3];
         st.tkey = (prefix << kDigit2Shift) | (uint32_t)d3.bin;
         // Tokens on the last key all carry the same mass: the mass bound needs
         // ceil(remaining units / units per token) of them.
@@ -408,57 +436,64 @@ __global__ __launch_bounds__(kRT) void resolve_kernel(SelectArgs a) {
         }
         st.ties_needed = need;
         st.k_eff = t1.above + above2 + above3 + need;
-        // Ties on the threshold key per chunk and candidates above it
-        // (integer, packed as ties + (above << 16): each at most 4096), and
-        // the weight of the candidates strictly below it (each thread over
-        // its fixed items, in order; summed with the chunk sums below).
-        if (one_chunk) {
-          int ties = 0;
+        // Ties on the threshold key per chunk and, for early stopping, the
+        // candidates above it (wave ballots; packed as ties + (above << 16),
+        // each at most 4096), and the weight of the candidates strictly below
+        // it (each thread over its fixed items, in order; summed with the
+        // chunk sums below).
+        const uint32_t tkey = st.tkey;
+        const bool want_above = a.stop_off != nullptr;  // only early stopping uses them
+        auto count = [&](uint32_t key, float w, bool v, int& packed) {
+          packed += __popcll(__ballot(v && key == tkey));
+          if (want_above) packed += __popcll(__ballot(v && key > tkey)) << 16;
+          if (v && key < tkey) cs += (double)w;
+        };
 #pragma unroll
-          for (int k = 0; k < kKeep; ++k) {
-            const int i = csub + k * tpc;
-            if (i < nm) {
-              ties += kr[k] == st.tkey ? 1 : (kr[k] > st.tkey ? 0x10000 : 0);
-              if (kr[k] < st.tkey) cs += (double)wr[k];
+        for (int j = 0; j < kRSlots; ++j) {
+          const int c = wave + kRW * j;
+          if (c < nc) {  // uniform over the wave
+            const int n = clamp_count(__builtin_amdgcn_readlane(cnt_l, j), kChunk);
+            int packed = 0;
+            count(kr[j], wr[j], lane < n, packed);
+            for (int i0 = 64; i0 < n; i0 += 64) {
+              const int i = i0 + lane;
+              const size_t at = (size_t)c * kChunk + min(i, kChunk - 1);
+              count(ckeys[at], cws[at], i < n, packed);
             }
+            if (lane == 0) ties_sh[c] = packed;
           }
-          for (int i = csub + kKeep * tpc; i < nm; i += tpc) {
-            const uint32_t key = ckm[i];
-            ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
-            if (key < st.tkey) cs += (double)cwm[i];
+        }
+        for (int c = wave + kRW * kRSlots; c < nc; c += kRW) {
+          const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
+          int packed = 0;
+          for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + lane;
+            const size_t at = (size_t)c * kChunk + min(i, kChunk - 1);
+            count(ckeys[at], cws[at], i < n, packed);
           }
-          if (ties) atomicAdd(&ties_sh[cm], ties);
-        } else {
-          for (int c = threadIdx.x / tpc; c < nc; c += cstep) {
-            const int n = clamp_count(a.cand_cnt[cu + c], kChunk);
-            const uint32_t* ck = ckeys + (size_t)c * kChunk;
-            const float* cw = cws + (size_t)c * kChunk;
-            int ties = 0;
-            for (int i = csub; i < n; i += tpc) {
-              const uint32_t key = ck[i];
-              ties += key == st.tkey ? 1 : (key > st.tkey ? 0x10000 : 0);
-              if (key < st.tkey) cs += (double)cw[i];
-            }
-            if (ties) atomicAdd(&ties_sh[c], ties);
-          }
+          if (lane == 0) ties_sh[c] = packed;
         }
         __syncthreads();  // the chunks' tie counts are complete
-        int run = 0;
-        for (int c0 = 0; c0 < nc; c0 += kRT) {
-          const int c = c0 + threadIdx.x;
-          const int v = c < nc ? ties_sh[c] & 0xffff : 0;
-          int tot;
-          const int ex = block_exclusive_scan<kRT>(v, scan_scr, &tot);
-          if (c < nc) {
-            a.ties_before[cu + c] = run + ex;
-            a.tiecnt[cu + c] = v;
+        if (wave == 0) {
+          // Exclusive scan of the tie counts over the chunks, 64 at a time.
+          int run = 0;
+          for (int c0 = 0; c0 < nc; c0 += 64) {
+            const int c = c0 + lane;
+            const int v = c < nc ? ties_sh[c] & 0xffff : 0;
+            const int inc = wave_inclusive_scan<int>(v);
+            if (c < nc) {
+              a.ties_before[cu + c] = run + inc - v;
+              a.tiecnt[cu + c] = v;
+            }
+            run += __builtin_amdgcn_readlane(inc, 63);
           }
-          run += tot;
+          total_ties = run;
         }
-        total_ties = run;
         if (a.stop_off) stop_offsets(a, u, cu, nc, ties_sh, scan_scr);
       }
       W = block_sum_f64<kRT>(acc + cs, dscr);  // every thread's share, one fixed tree
+      // The ties beyond the quota are tail tokens (wave 0 holds their count;
+      // only thread 0 writes W).
       if (t1.mode != 0) {
         const double wT = (double)sexp(key_to_float(st.tkey) - st.M);
         W += (double)(total_ties - st.ties_needed) * wT;
@@ -1031,32 +1066,40 @@ __global__ __launch_bounds__(kCutT) void stop_cut_kernel(SelectArgs a) {
 // Per chunk: membership of the listed tokens only -- above-threshold tokens
 // and candidates above the threshold key (or within the tie quota) form the
 // deterministic set; the other candidates and the listed sampling candidates
-// take the exact inclusion test with the final W.  The chunk's segment is then
-// written from an LDS membership map: deterministic tokens ascending, then
-// sampled tokens ascending.  With emit_rows the segment holds cache row
-// numbers (for the fused attention stage) instead of positions.
-// Membership of a chunk position: not selected, deterministic, or sampled
-// with its logit bias -log(pi) stored as the word itself (a finite float,
-// never one of the two marks, which are NaN patterns).
-constexpr uint32_t kMarkNone = 0xffffffffu;
-constexpr uint32_t kMarkDet = 0xfffffffeu;
+// take the exact inclusion test with the final W.  Membership is kept in two
+// LDS bitmaps (deterministic, sampled) with each sampled token's logit bias
+// -log(pi) beside them, and the chunk's segment is written from the bitmaps:
+// deterministic tokens ascending, then sampled tokens ascending.  With
+// emit_rows the segment holds cache row numbers (for the fused attention
+// stage) instead of positions.
+constexpr int kMapWords = kChunk / 32;
 
 __device__ __forceinline__ void sample_one(const UnitState& st, uint64_t seed, int b, int h,
                                            int grp, int t, float w, int c0, int nvalid,
-                                           uint32_t* mark) {
+                                           uint32_t* rbits, float* bias) {
   if ((unsigned)(t - c0) >= (unsigned)nvalid) return;  // not a position of this chunk
   const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, grp);
   const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
   const float mw = (float)st.m * w;
-  if (uniform24(words[t & 3]) * st.W < mw)
-    mark[t - c0] = __float_as_uint(-logf(fminf(1.0f, mw / st.W)));
+  if (uniform24(words[t & 3]) * st.W < mw) {
+    const int i = t - c0;
+    bias[i] = -logf(fminf(1.0f, mw / st.W));
+    atomicOr(&rbits[i >> 5], 1u << (i & 31));
+  }
+}
+
+__device__ __forceinline__ void mark_det(uint32_t* sbits, int i) {
+  atomicOr(&sbits[i >> 5], 1u << (i & 31));
 }
 
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void sample_kernel(
     SelectArgs a) {
-  __shared__ uint32_t mark[kChunk];  // kMarkNone, kMarkDet or a sampled token's bias
+  __shared__ uint32_t sbits[kMapWords];  // deterministic positions of the chunk
+  __shared__ uint32_t rbits[kMapWords];  // sampled positions
+  __shared__ float bias[kChunk];         // a sampled position's -log(pi)
   __shared__ int scan_scr[kNT / 64];
   static_assert(kPer == kBlockTokens, "a thread's positions are one cache block");
+  static_assert(kPer == 16 && kMapWords * 2 == kNT, "a thread's positions are half a bitmap word");
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -1075,10 +1118,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
   const float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
   const int32_t* cidx = a.cand_idx + (size_t)u * a.seg_ld + c0;
   const uint32_t* ckey = a.cand_key + (size_t)u * a.seg_ld + c0;
+  const float* cw = a.cand_w + (size_t)u * a.seg_ld + c0;
   const int l_first = lidx[tid];
   const float w_first = lw[tid];
   const int c_first = cidx[tid];
   const uint32_t k_first = ckey[tid];
+  const float cw_first = cw[tid];
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   // Counts are clamped to the segment and positions checked against the
   // chunk, so no value in the workspace can address outside it.
@@ -1086,6 +1131,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
   const int n_samp = clamp_count(a.list_cnt[2 * ci + 1], kChunk - n_above);
   const int ncand = clamp_count(a.cand_cnt[ci], kChunk);
   const int before = a.ties_before[ci];
+  const int ties_here = a.tiecnt[ci];
   const uint64_t seed = a.seed[b];
   int32_t* cnt = a.sel_cnt + ci * 2;
   if (c0 >= st.L || (st.flags & kFlagEmpty)) {
@@ -1104,8 +1150,16 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
     blk = a.block_table[(size_t)b * a.max_blocks + c0 / kBlockTokens + threadIdx.x];
     blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
   }
-  for (int i = threadIdx.x; i < kChunk; i += kNT)
-    mark[i] = (dense && i < nvalid) ? kMarkDet : kMarkNone;
+  {
+    // Dense units take every valid position; otherwise the maps start empty.
+    const int wi = tid & (kMapWords - 1);
+    const int lo = wi * 32;
+    const uint32_t full = nvalid >= lo + 32 ? ~0u : (nvalid <= lo ? 0u : (1u << (nvalid - lo)) - 1u);
+    if (tid < kMapWords)
+      sbits[wi] = dense ? full : 0u;
+    else
+      rbits[wi] = 0u;
+  }
   // Early stopping: the last stratum word kept (~0: the whole stratum).
   const unsigned long long cut = a.stop_cut && !dense ? a.stop_cut[u] : ~0ull;
   __syncthreads();
@@ -1119,14 +1173,17 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
       if (i < n_above) {
         if ((unsigned)(t - c0) < (unsigned)nvalid &&
             (cut == ~0ull || stratum_word(order_key(srow[t]), t) <= cut))
-          mark[t - c0] = kMarkDet;
+          mark_det(sbits, t - c0);
       } else {
-        sample_one(st, seed, b, h, ui.grp, t, i == tid ? w_first : lw[i], c0, nvalid, mark);
+        sample_one(st, seed, b, h, ui.grp, t, i == tid ? w_first : lw[i], c0, nvalid, rbits,
+                   bias);
       }
     }
     if (!(st.flags & kFlagNoTopk)) {
       // Threshold-digit candidates, in index order: key above T -> S; key == T
-      // -> S while the tie quota lasts; otherwise a tail token.
+      // -> S while the tie quota lasts; otherwise a tail token, whose weight
+      // the filter stored.  Ties are ranked by a block scan only in chunks
+      // that hold one (the resolve counted them).
       int run = 0;  // ties seen in earlier rounds of this loop
       for (int base = 0; base < ncand; base += kNT) {
         const int i = base + tid;
@@ -1134,32 +1191,32 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
         const uint32_t key = v ? (base == 0 ? k_first : ckey[i]) : 0u;
         const int t = v ? (base == 0 ? c_first : cidx[i]) : 0;
         const bool tie = v && key == st.tkey;
-        int tot;
-        const int rank = before + run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &tot);
-        run += tot;
+        int rank = 0;
+        if (ties_here != 0) {  // uniform over the workgroup
+          int tot;
+          rank = before + run + block_exclusive_scan<kNT>(tie ? 1 : 0, scan_scr, &tot);
+          run += tot;
+        }
         if (v) {
           if (key > st.tkey || (tie && rank < st.ties_needed)) {
             // stratum tokens past the early stop are neither read nor sampled
             if ((unsigned)(t - c0) < (unsigned)nvalid && stratum_word(key, t) <= cut)
-              mark[t - c0] = kMarkDet;
+              mark_det(sbits, t - c0);
           } else if (sampling) {
-            sample_one(st, seed, b, h, ui.grp, t, sexp(key_to_float(key) - st.M), c0, nvalid,
-                       mark);
+            sample_one(st, seed, b, h, ui.grp, t, base == 0 ? cw_first : cw[i], c0, nvalid,
+                       rbits, bias);
           }
         }
       }
     }
   }
   __syncthreads();
-  // Compaction from the membership map (16 consecutive positions per thread).
+  // Compaction from the bitmaps: the thread's 16 consecutive positions are
+  // half of one word of each map.
   const int tb = threadIdx.x * kPer;
-  uint32_t smask = 0u, rmask = 0u;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const uint32_t m = mark[tb + i];
-    smask |= (uint32_t)(m == kMarkDet) << i;
-    rmask |= (uint32_t)(m < kMarkDet) << i;
-  }
+  const int sh16 = (tid & 1) * 16;
+  const uint32_t smask = (sbits[tid >> 1] >> sh16) & 0xffffu;
+  const uint32_t rmask = (rbits[tid >> 1] >> sh16) & 0xffffu & ~smask;
   // One scan for both counts: deterministic count in the low 16 bits,
   // sampled count in the high 16 bits (each at most 4096).
   int packed_tot;
@@ -1170,21 +1227,19 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void s
   int32_t* sidx = a.sel_idx + (size_t)u * a.seg_ld + c0;
   float* slw = a.sel_logw + (size_t)u * a.seg_ld + c0;
   int ws = packed & 0xffff, wr = totS + (packed >> 16);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const uint32_t bit = 1u << i;
-    if ((smask | rmask) & bit) {
-      const int t = c0 + tb + i;
-      const int v = a.emit_rows ? (blk * a.Hkv + h) * kBlockTokens + (t & 15) : t;
-      if (smask & bit) {
-        sidx[ws] = v;
-        slw[ws] = 0.0f;
-        ++ws;
-      } else {
-        sidx[wr] = v;
-        slw[wr] = __uint_as_float(mark[tb + i]);
-        ++wr;
-      }
+  // Ascending bits keep both lists in index order.
+  for (uint32_t rest = smask | rmask; rest != 0u; rest &= rest - 1u) {
+    const int i = __builtin_ctz(rest);
+    const int t = c0 + tb + i;
+    const int v = a.emit_rows ? (blk * a.Hkv + h) * kBlockTokens + (t & 15) : t;
+    if ((smask >> i) & 1u) {
+      sidx[ws] = v;
+      slw[ws] = 0.0f;
+      ++ws;
+    } else {
+      sidx[wr] = v;
+      slw[wr] = bias[tb + i];
+      ++wr;
     }
   }
   if (threadIdx.x == 0) {

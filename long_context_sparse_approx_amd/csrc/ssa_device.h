@@ -381,6 +381,39 @@ __device__ __forceinline__ int count_above(const uint32_t* hist, int nbins, int 
   return block_sum_i32<NT>(v, scratch);
 }
 
+// The same two searches by one wave (all 64 lanes call; no barrier).  Lane l
+// sums its per = nbins / 64 bins from the top (top - l * per down), a wave
+// scan finds the lane where the running sum reaches k, and a second scan over
+// that lane's bins, one per lane, finds the bin.  A k beyond the histogram's
+// total ends at bin 0 (remainder k - sum(bins > 0)).  The result is in every
+// lane.  nbins is a multiple of 64 and at most 64 * 64.
+template <typename T, typename H>
+__device__ __forceinline__ void wave_find_bin(const H* hist, int nbins, T k, int* bin_out,
+                                              T* rem_out) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins >> 6;
+  const int top = nbins - 1 - lane * per;
+  T mine = 0;
+  for (int i = 0; i < per; ++i) mine += (T)hist[top - i];
+  const T inc = wave_inclusive_scan<T>(mine);
+  const unsigned long long hit = __ballot(inc >= k);
+  const int l = hit ? __builtin_ctzll(hit) : 63;
+  const T before = __shfl(inc - mine, l);  // the bins above lane l's
+  const int top_l = nbins - 1 - l * per;
+  const T c = lane < per ? (T)hist[top_l - lane] : (T)0;
+  const T inc2 = wave_inclusive_scan<T>(c) + before;
+  const unsigned long long hit2 = __ballot(lane < per && inc2 >= k);
+  const int i = hit2 ? __builtin_ctzll(hit2) : per - 1;
+  *bin_out = top_l - i;
+  *rem_out = k - __shfl(inc2 - c, i);
+}
+
+__device__ __forceinline__ int wave_count_above(const uint32_t* hist, int nbins, int bin) {
+  int v = 0;
+  for (int i = bin + 1 + (int)(threadIdx.x & 63); i < nbins; i += 64) v += (int)hist[i];
+  return wave_sum<int>(v);
+}
+
 // Where the stratum ends at one radix digit, given the open bounds `mode`:
 // the count bound ends in bin bc with remainder rc, the mass bound in bin bm
 // with remainder rm.  The bound reached first (the higher bin, as keys are
@@ -452,7 +485,11 @@ __device__ __forceinline__ SeqParams seq_params(int L, const int32_t* topk, cons
   p.m = max(mb, 0);
   p.topp = top_p != nullptr;
   p.p = p.topp ? pv : 1.0f;
-  p.dense = p.topp ? p.m >= p.L : (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
+  // Both rules evaluated and selected without a branch, so the caller's
+  // loads that follow stay in one basic block with these.
+  const bool dense_m = p.m >= p.L;
+  const bool dense_km = (int64_t)k + (int64_t)p.m >= (int64_t)p.L;
+  p.dense = (p.topp & dense_m) | (!p.topp & dense_km);
   p.k_eff = min(k, p.L);
   return p;
 }
