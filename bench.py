@@ -171,20 +171,26 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
             arrs.append((ctypes.c_void_p * (2 * nst))(*evs))
         return arrs
 
-    def timed_loop(arrs, graphs=None):
+    def timed_loop(arrs, graphs=None, every=1):
+        # arrs[i // every] brackets step i when i % every == 0.
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             if graphs is not None:
                 graphs[i % len(graphs)].replay()
             else:
+                ev = arrs[i // every] if arrs and i % every == 0 else None
                 step(*call, out=out, workspace=ws, stream=stream, top_p=tp,
-                     events=ctypes.addressof(arrs[i]) if arrs else None)
+                     events=ctypes.addressof(ev) if ev is not None else None)
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
-    # Timed region: K whole steps; HIP events bracket only the indexer launch
-    # (on the decode stream), for its roofline.
+    # Timed region: K whole steps; on every `event_every`-th of them HIP events
+    # bracket the indexer launch (on the decode stream), for its roofline.  An
+    # event record costs the GPU about 5 us between two kernels, so bracketing
+    # every step would add about 11 us to each.
+    every = max(1, args.event_every)
+    n_ev = (steps + every - 1) // every
     graphs = None
     if args.graph and not split:
         g = torch.cuda.CUDAGraph()
@@ -196,11 +202,11 @@ def run_gpu(args, name, steps, warmup, with_stage_events=True, top_p=None, wl=No
             g.replay()
         idx_arrs = None
     else:
-        idx_arrs = event_arrays(steps, [ix])
-    ms_step = timed_loop(idx_arrs, graphs)
+        idx_arrs = event_arrays(n_ev, [ix])
+    ms_step = timed_loop(idx_arrs, graphs, every)
     idx_ms = None
     if idx_arrs:
-        idx_ms = sum(hip.elapsed_ms(a[2 * ix], a[2 * ix + 1]) for a in idx_arrs) / steps
+        idx_ms = sum(hip.elapsed_ms(a[2 * ix], a[2 * ix + 1]) for a in idx_arrs) / n_ev
     # Separate pass (not the timed region): every stage bracketed by events.
     stage_ms = {s: 0.0 for s in ssa.STAGES}
     gpu_ms = 0.0
@@ -513,6 +519,8 @@ def main():
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="per-step medians over this many steps with and without a 512 MiB "
                          "cache-evicting read before each (0 = skip)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="bracket the indexer with HIP events on every N-th timed step")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip timing the measurement kernels (contiguous read and row gather "
                          "of the step's byte and row counts)")
