@@ -9,6 +9,25 @@ namespace ssa {
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
 
+// The chunk filter's tail weight e^x (x <= 0): the hardware exp2 of
+// t = x log2(e), with t carried past float32 precision (the product's rounding
+// error, exact by a fused multiply-add, and the tail of the constant, added
+// back as 2^t (1 + e ln 2)); within a few ulp of sexp(x), and 0 below -87
+// like it.  It feeds the fp64 tail sum W (whose terms thus differ from the
+// specified weights by a few ulp, well inside W's 1e-6 tolerance) and the
+// necessary inclusion test, whose 2^-10 margin covers it; every decision
+// that must match the oracle bit for bit uses sexp.
+__device__ __forceinline__ float tail_exp(float x) {
+  constexpr float kL2e = 0x1.715476p+0f;    // float32(log2 e)
+  constexpr float kL2eLo = 0x1.4ae0c0p-26f;  // float32(log2 e - kL2e)
+  constexpr float kLn2 = 0x1.62e430p-1f;    // float32(ln 2)
+  const float t = x * kL2e;
+  const float e = __builtin_fmaf(x, kL2e, -t) + x * kL2eLo;
+  const float r = __builtin_amdgcn_exp2f(t);
+  const float y = __builtin_fmaf(r * e, kLn2, r);
+  return x < -87.0f ? 0.0f : y;
+}
+
 // Filter of chunk c of unit u = (b, grp, h) by a 256-thread workgroup.  s4
 // holds the thread's 16 consecutive scores (entries at or past L are
 // ignored); sh is the chunk's score buffer in LDS, of which the thread uses
@@ -47,6 +66,11 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   uint32_t tailbits = 0u, abovebits = 0u, sampbits = 0u;
   double wsum = 0.0;
   const uint32_t vmask = nv >= kPer ? 0xffffu : (nv <= 0 ? 0u : (1u << nv) - 1u);
+  const bool ragged = c0 + kChunk > p.L;
+  // The necessary test's left side u * W_lb as (word >> 8) * (W_lb 2^-24):
+  // the same product, since both scalings by 2^-24 are exact, unless W_lb 2^-24
+  // would be subnormal; then 0, which lists every token with a weight.
+  const float wlb24 = t1.wlb >= 0x1.0p-100f ? t1.wlb * 0x1.0p-24f : 0.0f;
 #pragma unroll
   for (int g = 0; g < kPer / 4; ++g) {
     // One group at a time: its loads may still be in flight while the
@@ -58,7 +82,7 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
     float s[4] = {s4[g].x, s4[g].y, s4[g].z, s4[g].w};
     // Kept for the second pass (no other thread reads this thread's entries).
     *reinterpret_cast<float4*>(sh + tb + 4 * g) = s4[g];
-    if (nv < kPer) {
+    if (ragged && nv < kPer) {  // ragged: uniform over the workgroup
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (4 * g + r >= nv) s[r] = -INFINITY;
@@ -73,9 +97,9 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
       const uint32_t tbit = (uint32_t)d >> 31;
       tailbits |= tbit << i;
       abovebits |= ((uint32_t)(-d) >> 31) << i;
-      const float w = sexp(s[r] - M);
+      const float w = tail_exp(s[r] - M);
       wsum += (double)__uint_as_float(__float_as_uint(w) & (0u - tbit));
-      const uint32_t sbit = uniform24(words[r]) * t1.wlb < mf * w ? 1u : 0u;
+      const uint32_t sbit = (float)(words[r] >> 8) * wlb24 < mf * w ? 1u : 0u;
       sampbits |= (sbit & tbit) << i;
     }
   }
