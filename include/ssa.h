@@ -371,6 +371,12 @@ int ssa_debug_philox(uint64_t seed, int32_t b, int32_t h, int32_t group, int32_t
 /* Test hook: y[i] = the library's specified float32 exp of x[i], i < n. */
 int ssa_debug_sexp(const float* x, float* y, int32_t n, void* stream);
 
+/* Test hook: y[i] = the chunk filter's first-pass tail weight e^x[i] (the
+ * hardware exp2 with an extended-precision argument; 0 below -87), i < n.
+ * It enters only the library's own tail sum W and the necessary inclusion
+ * test, never an exact decision. */
+int ssa_debug_tail_exp(const float* x, float* y, int32_t n, void* stream);
+
 /* Measurement aids, not steps of the decode: the HBM read rate this device
  * delivers for the access patterns of the step's two bandwidth-bound
  * kernels, so that their achieved rates can be set beside what the memory

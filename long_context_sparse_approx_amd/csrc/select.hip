@@ -1265,6 +1265,11 @@ __global__ void debug_sexp_kernel(const float* x, float* y, int n) {
   if (i < n) y[i] = sexp(x[i]);
 }
 
+__global__ void debug_tail_exp_kernel(const float* x, float* y, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = tail_exp(x[i]);
+}
+
 }  // namespace
 
 hipError_t launch_mass(const SelectArgs& a, int units, hipStream_t stream) {
@@ -1321,6 +1326,11 @@ hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int
 
 hipError_t launch_debug_sexp(const float* x, float* y, int n, hipStream_t stream) {
   debug_sexp_kernel<<<(n + 255) / 256, 256, 0, stream>>>(x, y, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_tail_exp(const float* x, float* y, int n, hipStream_t stream) {
+  debug_tail_exp_kernel<<<(n + 255) / 256, 256, 0, stream>>>(x, y, n);
   return hipGetLastError();
 }
 

@@ -765,6 +765,13 @@ int ssa_debug_sexp(const float* x, float* y, int32_t n, void* stream) {
   return SSA_OK;
 }
 
+int ssa_debug_tail_exp(const float* x, float* y, int32_t n, void* stream) {
+  if (!x || !y || n < 0) return SSA_ERR_INVALID;
+  if (n == 0) return SSA_OK;
+  SSA_TRY(ssa::launch_debug_tail_exp(x, y, n, static_cast<hipStream_t>(stream)));
+  return SSA_OK;
+}
+
 const char* ssa_error_string(int code) {
   switch (code) {
     case SSA_OK: return "ok";

@@ -206,5 +206,6 @@ hipError_t launch_merge(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_debug_philox(uint64_t seed, int b, int h, int grp, int j0, int n,
                                uint32_t* words, hipStream_t stream);
 hipError_t launch_debug_sexp(const float* x, float* y, int n, hipStream_t stream);
+hipError_t launch_debug_tail_exp(const float* x, float* y, int n, hipStream_t stream);
 
 }  // namespace ssa

@@ -36,6 +36,7 @@ EXPORTS = ("ssa_workspace_bytes", "ssa_num_chunks", "ssa_decode", "ssa_decode_st
            "ssa_decode_timed",
            "ssa_decode_split", "ssa_score", "ssa_select", "ssa_attend", "ssa_attend_split",
            "ssa_append_kv", "ssa_host_device_address", "ssa_debug_philox", "ssa_debug_sexp",
+           "ssa_debug_tail_exp",
            "ssa_measure_stream", "ssa_measure_gather", "ssa_error_string")
 
 
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.ssa_debug_philox.restype = ctypes.c_int
         L.ssa_debug_sexp.argtypes = [_P, _P, ctypes.c_int32, _P]
         L.ssa_debug_sexp.restype = ctypes.c_int
+        L.ssa_debug_tail_exp.argtypes = [_P, _P, ctypes.c_int32, _P]
+        L.ssa_debug_tail_exp.restype = ctypes.c_int
         L.ssa_measure_stream.argtypes = [_P, ctypes.c_size_t, _P, _P]
         L.ssa_measure_stream.restype = ctypes.c_int
         L.ssa_measure_gather.argtypes = [_P, ctypes.c_size_t, ctypes.c_int64, _P, ctypes.c_int64,
@@ -368,6 +371,13 @@ def debug_philox(seed: int, b: int, h: int, j0: int, n: int, device="cuda", grou
 def debug_sexp(x: torch.Tensor):
     y = torch.empty_like(x)
     _check(lib().ssa_debug_sexp(_ptr(x), _ptr(y), x.numel(), _stream(None)), "ssa_debug_sexp")
+    return y
+
+
+def debug_tail_exp(x: torch.Tensor):
+    y = torch.empty_like(x)
+    _check(lib().ssa_debug_tail_exp(_ptr(x), _ptr(y), x.numel(), _stream(None)),
+           "ssa_debug_tail_exp")
     return y
 
 

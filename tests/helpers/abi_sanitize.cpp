@@ -37,6 +37,10 @@ hipError_t launch_debug_sexp(const float*, float*, int, hipStream_t) {
   ++g_launches;
   return hipErrorInvalidValue;
 }
+hipError_t launch_debug_tail_exp(const float*, float*, int, hipStream_t) {
+  ++g_launches;
+  return hipErrorInvalidValue;
+}
 }  // namespace ssa
 
 static int g_failures = 0;

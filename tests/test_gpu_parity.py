@@ -354,6 +354,27 @@ def test_sexp_bit_exact():
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+def test_tail_exp_within_two_ulp_of_sexp():
+    """The filter's first-pass weight against the specified exp (itself
+    bit-exact with the oracle's, above) on every 61st float32 in [-87, 0] and
+    the edges: within 2 ulp, 0 below -87 and at -inf."""
+    say("[rng] tail_exp")
+    bits = np.arange(0x80000000, 0xC2AE0001, 61, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([bits.view(np.float32),
+                        np.array([0.0, -0.0, -87.0, -87.00001, -1e-30, -np.inf], np.float32)])
+    xt = torch.from_numpy(x).to(DEV)
+    t = ssa.debug_tail_exp(xt)
+    s = ssa.debug_sexp(xt)
+    torch.cuda.synchronize()
+    t = t.cpu().numpy()
+    s = s.cpu().numpy()
+    assert np.all((t >= 0) & (t <= 1))
+    assert np.array_equal(t == 0, s == 0)
+    ulp = np.abs(t.view(np.int32).astype(np.int64) - s.view(np.int32).astype(np.int64))
+    say(f"[rng] tail_exp: {x.size} values, max {ulp.max()} ulp from sexp")
+    assert ulp.max() <= 2
+
+
 def test_decode_replays_from_a_hip_graph():
     """The step enqueues kernels only (no memset or allocation), so a caller
     can capture it; every replay must equal the eager result bitwise."""
