@@ -56,8 +56,11 @@ __device__ __forceinline__ unsigned long long member_word(uint32_t own_key, int 
 // scored query slices (nmem * G * 2 * pair_count floats).  LPT lanes per
 // candidate (one 16-byte slice of its scored dims each); all the group's
 // members are scored from one load of the slice.  A thread's candidates
-// (kPass passes of kRS / LPT) have their positions, block ids and slices
-// loaded in three rounds, each round's loads all in flight together.
+// (kPass passes of kRS / LPT) have their positions, then block ids and proxy
+// scores, then slices loaded in three rounds, each round's loads all in
+// flight together.  Each candidate's proxy weight sexp(s - M) is stored
+// beside the group's entry, so the member selections read it in order
+// instead of gathering scores.
 constexpr int kPass = 4;
 template <int LPT>
 __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
@@ -89,6 +92,9 @@ __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
   constexpr int TPP = kRS / LPT;  // candidates per pass
   const int32_t* pidx = a.gsel_idx + (size_t)u * a.seg_ld + c0;
   const int* btrow = a.block_table + (size_t)b * a.max_blocks;
+  const float* srow = a.scores + (size_t)u * a.score_ld;
+  float* pw = a.cand_pw + (size_t)u * a.seg_ld + c0;
+  const float M = reinterpret_cast<const UnitState*>(a.gstate)[u].M;
   __syncthreads();
   for (int base = 0; base < n_det; base += kPass * TPP) {  // uniform trip count
     int pos[kPass];
@@ -98,8 +104,12 @@ __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
       pos[p] = i < n_det ? min(max(pidx[i], 0), ui.L - 1) : 0;
     }
     int blk[kPass];
+    float ps[kPass];  // the candidate's proxy score
 #pragma unroll
-    for (int p = 0; p < kPass; ++p) blk[p] = btrow[pos[p] >> 4];
+    for (int p = 0; p < kPass; ++p) {
+      blk[p] = btrow[pos[p] >> 4];
+      ps[p] = srow[pos[p]];
+    }
     uint4 kv[kPass];
 #pragma unroll
     for (int p = 0; p < kPass; ++p) {
@@ -111,6 +121,7 @@ __global__ __launch_bounds__(kRS) void refine_score_kernel(RefineArgs a) {
     for (int p = 0; p < kPass; ++p) {
       const int i = base + p * TPP + tk;
       if (base + p * TPP >= n_det) break;  // uniform
+      if (i < n_det && sl == 0) pw[i] = sexp(ps[p] - M);
       const float kf[8] = {bf16_lo(kv[p].x), bf16_hi(kv[p].x), bf16_lo(kv[p].y),
                            bf16_hi(kv[p].y), bf16_lo(kv[p].z), bf16_hi(kv[p].z),
                            bf16_lo(kv[p].w), bf16_hi(kv[p].w)};
@@ -171,10 +182,12 @@ __device__ __forceinline__ void find_bin_up(const uint32_t* hist, int nbins, int
 // on every pass).
 constexpr int kKeep = 24;
 constexpr int kMaxChunks = SSA_MAX_SEQ_LEN / SSA_CHUNK_TOKENS;
+constexpr int kChunkTab = 4096;  // item-to-chunk table entries (groups of <= 2^18 candidates)
 __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
   constexpr int kDig = 8192;
   __shared__ uint32_t hist[kDig];
   __shared__ int cpre[kMaxChunks + 1];  // candidates in chunks before c
+  __shared__ int ctab[kChunkTab];  // chunk of item 64 m
   __shared__ int scan[kRT / 64];
   __shared__ int pair[2];
   __shared__ double dscr[kRT / 64];
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
   const size_t cu = (size_t)u * a.nchunk;
   const int32_t* gidx = a.gsel_idx + (size_t)u * a.seg_ld;
   const uint32_t* okey = a.own_key + (size_t)v * a.seg_ld;
-  const float* srow = a.scores + (size_t)u * a.score_ld;
+  const float* gpw = a.cand_pw + (size_t)u * a.seg_ld;
   if (threadIdx.x < 2) hist[threadIdx.x] = 0u;
   // Prefix of the chunks' candidate counts.
   {
@@ -209,14 +222,32 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
     __syncthreads();
   }
   const int N = cpre[nc];
-  // Item j's place in the group's segments: its chunk by binary search.
-  auto at_of = [&](int j) -> int {  // < nchunk * 4096 <= 2^24
-    int lo = 0, hi = nc;  // cpre[lo] <= j < cpre[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cpre[mid] <= j) lo = mid; else hi = mid;
+  // The chunk of every 64th item (a chunk holds ~80 at 50x sparsity, so an
+  // item's chunk is that entry's or one of the next few); groups too large
+  // for the table search the prefix instead.
+  const bool tab = N <= kChunkTab * 64;  // uniform
+  if (tab) {
+    for (int c = threadIdx.x; c < nc; c += kRT) {
+      const int first = (cpre[c] + 63) >> 6, end = (cpre[c + 1] + 63) >> 6;
+      for (int m = first; m < end; ++m) ctab[m] = c;
     }
-    return lo * kChunk + (j - cpre[lo]);
+    __syncthreads();
+  }
+  // Item j's place in the group's segments.
+  auto at_of = [&](int j) -> int {  // < nchunk * 4096 <= 2^24
+    int c;
+    if (tab) {
+      c = ctab[j >> 6];  // cpre[c] <= 64 (j >> 6) <= j
+      while (cpre[c + 1] <= j) ++c;
+    } else {
+      int lo = 0, hi = nc;  // cpre[lo] <= j < cpre[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cpre[mid] <= j) lo = mid; else hi = mid;
+      }
+      c = lo;
+    }
+    return c * kChunk + (j - cpre[c]);
   };
   auto word_of = [&](int j) -> unsigned long long {
     const int at = at_of(j);
@@ -319,28 +350,27 @@ __global__ __launch_bounds__(kRT) void refine_select_kernel(RefineArgs a) {
       vstar = ((unsigned long long)((uint32_t)(prefix >> 24) + lo) << 24) | (prefix & 0xffffffull);
     }
     // W_t: the group's tail sum plus the proxy weight of every candidate the
-    // member does not keep (those outside its span included).  The score
-    // loads of the register items go out together.
+    // member does not keep (those outside its span included).  The weights
+    // were stored by the score kernel beside the entries: one round of loads
+    // in order.
     double ws = 0.0;
-    constexpr int kBatch = 8;  // score loads in flight together
-    static_assert(kKeep % kBatch == 0, "whole batches");
+    float pwv[kKeep];
 #pragma unroll
-    for (int e0 = 0; e0 < kKeep; e0 += kBatch) {
-      float sv[kBatch];
+    for (int e = 0; e < kKeep; ++e) {
+      const int j = threadIdx.x + e * kRT;
+      pwv[e] = j < N ? gpw[at_of(j)] : 0.0f;
+    }
 #pragma unroll
-      for (int e = 0; e < kBatch; ++e)
-        sv[e] = threadIdx.x + (e0 + e) * kRT < N ? srow[pos_of(wv[e0 + e])] : 0.0f;
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const unsigned long long w = wv[e0 + e];
-        const bool kept = kt > 0 && pos_of(w) < Lt && w <= vstar;
-        if (threadIdx.x + (e0 + e) * kRT < N && !kept) ws += (double)sexp(sv[e] - gs.M);
-      }
+    for (int e = 0; e < kKeep; ++e) {
+      const unsigned long long w = wv[e];
+      const bool kept = kt > 0 && pos_of(w) < Lt && w <= vstar;
+      if (threadIdx.x + e * kRT < N && !kept) ws += (double)pwv[e];
     }
     for (int j = threadIdx.x + kKeep * kRT; j < N; j += kRT) {
-      const unsigned long long w = word_of(j);
+      const int at = at_of(j);
+      const unsigned long long w = member_word(okey[at], min(max(gidx[at], 0), max(Lg - 1, 0)));
       const bool kept = kt > 0 && pos_of(w) < Lt && w <= vstar;
-      if (!kept) ws += (double)sexp(srow[pos_of(w)] - gs.M);
+      if (!kept) ws += (double)gpw[at];
     }
     W = gw + block_sum_f64<kRT>(ws, dscr);
   }
@@ -396,11 +426,14 @@ __global__ __launch_bounds__(kRS) __attribute__((amdgpu_waves_per_eu(8))) void r
   // e * kRS) in registers; a chunk rarely holds more than kRS * kFast
   // entries, and further ones are computed again for every member.
   constexpr int kFast = 2;
+  // A candidate's weight was stored by the score kernel; a sample's is
+  // computed here.
+  const float* cpw = a.cand_pw + (size_t)u * a.seg_ld + c0;
   auto entry = [&](int i, int& p, float& w, float& un) {
     p = i < n_all ? gidx[i] : -1;
     const bool in = (unsigned)(p - c0) < (unsigned)kChunk && p < ui.L;
     if (!in) p = -1;
-    w = in ? sexp(srow[p] - M) : 0.0f;
+    w = !in ? 0.0f : (i < n_det ? cpw[i] : sexp(srow[p] - M));
     un = 0.0f;
     if (in) {
       const uint4 wd = philox_block(seed, b, h, (uint32_t)p >> 2, ui.grp);

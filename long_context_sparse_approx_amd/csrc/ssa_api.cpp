@@ -131,7 +131,7 @@ struct Layout {
       list_idx, list_w,
       list_cnt, wpart, tiecnt,
       ties_before, state, sel_idx, sel_logw, sel_cnt, part, stop_cut, stop_off, stop_n,
-      stop_words, stop_pair, stop_rword, stop_logit, stop_mkey, stop_gain, w64, own_key, mstate, msel_idx, msel_logw,
+      stop_words, stop_pair, stop_rword, stop_logit, stop_mkey, stop_gain, w64, own_key, cand_pw, mstate, msel_idx, msel_logw,
       msel_cnt, total;
 };
 
@@ -182,6 +182,7 @@ Layout layout_of(const Dims& d) {
   const size_t RM = d.refine > 0 ? (size_t)d.Um : 0;
   l.w64 = take(RU * 8);
   l.own_key = take(RM * SEG * 4);
+  l.cand_pw = take(RU * SEG * 4);
   l.mstate = take(RM * 32);
   l.msel_idx = take(RM * SEG * 4);
   l.msel_logw = take(RM * SEG * 4);
@@ -353,6 +354,7 @@ ssa::RefineArgs refine_args(const ssa_params* p, const Dims& d, const ssa::Selec
   r.k_cache = static_cast<const uint16_t*>(k_main);
   r.block_table = block_table;
   r.own_key = at<uint32_t>(ws, l.own_key);
+  r.cand_pw = at<float>(ws, l.cand_pw);
   r.mstate = at<void>(ws, l.mstate);
   r.msel_idx = msel_idx;
   r.msel_logw = msel_logw;

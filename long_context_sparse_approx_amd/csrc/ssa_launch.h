@@ -161,6 +161,7 @@ struct RefineArgs {
   const uint16_t* k_cache;    // the scored dims of row r at k_cache + r * key_ld + key_off
   const int32_t* block_table;
   uint32_t* own_key;          // [Um, seg_ld] member's order key of each group entry
+  float* cand_pw;             // [U, seg_ld] proxy weight sexp(s - M) of each group candidate
   void* mstate;               // [Um] MemberState
   int32_t* msel_idx;          // [Um, seg_ld] member selections (positions)
   float* msel_logw;           // [Um, seg_ld]
