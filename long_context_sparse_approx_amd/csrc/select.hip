@@ -32,10 +32,11 @@
 // Only one pass reads every score (the filter).  Besides the threshold-digit
 // candidates and the tail weights it lists, per chunk, the tokens above the
 // threshold digit and the tail tokens that pass a necessary inclusion test,
-// fl(u_j * W_lb) < fl(m * w_j), with W_lb <= W a lower bound of the
-// normaliser taken from the first-digit histogram (u_j * W_lb <= u_j * W and
-// rounding is monotone, so no token that the exact test would include is
-// dropped).  The final sample pass only visits these lists.
+// u_j < m w_j / W_lb up to a margin that covers every rounding, with
+// W_lb <= W (1 - 2^-10) a lower bound of the normaliser taken from the
+// first-digit histogram (u_j W_lb <= u_j W, so no token that the exact test
+// would include is dropped; the filter states the bound).  The final sample
+// pass only visits these lists.
 #include "select_device.h"
 #include "ssa_device.h"
 #include "ssa_launch.h"
@@ -165,8 +166,10 @@ __global__ __launch_bounds__(kNT) void threshold_kernel(SelectArgs a) {
     if (n && lo == lo) lb += (double)n * (double)sexp(lo - M);
   }
   lb = block_sum_f64<kNT>(lb, dscr);
+  // An injected W gets the same margin, so the filter's test stays necessary
+  // for the final test with that W.
   float wlb = (float)(lb * (1.0 - 0x1.0p-10));
-  if (a.w_in) wlb = fminf(wlb, a.w_in[u]);
+  if (a.w_in) wlb = fminf(wlb, (float)((double)a.w_in[u] * (1.0 - 0x1.0p-10)));
   if (threadIdx.x == 0)
     a.thresh[u] = Thresh1{b1, dig_sh[1], wlb, dig_sh[2], dig_m, dig_sh[3], 0};
 }
@@ -1255,7 +1258,9 @@ __global__ void debug_philox_kernel(uint64_t seed, int b, int h, int grp, int j0
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const uint32_t j = (uint32_t)(j0 + i);
-  const uint4 wd = philox_block(seed, b, h, j >> 2, grp);
+  // The filter's variant (the key is a kernel argument, uniform); the sample
+  // kernel's generic one decides every final inclusion the parity tests check.
+  const uint4 wd = philox_block_uniform_key(seed, b, h, j >> 2, grp);
   const uint32_t w4[4] = {wd.x, wd.y, wd.z, wd.w};
   words[i] = w4[j & 3u];
 }
