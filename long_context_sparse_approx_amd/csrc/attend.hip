@@ -30,6 +30,7 @@
 //   * PV's output column n of step j is head dim n*(d/16)+j, so lane n's V
 //     operand for all steps is one contiguous d/16-element slice of each of
 //     its 8 token rows: a wave-wide load reads 4 full 256-byte rows.
+#include "select_device.h"
 #include "ssa_device.h"
 #include "ssa_launch.h"
 
@@ -68,6 +69,127 @@ struct VSlice<64> {
 
 constexpr int kBatch = 256;  // selected items resolved to cache rows at a time
 
+// The tiles of one batch of nb resolved items (rows_sh: cache row or -1,
+// lw_sh: logit bias, pos_sh: position for the span mask; entries nb ..
+// nb + 31 are padding), folded into the wave's online-softmax state.
+template <int D, bool SPLIT>
+__device__ __forceinline__ void attend_tiles(const AttendArgs& a, int nb, const int* rows_sh,
+                                             const float* lw_sh, const int* pos_sh,
+                                             const bf16x8 (&qf)[D / 32],
+                                             const uint16_t* const (&kb)[D / 32],
+                                             const uint32_t (&kld)[D / 32], int L_col, int n16,
+                                             int q4, float& m_run, float& l_run,
+                                             f32x4 (&acc)[D / 16]) {
+  constexpr int KK = D / 32;
+  constexpr int DPL = D / 16;
+  using VS = VSlice<D>;
+  for (int t0 = 0; t0 < nb; t0 += 32) {
+    // QK for the two 16-token halves: A = K rows (token n16 of the half).
+    // Every K load of the tile is unconditional (a marked item reads row 0
+    // and is zeroed), so the eight loads are in flight together; the V
+    // loads follow the same way once the QK products are issued.
+    bf16x8 kf[2][KK];
+    bool kok[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = rows_sh[t0 + 16 * hh + n16];
+      kok[hh] = r >= 0;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kf[hh][kk] =
+            as_bf16x8(*reinterpret_cast<const uint4*>(kb[kk] + (size_t)max(r, 0) * kld[kk]));
+    }
+    f32x4 sc[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (!kok[hh]) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kf[hh][kk] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+      }
+      f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hh][kk], qf[kk], d, 0, 0, 0);
+      sc[hh] = d;
+    }
+    // V rows of this lane's 8 k-slots (issued before the softmax math, and
+    // kept after the QK products so that K and V registers are not live
+    // together).
+    __builtin_amdgcn_sched_barrier(0);
+    typename VS::T vr[8];
+    bool vok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+      const int r = rows_sh[t0 + tok];
+      vok[i] = r >= 0;
+      vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)max(r, 0) * D +
+                                                      n16 * DPL);
+    }
+    // Logits of (column n16, slot tokens), online softmax update; a
+    // column ignores positions past its member's span.
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
+      x[i] = pos_sh[t0 + tok] < L_col ? sc[i >> 2][i & 3] * a.scale + lw_sh[t0 + tok]
+                                      : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    // A tile of masked entries only (m_new still -inf) must add nothing:
+    // exponentiate against 0 instead of -inf.
+    const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __expf(m_run - m_ref);
+    float psum = 0.0f;
+    uint32_t phi[4], plo[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = __expf(x[i] - m_ref);
+      const float p1 = __expf(x[i + 1] - m_ref);
+      psum += p0 + p1;
+      const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
+      const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
+      phi[i >> 1] = h0 | (h1 << 16);
+      plo[i >> 1] = l0 | (l1 << 16);
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // Rescale the accumulators: rows 4*q4 + r belong to column 4*q4 + r,
+    // whose alpha sits in lane 4*q4 + r.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!vok[i]) vr[i] = VS::zero();
+    const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
+    const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) {
+      const int w = j >> 1;
+      uint32_t p[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w0 = VS::word(vr[2 * k], w), w1 = VS::word(vr[2 * k + 1], w);
+        p[k] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
+      }
+      const bf16x8 vb = as_bf16x8(make_uint4(p[0], p[1], p[2], p[3]));
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[j], 0, 0, 0);
+    }
+  }
+}
+
 // SPLIT: the keys are held in two arrays of the same row numbering: the
 // scored dims (2 * pair_count per row) apart from the others ("FASA:
 // Frequency-aware Sparse Attention", section 3, variants: FASA-M keeps the
@@ -78,7 +200,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
     AttendArgs a) {
   constexpr int KK = D / 32;   // QK steps over the head dim
   constexpr int DPL = D / 16;  // head dims per PV column = PV steps
-  using VS = VSlice<D>;
   __shared__ int rows_sh[kBatch + 32];
   __shared__ float lw_sh[kBatch + 32];
   __shared__ int pos_sh[kBatch + 32];
@@ -211,111 +332,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
         pos_sh[kBatch + lane] = 0;
       }
       __syncthreads();
-      for (int t0 = 0; t0 < nb; t0 += 32) {
-        // QK for the two 16-token halves: A = K rows (token n16 of the half).
-        // Every K load of the tile is unconditional (a marked item reads row 0
-        // and is zeroed), so the eight loads are in flight together; the V
-        // loads follow the same way once the QK products are issued.
-        bf16x8 kf[2][KK];
-        bool kok[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int r = rows_sh[t0 + 16 * hh + n16];
-          kok[hh] = r >= 0;
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            kf[hh][kk] =
-                as_bf16x8(*reinterpret_cast<const uint4*>(kb[kk] + (size_t)max(r, 0) * kld[kk]));
-        }
-        f32x4 sc[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          if (!kok[hh]) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) kf[hh][kk] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
-          }
-          f32x4 d = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[hh][kk], qf[kk], d, 0, 0, 0);
-          sc[hh] = d;
-        }
-        // V rows of this lane's 8 k-slots (issued before the softmax math, and
-        // kept after the QK products so that K and V registers are not live
-        // together).
-        __builtin_amdgcn_sched_barrier(0);
-        typename VS::T vr[8];
-        bool vok[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
-          const int r = rows_sh[t0 + tok];
-          vok[i] = r >= 0;
-          vr[i] = *reinterpret_cast<const typename VS::T*>(a.v_cache + (size_t)max(r, 0) * D +
-                                                          n16 * DPL);
-        }
-        // Logits of (column n16, slot tokens), online softmax update; a
-        // column ignores positions past its member's span.
-        float x[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int tok = (i < 4) ? (4 * q4 + i) : (16 + 4 * q4 + (i - 4));
-          x[i] = pos_sh[t0 + tok] < L_col ? sc[i >> 2][i & 3] * a.scale + lw_sh[t0 + tok]
-                                          : -INFINITY;
-          tmax = fmaxf(tmax, x[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        // A tile of masked entries only (m_new still -inf) must add nothing:
-        // exponentiate against 0 instead of -inf.
-        const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = __expf(m_run - m_ref);
-        float psum = 0.0f;
-        uint32_t phi[4], plo[4];
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float p0 = __expf(x[i] - m_ref);
-          const float p1 = __expf(x[i + 1] - m_ref);
-          psum += p0 + p1;
-          const uint32_t h0 = f32_to_bf16_bits(p0), h1 = f32_to_bf16_bits(p1);
-          const uint32_t l0 = f32_to_bf16_bits(p0 - __uint_as_float(h0 << 16));
-          const uint32_t l1 = f32_to_bf16_bits(p1 - __uint_as_float(h1 << 16));
-          phi[i >> 1] = h0 | (h1 << 16);
-          plo[i >> 1] = l0 | (l1 << 16);
-        }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // Rescale the accumulators: rows 4*q4 + r belong to column 4*q4 + r,
-        // whose alpha sits in lane 4*q4 + r.
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * q4 + r);
-#pragma unroll
-          for (int j = 0; j < DPL; ++j) acc[j][r] *= ar;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (!vok[i]) vr[i] = VS::zero();
-        const bf16x8 pa_hi = as_bf16x8(make_uint4(phi[0], phi[1], phi[2], phi[3]));
-        const bf16x8 pa_lo = as_bf16x8(make_uint4(plo[0], plo[1], plo[2], plo[3]));
-#pragma unroll
-        for (int j = 0; j < DPL; ++j) {
-          const int w = j >> 1;
-          uint32_t p[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t w0 = VS::word(vr[2 * k], w), w1 = VS::word(vr[2 * k + 1], w);
-            p[k] = (j & 1) ? pack_hi(w0, w1) : pack_lo(w0, w1);
-          }
-          const bf16x8 vb = as_bf16x8(make_uint4(p[0], p[1], p[2], p[3]));
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb, acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb, acc[j], 0, 0, 0);
-        }
-      }
+      attend_tiles<D, SPLIT>(a, nb, rows_sh, lw_sh, pos_sh, qf, kb, kld, L_col, n16, q4, m_run,
+                             l_run, acc);
       __syncthreads();
     }
   }
@@ -335,6 +353,431 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   }
   if (q4 == 0 && col_valid) {
     const int qrow = (b * a.T + col_t) * a.Hq + h * a.G + col_g;
+    float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + D;
+    dst[0] = m_run;
+    dst[1] = l_run;
+  }
+}
+
+// ------------------------------------------------------------------ fused
+// The decode step with one query per sequence takes the sample stage's
+// decisions in the attention wave, per chunk, instead of reading a written
+// selection ("Stratified Sparse Attention speeds up decoding 2.96x at 1M
+// context", "How SSA stratifies the cache": the deterministic stratum and
+// the Poisson-sampled tail with inclusion probability min(1, m w / W)).  The
+// decisions and their order are the sample kernel's: tokens above the
+// threshold digit and candidates above the threshold key (or within the tie
+// quota, ranked by position) are deterministic; the listed tail tokens and
+// the other candidates pass fl(u W) < fl(m w) with u from Philox4x32-10 and
+// carry the bias -log(min(1, m w / W)); the chunk's items are deterministic
+// positions ascending, then sampled positions ascending.  So the output is
+// bitwise that of the staged path (selection, then attention over it).
+//
+// Each wave marks the chunk's decisions in two LDS bitmaps, takes each
+// word's rank offset from a wave scan, and places every item at its rank.
+// Lists of up to 128 entries (the common case: about 80 selected tokens per
+// 4096-token chunk at 50x sparsity) are held in registers, two entries per
+// lane, with the sampled entries' biases; longer ones are read in rounds of
+// 64 and their biases go through a position-indexed scratch row.  Dense
+// units take every valid position.
+constexpr int kSelWords = kChunk / 32;
+constexpr int kChunkBlocks = kChunk / kBlockTokens;
+constexpr int kRegList = 128;  // entries of each list held in registers
+
+struct SelShared {
+  uint32_t map[2][kSelWords];  // positions of the chunk: [0] deterministic, [1] sampled
+  int blk[kChunkBlocks];       // the chunk's cache block ids (clamped)
+};
+
+// A chunk's counts and the first two rounds of its lists (entries past a
+// count are read from the segment and never used).
+struct ChunkLists {
+  int n_above, n_samp, ncand, before, ties_here;
+  int lt[2];
+  float lwv[2];
+  int ct[2];
+  uint32_t ck[2];
+  float cwv[2];
+  int blk[kChunkBlocks / 64];
+};
+
+__device__ __forceinline__ ChunkLists load_chunk_lists(const AttendArgs& a, size_t seg,
+                                                       size_t ci, int c, int b, int lane) {
+  ChunkLists r;
+  const size_t base = seg + (size_t)c * kChunk + lane;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    r.lt[k] = a.list_idx[base + 64 * k];
+    r.lwv[k] = a.list_w[base + 64 * k];
+    r.ct[k] = a.cand_idx[base + 64 * k];
+    r.ck[k] = a.cand_key[base + 64 * k];
+    r.cwv[k] = a.cand_w[base + 64 * k];
+  }
+  const int* bt = a.block_table + (size_t)b * a.max_blocks;
+#pragma unroll
+  for (int k = 0; k < kChunkBlocks / 64; ++k)
+    r.blk[k] = bt[min(c * kChunkBlocks + lane + 64 * k, a.max_blocks - 1)];
+  r.n_above = a.list_cnt[2 * ci];
+  r.n_samp = a.list_cnt[2 * ci + 1];
+  r.ncand = a.cand_cnt[ci];
+  r.before = a.ties_before[ci];
+  r.ties_here = a.tiecnt[ci];
+  return r;
+}
+
+// The sample stage's inclusion test of tail token t with weight w; *bias
+// gets -log(pi) when it passes.
+__device__ __forceinline__ bool fused_sample(const UnitState& st, uint64_t seed, int b, int h,
+                                             int t, float w, float* bias) {
+  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, 0);
+  const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
+  const float mw = (float)st.m * w;
+  if (uniform24(words[t & 3]) * st.W < mw) {
+    *bias = -logf(fminf(1.0f, mw / st.W));
+    return true;
+  }
+  return false;
+}
+
+// The same test without a branch, for slots computed side by side: *bias is
+// written whatever the outcome (used only where the test passes).
+__device__ __forceinline__ bool sample_test(const UnitState& st, uint64_t seed, int b, int h,
+                                            int t, float w, float* bias) {
+  const uint4 wd = philox_block_uniform_key(seed, b, h, (uint32_t)t >> 2, 0);
+  const uint32_t word = (t & 2) ? ((t & 1) ? wd.w : wd.z) : ((t & 1) ? wd.y : wd.x);
+  const float mw = (float)st.m * w;
+  *bias = -logf(fminf(1.0f, mw / st.W));
+  return uniform24(word) * st.W < mw;
+}
+
+__device__ __forceinline__ void mark(uint32_t* map, int p) {
+  atomicOr(&map[p >> 5], 1u << (p & 31));
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attend_select_kernel(
+    AttendArgs a) {
+  constexpr int KK = D / 32;
+  constexpr int DPL = D / 16;
+  __shared__ int rows_sh[kBatch + 32];
+  __shared__ float lw_sh[kBatch + 32];
+  __shared__ int pos_sh[kBatch + 32];
+  __shared__ SelShared ssh;
+
+  const int slot = blockIdx.x;
+  const int s = slot / a.nsub;
+  const int sub = slot - s * a.nsub;
+  const int nslot = a.nsplit * a.nsub;
+  const int u = blockIdx.y;  // one query per sequence: unit u = b * Hkv + h
+  const int b = u / a.Hkv;
+  const int h = u - b * a.Hkv;
+  const int lane = threadIdx.x;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+  const uint64_t ltmask = (1ull << lane) - 1ull;
+  const size_t seg = (size_t)u * a.seg_ld;
+  // The split's first chunk when the sequence covers every chunk: its counts,
+  // lists and block ids are read with the unit state and the query, ahead of
+  // the sequence length that decides the range (used only if it matches).
+  // Index arithmetic in 32 bits: s * chunks < 4096 * 4096.
+  const int c_guess = (int)((uint32_t)s * (uint32_t)a.nchunk / (uint32_t)a.nsplit);
+  const ChunkLists pf = load_chunk_lists(a, seg, (size_t)u * a.nchunk + c_guess, c_guess, b, lane);
+  const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
+  const uint64_t seed = a.seed[b];
+  const bool col_valid = n16 < a.G;
+  const int col_g = col_valid ? n16 : 0;
+  bf16x8 qf[KK];
+  {
+    // Loaded for every column, with no branch: a column past the group reads
+    // head 0's row, and its span is empty (L_col = 0), so its logits are -inf,
+    // its probabilities 0 and its state is never written; an MFMA output
+    // column depends on its own query column only.
+    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h * a.G + col_g) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8));
+  }
+  // The loads above stay here (a scheduling barrier), in flight while the
+  // sequence length and the chunk range are worked out, instead of sinking
+  // into the branch that uses them.
+  __builtin_amdgcn_sched_barrier(0);
+  const int P = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int L_col = col_valid ? P : 0;
+  const int ncL = (P + kChunk - 1) / kChunk;
+  const int c_begin = (int)((uint32_t)s * (uint32_t)ncL / (uint32_t)a.nsplit);
+  const int c_end = (int)((uint32_t)(s + 1) * (uint32_t)ncL / (uint32_t)a.nsplit);
+
+  const uint16_t* kb[KK];
+  uint32_t kld[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int dim = kk * 32 + q4 * 8;
+    if (!SPLIT) {
+      kb[kk] = a.k_cache + dim;
+      kld[kk] = D;
+    } else {
+      const int lo = 2 * a.pair_begin;
+      const int nd = 2 * a.pair_count;
+      const bool scored = dim >= lo && dim < lo + nd;
+      const uint16_t* rest = a.k_rest ? a.k_rest : a.k_cache;
+      kb[kk] = scored ? a.k_cache + (dim - lo) : rest + (dim < lo ? dim : dim - nd);
+      kld[kk] = scored ? nd : D - nd;
+    }
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.0f;
+  f32x4 acc[DPL];
+#pragma unroll
+  for (int j = 0; j < DPL; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const bool empty = (st.flags & kFlagEmpty) != 0;
+  const bool dense = (st.flags & kFlagDense) != 0;
+  const bool sampling = (st.flags & kFlagSample) != 0;
+  const bool use_topk = !(st.flags & kFlagNoTopk);
+  // One chunk of the split; false once the unit's span has ended.
+  auto do_chunk = [&](int c, const ChunkLists& cl) -> bool {
+    const int c0 = c * kChunk;
+    if (empty || c0 >= st.L) return false;  // uniform
+    const int nvalid = min(kChunk, st.L - c0);
+    const int n_above = clamp_count(cl.n_above, kChunk);
+    const int n_samp = clamp_count(cl.n_samp, kChunk - n_above);
+    const int n_list = n_above + (sampling ? n_samp : 0);
+    const int ncand = use_topk ? clamp_count(cl.ncand, kChunk) : 0;
+#pragma unroll
+    for (int k = 0; k < kChunkBlocks / 64; ++k) {
+      const int v = cl.blk[k];
+      ssh.blk[lane + 64 * k] = v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v);
+    }
+    // mode 0: dense (every valid position, in order); 1: lists in registers;
+    // 2: lists read in rounds.
+    const int mode = dense ? 0 : (n_list <= kRegList && ncand <= kRegList ? 1 : 2);
+    int kd[4] = {0, 0, 0, 0};  // 0 none, 1 deterministic, 2 sampled
+    int ps[4] = {0, 0, 0, 0};  // position in the chunk, then rank
+    int rw[4] = {0, 0, 0, 0};  // cache row
+    float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    int totS = nvalid, totR = 0, ex = 0;
+    ssh.map[0][lane] = 0u;
+    ssh.map[0][lane + 64] = 0u;
+    ssh.map[1][lane] = 0u;
+    ssh.map[1][lane + 64] = 0u;
+    __syncthreads();
+    if (mode != 0) {
+      if (mode == 1) {
+        // Slots 0, 1: list entries lane, lane + 64; slots 2, 3: candidates.
+        // Every slot's inclusion test is computed (four independent Philox
+        // blocks side by side) and used where the slot is a tail token.
+        const int tt[4] = {cl.lt[0], cl.lt[1], cl.ct[0], cl.ct[1]};
+        const float wv[4] = {cl.lwv[0], cl.lwv[1], cl.cwv[0], cl.cwv[1]};
+        bool pass[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          ps[k] = tt[k] - c0;
+          pass[k] = sample_test(st, seed, b, h, tt[k], wv[k], &bs[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int i = lane + 64 * k;
+          const bool valid = (unsigned)ps[k] < (unsigned)nvalid;
+          if (i < n_above)
+            kd[k] = valid ? 1 : 0;
+          else if (i < n_list && valid && pass[k])
+            kd[k] = 2;
+        }
+        bool tie[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) tie[k] = lane + 64 * k < ncand && cl.ck[k] == st.tkey;
+        const uint64_t tb0 = __ballot(tie[0]);
+        const uint64_t tb1 = __ballot(tie[1]);
+        const int pre[2] = {(int)__popcll(tb0 & ltmask),
+                            (int)(__popcll(tb0) + __popcll(tb1 & ltmask))};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int i = lane + 64 * k;
+          const bool valid = (unsigned)ps[2 + k] < (unsigned)nvalid;
+          if (i < ncand) {
+            const int rank = cl.ties_here != 0 ? cl.before + pre[k] : 0;
+            if (cl.ck[k] > st.tkey || (tie[k] && rank < st.ties_needed))
+              kd[2 + k] = valid ? 1 : 0;
+            else if (sampling && valid && pass[2 + k])
+              kd[2 + k] = 2;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (kd[k] != 0) mark(ssh.map[kd[k] - 1], ps[k]);
+          // The cache row, read before the ranks are known.
+          rw[k] = (ssh.blk[(ps[k] >> 4) & (kChunkBlocks - 1)] * a.Hkv + h) * kBlockTokens +
+                  (ps[k] & 15);
+        }
+      } else {
+        float* scr = a.sel_scratch + seg + (size_t)c * kChunk;
+        const int32_t* lidx = a.list_idx + seg + (size_t)c * kChunk;
+        const float* lw = a.list_w + seg + (size_t)c * kChunk;
+        for (int i = lane; i < n_list; i += 64) {
+          const int t = lidx[i];
+          const int p = t - c0;
+          if ((unsigned)p >= (unsigned)nvalid) continue;
+          float bias;
+          if (i < n_above)
+            mark(ssh.map[0], p);
+          else if (fused_sample(st, seed, b, h, t, lw[i], &bias)) {
+            scr[p] = bias;
+            mark(ssh.map[1], p);
+          }
+        }
+        const int32_t* cidx = a.cand_idx + seg + (size_t)c * kChunk;
+        const uint32_t* ckey = a.cand_key + seg + (size_t)c * kChunk;
+        const float* cw = a.cand_w + seg + (size_t)c * kChunk;
+        int run = 0;
+        for (int base = 0; base < ncand; base += 64) {
+          const int i = base + lane;
+          const bool v = i < ncand;
+          const uint32_t key = v ? ckey[i] : 0u;
+          const int t = v ? cidx[i] : 0;
+          const bool tie = v && key == st.tkey;
+          const uint64_t tb = __ballot(tie);
+          const int rank = cl.ties_here != 0 ? cl.before + run + __popcll(tb & ltmask) : 0;
+          run += __popcll(tb);
+          const int p = t - c0;
+          if (v && (unsigned)p < (unsigned)nvalid) {
+            float bias;
+            if (key > st.tkey || (tie && rank < st.ties_needed))
+              mark(ssh.map[0], p);
+            else if (sampling && fused_sample(st, seed, b, h, t, cw[i], &bias)) {
+              scr[p] = bias;
+              mark(ssh.map[1], p);
+            }
+          }
+        }
+        __threadfence_block();  // the biases, read back by other lanes below
+      }
+      __syncthreads();
+      // Each word's rank offsets: lane l takes words 2l and 2l + 1 (positions
+      // 64 l .. 64 l + 63).
+      const uint32_t d0 = ssh.map[0][2 * lane], d1 = ssh.map[0][2 * lane + 1];
+      const uint32_t s0 = ssh.map[1][2 * lane] & ~d0, s1 = ssh.map[1][2 * lane + 1] & ~d1;
+      const int packed = (__popc(d0) + __popc(d1)) | ((__popc(s0) + __popc(s1)) << 16);
+      const int inc = wave_inclusive_scan<int>(packed);
+      const int tot = __builtin_amdgcn_readlane(inc, 63);
+      totS = tot & 0xffff;
+      totR = tot >> 16;
+      ex = inc - packed;
+      if (mode == 1) {
+        // Items to ranks, from the owning lane's offsets and words (a sampled
+        // item that is also deterministic is dropped, as in the sample
+        // kernel; the lists never make one).
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int p = ps[k] & (kChunk - 1);
+          const int src = p >> 6;
+          const int o_ex = __shfl(ex, src);
+          const uint32_t o_d0 = __shfl(d0, src), o_d1 = __shfl(d1, src);
+          const uint32_t o_s0 = __shfl(s0, src), o_s1 = __shfl(s1, src);
+          const int bit = p & 63;
+          const uint64_t below = bit == 0 ? 0ull : (~0ull >> (64 - bit));
+          const uint64_t dw = ((uint64_t)o_d1 << 32) | o_d0;
+          const uint64_t sw = ((uint64_t)o_s1 << 32) | o_s0;
+          if (kd[k] == 1) {
+            ps[k] = (o_ex & 0xffff) + __popcll(dw & below);
+            bs[k] = 0.0f;
+          } else if (kd[k] == 2) {
+            if ((dw >> bit) & 1ull) kd[k] = 0;
+            ps[k] = totS + (o_ex >> 16) + __popcll(sw & below);
+          }
+        }
+      }
+    }
+    const int cnt = totS + totR;
+    const int i_lo = (int)((uint32_t)sub * (uint32_t)cnt / (uint32_t)a.nsub);
+    const int i_hi = (int)((uint32_t)(sub + 1) * (uint32_t)cnt / (uint32_t)a.nsub);
+    if (mode == 1) {
+      // At most 2 * kRegList = kBatch items: one batch, placed here so that
+      // the items' registers are free during the tiles.
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int j = ps[k] - i_lo;
+        if (kd[k] != 0 && (unsigned)j < (unsigned)(i_hi - i_lo)) {
+          rows_sh[j] = rw[k];
+          lw_sh[j] = bs[k];
+          pos_sh[j] = 0;
+        }
+      }
+    }
+    static_assert(2 * kRegList <= kBatch, "the register-held lists fill one batch");
+    for (int b0 = i_lo; b0 < i_hi; b0 += kBatch) {
+      const int nb = min(kBatch, i_hi - b0);
+#pragma unroll
+      for (int k = 0; k < kBatch / 64; ++k) {
+        const int i = lane + 64 * k;
+        if (mode == 0 && i < nb) {
+          const int p = b0 + i;
+          rows_sh[i] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
+          lw_sh[i] = 0.0f;
+          pos_sh[i] = 0;
+        } else if (i >= nb) {
+          rows_sh[i] = -1;
+          lw_sh[i] = -INFINITY;
+          pos_sh[i] = 0;
+        }
+      }
+      if (lane < 32) {
+        rows_sh[kBatch + lane] = -1;
+        lw_sh[kBatch + lane] = -INFINITY;
+        pos_sh[kBatch + lane] = 0;
+      }
+      if (mode == 2) {
+        // Lane l's positions 64 l .. 64 l + 63, deterministic then sampled.
+        const float* scr = a.sel_scratch + seg + (size_t)c * kChunk;
+#pragma unroll
+        for (int cls = 0; cls < 2; ++cls) {
+          int r = cls == 0 ? (ex & 0xffff) : totS + (ex >> 16);
+#pragma unroll
+          for (int wj = 0; wj < 2; ++wj) {
+            const uint32_t dm = ssh.map[0][2 * lane + wj];
+            uint32_t bits = cls == 0 ? dm : ssh.map[1][2 * lane + wj] & ~dm;
+            for (; bits != 0u; bits &= bits - 1u, ++r) {
+              const int j = r - b0;
+              if ((unsigned)j >= (unsigned)nb) continue;
+              const int p = 64 * lane + 32 * wj + __builtin_ctz(bits);
+              rows_sh[j] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
+              lw_sh[j] = cls == 0 ? 0.0f : scr[p];
+              pos_sh[j] = 0;
+            }
+          }
+        }
+      }
+      __syncthreads();
+      attend_tiles<D, SPLIT>(a, nb, rows_sh, lw_sh, pos_sh, qf, kb, kld, L_col, n16, q4, m_run,
+                             l_run, acc);
+      __syncthreads();
+    }
+    return true;
+  };
+  // The first chunk takes the prefetched lists when the range starts at the
+  // guessed chunk (peeled, so that they are not live across later chunks).
+  if (c_begin < c_end) {
+    bool go = do_chunk(c_begin, c_begin == c_guess
+                                    ? pf
+                                    : load_chunk_lists(a, seg, (size_t)u * a.nchunk + c_begin,
+                                                       c_begin, b, lane));
+    for (int c = c_begin + 1; go && c < c_end; ++c)
+      go = do_chunk(c, load_chunk_lists(a, seg, (size_t)u * a.nchunk + c, c, b, lane));
+  }
+
+  const int stride = D + 2;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int col = 4 * q4 + r;
+    if (col < a.G) {
+      const int qrow = b * a.Hq + h * a.G + col;
+      float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + n16 * DPL;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
+    }
+  }
+  if (q4 == 0 && col_valid) {
+    const int qrow = b * a.Hq + h * a.G + col_g;
     float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + D;
     dst[0] = m_run;
     dst[1] = l_run;
@@ -442,6 +885,23 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
     attend_kernel<64, false><<<grid, 64, 0, stream>>>(a);
   else if (a.d == 64)
     attend_kernel<64, true><<<grid, 64, 0, stream>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_select(const AttendArgs& a, hipStream_t stream) {
+  if (!a.fused_select || a.T != 1 || a.mblocks != 1) return hipErrorInvalidValue;
+  dim3 grid(a.nsplit * a.nsub, a.B * a.Hkv);
+  const bool split = a.k_rest != nullptr;
+  if (a.d == 128 && !split)
+    attend_select_kernel<128, false><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 128)
+    attend_select_kernel<128, true><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 64 && !split)
+    attend_select_kernel<64, false><<<grid, 64, 0, stream>>>(a);
+  else if (a.d == 64)
+    attend_select_kernel<64, true><<<grid, 64, 0, stream>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -422,7 +422,39 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, K
   a.pair_count = p->pair_count;
   a.seg_ld = d.SEG;
   a.scale = d.scale;
+  a.fused_select = 0;
+  a.list_idx = nullptr;
+  a.list_w = nullptr;
+  a.list_cnt = nullptr;
+  a.cand_idx = nullptr;
+  a.cand_key = nullptr;
+  a.cand_w = nullptr;
+  a.cand_cnt = nullptr;
+  a.tiecnt = nullptr;
+  a.ties_before = nullptr;
+  a.state = nullptr;
+  a.seed = nullptr;
+  a.sel_scratch = nullptr;
   return a;
+}
+
+// The attention stage takes the sample stage's decisions from the selection
+// stage's lists (one query per sequence, no early stop); the position-indexed
+// scratch row is the selection's bias array, which nothing else reads then.
+void fuse_select(ssa::AttendArgs* a, const ssa::SelectArgs& s) {
+  a->fused_select = 1;
+  a->list_idx = s.list_idx;
+  a->list_w = s.list_w;
+  a->list_cnt = s.list_cnt;
+  a->cand_idx = s.cand_idx;
+  a->cand_key = s.cand_key;
+  a->cand_w = s.cand_w;
+  a->cand_cnt = s.cand_cnt;
+  a->tiecnt = s.tiecnt;
+  a->ties_before = s.ties_before;
+  a->state = s.state;
+  a->seed = s.seed;
+  a->sel_scratch = s.sel_logw;
 }
 
 #define SSA_TRY(expr)                        \
@@ -517,8 +549,10 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
     ra = refine_args(p, d, sa, q, keys.main, block_table, nullptr, a_idx, a_logw, a_cnt, nullptr,
                      workspace, l);
   }
-  const ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, a_idx,
-                                         a_logw, a_cnt, rows, out, workspace, l);
+  ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, a_idx, a_logw,
+                                   a_cnt, rows, out, workspace, l);
+  const bool fused = rows && !sa.stop_cut;
+  if (fused) fuse_select(&aa, sa);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(launch_init_for(sa, d.U, s));
   rec.end(SSA_STAGE_INIT);
@@ -532,11 +566,11 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
   SSA_TRY(launch_resolve_for(sa, d.U, s));
   rec.end(SSA_STAGE_RESOLVE);
   rec.begin(SSA_STAGE_SAMPLE);
-  SSA_TRY(ssa::launch_sample(sa, d.U, s));
+  if (!fused) SSA_TRY(ssa::launch_sample(sa, d.U, s));
   if (d.refine > 0) SSA_TRY(ssa::launch_refine(ra, d.U, d.Um, s));
   rec.end(SSA_STAGE_SAMPLE);
   rec.begin(SSA_STAGE_ATTEND);
-  SSA_TRY(ssa::launch_attend(aa, s));
+  SSA_TRY(fused ? ssa::launch_attend_select(aa, s) : ssa::launch_attend(aa, s));
   rec.end(SSA_STAGE_ATTEND);
   rec.begin(SSA_STAGE_MERGE);
   SSA_TRY(ssa::launch_merge(aa, s));

@@ -140,6 +140,23 @@ struct AttendArgs {
   int pair_begin, pair_count; // the scored dims, for split keys
   int64_t seg_ld;
   float scale;
+  // Selection taken by the attention waves (one query per sequence, no early
+  // stop): the selection stage's per-chunk lists and unit states replace
+  // sel_idx / sel_logw / sel_cnt, and the sample kernel is not run.
+  int fused_select;
+  const int32_t* list_idx;    // as in SelectArgs
+  const float* list_w;
+  const int32_t* list_cnt;
+  const int32_t* cand_idx;
+  const uint32_t* cand_key;
+  const float* cand_w;
+  const int32_t* cand_cnt;
+  const int32_t* tiecnt;
+  const int32_t* ties_before;
+  const void* state;          // [U] UnitState
+  const uint64_t* seed;
+  float* sel_scratch;         // [U, seg_ld]: a sampled position's logit bias, for chunks
+                              //   whose lists exceed what the waves hold in registers
 };
 
 // Refine mode of query groups: every member re-ranks the group's candidate
@@ -200,6 +217,8 @@ hipError_t launch_resolve(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_stop(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_sample(const SelectArgs& a, int units, hipStream_t stream);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+// The attention stage taking the sample stage's decisions itself (fused_select).
+hipError_t launch_attend_select(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_refine(const RefineArgs& a, int group_units, int member_units,
                          hipStream_t stream);

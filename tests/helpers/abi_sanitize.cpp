@@ -26,6 +26,7 @@ hipError_t launch_resolve(const SelectArgs&, int, hipStream_t) { ++g_launches; r
 hipError_t launch_stop(const SelectArgs&, int, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_sample(const SelectArgs&, int, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_attend(const AttendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
+hipError_t launch_attend_select(const AttendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_append(const AppendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_merge(const AttendArgs&, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
 hipError_t launch_refine(const RefineArgs&, int, int, hipStream_t) { ++g_launches; return hipErrorInvalidValue; }
