@@ -126,6 +126,8 @@ extern "C" {
                              /* candidates, tail weight sums                        */
 #define SSA_STAGE_RESOLVE 3  /* exact top-k threshold, tie quota, tail normaliser  */
 #define SSA_STAGE_SAMPLE 4   /* deterministic set + Poisson sample, per chunk      */
+                             /* (with one query per sequence and no early stop,   */
+                             /* taken by the attention kernel: no kernel here)    */
 #define SSA_STAGE_ATTEND 5   /* gather attention over the selection, split-K       */
 #define SSA_STAGE_MERGE 6    /* merge of the split partials                        */
 #define SSA_NUM_STAGES 7
@@ -204,10 +206,11 @@ int32_t ssa_num_chunks(const ssa_params* p);
  * num_queries) x Hq / Hkv) at most SSA_STOP_MAX_ROWS; otherwise every entry
  * point returns SSA_ERR_INVALID.  Cost: ordering the stratum and weighing it
  * takes seven short kernels, about 50 us per step for a 1M-token layer of 8
- * kv heads with a 10486-token stratum (measured: 256 us -> 310 us per step
- * at tau = 0.01, which cuts the stratum by 57%), far more than the attention
- * it saves at 50x sparsity (about 2 us); it pays only where attention over
- * the stratum dominates the step.
+ * kv heads with a 10486-token stratum, and the step then runs the sample
+ * stage as its own kernel (measured: 233 us -> 293 us per step at tau =
+ * 0.01, which cuts the stratum by 57%), far more than the attention it saves
+ * at 50x sparsity (about 2 us); it pays only where attention over the stratum
+ * dominates the step.
  *
  * Refine mode ("PIVOT slashes sparse-attention indexer cost", "The two
  * observations behind PIVOT" and "Two operating modes": the proxy's
