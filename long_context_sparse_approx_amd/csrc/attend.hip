@@ -569,11 +569,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
         // blocks side by side) and used where the slot is a tail token.
         const int tt[4] = {cl.lt[0], cl.lt[1], cl.ct[0], cl.ct[1]};
         const float wv[4] = {cl.lwv[0], cl.lwv[1], cl.cwv[0], cl.cwv[1]};
+        // A slot none of whose entries is a tail token skips the test (a
+        // condition uniform over the wave).
+        const bool need[4] = {n_list > n_above, n_list > max(n_above, 64),
+                              sampling && ncand > 0, sampling && ncand > 64};
         bool pass[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           ps[k] = tt[k] - c0;
-          pass[k] = sample_test(st, seed, b, h, tt[k], wv[k], &bs[k]);
+          pass[k] = need[k] ? sample_test(st, seed, b, h, tt[k], wv[k], &bs[k]) : false;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -666,25 +670,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
       if (mode == 1) {
         // Items to ranks, from the owning lane's offsets and words (a sampled
         // item that is also deterministic is dropped, as in the sample
-        // kernel; the lists never make one).
+        // kernel; the lists never make one).  Every lane reads go out before
+        // any rank is formed.
+        int o_ex[4];
+        uint32_t o_d0[4], o_d1[4], o_s0[4], o_s1[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int p = ps[k] & (kChunk - 1);
-          const int src = p >> 6;
-          const int o_ex = __shfl(ex, src);
-          const uint32_t o_d0 = __shfl(d0, src), o_d1 = __shfl(d1, src);
-          const uint32_t o_s0 = __shfl(s0, src), o_s1 = __shfl(s1, src);
-          const int bit = p & 63;
+          const int addr = ((ps[k] & (kChunk - 1)) >> 6) << 2;  // owning lane, in bytes
+          o_ex[k] = __builtin_amdgcn_ds_bpermute(addr, ex);
+          o_d0[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)d0);
+          o_d1[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)d1);
+          o_s0[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)s0);
+          o_s1[k] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)s1);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int bit = ps[k] & 63;
           const uint64_t below = bit == 0 ? 0ull : (~0ull >> (64 - bit));
-          const uint64_t dw = ((uint64_t)o_d1 << 32) | o_d0;
-          const uint64_t sw = ((uint64_t)o_s1 << 32) | o_s0;
-          if (kd[k] == 1) {
-            ps[k] = (o_ex & 0xffff) + __popcll(dw & below);
-            bs[k] = 0.0f;
-          } else if (kd[k] == 2) {
-            if ((dw >> bit) & 1ull) kd[k] = 0;
-            ps[k] = totS + (o_ex >> 16) + __popcll(sw & below);
-          }
+          const uint64_t dw = ((uint64_t)o_d1[k] << 32) | o_d0[k];
+          const uint64_t sw = ((uint64_t)o_s1[k] << 32) | o_s0[k];
+          const int rd = (o_ex[k] & 0xffff) + (int)__popcll(dw & below);
+          const int rs = totS + (o_ex[k] >> 16) + (int)__popcll(sw & below);
+          const bool drop = kd[k] == 2 && ((dw >> bit) & 1ull);
+          ps[k] = kd[k] == 1 ? rd : rs;
+          bs[k] = kd[k] == 1 ? 0.0f : bs[k];
+          kd[k] = drop ? 0 : kd[k];
         }
       }
     }
@@ -707,24 +717,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
     static_assert(2 * kRegList <= kBatch, "the register-held lists fill one batch");
     for (int b0 = i_lo; b0 < i_hi; b0 += kBatch) {
       const int nb = min(kBatch, i_hi - b0);
+      if (mode == 0) {
 #pragma unroll
-      for (int k = 0; k < kBatch / 64; ++k) {
-        const int i = lane + 64 * k;
-        if (mode == 0 && i < nb) {
-          const int p = b0 + i;
-          rows_sh[i] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
-          lw_sh[i] = 0.0f;
-          pos_sh[i] = 0;
-        } else if (i >= nb) {
-          rows_sh[i] = -1;
-          lw_sh[i] = -INFINITY;
-          pos_sh[i] = 0;
+        for (int k = 0; k < kBatch / 64; ++k) {
+          const int i = lane + 64 * k;
+          if (i < nb) {
+            const int p = b0 + i;
+            rows_sh[i] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
+            lw_sh[i] = 0.0f;
+            pos_sh[i] = 0;
+          }
         }
       }
+      // Padding: a tile reads at most 31 entries past the batch's last item.
       if (lane < 32) {
-        rows_sh[kBatch + lane] = -1;
-        lw_sh[kBatch + lane] = -INFINITY;
-        pos_sh[kBatch + lane] = 0;
+        rows_sh[nb + lane] = -1;
+        lw_sh[nb + lane] = -INFINITY;
+        pos_sh[nb + lane] = 0;
       }
       if (mode == 2) {
         // Lane l's positions 64 l .. 64 l + 63, deterministic then sampled.
