@@ -126,8 +126,8 @@ extern "C" {
                              /* candidates, tail weight sums                        */
 #define SSA_STAGE_RESOLVE 3  /* exact top-k threshold, tie quota, tail normaliser  */
 #define SSA_STAGE_SAMPLE 4   /* deterministic set + Poisson sample, per chunk      */
-                             /* (with one query per sequence and no early stop,   */
-                             /* taken by the attention kernel: no kernel here)    */
+                             /* (without early stopping or refine, taken by the    */
+                             /* attention kernel: no kernel here)                 */
 #define SSA_STAGE_ATTEND 5   /* gather attention over the selection, split-K       */
 #define SSA_STAGE_MERGE 6    /* merge of the split partials                        */
 #define SSA_NUM_STAGES 7

@@ -360,9 +360,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 }
 
 // ------------------------------------------------------------------ fused
-// The decode step with one query per sequence takes the sample stage's
-// decisions in the attention wave, per chunk, instead of reading a written
-// selection ("Stratified Sparse Attention speeds up decoding 2.96x at 1M
+// The decode step (without early stopping or refine) takes the sample
+// stage's decisions in the attention wave, per chunk, instead of reading a
+// written selection ("Stratified Sparse Attention speeds up decoding 2.96x at 1M
 // context", "How SSA stratifies the cache": the deterministic stratum and
 // the Poisson-sampled tail with inclusion probability min(1, m w / W)).  The
 // decisions and their order are the sample kernel's: tokens above the
@@ -428,8 +428,8 @@ __device__ __forceinline__ ChunkLists load_chunk_lists(const AttendArgs& a, size
 // The sample stage's inclusion test of tail token t with weight w; *bias
 // gets -log(pi) when it passes.
 __device__ __forceinline__ bool fused_sample(const UnitState& st, uint64_t seed, int b, int h,
-                                             int t, float w, float* bias) {
-  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, 0);
+                                             int grp, int t, float w, float* bias) {
+  const uint4 wd = philox_block(seed, b, h, (uint32_t)t >> 2, grp);
   const uint32_t words[4] = {wd.x, wd.y, wd.z, wd.w};
   const float mw = (float)st.m * w;
   if (uniform24(words[t & 3]) * st.W < mw) {
@@ -442,8 +442,8 @@ __device__ __forceinline__ bool fused_sample(const UnitState& st, uint64_t seed,
 // The same test without a branch, for slots computed side by side: *bias is
 // written whatever the outcome (used only where the test passes).
 __device__ __forceinline__ bool sample_test(const UnitState& st, uint64_t seed, int b, int h,
-                                            int t, float w, float* bias) {
-  const uint4 wd = philox_block_uniform_key(seed, b, h, (uint32_t)t >> 2, 0);
+                                            int grp, int t, float w, float* bias) {
+  const uint4 wd = philox_block_uniform_key(seed, b, h, (uint32_t)t >> 2, grp);
   const uint32_t word = (t & 2) ? ((t & 1) ? wd.w : wd.z) : ((t & 1) ? wd.y : wd.x);
   const float mw = (float)st.m * w;
   *bias = -logf(fminf(1.0f, mw / st.W));
@@ -454,7 +454,10 @@ __device__ __forceinline__ void mark(uint32_t* map, int p) {
   atomicOr(&map[p >> 5], 1u << (p & 31));
 }
 
-template <int D, bool SPLIT>
+// MULTI: several query positions per sequence (member blocks on grid z, each
+// column its own causal span, entries placed with their positions); without
+// it, one query per sequence (grid y = unit = b * Hkv + h, rows only).
+template <int D, bool SPLIT, bool MULTI>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void attend_select_kernel(
     AttendArgs a) {
   constexpr int KK = D / 32;
@@ -468,9 +471,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   const int s = slot / a.nsub;
   const int sub = slot - s * a.nsub;
   const int nslot = a.nsplit * a.nsub;
-  const int u = blockIdx.y;  // one query per sequence: unit u = b * Hkv + h
-  const int b = u / a.Hkv;
-  const int h = u - b * a.Hkv;
+  const int u = blockIdx.y;
+  const int bg = u / a.Hkv;
+  const int h = u - bg * a.Hkv;
+  int b = bg, grp = 0, t_a = 0, nmem = 1;
+  if (MULTI) {
+    b = bg / a.NG;
+    grp = bg - b * a.NG;
+    t_a = grp * a.g + (int)blockIdx.z * a.mpw;  // first member of this block
+    nmem = min(min(a.mpw, (grp + 1) * a.g - t_a), a.T - t_a);
+    if (nmem <= 0) return;  // uniform over the wave
+  }
   const int lane = threadIdx.x;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
@@ -484,15 +495,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   const ChunkLists pf = load_chunk_lists(a, seg, (size_t)u * a.nchunk + c_guess, c_guess, b, lane);
   const UnitState st = reinterpret_cast<const UnitState*>(a.state)[u];
   const uint64_t seed = a.seed[b];
-  const bool col_valid = n16 < a.G;
-  const int col_g = col_valid ? n16 : 0;
+  // Column n16 = (member t_a + n16 / G, head n16 % G).
+  const bool col_valid = n16 < nmem * a.G;
+  const int col_t = MULTI ? t_a + (col_valid ? n16 / a.G : 0) : 0;
+  const int col_g = col_valid ? (MULTI ? n16 - (n16 / a.G) * a.G : n16) : 0;
   bf16x8 qf[KK];
   {
-    // Loaded for every column, with no branch: a column past the group reads
-    // head 0's row, and its span is empty (L_col = 0), so its logits are -inf,
-    // its probabilities 0 and its state is never written; an MFMA output
-    // column depends on its own query column only.
-    const uint16_t* qrow = a.q + ((size_t)b * a.Hq + h * a.G + col_g) * D;
+    // Loaded for every column, with no branch: a column past the block reads
+    // its first member's head 0, and its span is empty (L_col = 0), so its
+    // logits are -inf, its probabilities 0 and its state is never written; an
+    // MFMA output column depends on its own query column only.
+    const uint16_t* qrow = a.q + ((size_t)(b * a.T + col_t) * a.Hq + h * a.G + col_g) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qrow + kk * 32 + q4 * 8));
@@ -502,8 +515,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
   // into the branch that uses them.
   __builtin_amdgcn_sched_barrier(0);
   const int P = clamp_len(a.seq_lens[b], a.max_seq_len);
-  const int L_col = col_valid ? P : 0;
-  const int ncL = (P + kChunk - 1) / kChunk;
+  const int L_col = col_valid ? (MULTI ? member_span(P, a.T, col_t) : P) : 0;
+  const int L = MULTI ? member_span(P, a.T, t_a + nmem - 1) : P;  // the block's widest span
+  const int ncL = (L + kChunk - 1) / kChunk;
   const int c_begin = (int)((uint32_t)s * (uint32_t)ncL / (uint32_t)a.nsplit);
   const int c_end = (int)((uint32_t)(s + 1) * (uint32_t)ncL / (uint32_t)a.nsplit);
 
@@ -554,6 +568,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
     const int mode = dense ? 0 : (n_list <= kRegList && ncand <= kRegList ? 1 : 2);
     int kd[4] = {0, 0, 0, 0};  // 0 none, 1 deterministic, 2 sampled
     int ps[4] = {0, 0, 0, 0};  // position in the chunk, then rank
+    int pp[4] = {0, 0, 0, 0};  // position in the chunk
     int rw[4] = {0, 0, 0, 0};  // cache row
     float bs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     int totS = nvalid, totR = 0, ex = 0;
@@ -577,7 +592,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           ps[k] = tt[k] - c0;
-          pass[k] = need[k] ? sample_test(st, seed, b, h, tt[k], wv[k], &bs[k]) : false;
+          pass[k] = need[k] ? sample_test(st, seed, b, h, grp, tt[k], wv[k], &bs[k]) : false;
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -609,6 +624,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
+          pp[k] = ps[k];
           if (kd[k] != 0) mark(ssh.map[kd[k] - 1], ps[k]);
           // The cache row, read before the ranks are known.
           rw[k] = (ssh.blk[(ps[k] >> 4) & (kChunkBlocks - 1)] * a.Hkv + h) * kBlockTokens +
@@ -625,7 +641,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
           float bias;
           if (i < n_above)
             mark(ssh.map[0], p);
-          else if (fused_sample(st, seed, b, h, t, lw[i], &bias)) {
+          else if (fused_sample(st, seed, b, h, grp, t, lw[i], &bias)) {
             scr[p] = bias;
             mark(ssh.map[1], p);
           }
@@ -648,7 +664,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
             float bias;
             if (key > st.tkey || (tie && rank < st.ties_needed))
               mark(ssh.map[0], p);
-            else if (sampling && fused_sample(st, seed, b, h, t, cw[i], &bias)) {
+            else if (sampling && fused_sample(st, seed, b, h, grp, t, cw[i], &bias)) {
               scr[p] = bias;
               mark(ssh.map[1], p);
             }
@@ -698,6 +714,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
         }
       }
     }
+    // An entry at or past the block's widest span takes its slot with no row
+    // (the staged attention drops it the same way); the others carry their
+    // position for the members' span masks.
+    auto place = [&](int j, int p, int row, float lw) {
+      if (MULTI) {
+        const int pos = c0 + p;
+        const bool in = pos < L;
+        rows_sh[j] = in ? row : -1;
+        lw_sh[j] = in ? lw : -INFINITY;
+        pos_sh[j] = in ? pos : 0;
+      } else {  // every entry lies inside the one query's span
+        rows_sh[j] = row;
+        lw_sh[j] = lw;
+        pos_sh[j] = 0;
+      }
+    };
     const int cnt = totS + totR;
     const int i_lo = (int)((uint32_t)sub * (uint32_t)cnt / (uint32_t)a.nsub);
     const int i_hi = (int)((uint32_t)(sub + 1) * (uint32_t)cnt / (uint32_t)a.nsub);
@@ -707,11 +739,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int j = ps[k] - i_lo;
-        if (kd[k] != 0 && (unsigned)j < (unsigned)(i_hi - i_lo)) {
-          rows_sh[j] = rw[k];
-          lw_sh[j] = bs[k];
-          pos_sh[j] = 0;
-        }
+        if (kd[k] != 0 && (unsigned)j < (unsigned)(i_hi - i_lo)) place(j, pp[k], rw[k], bs[k]);
       }
     }
     static_assert(2 * kRegList <= kBatch, "the register-held lists fill one batch");
@@ -723,9 +751,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
           const int i = lane + 64 * k;
           if (i < nb) {
             const int p = b0 + i;
-            rows_sh[i] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
-            lw_sh[i] = 0.0f;
-            pos_sh[i] = 0;
+            place(i, p, (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15), 0.0f);
           }
         }
       }
@@ -749,9 +775,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
               const int j = r - b0;
               if ((unsigned)j >= (unsigned)nb) continue;
               const int p = 64 * lane + 32 * wj + __builtin_ctz(bits);
-              rows_sh[j] = (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15);
-              lw_sh[j] = cls == 0 ? 0.0f : scr[p];
-              pos_sh[j] = 0;
+              place(j, p, (ssh.blk[p >> 4] * a.Hkv + h) * kBlockTokens + (p & 15),
+                    cls == 0 ? 0.0f : scr[p]);
             }
           }
         }
@@ -778,15 +803,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void at
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int col = 4 * q4 + r;
-    if (col < a.G) {
-      const int qrow = b * a.Hq + h * a.G + col;
+    if (col < nmem * a.G) {
+      const int qrow = (b * a.T + t_a + col / a.G) * a.Hq + h * a.G + col % a.G;
       float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + n16 * DPL;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) dst[j] = acc[j][r];
     }
   }
   if (q4 == 0 && col_valid) {
-    const int qrow = b * a.Hq + h * a.G + col_g;
+    const int qrow = (b * a.T + col_t) * a.Hq + h * a.G + col_g;
     float* dst = a.part + ((size_t)qrow * nslot + slot) * stride + D;
     dst[0] = m_run;
     dst[1] = l_run;
@@ -900,19 +925,22 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attend_select(const AttendArgs& a, hipStream_t stream) {
-  if (!a.fused_select || a.T != 1 || a.mblocks != 1) return hipErrorInvalidValue;
-  dim3 grid(a.nsplit * a.nsub, a.B * a.Hkv);
+  if (!a.fused_select) return hipErrorInvalidValue;
+  dim3 grid(a.nsplit * a.nsub, a.B * a.NG * a.Hkv, a.mblocks);
   const bool split = a.k_rest != nullptr;
+  const bool multi = a.T > 1;
+#define SSA_SEL(d, s, m) attend_select_kernel<d, s, m><<<grid, 64, 0, stream>>>(a)
   if (a.d == 128 && !split)
-    attend_select_kernel<128, false><<<grid, 64, 0, stream>>>(a);
+    multi ? SSA_SEL(128, false, true) : SSA_SEL(128, false, false);
   else if (a.d == 128)
-    attend_select_kernel<128, true><<<grid, 64, 0, stream>>>(a);
+    multi ? SSA_SEL(128, true, true) : SSA_SEL(128, true, false);
   else if (a.d == 64 && !split)
-    attend_select_kernel<64, false><<<grid, 64, 0, stream>>>(a);
+    multi ? SSA_SEL(64, false, true) : SSA_SEL(64, false, false);
   else if (a.d == 64)
-    attend_select_kernel<64, true><<<grid, 64, 0, stream>>>(a);
+    multi ? SSA_SEL(64, true, true) : SSA_SEL(64, true, false);
   else
     return hipErrorInvalidValue;
+#undef SSA_SEL
   return hipGetLastError();
 }
 

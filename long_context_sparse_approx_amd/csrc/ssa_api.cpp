@@ -439,7 +439,7 @@ ssa::AttendArgs attend_args(const ssa_params* p, const Dims& d, const void* q, K
 }
 
 // The attention stage takes the sample stage's decisions from the selection
-// stage's lists (one query per sequence, no early stop); the position-indexed
+// stage's lists (no early stop, no refine); the position-indexed
 // scratch row is the selection's bias array, which nothing else reads then.
 void fuse_select(ssa::AttendArgs* a, const ssa::SelectArgs& s) {
   a->fused_select = 1;
@@ -551,7 +551,7 @@ int decode_impl(const ssa_params* p, const void* q, Keys keys, const void* v_cac
   }
   ssa::AttendArgs aa = attend_args(p, d, q, keys, v_cache, block_table, seq_lens, a_idx, a_logw,
                                    a_cnt, rows, out, workspace, l);
-  const bool fused = rows && !sa.stop_cut;
+  const bool fused = d.refine == 0 && !sa.stop_cut;
   if (fused) fuse_select(&aa, sa);
   rec.begin(SSA_STAGE_INIT);
   SSA_TRY(launch_init_for(sa, d.U, s));

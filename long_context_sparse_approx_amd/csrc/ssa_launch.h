@@ -140,8 +140,8 @@ struct AttendArgs {
   int pair_begin, pair_count; // the scored dims, for split keys
   int64_t seg_ld;
   float scale;
-  // Selection taken by the attention waves (one query per sequence, no early
-  // stop): the selection stage's per-chunk lists and unit states replace
+  // Selection taken by the attention waves (no early stop, no refine): the
+  // selection stage's per-chunk lists and unit states replace
   // sel_idx / sel_logw / sel_cnt, and the sample kernel is not run.
   int fused_select;
   const int32_t* list_idx;    // as in SelectArgs

@@ -45,9 +45,9 @@ def staged(wl, p, ws, top_p=None):
     return out, sn
 
 
-def check_equal(wl, label, top_p=None):
+def check_equal(wl, label, top_p=None, **kw):
     p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
-                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count, **kw)
     ws = ssa.alloc_workspace(p, DEV)
     fused = ssa.decode(p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
                        wl.sample_budget, wl.seed, workspace=ws, top_p=top_p).clone()
@@ -132,3 +132,38 @@ def test_split_keys_fused_equals_staged():
     torch.cuda.synchronize()
     say(f"[fused] split keys: max |diff| {float((out.double() - ref.double()).abs().max()):.3g}")
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_splits_spanning_several_chunks(splits):
+    """A split that spans several chunks takes each chunk's decisions in turn
+    (only the first can use the lists read with the query)."""
+    wl = synth.make_workload(cfg(B=3, L=[40000, 17000, 4097], topk=[400, 2500, 60],
+                                 m=[400, 1500, 40], seeds=[19, 20, 21]), DEV)
+    check_equal(wl, f"{splits} splits", num_splits=splits)
+
+
+def test_batched_mixed_lengths():
+    """Sequences of log-uniform lengths (8K-128K), the 50x budget rule: the
+    split whose guessed first chunk is past a short sequence's range."""
+    wl = synth.make_workload("batched", DEV, B=6)
+    check_equal(wl, "batched")
+
+
+@pytest.mark.parametrize("T,g,L,topk,m", [
+    (4, 4, [9000], 60, 40),          # one group of four queries
+    (5, 2, [6000, 4100], 50, 30),    # a ragged last group
+    (3, 1, [5000], 40, 20),          # one selection per query
+    (4, 2, [700], 600, 200),         # dense units
+    (5, 2, [3, 4099], 20, 10),       # caches shorter than the step
+    (3, 8, [8200], 30, 30),          # a group wider than the step
+    (4, 4, [20000], 3000, 2000),     # crowded chunks, lists read in rounds
+])
+def test_query_groups(T, g, L, topk, m):
+    """Several query positions per step, groups of g sharing one selection
+    (PIVOT reuse): the decisions are the group's, placed with their positions
+    so that every member keeps its own causal span."""
+    B = len(L)
+    wl = synth.make_workload(cfg(B=B, L=L, topk=topk, m=m, seeds=list(range(30, 30 + B))),
+                             DEV, num_queries=T)
+    check_equal(wl, f"T={T} g={g}", query_group=g)
