@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void f
   __shared__ float sh[kChunk];
   __shared__ int scan_scr[kNT / 64];
   __shared__ double dscr[kNT / 64];
+  __shared__ uint32_t stage[kNT / 64][kStage];  // each wave's second-pass entries
 
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(8))) void f
 #pragma unroll
     for (int g = 0; g < kPer / 4; ++g) s4[g] = *reinterpret_cast<const float4*>(sh + tb + 4 * g);
   }
-  filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, s4, sh, scan_scr, dscr);
+  filter_chunk(a, p, t1, M, u, b, h, ui.grp, c, s4, sh, scan_scr, dscr, stage[threadIdx.x >> 6]);
 }
 
 // ------------------------------------------------------------------ resolve

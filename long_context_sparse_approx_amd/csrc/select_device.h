@@ -8,6 +8,7 @@ namespace ssa {
 
 constexpr int kNT = 256;             // threads per chunk workgroup
 constexpr int kPer = kChunk / kNT;   // 16 consecutive tokens per thread
+constexpr int kStage = 128;          // second-pass entries a wave stages in LDS
 
 // The chunk filter's tail weight e^x (x <= 0): the hardware exp2 of
 // t = x log2(e), with t carried past float32 precision (the product's rounding
@@ -190,7 +191,8 @@ __device__ __forceinline__ FirstPass filter_first_pass(const float4 (&s4)[kPer /
 __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParams& p,
                                              const Thresh1& t1, float M, int u, int b, int h,
                                              int grp, int c, const float4 (&s4)[kPer / 4],
-                                             float* sh, int* scan_scr, double* dscr) {
+                                             float* sh, int* scan_scr, double* dscr,
+                                             uint32_t* stage) {
   const int c0 = c * kChunk;
   const int b1 = t1.b1;  // 2048 when there is no deterministic set
   // With top-p the stratum size is not known yet: list sampling candidates
@@ -229,31 +231,68 @@ __device__ __forceinline__ void filter_chunk(const SelectArgs& a, const SeqParam
   float* cw = a.cand_w + (size_t)u * a.seg_ld + c0;
   int32_t* lidx = a.list_idx + (size_t)u * a.seg_ld + c0;
   float* lw = a.list_w + (size_t)u * a.seg_ld + c0;
-  int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
-  // The classes are disjoint; ascending bits keep every list in index order.
-  for (uint32_t rest = candmask | abovemask | sampmask; rest != 0u; rest &= rest - 1u) {
-    const int i = __builtin_ctz(rest);
-    const uint32_t bit = 1u << i;
-    const int t = c0 + tb + i;
-    const float s = sh[tb + i];
-    if (candmask & bit) {
+  // One entry: its token (offset ti in the chunk), class (0 candidate, 1 above
+  // the threshold digit, 2 listed tail token) and slot in its list.
+  auto emit = [&](int ti, int cls, int out) {
+    const int t = c0 + ti;
+    const float s = sh[ti];
+    if (cls == 0) {
       const uint32_t key = order_key(s);
       const float w = sexp(s - M);
-      cidx[wc] = t;
-      ckey[wc] = key;
-      cw[wc] = w;
-      ++wc;
+      cidx[out] = t;
+      ckey[out] = key;
+      cw[out] = w;
       const int d2 = (key >> kDigit2Shift) & (kBins - 1);
       atomicAdd(&a.hist2[(size_t)u * kBins + d2], 1u);
       if (mass) atomicAdd(&a.hist2m[(size_t)u * kBins + d2], mass_units(w));
-    } else if (abovemask & bit) {
-      lidx[wa++] = t;
+    } else if (cls == 1) {
+      lidx[out] = t;
     } else {
-      lidx[ws] = t;
-      lw[ws] = sexp(s - M);
-      ++ws;
+      lidx[out] = t;
+      lw[out] = sexp(s - M);
+    }
+  };
+  // The classes are disjoint; ascending bits keep every list in index order.
+  // The wave's entries are staged (token, class and slot packed in a word) so
+  // that each lane then emits one of them: one round for the usual few dozen,
+  // instead of as many rounds as the busiest lane has entries.
+  const uint32_t rest0 = candmask | abovemask | sampmask;
+  const int nmine = __popc(rest0);
+  const int incl = wave_inclusive_scan<int>(nmine);
+  const int q_total = __builtin_amdgcn_readlane(incl, 63);
+  int wc = off, wa = lst & 0xffff, ws = n_above + (lst >> 16);
+  // Class and slot of the entry at bit i, counted in each class's list.
+#define SSA_NEXT_SLOT(i, cls, out)                             \
+  const uint32_t bit_ = 1u << (i);                             \
+  const bool isc_ = (candmask & bit_) != 0u;                   \
+  const bool isa_ = !isc_ && (abovemask & bit_) != 0u;         \
+  const int cls = isc_ ? 0 : (isa_ ? 1 : 2);                   \
+  const int out = isc_ ? wc : (isa_ ? wa : ws);                \
+  wc += isc_ ? 1 : 0;                                          \
+  wa += isa_ ? 1 : 0;                                          \
+  ws += (!isc_ && !isa_) ? 1 : 0
+  if (q_total <= kStage) {  // uniform over the wave
+    int k = incl - nmine;
+    for (uint32_t r = rest0; r != 0u; r &= r - 1u) {
+      const int i = __builtin_ctz(r);
+      SSA_NEXT_SLOT(i, cls, out);
+      stage[k++] = (uint32_t)(tb + i) | ((uint32_t)cls << 12) | ((uint32_t)out << 14);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = (int)(threadIdx.x & 63); j < q_total; j += 64) {
+      const uint32_t e = stage[j];
+      emit((int)(e & 4095u), (int)((e >> 12) & 3u), (int)(e >> 14));
+    }
+  } else {
+    for (uint32_t r = rest0; r != 0u; r &= r - 1u) {
+      const int i = __builtin_ctz(r);
+      SSA_NEXT_SLOT(i, cls, out);
+      emit(tb + i, cls, out);
     }
   }
+#undef SSA_NEXT_SLOT
   const double wtot = block_sum_f64<kNT>(wsum, dscr);
   if (threadIdx.x == 0) {
     const size_t ci = (size_t)u * a.nchunk + c;
