@@ -44,6 +44,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Streaming 16-byte load that does not keep the line in the caches (the key
 // slices are read once per step).
+// Raw (untyped) buffer resources: the fourth descriptor word for 32-bit
+// data on this family, and the cache-policy bits of a buffer access (sc0 = 1,
+// nt = 2, sc1 = 16).
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kPolicySystem = 1 | 16;
+
 __device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
@@ -293,15 +299,23 @@ __device__ __forceinline__ void index_tile(const IndexArgs& a, int u, int t0, in
     const uint32_t c = (hist[i >> 1] >> (16 * (i & 1))) & 0xffffu;
     if (c) atomicAdd(&a.hist1[(size_t)u * kBins + i], c);
   }
-  // The tile's scores, written in one burst (16-byte stores when aligned).
+  // The tile's scores, written in one burst (16-byte stores when aligned)
+  // with the system-scope cache policy (sc0 sc1): written through instead of
+  // left dirty in L2 for the key stream to evict piecemeal, which costs the
+  // stream less HBM time (1M layer: 173 -> 169 us).  The buffer resource
+  // spans the unit's score row, so every store is range-checked against it.
   const int n = t_end - t0;
   float* dst = srow + t0;
   if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+    const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(
+        srow, (short)0, (int)(uint32_t)(a.score_ld * (int64_t)sizeof(float)), kRawBufferWord3);
     for (int i = 4 * tid; i < n; i += 4 * 256) {
-      if (i + 4 <= n)
-        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(sbuf + i);
-      else
+      if (i + 4 <= n) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sbuf + i);
+        __builtin_amdgcn_raw_buffer_store_b128(v, row, (uint32_t)(t0 + i) * 4u, 0, kPolicySystem);
+      } else {
         for (int j = i; j < n; ++j) dst[j] = sbuf[j];
+      }
     }
   } else {
     for (int i = tid; i < n; i += 256) dst[i] = sbuf[i];
