@@ -207,7 +207,7 @@ int32_t ssa_num_chunks(const ssa_params* p);
  * point returns SSA_ERR_INVALID.  Cost: ordering the stratum and weighing it
  * takes seven short kernels, about 50 us per step for a 1M-token layer of 8
  * kv heads with a 10486-token stratum, and the step then runs the sample
- * stage as its own kernel (measured: 233 us -> 293 us per step at tau =
+ * stage as its own kernel (measured: 230 us -> 292 us per step at tau =
  * 0.01, which cuts the stratum by 57%), far more than the attention it saves
  * at 50x sparsity (about 2 us); it pays only where attention over the stratum
  * dominates the step.
