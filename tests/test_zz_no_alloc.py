@@ -64,3 +64,35 @@ def test_static_workspace_limit_refused():
     assert e.value.code == ssa.SSA_ERR_STATIC_LIMIT
     torch.cuda.synchronize()
     assert float(out.abs().max()) == 0.0  # nothing was launched
+
+
+def test_static_workspace_decode_replays_from_a_hip_graph():
+    """The callers the entry point is for include code under graph capture: a
+    captured ssa_decode_static replays bitwise equal to the eager ssa_decode,
+    with eager work on the device between the replays."""
+    wl = synth.make_workload(dict(SMALL), DEV)
+    p = ssa.params_for(wl.q, wl.k_cache, wl.block_table, wl.max_seq_len,
+                       pair_begin=wl.pair_begin, pair_count=wl.pair_count)
+    args = (p, wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.topk,
+            wl.sample_budget, wl.seed)
+    say("[no-alloc] graph capture of ssa_decode_static")
+    ref = ssa.decode(*args).clone()
+    out = torch.zeros_like(ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # an eager call first, on a side stream, as capture wants
+        ssa.decode_static(*args, out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssa.decode_static(*args, out=out, stream=torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs"
+        del junk
+    say("[no-alloc] three replays bitwise equal to ssa_decode")
